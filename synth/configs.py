@@ -1,0 +1,103 @@
+"""Named workload configurations (shapes and policy constants only)."""
+from dataclasses import dataclass, field, replace
+from typing import Optional, Tuple
+
+
+@dataclass(frozen=True)
+class Policy:
+    """CONF-KV hyper-parameters.
+
+    tau, N_high (tight budget when confident), N_low (loose budget), P
+    (protected newest tokens), alpha (rank mix), W (FP16 window), lambda (EMA
+    decay) and the confidence weights (w_H, w_m, w_p) = (0.4, 0.3, 0.3).
+    """
+    tau: float = 0.7
+    alpha: float = 0.65
+    lam: float = 0.9
+    w_h: float = 0.4
+    w_m: float = 0.3
+    w_p: float = 0.3
+    n_high: int = 256
+    n_low: int = 512
+    protect: int = 32
+    window: int = 64
+
+
+@dataclass(frozen=True)
+class Config:
+    name: str
+    layers: int
+    batch: int
+    hq: int
+    hkv: int
+    d: int
+    vocab: int
+    prefill: int          # tokens in the cache before the first decode step
+    steps: int            # decode steps of the full workload
+    policy: Policy
+    logit_scales: Tuple[float, ...] = (0.5, 2.0, 8.0)
+    sinks: int = 0        # number of high-norm keys placed among the first 16 positions
+    sink_gain: float = 4.0
+    # per-layer budgets (CONF-KV-L); None means uniform budgets
+    layer_n_low: Optional[Tuple[int, ...]] = None
+    layer_n_high: Optional[Tuple[int, ...]] = None
+
+    @property
+    def cap(self) -> int:
+        """Token capacity per (layer, sequence): the largest cache before a step, plus one."""
+        n_low = max(self.layer_n_low) if self.layer_n_low else self.policy.n_low
+        return max(self.prefill, n_low) + 1
+
+    @property
+    def group(self) -> int:
+        return self.hq // self.hkv
+
+    def with_(self, **kw) -> "Config":
+        return replace(self, **kw)
+
+
+def _pyramid(layers: int, top: int, bottom: int):
+    # budgets fall linearly with depth from `top` (layer 0) to `bottom` (last layer)
+    lo = []
+    for l in range(layers):
+        num = top * (layers - 1) - (top - bottom) * l
+        q, r = divmod(num, layers - 1)
+        lo.append(q + (1 if 2 * r >= layers - 1 else 0))
+    hi = [x // 2 for x in lo]
+    return tuple(lo), tuple(hi)
+
+
+_PYR_LO, _PYR_HI = _pyramid(64, 4096, 1024)
+
+CONFIGS = {
+    # Single decode layer, GPT-2-small shape, 1024 cached tokens (newest 64 FP16)
+    "gpt2_layer": Config(
+        name="gpt2_layer", layers=1, batch=1, hq=12, hkv=12, d=64, vocab=50257,
+        prefill=1024, steps=64,
+        policy=Policy(n_high=256, n_low=512, protect=32, window=64)),
+    # GPT-2-small full stack from an empty cache
+    "gpt2_stack": Config(
+        name="gpt2_stack", layers=12, batch=1, hq=12, hkv=12, d=64, vocab=50257,
+        prefill=0, steps=2048,
+        policy=Policy(n_high=256, n_low=512, protect=64, window=128), sinks=4),
+    # Qwen-14B shape, GQA 5:1
+    "qwen14b": Config(
+        name="qwen14b", layers=48, batch=8, hq=40, hkv=8, d=128, vocab=152064,
+        prefill=8192, steps=1024,
+        policy=Policy(n_high=2048, n_low=4096, protect=64, window=256)),
+    # Qwen-32B shape, GQA 5:1, batch 8 (the throughput workload)
+    "qwen32b": Config(
+        name="qwen32b", layers=64, batch=8, hq=40, hkv=8, d=128, vocab=152064,
+        prefill=2048, steps=4096,
+        policy=Policy(n_high=1024, n_low=2048, protect=64, window=256)),
+    # Long-context pyramid (CONF-KV-L), Qwen-32B layer shape, batch 1
+    "qwen32b_pyramid": Config(
+        name="qwen32b_pyramid", layers=64, batch=1, hq=40, hkv=8, d=128, vocab=152064,
+        prefill=32768, steps=512,
+        policy=Policy(n_high=_PYR_HI[0], n_low=_PYR_LO[0], protect=64, window=256),
+        layer_n_low=_PYR_LO, layer_n_high=_PYR_HI),
+}
+
+
+def get_config(name: str) -> Config:
+    return CONFIGS[name]

@@ -1,0 +1,61 @@
+"""Seeded generators. Each draw is keyed by (seed, purpose, step) so that any
+single step can be regenerated without replaying the others."""
+import numpy as np
+
+_PURPOSE = {"prefill": 1, "logits": 2, "decode": 3, "scale": 4, "sink": 5}
+
+
+def step_rng(seed: int, purpose: str, step: int = 0, extra: int = 0) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64([seed, _PURPOSE[purpose], step, extra]))
+
+
+def logit_scale(cfg, seed: int, step: int) -> np.ndarray:
+    """Per-sequence standard deviation of this step's logits, drawn from cfg.logit_scales."""
+    r = step_rng(seed, "scale", step)
+    return np.asarray(cfg.logit_scales, dtype=np.float64)[r.integers(0, len(cfg.logit_scales), size=cfg.batch)]
+
+
+def logits_for_step(cfg, seed: int, step: int) -> np.ndarray:
+    """fp32 [B, V] logits, N(0, s_b) with s_b drawn per (step, sequence)."""
+    s = logit_scale(cfg, seed, step)
+    r = step_rng(seed, "logits", step)
+    z = r.standard_normal((cfg.batch, cfg.vocab), dtype=np.float32)
+    return (z * s[:, None].astype(np.float32)).astype(np.float32)
+
+
+def decode_inputs(cfg, seed: int, step: int):
+    """q fp16 [L,B,Hq,d], k_new/v_new fp16 [L,B,Hkv,d] for one decode step (N(0,1))."""
+    r = step_rng(seed, "decode", step)
+    L, B = cfg.layers, cfg.batch
+    q = r.standard_normal((L, B, cfg.hq, cfg.d), dtype=np.float32).astype(np.float16)
+    k = r.standard_normal((L, B, cfg.hkv, cfg.d), dtype=np.float32).astype(np.float16)
+    v = r.standard_normal((L, B, cfg.hkv, cfg.d), dtype=np.float32).astype(np.float16)
+    return q, k, v
+
+
+def sink_positions(cfg, seed: int):
+    """Positions (among the first 16) whose keys are scaled by cfg.sink_gain."""
+    if cfg.sinks == 0:
+        return np.zeros(0, dtype=np.int64)
+    r = step_rng(seed, "sink")
+    return np.sort(r.choice(16, size=cfg.sinks, replace=False)).astype(np.int64)
+
+
+def apply_sinks(cfg, seed: int, step: int, k_new: np.ndarray) -> np.ndarray:
+    """High-norm keys at the seeded sink positions (used by the empty-cache stack)."""
+    if step in set(sink_positions(cfg, seed).tolist()):
+        k_new = (k_new.astype(np.float32) * cfg.sink_gain).astype(np.float16)
+    return k_new
+
+
+def prefill_kv(cfg, seed: int, layer0: int = 0, nlayers: int = None):
+    """Prefill K/V, fp16 [nl,B,Hkv,L0,d] (N(0,1))."""
+    nl = cfg.layers - layer0 if nlayers is None else nlayers
+    shape = (nl, cfg.batch, cfg.hkv, cfg.prefill, cfg.d)
+    out_k = np.empty(shape, dtype=np.float16)
+    out_v = np.empty(shape, dtype=np.float16)
+    for i in range(nl):
+        r = step_rng(seed, "prefill", 0, layer0 + i)
+        out_k[i] = r.standard_normal(shape[1:], dtype=np.float32).astype(np.float16)
+        out_v[i] = r.standard_normal(shape[1:], dtype=np.float32).astype(np.float16)
+    return out_k, out_v
