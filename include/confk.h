@@ -1,0 +1,244 @@
+/*
+ * confk.h -- C ABI of libconfk, the CONF-KV decode-step library for AMD
+ * MI355X (gfx950).
+ *
+ * CONF-KV ("CONF-KV: Confidence-Aware KV Cache Eviction with Mixed-Precision
+ * Storage for Long-Horizon LLM"; gist.science technical summary, section
+ * "Methodik: CONF-KV"; paper.rainbus.top review, sections "核心方法" and
+ * "方法步骤详情" (Algorithm 1)) turns each decode step's logits into a
+ * confidence score, picks a tight or loose KV budget from it, attends over a
+ * densely packed cache whose newest W tokens are FP16 and older tokens INT8
+ * per (head, channel), tracks an EMA of each token's attention mass, and
+ * evicts the lowest-ranked tokens outside a protected recent window.
+ *
+ * One decode step at position t is, in this order (each call enqueues work
+ * on `stream` and returns without waiting):
+ *   confk_confidence   logits -> c[B], budget[.][B]            (steps 3-4)
+ *   confk_attn_decode  q, cache, new k/v -> o, per-key mass    (steps 1-2)
+ *   confk_ema_rank     mass -> EMA update, new-token metadata, rank scores
+ *   confk_compact      scores, budget -> evict, compact, append new token
+ *   confk_quantize     FP16 token that left the window -> INT8   (step 10)
+ *
+ * Conventions for every entry point:
+ *  - Pointers named in a confk_cache and every tensor argument are DEVICE
+ *    pointers owned by the caller, which keeps them alive until the stream
+ *    work finishes. confk_policy and confk_cache structs are HOST memory,
+ *    read during the call only. The library allocates nothing and keeps no
+ *    state between calls.
+ *  - fp16 tensors are passed as uint16_t holding IEEE binary16 bits.
+ *  - `stream` is a hipStream_t (NULL = default stream).
+ *  - Return value: CONFK_OK (0) or a negative CONFK_ERR_* code. Arguments are
+ *    validated before anything is launched; on an error nothing is enqueued.
+ *    Conditions only the device can see set bits in cache->status (sticky,
+ *    cleared by the caller), readable after the stream synchronises.
+ *  - Calls on one cache must be stream-ordered; concurrent calls on the same
+ *    cache race.
+ */
+#ifndef CONFK_H
+#define CONFK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- error codes ------------------------------------------------------- */
+#define CONFK_OK 0
+#define CONFK_ERR_INVALID_ARG -1 /* null pointer, bad dimension, bad mode    */
+#define CONFK_ERR_BUDGET -2      /* N < P, budget or prefill above capacity  */
+#define CONFK_ERR_WORKSPACE -3   /* workspace missing or too small           */
+#define CONFK_ERR_UNSUPPORTED -4 /* head dim / group size not built          */
+#define CONFK_ERR_LAUNCH -5      /* the HIP runtime rejected a launch        */
+
+/* ---- device status bits (cache->status[0] / status argument) ---------- */
+#define CONFK_STATUS_NONFINITE_LOGITS 1u /* NaN, +inf, all -inf logits      */
+#define CONFK_STATUS_CAPACITY 2u         /* a (layer, seq) ran out of slots */
+
+/* ---- per-(layer, sequence) header words (cache->meta) ------------------ */
+#define CONFK_META_N 0       /* tokens retained                                 */
+#define CONFK_META_N8 1      /* of which INT8 (the oldest ones)                 */
+#define CONFK_META_BASE8 2   /* INT8 ring slot of the oldest token              */
+#define CONFK_META_BASE16 3  /* FP16 ring slot of the oldest FP16 token         */
+#define CONFK_META_CALIB 4   /* 1 once the INT8 scales are set                  */
+#define CONFK_META_SAT 5     /* INT8 codes clamped at +-127 so far              */
+#define CONFK_META_EVICTED 6 /* tokens evicted by the last confk_compact        */
+#define CONFK_META_MOVED 7   /* K/V rows moved by the last confk_compact        */
+#define CONFK_META_WORDS 8
+
+/* ---- confk_quantize modes ---------------------------------------------- */
+#define CONFK_QUANT_STEP 0    /* move the token that left the FP16 window     */
+#define CONFK_QUANT_PREFILL 1 /* build the cache from L0 prefill tokens       */
+
+/* ---- confk_workspace_size selectors ------------------------------------ */
+#define CONFK_WS_CONFIDENCE 0
+#define CONFK_WS_ATTENTION 1
+
+/*
+ * Policy (hyper-parameters of the review's "复现评估" section and the
+ * summary's "Methodik" section): tau is the confidence threshold, n_high the
+ * tight budget taken when c >= tau, n_low the loose budget, protect (P) the
+ * newest tokens never evicted, window (W) the FP16 window, alpha the rank
+ * mix, lambda the EMA decay, (w_h, w_m, w_p) the confidence weights.
+ */
+typedef struct confk_policy {
+  float tau, alpha, lambda, w_h, w_m, w_p;
+  int32_t n_high, n_low, protect, window;
+} confk_policy;
+
+/*
+ * Cache of L layers x B sequences with Hkv kv heads of dimension d.
+ * Per (layer l, sequence b) the retained tokens are ordered by position; the
+ * oldest meta[N8] are INT8 and the rest FP16. Logical token i < n8 lives in
+ * INT8 ring slot (base8 + i) % cap, logical token i >= n8 in FP16 ring slot
+ * (base16 + i - n8) % cap16. ema and pos are dense in logical order.
+ * Layouts (row-major):
+ *   k8, v8       int8   [L][B][Hkv][cap][d]      INT8 codes
+ *   k16, v16     fp16   [L][B][Hkv][cap16][d]    FP16 window
+ *   kscale,vscale fp32  [L][B][Hkv][d]           per-(head, channel) scales
+ *   ema          fp32   [L][B][cap]              EMA attention mass
+ *   pos          int32  [L][B][cap]              token positions
+ *   meta         int32  [L][B][CONFK_META_WORDS]
+ *   status       uint32 [1]
+ * cap must be at least max(L0, N_low + 1) + 1 (the largest cache before a
+ * step plus the new token); cap16 at least window + 1.
+ */
+typedef struct confk_cache {
+  int32_t layers, batch, hq, hkv, d, cap, cap16;
+  int8_t *k8, *v8;
+  uint16_t *k16, *v16;
+  float *kscale, *vscale;
+  float *ema;
+  int32_t *pos;
+  int32_t *meta;
+  uint32_t *status;
+} confk_cache;
+
+/*
+ * confk_confidence -- confidence score and budget per sequence.
+ * Summary "Methodik: CONF-KV" (Konfidenzschaetzung, adaptive Budgetauswahl);
+ * review "核心方法": c = w_h(1 - H/ln V) + w_m*sigmoid(ln p1 - ln p2) + w_p*p1
+ * with p = softmax(logits[b]); budget = n_high if c >= tau else n_low.
+ *   logits        fp32 [batch][ld] device, first `vocab` entries used
+ *   layer_n_high, layer_n_low  int32 [nbl] device, or both NULL with nbl = 1
+ *                 to use pol->n_high / pol->n_low (per-layer budgets give the
+ *                 pyramid variant)
+ *   c_out         fp32 [batch]
+ *   budget_out    int32 [nbl][batch]
+ *   status        uint32 [1] device or NULL; NaN / +inf / all -inf logits
+ *                 set CONFK_STATUS_NONFINITE_LOGITS, give c = NaN and the
+ *                 loose budget
+ *   ws            >= confk_workspace_size(CONFK_WS_CONFIDENCE, ...) bytes
+ * Errors: INVALID_ARG (null, batch < 1, vocab < 2, ld < vocab, nbl < 1,
+ * only one of the layer arrays given), WORKSPACE.
+ */
+int confk_confidence(const float* logits, int64_t ld, int32_t batch, int32_t vocab,
+                     const confk_policy* pol, const int32_t* layer_n_high,
+                     const int32_t* layer_n_low, int32_t nbl, float* c_out,
+                     int32_t* budget_out, uint32_t* status, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/*
+ * confk_attn_decode -- decode attention over the cache plus the new token,
+ * with INT8 dequantisation fused into the tile reads, and the per-key
+ * attention mass. Summary "Methodik" (Implementierung: compact layout,
+ * dequantisation fused into blockwise attention reads); review "前置知识"
+ * (blockwise online softmax gives the exact softmax) and Algorithm 1 steps
+ * 1-2. For query head h (kv head j = h / (hq/hkv)) over keys i = 0..n
+ * (i = n the new token): u = q_h . k_i / sqrt(d), P_h = softmax(u),
+ * o_h = sum_i P_h,i v_i.
+ *   q             fp16 [nlayers][B][hq][d]
+ *   k_new, v_new  fp16 [nlayers][B][hkv][d]
+ *   out           fp16 [nlayers][B][hq][d]
+ *   mass          fp32 [nlayers][B][hkv][cap]: mass[..][j][i] = sum over the
+ *                 query heads of kv head j of P_h,i, for i = 0..n (the
+ *                 per-key mean over all query heads is sum_j / hq)
+ *   ws            >= confk_workspace_size(CONFK_WS_ATTENTION, ...) bytes
+ *                 (score spill for caches too long for on-chip memory)
+ * Layers layer0 .. layer0+nlayers-1 of the cache are processed; tensor
+ * arguments are indexed from layer0. Supported: d in {64, 128},
+ * hq/hkv in 1..16.
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, LAUNCH.
+ */
+int confk_attn_decode(const confk_cache* cache, int32_t layer0, int32_t nlayers,
+                      const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                      uint16_t* out, float* mass, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * confk_ema_rank -- EMA update of the attention mass and rank scores.
+ * Review "前置知识" (EMA: a_i <- lambda a_i + (1-lambda) Abar_i) and "核心方法"
+ * (s_i = alpha a^_i + (1-alpha) r^_i). Abar_i = sum_j mass[j][i] / hq.
+ * For cached tokens i < n: ema[i] is updated in place, then
+ * score[i] = alpha * ema[i] / max(ema) + (1 - alpha) * (pos[i]-pos[0]) /
+ * (pos[n-1]-pos[0]) (first term 0 when max(ema) = 0, second 1 when n = 1).
+ * The new token's metadata is written to slot n: ema[n] = (1-lambda) Abar_n,
+ * pos[n] = t.
+ *   mass   fp32 [nlayers][B][hkv][cap] from confk_attn_decode
+ *   score  fp32 [nlayers][B][cap]
+ * Errors: INVALID_ARG.
+ */
+int confk_ema_rank(const confk_cache* cache, int32_t layer0, int32_t nlayers, const float* mass,
+                   const confk_policy* pol, int32_t t, float* score, void* stream);
+
+/*
+ * confk_compact -- budget eviction, stable compaction and append.
+ * Summary "Methodik" (Token-Ranking und Eviktion; zusammenhaengende
+ * Komprimierung without indirection tables); review Algorithm 1 steps 5-11
+ * and 13. Per (layer, sequence) with n tokens and budget N: if n > N, the
+ * k = n - N tokens with the smallest (score, position) among all but the
+ * newest `protect` tokens are evicted; survivors keep their order, the new
+ * token (slot n metadata from confk_ema_rank, K/V from k_new/v_new) is
+ * appended as FP16. Rows move only as far as needed: each region (INT8,
+ * FP16) is packed toward whichever end moves fewer rows.
+ *   budget       int32, entry for (l, b) at budget[l * budget_layer_stride + b]
+ *                (stride 0: one budget per sequence; stride B: per layer)
+ *   score        fp32 [nlayers][B][cap] from confk_ema_rank
+ *   k_new,v_new  fp16 [nlayers][B][hkv][d]
+ *   evicted_out  int32 [nlayers][B] device or NULL: tokens evicted
+ * Sets CONFK_STATUS_CAPACITY (and skips the append) if a sequence has no
+ * free slot. Errors: INVALID_ARG, BUDGET (protect > n_low or > n_high).
+ */
+int confk_compact(const confk_cache* cache, int32_t layer0, int32_t nlayers, const int32_t* budget,
+                  int32_t budget_layer_stride, const float* score, const confk_policy* pol,
+                  const uint16_t* k_new, const uint16_t* v_new, int32_t* evicted_out,
+                  void* stream);
+
+/*
+ * confk_quantize -- FP16 -> INT8 storage per (head, channel).
+ * Summary "Methodik" (gemischte Praezisionsspeicherung: newest W tokens FP16,
+ * older retained tokens INT8 per head and channel); review Algorithm 1
+ * step 10. Symmetric absmax scales, scale = fp32(absmax)/127, set once per
+ * (layer, sequence) when the INT8 region is first populated (over every
+ * token then cached) and frozen; code = clamp(rint(fp32(x) / scale), -127,
+ * 127) with the IEEE fp32 quotient (0 when the scale is 0).
+ *   CONFK_QUANT_STEP: every FP16 token with position <= t - window moves to
+ *     the INT8 region (one per step in steady state). k_src/v_src unused.
+ *   CONFK_QUANT_PREFILL: (re)initialise layers layer0.. from n_src prefill
+ *     tokens k_src/v_src fp16 [nlayers][B][hkv][n_src][d] at positions
+ *     0..n_src-1: EMA 0, INT8 for positions <= n_src-1-window, FP16 for the
+ *     rest, scales over all n_src tokens when any token is INT8. n_src = 0
+ *     gives an empty cache. Also clears the status word.
+ * Errors: INVALID_ARG, BUDGET (n_src > cap - 1).
+ */
+int confk_quantize(const confk_cache* cache, int32_t layer0, int32_t nlayers, int32_t t,
+                   const confk_policy* pol, int32_t mode, const uint16_t* k_src,
+                   const uint16_t* v_src, int32_t n_src, void* stream);
+
+/* Workspace bytes needed by confk_confidence (which = CONFK_WS_CONFIDENCE;
+ * uses batch, vocab) or confk_attn_decode (CONFK_WS_ATTENTION; uses the cache
+ * dims and nlayers). Returns 0 when none is needed. */
+size_t confk_workspace_size(int32_t which, const confk_cache* cache, int32_t nlayers,
+                            int32_t batch, int32_t vocab);
+
+/* Static text for an error code. */
+const char* confk_strerror(int code);
+
+/* ABI version (major * 100 + minor). */
+int confk_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CONFK_H */

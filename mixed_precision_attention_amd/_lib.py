@@ -1,0 +1,101 @@
+"""ctypes view of libconfk's C ABI (include/confk.h). Marshalling only."""
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libconfk.so")
+
+c_int32 = ctypes.c_int32
+c_float = ctypes.c_float
+c_void_p = ctypes.c_void_p
+c_size_t = ctypes.c_size_t
+c_int64 = ctypes.c_int64
+
+OK = 0
+ERR_INVALID_ARG = -1
+ERR_BUDGET = -2
+ERR_WORKSPACE = -3
+ERR_UNSUPPORTED = -4
+ERR_LAUNCH = -5
+
+STATUS_NONFINITE_LOGITS = 1
+STATUS_CAPACITY = 2
+
+META_N, META_N8, META_BASE8, META_BASE16, META_CALIB, META_SAT, META_EVICTED, META_MOVED = range(8)
+META_WORDS = 8
+
+QUANT_STEP = 0
+QUANT_PREFILL = 1
+WS_CONFIDENCE = 0
+WS_ATTENTION = 1
+
+EXPORTS = [
+    "confk_confidence", "confk_attn_decode", "confk_ema_rank", "confk_compact",
+    "confk_quantize", "confk_workspace_size", "confk_strerror", "confk_version",
+]
+
+
+class Policy(ctypes.Structure):
+    _fields_ = [
+        ("tau", c_float), ("alpha", c_float), ("lambda_", c_float),
+        ("w_h", c_float), ("w_m", c_float), ("w_p", c_float),
+        ("n_high", c_int32), ("n_low", c_int32), ("protect", c_int32), ("window", c_int32),
+    ]
+
+
+class Cache(ctypes.Structure):
+    _fields_ = [
+        ("layers", c_int32), ("batch", c_int32), ("hq", c_int32), ("hkv", c_int32),
+        ("d", c_int32), ("cap", c_int32), ("cap16", c_int32),
+        ("k8", c_void_p), ("v8", c_void_p), ("k16", c_void_p), ("v16", c_void_p),
+        ("kscale", c_void_p), ("vscale", c_void_p), ("ema", c_void_p), ("pos", c_void_p),
+        ("meta", c_void_p), ("status", c_void_p),
+    ]
+
+
+class ConfkError(RuntimeError):
+    def __init__(self, fn, code, text):
+        super().__init__(f"{fn} failed: {code} ({text})")
+        self.code = code
+
+
+_lib = None
+
+
+def load():
+    """Loads libconfk.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m mixed_precision_attention_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER
+    lib.confk_confidence.argtypes = [c_void_p, c_int64, c_int32, c_int32, P(Policy), c_void_p,
+                                     c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+                                     c_size_t, c_void_p]
+    lib.confk_attn_decode.argtypes = [P(Cache), c_int32, c_int32, c_void_p, c_void_p, c_void_p,
+                                      c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.confk_ema_rank.argtypes = [P(Cache), c_int32, c_int32, c_void_p, P(Policy), c_int32,
+                                   c_void_p, c_void_p]
+    lib.confk_compact.argtypes = [P(Cache), c_int32, c_int32, c_void_p, c_int32, c_void_p,
+                                  P(Policy), c_void_p, c_void_p, c_void_p, c_void_p]
+    lib.confk_quantize.argtypes = [P(Cache), c_int32, c_int32, c_int32, P(Policy), c_int32,
+                                   c_void_p, c_void_p, c_int32, c_void_p]
+    lib.confk_workspace_size.argtypes = [c_int32, P(Cache), c_int32, c_int32, c_int32]
+    lib.confk_workspace_size.restype = c_size_t
+    lib.confk_strerror.argtypes = [ctypes.c_int]
+    lib.confk_strerror.restype = ctypes.c_char_p
+    lib.confk_version.restype = ctypes.c_int
+    for name in ("confk_confidence", "confk_attn_decode", "confk_ema_rank", "confk_compact",
+                 "confk_quantize"):
+        getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def check(fn, code):
+    if code != OK:
+        raise ConfkError(fn, code, load().confk_strerror(code).decode())
+    return code

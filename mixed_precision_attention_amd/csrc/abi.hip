@@ -1,0 +1,194 @@
+// Host side of the C ABI: argument validation, launch planning, error codes.
+// Every entry point validates all arguments before enqueuing anything.
+#include <string.h>
+
+#include "confk_internal.h"
+
+using namespace confk;
+
+namespace {
+
+bool cache_ok(const confk_cache* c) {
+  if (!c) return false;
+  if (c->layers < 1 || c->batch < 1 || c->hkv < 1 || c->hq < c->hkv || c->hq % c->hkv) return false;
+  if (c->d < 16 || c->cap < 2 || c->cap16 < 2) return false;
+  if (!c->k8 || !c->v8 || !c->k16 || !c->v16 || !c->kscale || !c->vscale || !c->ema ||
+      !c->pos || !c->meta || !c->status)
+    return false;
+  return true;
+}
+
+bool layers_ok(const confk_cache* c, int32_t layer0, int32_t nlayers) {
+  return layer0 >= 0 && nlayers >= 1 && layer0 + nlayers <= c->layers;
+}
+
+bool policy_ok(const confk_policy* p) {
+  if (!p) return false;
+  if (p->n_high < 1 || p->n_low < 1 || p->protect < 0 || p->window < 1) return false;
+  if (!(p->lambda >= 0.f && p->lambda <= 1.f) || !(p->alpha >= 0.f && p->alpha <= 1.f)) return false;
+  return true;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? CONFK_OK : CONFK_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int confk_version(void) { return 100; }
+
+const char* confk_strerror(int code) {
+  switch (code) {
+    case CONFK_OK: return "ok";
+    case CONFK_ERR_INVALID_ARG: return "invalid argument";
+    case CONFK_ERR_BUDGET: return "budget below the protected window or above capacity";
+    case CONFK_ERR_WORKSPACE: return "workspace missing or too small";
+    case CONFK_ERR_UNSUPPORTED: return "unsupported head dimension or group size";
+    case CONFK_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown error";
+  }
+}
+
+size_t confk_workspace_size(int32_t which, const confk_cache* cache, int32_t nlayers, int32_t batch,
+                            int32_t vocab) {
+  if (which == CONFK_WS_CONFIDENCE) {
+    if (batch < 1 || vocab < 1) return 0;
+    return confidence_ws_bytes(batch, vocab);
+  }
+  if (which == CONFK_WS_ATTENTION) {
+    if (!cache || nlayers < 1 || cache->hkv < 1 || cache->hq % cache->hkv) return 0;
+    const int g = cache->hq / cache->hkv;
+    int stride = 0;
+    attention_plan_n_lds(cache->d, g, cache->cap, &stride);
+    return (size_t)nlayers * cache->batch * cache->hkv * g * (size_t)stride * sizeof(float);
+  }
+  return 0;
+}
+
+int confk_confidence(const float* logits, int64_t ld, int32_t batch, int32_t vocab,
+                     const confk_policy* pol, const int32_t* layer_n_high,
+                     const int32_t* layer_n_low, int32_t nbl, float* c_out, int32_t* budget_out,
+                     uint32_t* status, void* ws, size_t ws_bytes, void* stream) {
+  if (!logits || !c_out || !budget_out || !pol) return CONFK_ERR_INVALID_ARG;
+  if (batch < 1 || vocab < 2 || ld < vocab || nbl < 1) return CONFK_ERR_INVALID_ARG;
+  if ((layer_n_high == nullptr) != (layer_n_low == nullptr)) return CONFK_ERR_INVALID_ARG;
+  if (!layer_n_high && nbl != 1) return CONFK_ERR_INVALID_ARG;
+  if (pol->n_high < 1 || pol->n_low < 1) return CONFK_ERR_INVALID_ARG;
+  const size_t need = confidence_ws_bytes(batch, vocab);
+  if (!ws || ws_bytes < need) return CONFK_ERR_WORKSPACE;
+  ConfArgs a{};
+  a.logits = logits;
+  a.ld = ld;
+  a.batch = batch;
+  a.vocab = vocab;
+  a.nbl = nbl;
+  a.tau = pol->tau;
+  a.w_h = pol->w_h;
+  a.w_m = pol->w_m;
+  a.w_p = pol->w_p;
+  a.n_high = pol->n_high;
+  a.n_low = pol->n_low;
+  a.layer_n_high = layer_n_high;
+  a.layer_n_low = layer_n_low;
+  a.partial = (float*)ws;
+  a.c_out = c_out;
+  a.budget_out = budget_out;
+  a.status = status;
+  return launch_status(launch_confidence(a, (hipStream_t)stream));
+}
+
+int confk_attn_decode(const confk_cache* cache, int32_t layer0, int32_t nlayers, const uint16_t* q,
+                      const uint16_t* k_new, const uint16_t* v_new, uint16_t* out, float* mass,
+                      void* ws, size_t ws_bytes, void* stream) {
+  if (!cache_ok(cache) || !layers_ok(cache, layer0, nlayers)) return CONFK_ERR_INVALID_ARG;
+  if (!q || !k_new || !v_new || !out || !mass) return CONFK_ERR_INVALID_ARG;
+  const int g = cache->hq / cache->hkv;
+  if ((cache->d != 64 && cache->d != 128) || g > 16) return CONFK_ERR_UNSUPPORTED;
+  int stride = 0;
+  const int n_lds = attention_plan_n_lds(cache->d, g, cache->cap, &stride);
+  const size_t need = (size_t)nlayers * cache->batch * cache->hkv * g * (size_t)stride * sizeof(float);
+  if (need && (!ws || ws_bytes < need)) return CONFK_ERR_WORKSPACE;
+  AttnArgs a{};
+  a.c = view_of(cache);
+  a.layer0 = layer0;
+  a.nl = nlayers;
+  a.g = g;
+  a.n_lds = n_lds;
+  a.spill_stride = stride;
+  a.q = q;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.out = out;
+  a.mass = mass;
+  a.spill = need ? (float*)ws : nullptr;
+  return launch_status(launch_attention(a, attention_lds_bytes(cache->d, g, n_lds), (hipStream_t)stream));
+}
+
+int confk_ema_rank(const confk_cache* cache, int32_t layer0, int32_t nlayers, const float* mass,
+                   const confk_policy* pol, int32_t t, float* score, void* stream) {
+  if (!cache_ok(cache) || !layers_ok(cache, layer0, nlayers)) return CONFK_ERR_INVALID_ARG;
+  if (!mass || !score || !policy_ok(pol) || t < 0) return CONFK_ERR_INVALID_ARG;
+  EmaArgs a{};
+  a.c = view_of(cache);
+  a.layer0 = layer0;
+  a.nl = nlayers;
+  a.t = t;
+  a.lambda = pol->lambda;
+  a.alpha = pol->alpha;
+  a.mass = mass;
+  a.score = score;
+  return launch_status(launch_ema_rank(a, (hipStream_t)stream));
+}
+
+int confk_compact(const confk_cache* cache, int32_t layer0, int32_t nlayers, const int32_t* budget,
+                  int32_t budget_layer_stride, const float* score, const confk_policy* pol,
+                  const uint16_t* k_new, const uint16_t* v_new, int32_t* evicted_out, void* stream) {
+  if (!cache_ok(cache) || !layers_ok(cache, layer0, nlayers)) return CONFK_ERR_INVALID_ARG;
+  if (!budget || !score || !k_new || !v_new || !policy_ok(pol)) return CONFK_ERR_INVALID_ARG;
+  if (budget_layer_stride != 0 && budget_layer_stride != cache->batch) return CONFK_ERR_INVALID_ARG;
+  if (cache->d % 16) return CONFK_ERR_UNSUPPORTED;
+  if (pol->protect > pol->n_high || pol->protect > pol->n_low) return CONFK_ERR_BUDGET;
+  if (pol->n_low + 1 > cache->cap - 1 || pol->n_high + 1 > cache->cap - 1) return CONFK_ERR_BUDGET;
+  if (pol->window + 1 > cache->cap16) return CONFK_ERR_BUDGET;
+  CompactArgs a{};
+  a.c = view_of(cache);
+  a.layer0 = layer0;
+  a.nl = nlayers;
+  a.budget_stride = budget_layer_stride;
+  a.protect = pol->protect;
+  a.budget = budget;
+  a.score = score;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.evicted_out = evicted_out;
+  return launch_status(launch_compact(a, (hipStream_t)stream));
+}
+
+int confk_quantize(const confk_cache* cache, int32_t layer0, int32_t nlayers, int32_t t,
+                   const confk_policy* pol, int32_t mode, const uint16_t* k_src,
+                   const uint16_t* v_src, int32_t n_src, void* stream) {
+  if (!cache_ok(cache) || !layers_ok(cache, layer0, nlayers)) return CONFK_ERR_INVALID_ARG;
+  if (!policy_ok(pol)) return CONFK_ERR_INVALID_ARG;
+  if (pol->window + 1 > cache->cap16) return CONFK_ERR_BUDGET;
+  QuantArgs a{};
+  a.c = view_of(cache);
+  a.layer0 = layer0;
+  a.nl = nlayers;
+  a.t = t;
+  a.window = pol->window;
+  if (mode == CONFK_QUANT_STEP) {
+    return launch_status(launch_quantize_step(a, (hipStream_t)stream));
+  }
+  if (mode == CONFK_QUANT_PREFILL) {
+    if (n_src < 0) return CONFK_ERR_INVALID_ARG;
+    if (n_src > 0 && (!k_src || !v_src)) return CONFK_ERR_INVALID_ARG;
+    if (n_src > cache->cap - 1) return CONFK_ERR_BUDGET;
+    a.n_src = n_src;
+    a.k_src = k_src;
+    a.v_src = v_src;
+    return launch_status(launch_prefill(a, (hipStream_t)stream));
+  }
+  return CONFK_ERR_INVALID_ARG;
+}
+
+}  // extern "C"

@@ -1,0 +1,493 @@
+// Decode attention over the mixed FP16/INT8 cache with fused dequantisation,
+// plus the per-key attention mass.
+//
+// CONF-KV summary, "Methodik: CONF-KV" (Implementierung): survivors sit in a
+// dense layout without indirection tables and dequantisation is fused into
+// the blockwise attention reads; the review's "前置知识" section: blockwise
+// online softmax keeps a running max and normaliser and is exact. The mass
+// feeds the EMA of the review's "前置知识"/"核心方法" sections.
+//
+// One workgroup (4 waves) per (layer, sequence, kv head). The g query heads
+// sharing the kv head form the N side of the matrix-core tiles, keys the M
+// side, so every K/V byte is read from HBM once per step:
+//   scores  S^T[16 keys x 16 heads] = K_tile[16 x d] . Q^T      (16x16x32 f16)
+//   output  O^T[16 ch x 16 heads]  += V^T[16 ch x 16 keys] . P^T (16x16x16 f16)
+// The score accumulator layout (lane = head + 16*key-group, 4 keys per lane)
+// is exactly the B-operand layout of the second product, so P^T goes from
+// registers to the matrix core with one fp16 conversion.
+//
+// Dequantisation: per-channel K scales are folded into the query once
+// (q' = q * s_K * log2(e)/sqrt(d)); INT8 codes become fp16 exactly through a
+// byte permute (0x64 exponent byte) and one packed subtract; per-channel V
+// scales multiply the INT8 part of the accumulator once, when the wave moves
+// from the INT8 region to the FP16 region.
+//
+// Score accuracy: q' is split into fp16 hi + lo parts (after scaling by a
+// power of two into fp16's normal range), so the fp32 scores carry ~22 bits;
+// the probabilities fed to the second product are fp16.
+//
+// Mass: the log2-domain scores are kept in LDS (or a global spill area for
+// very long caches); once the waves' running maxima and normalisers are
+// merged, each key's mass sum_h 2^(s_h - M_h) / L_h is formed exactly.
+#include "confk_internal.h"
+
+namespace confk {
+
+namespace {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Two INT8 codes (bytes b0/b1 or b2/b3 of x = codes ^ 0x80808080) -> two fp16.
+// perm places each biased code under an 0x64 exponent byte: fp16 value
+// 1024 + (code + 128); subtracting 1152 leaves the code, exactly.
+__device__ __forceinline__ uint32_t codes_to_h2(uint32_t x, uint32_t sel) {
+  const uint32_t p = __builtin_amdgcn_perm(0x64646464u, x, sel);
+  half2_t h = __builtin_bit_cast(half2_t, p);
+  h = h - (half2_t){(_Float16)1152.0f, (_Float16)1152.0f};
+  return __builtin_bit_cast(uint32_t, h);
+}
+constexpr uint32_t kSelLo = 0x04010400u;  // [b0, 0x64, b1, 0x64]
+constexpr uint32_t kSelHi = 0x04030402u;  // [b2, 0x64, b3, 0x64]
+
+// Byte bb of row0 and of row1 -> fp16 pair (row0, row1).
+__device__ __forceinline__ uint32_t code_pair_rows(uint32_t row0w, uint32_t row1w, int bb) {
+  const uint32_t sel = 0x0c000c00u | ((uint32_t)(4 + bb) << 16) | (uint32_t)bb;
+  uint32_t p = __builtin_amdgcn_perm(row1w, row0w, sel) ^ 0x64806480u;
+  half2_t h = __builtin_bit_cast(half2_t, p);
+  h = h - (half2_t){(_Float16)1152.0f, (_Float16)1152.0f};
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+// Half hf (0/1) of row0w and of row1w -> fp16 pair (row0, row1).
+__device__ __forceinline__ uint32_t half_pair_rows(uint32_t row0w, uint32_t row1w, int hf) {
+  return __builtin_amdgcn_perm(row1w, row0w, hf ? 0x07060302u : 0x05040100u);
+}
+
+__device__ __forceinline__ half8_t as_half8(u32x4 v) { return __builtin_bit_cast(half8_t, v); }
+__device__ __forceinline__ half4_t as_half4(u32x2 v) { return __builtin_bit_cast(half4_t, v); }
+
+template <int D>
+struct Tile {
+  static constexpr int KC = D / 32;  // 16x16x32 chunks along d
+  static constexpr int CB = D / 16;  // 16-channel blocks of the output
+  static constexpr int KU = D / 64;  // 16-byte loads per INT8 K row per lane
+};
+
+// Physical d of element j of chunk kc in the query/key operands of lane
+// group kg. INT8 rows: each lane reads 16 contiguous bytes per 64-byte half
+// of the row; FP16 rows: 8 contiguous halves per chunk.
+template <int D>
+__device__ __forceinline__ int d_int8(int kc, int kg) {
+  return (kc >> 1) * 64 + 16 * kg + 8 * (kc & 1);
+}
+__device__ __forceinline__ int d_fp16(int kc, int kg) { return 32 * kc + 8 * kg; }
+
+// Builds the hi/lo fp16 query operands of this lane (head hh, group kg) for
+// one key region; returns the power-of-two factor that undoes the scaling.
+template <int D, bool INT8>
+__device__ __forceinline__ float build_q(const uint16_t* qrow, const float* kscale, bool active,
+                                         int kg, half8_t* qhi, half8_t* qlo) {
+  constexpr int KC = Tile<D>::KC;
+  const float cq = kLog2e / sqrtf((float)D);
+  float x[KC][8];
+  float mx = 0.f;
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) {
+    const int d0 = INT8 ? d_int8<D>(kc, kg) : d_fp16(kc, kg);
+    if (active) {
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(qrow + d0);
+      const half8_t h = as_half8(raw);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float v = (float)h[j] * cq;
+        if (INT8) v *= kscale[d0 + j];
+        x[kc][j] = v;
+        mx = fmaxf(mx, fabsf(v));
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[kc][j] = 0.f;
+    }
+  }
+  mx = wave_max(mx);
+  int e = 0;
+  if (mx > 0.f) {
+    frexpf(mx, &e);  // mx in [2^(e-1), 2^e)
+  }
+  int sh = 12 - e;  // scaled max in [2^11, 2^12)
+  sh = max(-100, min(100, sh));
+  const float up = ldexpf(1.f, sh);
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float v = x[kc][j] * up;
+      const _Float16 hi = (_Float16)v;
+      qhi[kc][j] = hi;
+      qlo[kc][j] = (_Float16)(v - (float)hi);
+    }
+  }
+  return ldexpf(1.f, -sh);
+}
+
+struct SoftState {
+  float m;  // running max of this lane's head (log2 units)
+  float l;  // partial normaliser over this lane's keys
+};
+
+// Online-softmax update for one 16-key tile; returns P^T operand.
+template <int CB>
+__device__ __forceinline__ half4_t softmax_tile(float4_t s, SoftState& st, float4_t* acc) {
+  float tmax = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+  const float mnew = fmaxf(st.m, tmax);
+  if (__any(mnew > st.m)) {
+    const float corr = exp2f(st.m - mnew);
+    st.l *= corr;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) acc[cb] *= corr;
+  }
+  st.m = mnew;
+  half4_t p;
+  float lsum = 0.f;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const float e = exp2f(s[v] - mnew);
+    lsum += e;
+    p[v] = (_Float16)e;
+  }
+  st.l += lsum;
+  return p;
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void attn_decode_kernel(AttnArgs a) {
+  constexpr int KC = Tile<D>::KC;
+  constexpr int CB = Tile<D>::CB;
+  constexpr int KU = Tile<D>::KU;
+  extern __shared__ float lds[];
+
+  const CacheView& c = a.c;
+  const int u = blockIdx.x;
+  const int H = c.hkv;
+  const int h = u % H;
+  const int lb = u / H;  // local (layer, sequence)
+  const int l = lb / c.B;
+  const int b = lb - l * c.B;
+  const int lbc = (a.layer0 + l) * c.B + b;
+  const int g = a.g;
+
+  const int32_t* meta = c.meta + lbc * CONFK_META_WORDS;
+  const int n = meta[CONFK_META_N];
+  const int n8 = meta[CONFK_META_N8];
+  const int base8 = meta[CONFK_META_BASE8];
+  const int base16 = meta[CONFK_META_BASE16];
+  const int f = n - n8;
+  const int nk = n + 1;
+  if (!meta_ok(n, n8, base8, base16, c.cap, c.cap16)) {  // uniform per workgroup
+    if (threadIdx.x == 0) atomicOr(c.status, (uint32_t)CONFK_STATUS_CAPACITY);
+    return;
+  }
+  const int nt8 = (n8 + 15) >> 4;
+  const int nt16 = (f + 1 + 15) >> 4;
+  const int p16 = nt8 * 16;  // first score slot of the FP16 region
+
+  const size_t hrow = (size_t)lbc * H + h;
+  const int8_t* k8 = c.k8 + hrow * c.cap * D;
+  const int8_t* v8 = c.v8 + hrow * c.cap * D;
+  const uint16_t* k16 = c.k16 + hrow * c.cap16 * D;
+  const uint16_t* v16 = c.v16 + hrow * c.cap16 * D;
+  const float* ks = c.ks + hrow * D;
+  const float* vs = c.vs + hrow * D;
+  const size_t qoff = ((size_t)lb * c.hq + (size_t)h * g) * D;
+  const uint16_t* qb = a.q + qoff;
+  const uint16_t* kn = a.k_new + ((size_t)lb * H + h) * D;
+  const uint16_t* vn = a.v_new + ((size_t)lb * H + h) * D;
+  float* spill = a.spill ? a.spill + (size_t)u * g * a.spill_stride : nullptr;
+
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int r16 = lane & 15;
+  const int kg = lane >> 4;
+  const bool head_ok = r16 < g;
+  const uint16_t* qrow = qb + (size_t)r16 * D;
+
+  float* sc = lds;  // [g][n_lds]
+  const int n_lds = a.n_lds;
+
+  float4_t acc[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) acc[cb] = (float4_t){0.f, 0.f, 0.f, 0.f};
+  SoftState st{-INFINITY, 0.f};
+
+  auto store_scores = [&](int p0, float4_t s) {
+    if (!head_ok) return;
+    const int p = p0 + 4 * kg;
+    if (p0 < n_lds) {
+      *reinterpret_cast<float4_t*>(sc + (size_t)r16 * n_lds + p) = s;
+    } else {
+      *reinterpret_cast<float4_t*>(spill + (size_t)r16 * a.spill_stride + p) = s;
+    }
+  };
+
+  // ------------------------------------------------------------ INT8 region
+  if (nt8 > w) {
+    half8_t qhi[KC], qlo[KC];
+    const float unscale = build_q<D, true>(qrow, ks, head_ok, kg, qhi, qlo);
+    for (int t = w; t < nt8; t += kWaves) {
+      const int i0 = t * 16;
+      // K rows: lane reads key r16
+      u32x4 kx[KU];
+      {
+        const int i = i0 + r16;
+        if (i < n8) {
+          int slot = base8 + i;
+          if (slot >= c.cap) slot -= c.cap;
+          const int8_t* row = k8 + (size_t)slot * D;
+#pragma unroll
+          for (int uu = 0; uu < KU; ++uu)
+            kx[uu] = *reinterpret_cast<const u32x4*>(row + 64 * uu + 16 * kg);
+        } else {
+#pragma unroll
+          for (int uu = 0; uu < KU; ++uu) kx[uu] = (u32x4){0x80808080u, 0x80808080u, 0x80808080u, 0x80808080u};
+        }
+      }
+      // V rows: lane reads keys i0+4kg+j, channels [ (D/16)*r16, +D/16 )
+      uint32_t vx[4][CB / 4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = i0 + 4 * kg + j;
+        if (i < n8) {
+          int slot = base8 + i;
+          if (slot >= c.cap) slot -= c.cap;
+          const int8_t* row = v8 + (size_t)slot * D + (D / 16) * r16;
+          if constexpr (CB == 8) {
+            const u32x2 t2 = *reinterpret_cast<const u32x2*>(row);
+            vx[j][0] = t2[0];
+            vx[j][1] = t2[1];
+          } else {
+            vx[j][0] = *reinterpret_cast<const uint32_t*>(row);
+          }
+        } else {
+#pragma unroll
+          for (int z = 0; z < CB / 4; ++z) vx[j][z] = 0u;
+        }
+      }
+      // scores
+      float4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const u32x4 xw = kx[kc >> 1] ^ 0x80808080u;
+        const int o = 2 * (kc & 1);
+        u32x4 hv;
+        hv[0] = codes_to_h2(xw[o], kSelLo);
+        hv[1] = codes_to_h2(xw[o], kSelHi);
+        hv[2] = codes_to_h2(xw[o + 1], kSelLo);
+        hv[3] = codes_to_h2(xw[o + 1], kSelHi);
+        const half8_t ak = as_half8(hv);
+        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, qhi[kc], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, qlo[kc], s, 0, 0, 0);
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int i = i0 + 4 * kg + v;
+        s[v] = !head_ok ? 0.f : (i < n8 ? s[v] * unscale : -INFINITY);
+      }
+      store_scores(i0, s);
+      const half4_t pT = softmax_tile<CB>(s, st, acc);
+      // P.V
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const int wd = cb >> 2, bb = cb & 3;
+        u32x2 av;
+        av[0] = code_pair_rows(vx[0][wd], vx[1][wd], bb);
+        av[1] = code_pair_rows(vx[2][wd], vx[3][wd], bb);
+        acc[cb] = __builtin_amdgcn_mfma_f32_16x16x16f16(as_half4(av), pT, acc[cb], 0, 0, 0);
+      }
+    }
+    // V scales of the INT8 part: channel of acc[cb][v] is CB*(4kg+v)+cb
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[cb][v] *= vs[CB * (4 * kg + v) + cb];
+  }
+
+  // ------------------------------------------------------ FP16 region + new
+  if (nt16 > w) {
+    half8_t qhi[KC], qlo[KC];
+    const float unscale = build_q<D, false>(qrow, nullptr, head_ok, kg, qhi, qlo);
+    for (int t = w; t < nt16; t += kWaves) {
+      const int j0 = t * 16;  // FP16-local index of the tile's first key
+      u32x4 kx[KC];
+      {
+        const int jj = j0 + r16;
+        const uint16_t* row = nullptr;
+        if (jj < f) {
+          int slot = base16 + jj;
+          if (slot >= c.cap16) slot -= c.cap16;
+          row = k16 + (size_t)slot * D;
+        } else if (jj == f) {
+          row = kn;
+        }
+        if (row) {
+#pragma unroll
+          for (int kc = 0; kc < KC; ++kc)
+            kx[kc] = *reinterpret_cast<const u32x4*>(row + d_fp16(kc, kg));
+        } else {
+#pragma unroll
+          for (int kc = 0; kc < KC; ++kc) kx[kc] = (u32x4){0u, 0u, 0u, 0u};
+        }
+      }
+      uint32_t vx[4][CB / 2];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int jj = j0 + 4 * kg + j;
+        const uint16_t* row = nullptr;
+        if (jj < f) {
+          int slot = base16 + jj;
+          if (slot >= c.cap16) slot -= c.cap16;
+          row = v16 + (size_t)slot * D;
+        } else if (jj == f) {
+          row = vn;
+        }
+        if (row) {
+          row += (D / 16) * r16;
+          if constexpr (CB == 8) {
+            const u32x4 t4 = *reinterpret_cast<const u32x4*>(row);
+#pragma unroll
+            for (int z = 0; z < 4; ++z) vx[j][z] = t4[z];
+          } else {
+            const u32x2 t2 = *reinterpret_cast<const u32x2*>(row);
+            vx[j][0] = t2[0];
+            vx[j][1] = t2[1];
+          }
+        } else {
+#pragma unroll
+          for (int z = 0; z < CB / 2; ++z) vx[j][z] = 0u;
+        }
+      }
+      float4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const half8_t ak = as_half8(kx[kc]);
+        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, qhi[kc], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, qlo[kc], s, 0, 0, 0);
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int jj = j0 + 4 * kg + v;
+        s[v] = !head_ok ? 0.f : (jj <= f ? s[v] * unscale : -INFINITY);
+      }
+      store_scores(p16 + j0, s);
+      const half4_t pT = softmax_tile<CB>(s, st, acc);
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const int wd = cb >> 1, hf = cb & 1;
+        u32x2 av;
+        av[0] = half_pair_rows(vx[0][wd], vx[1][wd], hf);
+        av[1] = half_pair_rows(vx[2][wd], vx[3][wd], hf);
+        acc[cb] = __builtin_amdgcn_mfma_f32_16x16x16f16(as_half4(av), pT, acc[cb], 0, 0, 0);
+      }
+    }
+  }
+
+  // -------------------------------------------------------------- merge
+  __shared__ float wm[kWaves][16], wl[kWaves][16], Mh[16], iL[16];
+  float lt = st.l + __shfl_xor(st.l, 16, 64);
+  lt += __shfl_xor(lt, 32, 64);
+  if (kg == 0) {
+    wm[w][r16] = st.m;
+    wl[w][r16] = lt;
+  }
+  __syncthreads();
+  if (threadIdx.x < g) {
+    const int hh = threadIdx.x;
+    float M = -INFINITY;
+    for (int q = 0; q < kWaves; ++q) M = fmaxf(M, wm[q][hh]);
+    float L = 0.f;
+    for (int q = 0; q < kWaves; ++q)
+      if (wl[q][hh] > 0.f) L += wl[q][hh] * exp2f(wm[q][hh] - M);
+    Mh[hh] = M;
+    iL[hh] = 1.f / L;
+  }
+  __syncthreads();
+
+  // per-key mass (summed over this kv head's query heads)
+  float* mout = a.mass + ((size_t)lb * H + h) * c.cap;
+  for (int i = threadIdx.x; i < nk; i += kThreads) {
+    const int p = i < n8 ? i : p16 + (i - n8);
+    float sum = 0.f;
+    for (int hh = 0; hh < g; ++hh) {
+      const float s = p < n_lds ? sc[(size_t)hh * n_lds + p] : spill[(size_t)hh * a.spill_stride + p];
+      sum += exp2f(s - Mh[hh]) * iL[hh];
+    }
+    mout[i] = sum;
+  }
+  __syncthreads();
+
+  // output: scale each wave's accumulator to the merged normaliser, sum waves
+  float* red = lds;  // [kWaves][g][D], aliases the score area
+  if (head_ok) {
+    const float fct = (wl[w][r16] > 0.f) ? exp2f(st.m - Mh[r16]) * iL[r16] : 0.f;
+    float* dst = red + ((size_t)w * g + r16) * D;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) dst[CB * (4 * kg + v) + cb] = acc[cb][v] * fct;
+  }
+  __syncthreads();
+  uint16_t* ob = a.out + qoff;
+  for (int idx = threadIdx.x; idx < g * D; idx += kThreads) {
+    float o = 0.f;
+#pragma unroll
+    for (int q = 0; q < kWaves; ++q) o += red[(size_t)q * g * D + idx];
+    ob[idx] = float_to_half_bits(o);
+  }
+}
+
+}  // namespace
+
+int attention_lds_bytes(int d, int g, int n_lds) {
+  const int sc = g * n_lds;
+  const int red = kWaves * g * d;
+  return 4 * (sc > red ? sc : red);
+}
+
+// Score slots per head: padded INT8 tiles + padded FP16 tiles (incl. new).
+static int score_slots(int cap) { return ((cap + 30 + 15) / 16) * 16; }
+
+int attention_plan_n_lds(int d, int g, int cap, int* spill_stride) {
+  const int need = score_slots(cap);
+  const int budget = 40 * 1024;  // LDS bytes per workgroup for scores
+  int fit = (budget / (4 * g)) / 16 * 16;
+  const int min_slots = (kWaves * d + 15) / 16 * 16;  // room for the output reduction
+  if (fit < min_slots) fit = min_slots;
+  if (need <= fit) {
+    *spill_stride = 0;
+    return need;
+  }
+  *spill_stride = need;
+  return fit;
+}
+
+hipError_t launch_attention(const AttnArgs& a, int lds_bytes, hipStream_t s) {
+  const int units = a.nl * a.c.B * a.c.hkv;
+  if (a.c.d == 128) {
+    hipLaunchKernelGGL(attn_decode_kernel<128>, dim3(units), dim3(kThreads), lds_bytes, s, a);
+  } else {
+    hipLaunchKernelGGL(attn_decode_kernel<64>, dim3(units), dim3(kThreads), lds_bytes, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace confk

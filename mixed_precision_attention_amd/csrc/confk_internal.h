@@ -1,0 +1,133 @@
+// Internal declarations shared by the libconfk HIP sources (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "confk.h"
+
+namespace confk {
+
+// ---------------------------------------------------------------------------
+// Kernel argument blocks (passed by value).
+// ---------------------------------------------------------------------------
+
+struct CacheView {
+  int32_t L, B, hq, hkv, d, cap, cap16;
+  int8_t* k8;
+  int8_t* v8;
+  uint16_t* k16;
+  uint16_t* v16;
+  float* ks;
+  float* vs;
+  float* ema;
+  int32_t* pos;
+  int32_t* meta;
+  uint32_t* status;
+};
+
+inline CacheView view_of(const confk_cache* c) {
+  return CacheView{c->layers, c->batch, c->hq, c->hkv, c->d, c->cap, c->cap16,
+                   c->k8,     c->v8,    c->k16, c->v16, c->kscale, c->vscale,
+                   c->ema,    c->pos,   c->meta, c->status};
+}
+
+struct ConfArgs {
+  const float* logits;
+  int64_t ld;
+  int32_t batch, vocab, chunk, nchunks, nbl;
+  float tau, w_h, w_m, w_p;
+  int32_t n_high, n_low;
+  const int32_t* layer_n_high;
+  const int32_t* layer_n_low;
+  float* partial;  // [batch][nchunks][6]
+  float* c_out;
+  int32_t* budget_out;
+  uint32_t* status;
+};
+
+struct AttnArgs {
+  CacheView c;
+  int32_t layer0, nl, g;
+  int32_t n_lds;  // score slots (padded key positions) held in LDS per head
+  int32_t spill_stride;  // score slots per head in the global spill area
+  const uint16_t* q;
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  uint16_t* out;
+  float* mass;
+  float* spill;  // [nl*B*hkv][g][spill_stride] or null
+};
+
+struct EmaArgs {
+  CacheView c;
+  int32_t layer0, nl, t;
+  float lambda, alpha;
+  const float* mass;
+  float* score;
+};
+
+struct CompactArgs {
+  CacheView c;
+  int32_t layer0, nl, budget_stride, protect;
+  const int32_t* budget;
+  const float* score;
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  int32_t* evicted_out;
+};
+
+struct QuantArgs {
+  CacheView c;
+  int32_t layer0, nl, t, window, n_src;
+  const uint16_t* k_src;
+  const uint16_t* v_src;
+};
+
+// ---------------------------------------------------------------------------
+// Launchers (defined next to their kernels). Return hipError_t of the launch.
+// ---------------------------------------------------------------------------
+hipError_t launch_confidence(const ConfArgs& a, hipStream_t s);
+size_t confidence_ws_bytes(int32_t batch, int32_t vocab);
+hipError_t launch_attention(const AttnArgs& a, int lds_bytes, hipStream_t s);
+int attention_lds_bytes(int d, int g, int n_lds);
+int attention_plan_n_lds(int d, int g, int cap, int* spill_stride);
+hipError_t launch_ema_rank(const EmaArgs& a, hipStream_t s);
+hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
+hipError_t launch_quantize_step(const QuantArgs& a, hipStream_t s);
+hipError_t launch_prefill(const QuantArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Small device helpers.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+__device__ __forceinline__ int wave_sum_i(int x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+// A (layer, sequence) header the kernels can act on: room for the new token
+// in the metadata and in the FP16 ring, ring bases inside their rings.
+__device__ __forceinline__ bool meta_ok(int n, int n8, int base8, int base16, int cap, int cap16) {
+  return n >= 0 && n8 >= 0 && n8 <= n && n + 1 <= cap && n - n8 + 1 <= cap16 && base8 >= 0 &&
+         base8 < cap && base16 >= 0 && base16 < cap16;
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint16_t b) {
+  return (float)__builtin_bit_cast(_Float16, b);
+}
+__device__ __forceinline__ uint16_t float_to_half_bits(float f) {
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+}  // namespace confk

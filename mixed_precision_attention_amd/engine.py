@@ -1,0 +1,194 @@
+"""Device memory (PyTorch) and the call sequence of one CONF-KV decode step.
+
+Algorithm 1 of the CONF-KV review ("方法步骤详情"): confidence and budget from
+the logits, attention with per-key mass, EMA and rank, eviction/compaction
+with the append of the new token, and quantisation of the token that left
+the FP16 window. Each function below forwards pointers, sizes and the
+current HIP stream to one C-ABI entry point; nothing is computed here.
+"""
+import ctypes
+import dataclasses
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def make_policy(p) -> L.Policy:
+    """C policy struct from any object with tau, alpha, lam, w_h, w_m, w_p,
+    n_high, n_low, protect and window attributes."""
+    return L.Policy(float(p.tau), float(p.alpha), float(p.lam), float(p.w_h), float(p.w_m),
+                    float(p.w_p), int(p.n_high), int(p.n_low), int(p.protect), int(p.window))
+
+
+class DeviceCache:
+    """The cache tensors of include/confk.h, owned by PyTorch."""
+
+    def __init__(self, layers, batch, hq, hkv, d, cap, cap16, device="cuda"):
+        self.layers, self.batch, self.hq, self.hkv, self.d = layers, batch, hq, hkv, d
+        self.cap, self.cap16 = cap, cap16
+        z = lambda shape, dt: torch.zeros(shape, dtype=dt, device=device)  # noqa: E731
+        self.k8 = z((layers, batch, hkv, cap, d), torch.int8)
+        self.v8 = z((layers, batch, hkv, cap, d), torch.int8)
+        self.k16 = z((layers, batch, hkv, cap16, d), torch.float16)
+        self.v16 = z((layers, batch, hkv, cap16, d), torch.float16)
+        self.kscale = z((layers, batch, hkv, d), torch.float32)
+        self.vscale = z((layers, batch, hkv, d), torch.float32)
+        self.ema = z((layers, batch, cap), torch.float32)
+        self.pos = z((layers, batch, cap), torch.int32)
+        self.meta = z((layers, batch, L.META_WORDS), torch.int32)
+        self.status = z((1,), torch.int32)
+        self.struct = L.Cache(layers, batch, hq, hkv, d, cap, cap16,
+                              self.k8.data_ptr(), self.v8.data_ptr(), self.k16.data_ptr(),
+                              self.v16.data_ptr(), self.kscale.data_ptr(), self.vscale.data_ptr(),
+                              self.ema.data_ptr(), self.pos.data_ptr(), self.meta.data_ptr(),
+                              self.status.data_ptr())
+
+    @classmethod
+    def for_config(cls, cfg, device="cuda"):
+        return cls(cfg.layers, cfg.batch, cfg.hq, cfg.hkv, cfg.d, cfg.cap, cfg.policy.window + 1,
+                   device)
+
+    def ref(self):
+        return ctypes.byref(self.struct)
+
+    # -------------------------------------------------------- inspection
+    def lengths(self):
+        m = self.meta.cpu().numpy()
+        return m[..., L.META_N], m[..., L.META_N8]
+
+    def snapshot(self, l, b):
+        """Host copy of one (layer, sequence) in logical order (oldest first)."""
+        m = self.meta[l, b].cpu().numpy()
+        n, n8, b8, b16 = int(m[L.META_N]), int(m[L.META_N8]), int(m[L.META_BASE8]), int(m[L.META_BASE16])
+        f = n - n8
+        i8 = torch.as_tensor((b8 + np.arange(n8)) % self.cap, device=self.k8.device, dtype=torch.long)
+        i16 = torch.as_tensor((b16 + np.arange(f)) % self.cap16, device=self.k8.device, dtype=torch.long)
+        g = lambda t, idx: t[l, b].index_select(1, idx).permute(1, 0, 2).cpu().numpy()  # noqa: E731
+        return dict(
+            n=n, n8=n8, base8=b8, base16=b16, calibrated=bool(m[L.META_CALIB]),
+            saturated=int(m[L.META_SAT]), evicted=int(m[L.META_EVICTED]), moved=int(m[L.META_MOVED]),
+            k8=g(self.k8, i8), v8=g(self.v8, i8), k16=g(self.k16, i16), v16=g(self.v16, i16),
+            ks=self.kscale[l, b].cpu().numpy(), vs=self.vscale[l, b].cpu().numpy(),
+            ema=self.ema[l, b, :n].cpu().numpy(), pos=self.pos[l, b, :n].cpu().numpy(),
+        )
+
+
+# ------------------------------------------------------------------ calls
+
+def confidence(logits, pol, c_out, budget_out, status, ws, layer_n_high=None, layer_n_low=None):
+    lib = L.load()
+    nbl = 1 if layer_n_high is None else int(layer_n_high.numel())
+    L.check("confk_confidence", lib.confk_confidence(
+        _p(logits), logits.stride(0), logits.shape[0], logits.shape[1], ctypes.byref(pol),
+        _p(layer_n_high), _p(layer_n_low), nbl, _p(c_out), _p(budget_out), _p(status),
+        _p(ws), ws.numel() * ws.element_size(), _stream()))
+
+
+def attn_decode(cache, q, k_new, v_new, out, mass, ws, layer0=0, nlayers=None):
+    lib = L.load()
+    nl = cache.layers - layer0 if nlayers is None else nlayers
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    L.check("confk_attn_decode", lib.confk_attn_decode(
+        cache.ref(), layer0, nl, _p(q), _p(k_new), _p(v_new), _p(out), _p(mass), _p(ws), wsb,
+        _stream()))
+
+
+def ema_rank(cache, mass, pol, t, score, layer0=0, nlayers=None):
+    lib = L.load()
+    nl = cache.layers - layer0 if nlayers is None else nlayers
+    L.check("confk_ema_rank", lib.confk_ema_rank(
+        cache.ref(), layer0, nl, _p(mass), ctypes.byref(pol), int(t), _p(score), _stream()))
+
+
+def compact(cache, budget, budget_stride, score, pol, k_new, v_new, evicted=None, layer0=0,
+            nlayers=None):
+    lib = L.load()
+    nl = cache.layers - layer0 if nlayers is None else nlayers
+    L.check("confk_compact", lib.confk_compact(
+        cache.ref(), layer0, nl, _p(budget), int(budget_stride), _p(score), ctypes.byref(pol),
+        _p(k_new), _p(v_new), _p(evicted), _stream()))
+
+
+def quantize(cache, pol, t, mode=L.QUANT_STEP, k_src=None, v_src=None, n_src=0, layer0=0,
+             nlayers=None):
+    lib = L.load()
+    nl = cache.layers - layer0 if nlayers is None else nlayers
+    L.check("confk_quantize", lib.confk_quantize(
+        cache.ref(), layer0, nl, int(t), ctypes.byref(pol), int(mode), _p(k_src), _p(v_src),
+        int(n_src), _stream()))
+
+
+def workspace_bytes(which, cache=None, nlayers=0, batch=0, vocab=0):
+    lib = L.load()
+    ref = cache.ref() if cache is not None else None
+    return int(lib.confk_workspace_size(which, ref, nlayers, batch, vocab))
+
+
+class DecodeEngine:
+    """Buffers of one decode step for a workload config, and the step itself."""
+
+    def __init__(self, cfg, device="cuda"):
+        self.cfg = cfg
+        self.pol = make_policy(cfg.policy)
+        self.cache = DeviceCache.for_config(cfg, device)
+        Lr, B = cfg.layers, cfg.batch
+        self.layer_n_low = self.layer_n_high = None
+        nbl = 1
+        if cfg.layer_n_low is not None:
+            self.layer_n_low = torch.tensor(cfg.layer_n_low, dtype=torch.int32, device=device)
+            self.layer_n_high = torch.tensor(cfg.layer_n_high, dtype=torch.int32, device=device)
+            nbl = Lr
+            # the host checks capacity and protection against the largest budgets
+            self.pol = make_policy(dataclasses.replace(
+                cfg.policy, n_low=max(cfg.layer_n_low), n_high=max(cfg.layer_n_high)))
+        self.budget_stride = B if nbl > 1 else 0
+        self.c = torch.zeros(B, dtype=torch.float32, device=device)
+        self.budget = torch.zeros((nbl, B), dtype=torch.int32, device=device)
+        cws = workspace_bytes(L.WS_CONFIDENCE, batch=B, vocab=cfg.vocab)
+        self.conf_ws = torch.zeros(max(cws, 4), dtype=torch.uint8, device=device)
+        aws = workspace_bytes(L.WS_ATTENTION, self.cache, nlayers=Lr)
+        self.attn_ws = torch.zeros(aws, dtype=torch.uint8, device=device) if aws else None
+        self.out = torch.zeros((Lr, B, cfg.hq, cfg.d), dtype=torch.float16, device=device)
+        self.mass = torch.zeros((Lr, B, cfg.hkv, cfg.cap), dtype=torch.float32, device=device)
+        self.score = torch.zeros((Lr, B, cfg.cap), dtype=torch.float32, device=device)
+        self.evicted = torch.zeros((Lr, B), dtype=torch.int32, device=device)
+
+    def prefill(self, k_src, v_src):
+        """k_src, v_src fp16 [L, B, Hkv, L0, d] on the device (L0 may be 0)."""
+        n_src = 0 if k_src is None else k_src.shape[3]
+        quantize(self.cache, self.pol, 0, L.QUANT_PREFILL, k_src, v_src, n_src)
+
+    # the five calls of one step, in the order of the method
+    def step_confidence(self, logits):
+        confidence(logits, self.pol, self.c, self.budget, self.cache.status, self.conf_ws,
+                   self.layer_n_high, self.layer_n_low)
+
+    def step_attention(self, q, k_new, v_new):
+        attn_decode(self.cache, q, k_new, v_new, self.out, self.mass, self.attn_ws)
+
+    def step_ema_rank(self, t):
+        ema_rank(self.cache, self.mass, self.pol, t, self.score)
+
+    def step_compact(self, k_new, v_new):
+        compact(self.cache, self.budget, self.budget_stride, self.score, self.pol, k_new, v_new,
+                self.evicted)
+
+    def step_quantize(self, t):
+        quantize(self.cache, self.pol, t)
+
+    def step(self, logits, q, k_new, v_new, t):
+        self.step_confidence(logits)
+        self.step_attention(q, k_new, v_new)
+        self.step_ema_rank(t)
+        self.step_compact(k_new, v_new)
+        self.step_quantize(t)

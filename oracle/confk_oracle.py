@@ -351,6 +351,29 @@ class StepOut:
     caches: list               # [L][B] -> SeqCache after the step
 
 
+def step_one(cache, q, k_new, v_new, t, pol, N, score_given=None):
+    """Steps 1-2 and 5-13 of Algorithm 1 for one (layer, sequence) with budget N.
+
+    Returns dict(o, mass, ema, a_new, score, keep, cache) where ema is the
+    updated EMA of the cached tokens and cache the state after the step.
+    Order (reading S1): attention over C plus the new token; EMA update;
+    rank; evict and compact; append the new token; quantise tokens that left
+    the FP16 window. score_given replaces the computed scores in the
+    selection (lock-step comparison on identical inputs).
+    """
+    o, m = attention(q, cache, k_new, v_new)
+    a, a_new = ema_update(cache.ema, m, pol.lam)
+    s = rank_scores(a, cache.pos, pol.alpha)
+    s_sel = s if score_given is None else np.asarray(score_given, np.float64)
+    kp = select_keep(s_sel, cache.pos, N, pol.protect)
+    c1 = cache.copy()
+    c1.ema = a
+    c1 = compact(c1, kp)
+    c1 = append(c1, k_new, v_new, t, a_new)
+    c1 = quantize_window(c1, t, pol.window)
+    return dict(o=o, mass=m, ema=a, a_new=a_new, score=s, keep=kp, cache=c1)
+
+
 def step(caches, logits, q, k_new, v_new, t, pol, layer_budgets=None,
          c_given=None, score_given=None):
     """One CONF-KV decode step over every (layer, sequence).
@@ -363,10 +386,6 @@ def step(caches, logits, q, k_new, v_new, t, pol, layer_budgets=None,
     Lock-step hooks: c_given [B] replaces the computed confidence in the
     budget decision and score_given[l][b] replaces the computed scores in the
     selection (so that integer decisions are compared on identical inputs).
-
-    Order (reading S1): confidence and budget; attention over C plus the new
-    token; EMA update; rank; evict and compact; append the new token;
-    quantise tokens that left the FP16 window.
     """
     L, B = len(caches), len(caches[0])
     cs = np.zeros(B)
@@ -382,22 +401,15 @@ def step(caches, logits, q, k_new, v_new, t, pol, layer_budgets=None,
         nh, nl = pol.n_high, pol.n_low
         if layer_budgets is not None:
             nl, nh = layer_budgets[0][l], layer_budgets[1][l]
-        row_m, row_e, row_s, row_k, row_c = [], [], [], [], []
+        row = [[], [], [], [], []]
         for b in range(B):
             N = budget(cdec[b], pol.tau, nh, nl)
             budgets[l, b] = N
-            c0 = caches[l][b]
-            o[l, b], m = attention(q[l, b], c0, k_new[l, b], v_new[l, b])
-            a, a_new = ema_update(c0.ema, m, pol.lam)
-            s = rank_scores(a, c0.pos, pol.alpha)
-            s_sel = s if score_given is None else np.asarray(score_given[l][b], np.float64)
-            kp = select_keep(s_sel, c0.pos, N, pol.protect)
-            c1 = c0.copy()
-            c1.ema = a
-            c1 = compact(c1, kp)
-            c1 = append(c1, k_new[l, b], v_new[l, b], t, a_new)
-            c1 = quantize_window(c1, t, pol.window)
-            a_news[l, b] = a_new
-            row_m.append(m); row_e.append(a); row_s.append(s); row_k.append(kp); row_c.append(c1)
-        mass.append(row_m); ema.append(row_e); score.append(row_s); keep.append(row_k); new.append(row_c)
+            sg = None if score_given is None else score_given[l][b]
+            r = step_one(caches[l][b], q[l, b], k_new[l, b], v_new[l, b], t, pol, N, sg)
+            o[l, b] = r["o"]
+            a_news[l, b] = r["a_new"]
+            for lst, key in zip(row, ("mass", "ema", "score", "keep", "cache")):
+                lst.append(r[key])
+        mass.append(row[0]); ema.append(row[1]); score.append(row[2]); keep.append(row[3]); new.append(row[4])
     return StepOut(cs, st, budgets, o, mass, ema, a_news, score, keep, new)

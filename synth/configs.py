@@ -44,9 +44,14 @@ class Config:
 
     @property
     def cap(self) -> int:
-        """Token capacity per (layer, sequence): the largest cache before a step, plus one."""
+        """Token slots per (layer, sequence).
+
+        A cache holds at most max(prefill, N_low + 1) tokens before a step
+        (after a step it holds at most N + 1), and the step needs one more
+        slot for the new token.
+        """
         n_low = max(self.layer_n_low) if self.layer_n_low else self.policy.n_low
-        return max(self.prefill, n_low) + 1
+        return max(self.prefill, n_low + 1) + 1
 
     @property
     def group(self) -> int:

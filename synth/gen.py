@@ -59,3 +59,41 @@ def prefill_kv(cfg, seed: int, layer0: int = 0, nlayers: int = None):
         out_k[i] = r.standard_normal(shape[1:], dtype=np.float32).astype(np.float16)
         out_v[i] = r.standard_normal(shape[1:], dtype=np.float32).astype(np.float16)
     return out_k, out_v
+
+
+def prefill_kv_device(cfg, seed: int, device, layer0: int = 0, nlayers: int = None):
+    """Prefill K/V, fp16 [nl,B,Hkv,L0,d] N(0,1), drawn on the device with a
+    seeded torch generator (fast for the large workloads). The oracle reads
+    the same tensors back through a host copy."""
+    import torch
+    nl = cfg.layers - layer0 if nlayers is None else nlayers
+    shape = (cfg.batch, cfg.hkv, cfg.prefill, cfg.d)
+    k = torch.empty((nl,) + shape, dtype=torch.float16, device=device)
+    v = torch.empty((nl,) + shape, dtype=torch.float16, device=device)
+    gen = torch.Generator(device=device)
+    for i in range(nl):
+        gen.manual_seed(seed * 1_000_003 + (layer0 + i) * 7919 + 1)
+        k[i] = torch.randn(shape, generator=gen, device=device, dtype=torch.float32).half()
+        v[i] = torch.randn(shape, generator=gen, device=device, dtype=torch.float32).half()
+    return k, v
+
+
+def decode_inputs_device(cfg, seed: int, step: int, device):
+    """q, k_new, v_new for one step drawn on the device (throughput runs)."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed * 1_000_003 + step * 104729 + 2)
+    L, B = cfg.layers, cfg.batch
+    q = torch.randn((L, B, cfg.hq, cfg.d), generator=gen, device=device).half()
+    k = torch.randn((L, B, cfg.hkv, cfg.d), generator=gen, device=device).half()
+    v = torch.randn((L, B, cfg.hkv, cfg.d), generator=gen, device=device).half()
+    return q, k, v
+
+
+def logits_device(cfg, seed: int, step: int, device):
+    """fp32 [B, V] logits N(0, s_b) drawn on the device, s_b from logit_scale()."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed * 1_000_003 + step * 15485863 + 3)
+    s = torch.as_tensor(logit_scale(cfg, seed, step), dtype=torch.float32, device=device)
+    return torch.randn((cfg.batch, cfg.vocab), generator=gen, device=device) * s[:, None]

@@ -1,0 +1,140 @@
+"""CPU checks of the C-ABI library: it loads, exports every declared entry
+point, and rejects bad arguments before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixed_precision_attention_amd as M
+from mixed_precision_attention_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "confk.h")
+
+
+def declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(confk_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_header_declares_the_five_calls():
+    names = declared()
+    for n in ("confk_confidence", "confk_attn_decode", "confk_ema_rank", "confk_compact", "confk_quantize"):
+        assert n in names
+    assert set(names) == set(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in declared():
+        assert hasattr(lib, n), n
+    assert lib.confk_version() == 100
+    assert lib.confk_strerror(-1) == b"invalid argument"
+    assert lib.confk_strerror(12345) == b"unknown error"
+
+
+def test_struct_layout_matches_header():
+    # 7 int32 dims, 4 bytes padding, 10 pointers
+    assert ctypes.sizeof(_lib.Cache) == 7 * 4 + 4 + 10 * 8
+    assert _lib.Cache.k8.offset == 32
+    assert ctypes.sizeof(_lib.Policy) == 10 * 4
+
+
+def _fake_cache(**kw):
+    dims = dict(layers=2, batch=3, hq=10, hkv=2, d=128, cap=100, cap16=65)
+    dims.update(kw)
+    c = _lib.Cache(dims["layers"], dims["batch"], dims["hq"], dims["hkv"], dims["d"], dims["cap"],
+                   dims["cap16"], *([0x1000] * 10))
+    return c
+
+
+def _pol(**kw):
+    p = dict(tau=0.7, alpha=0.65, lam=0.9, w_h=0.4, w_m=0.3, w_p=0.3, n_high=24, n_low=48,
+             protect=8, window=64)
+    p.update(kw)
+    return _lib.Policy(p["tau"], p["alpha"], p["lam"], p["w_h"], p["w_m"], p["w_p"], p["n_high"],
+                       p["n_low"], p["protect"], p["window"])
+
+
+FAKE = ctypes.c_void_p(0x1000)
+
+
+def test_confidence_validation(lib):
+    pol = _pol()
+    ok_args = dict(logits=FAKE, ld=10, batch=2, vocab=10, nbl=1, ws=FAKE, wsb=1 << 20)
+
+    def call(**kw):
+        a = dict(ok_args)
+        a.update(kw)
+        return lib.confk_confidence(a["logits"], a["ld"], a["batch"], a["vocab"], ctypes.byref(pol),
+                                    None, None, a["nbl"], FAKE, FAKE, None, a["ws"], a["wsb"], None)
+    assert call(logits=None) == M.ERR_INVALID_ARG
+    assert call(vocab=1) == M.ERR_INVALID_ARG
+    assert call(ld=5) == M.ERR_INVALID_ARG
+    assert call(batch=0) == M.ERR_INVALID_ARG
+    assert call(nbl=2) == M.ERR_INVALID_ARG          # per-layer count without arrays
+    assert call(ws=None) == M.ERR_WORKSPACE
+    assert call(wsb=4) == M.ERR_WORKSPACE
+    assert lib.confk_confidence(FAKE, 10, 2, 10, ctypes.byref(pol), FAKE, None, 2, FAKE, FAKE, None,
+                                FAKE, 1 << 20, None) == M.ERR_INVALID_ARG
+
+
+def test_attention_validation(lib):
+    c = _fake_cache()
+    r = lambda cc, l0=0, nl=2, ws=FAKE, wsb=1 << 30: lib.confk_attn_decode(  # noqa: E731
+        ctypes.byref(cc), l0, nl, FAKE, FAKE, FAKE, FAKE, FAKE, ws, wsb, None)
+    assert r(_fake_cache(d=96)) == M.ERR_UNSUPPORTED
+    assert r(_fake_cache(hq=40, hkv=2)) == M.ERR_UNSUPPORTED     # group of 20 > 16
+    assert r(_fake_cache(hq=9, hkv=2)) == M.ERR_INVALID_ARG      # not a multiple
+    assert r(c, l0=1, nl=2) == M.ERR_INVALID_ARG
+    assert r(c, nl=0) == M.ERR_INVALID_ARG
+    bad = _fake_cache()
+    bad.meta = None
+    assert r(bad) == M.ERR_INVALID_ARG
+    assert lib.confk_attn_decode(ctypes.byref(c), 0, 2, None, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) \
+        == M.ERR_INVALID_ARG
+
+
+def test_attention_workspace_needed_only_for_long_caches(lib):
+    small = _fake_cache(cap=300)
+    assert lib.confk_workspace_size(M._lib.WS_ATTENTION, ctypes.byref(small), 2, 0, 0) == 0
+    big = _fake_cache(cap=40000, hq=40, hkv=8)
+    need = lib.confk_workspace_size(M._lib.WS_ATTENTION, ctypes.byref(big), 2, 0, 0)
+    assert need > 0
+    assert lib.confk_attn_decode(ctypes.byref(big), 0, 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 4,
+                                 None) == M.ERR_WORKSPACE
+    assert lib.confk_workspace_size(M._lib.WS_CONFIDENCE, None, 0, 8, 152064) == 8 * 38 * 6 * 4
+
+
+def test_compact_quantize_ema_validation(lib):
+    c = _fake_cache(cap=100, cap16=65)
+    pol = _pol()
+    cp = lambda cc, p, stride=0: lib.confk_compact(  # noqa: E731
+        ctypes.byref(cc), 0, 2, FAKE, stride, FAKE, ctypes.byref(p), FAKE, FAKE, None, None)
+    assert cp(c, _pol(protect=30)) == M.ERR_BUDGET             # P > N_high
+    assert cp(c, _pol(n_low=99)) == M.ERR_BUDGET               # no slot for N_low + 1 + new
+    assert cp(c, _pol(window=64), stride=5) == M.ERR_INVALID_ARG
+    assert cp(c, _pol(window=80)) == M.ERR_BUDGET              # FP16 ring too small
+    assert cp(c, _pol(lam=1.5)) == M.ERR_INVALID_ARG
+    q = lambda mode, n_src=10, k=FAKE: lib.confk_quantize(  # noqa: E731
+        ctypes.byref(c), 0, 2, 0, ctypes.byref(pol), mode, k, FAKE, n_src, None)
+    assert q(7) == M.ERR_INVALID_ARG
+    assert q(M.QUANT_PREFILL, n_src=100) == M.ERR_BUDGET
+    assert q(M.QUANT_PREFILL, k=None) == M.ERR_INVALID_ARG
+    assert q(M.QUANT_PREFILL, n_src=-1) == M.ERR_INVALID_ARG
+    assert lib.confk_ema_rank(ctypes.byref(c), 0, 2, FAKE, ctypes.byref(pol), -1, FAKE, None) \
+        == M.ERR_INVALID_ARG
+    assert lib.confk_ema_rank(ctypes.byref(c), 0, 2, None, ctypes.byref(pol), 3, FAKE, None) \
+        == M.ERR_INVALID_ARG
+
+
+def test_binding_raises_on_error_code():
+    with pytest.raises(M.ConfkError) as e:
+        M.check("confk_compact", M.ERR_BUDGET)
+    assert e.value.code == M.ERR_BUDGET

@@ -1,0 +1,267 @@
+"""GPU parity: every C-ABI call against the fp64 oracle on seeded inputs.
+
+Protocol: the oracle runs free. It builds its own cache from the same seeded
+prefill, computes its own confidence, attention, EMA and scores in fp64, and
+takes its own decisions; the device runs the five calls on the same inputs.
+After every step the two are compared:
+  - budget choice, survivor positions and order, INT8 codes, scales and
+    FP16 rows: bit-exact. A confidence within 1e-5 of tau lies in the
+    rounding band where both budgets are correct; such steps (counted, and
+    expected to be rare) follow the device's choice.
+  - attention output: max |o - o_ref| <= 2e-3 * max |o_ref| per (layer, seq).
+  - confidence, per-key mass, EMA and rank scores: absolute error <= 1e-5.
+Selection compares fp32 device scores with fp64 oracle scores; a mismatch is
+reported with the score gap at the eviction boundary.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import confk_oracle as O
+from tests.helpers import assert_state_equal, rel_maxabs
+
+pytestmark = pytest.mark.gpu
+
+ATOL = 1e-5
+OTOL = 2e-3
+
+
+def _dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import mixed_precision_attention_amd as M
+    M.load()  # raises if the HIP library is missing
+    return torch.device("cuda")
+
+
+def _cfg(name, layers, batch, hq, hkv, d, vocab, prefill, n_high, n_low, protect, window, **kw):
+    pol = synth.Policy(n_high=n_high, n_low=n_low, protect=protect, window=window)
+    return synth.Config(name=name, layers=layers, batch=batch, hq=hq, hkv=hkv, d=d, vocab=vocab,
+                        prefill=prefill, steps=0, policy=pol, **kw)
+
+
+# Small shapes spanning several 16-key tiles with ragged tails.
+TINY = {
+    "g5_d128": _cfg("g5_d128", 2, 3, 10, 2, 128, 1000, 300, 96, 200, 16, 64),
+    "mha_d64": _cfg("mha_d64", 2, 2, 4, 4, 64, 777, 150, 40, 80, 8, 32),
+    "g3_d64_empty": _cfg("g3_d64_empty", 1, 2, 6, 2, 64, 333, 0, 24, 48, 8, 16, sinks=2),
+    "g16_d128": _cfg("g16_d128", 1, 2, 16, 1, 128, 500, 90, 40, 70, 4, 20),
+}
+
+
+def _t(x, dev):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+
+def _inputs(cfg, seed, i):
+    logits = synth.logits_for_step(cfg, seed, i)
+    q, kn, vn = synth.decode_inputs(cfg, seed, i)
+    t = cfg.prefill + i
+    if cfg.sinks:
+        kn = synth.gen.apply_sinks(cfg, seed, t, kn)
+    return logits, q, kn, vn, t
+
+
+class Run:
+    """Device engine plus the oracle states of the checked (layer, seq) pairs."""
+
+    def __init__(self, cfg, seed, pairs=None, device_prefill=False):
+        import mixed_precision_attention_amd as M
+        self.dev = _dev()
+        self.cfg, self.seed = cfg, seed
+        self.pairs = pairs or [(l, b) for l in range(cfg.layers) for b in range(cfg.batch)]
+        self.eng = M.DecodeEngine(cfg, self.dev)
+        self.band = 0
+        W = cfg.policy.window
+        if cfg.prefill == 0:
+            self.eng.prefill(None, None)
+            self.orc = {p: O.empty_cache(cfg.hkv, cfg.d) for p in self.pairs}
+        elif device_prefill:
+            kp, vp = synth.gen.prefill_kv_device(cfg, seed, self.dev)
+            self.eng.prefill(kp, vp)
+            self.orc = {(l, b): O.prefill(kp[l, b].cpu().numpy(), vp[l, b].cpu().numpy(), W)
+                        for (l, b) in self.pairs}
+            del kp, vp
+        else:
+            kp, vp = synth.prefill_kv(cfg, seed)
+            self.eng.prefill(_t(kp, self.dev), _t(vp, self.dev))
+            self.orc = {(l, b): O.prefill(kp[l, b], vp[l, b], W) for (l, b) in self.pairs}
+        torch.cuda.synchronize()
+        for (l, b) in self.pairs:
+            assert_state_equal(self.eng.cache.snapshot(l, b), self.orc[(l, b)],
+                               what=f"prefill l={l} b={b}")
+
+    def budgets(self, l):
+        cfg = self.cfg
+        if cfg.layer_n_low is not None:
+            return cfg.layer_n_low[l], cfg.layer_n_high[l]
+        return cfg.policy.n_low, cfg.policy.n_high
+
+    def step(self, i, scores=None):
+        """One step on both sides; `scores` optionally replaces the rank scores
+        (same array on both sides) to exercise selection with crafted ties."""
+        cfg, eng, dev, pol = self.cfg, self.eng, self.dev, self.cfg.policy
+        logits, q, kn, vn, t = _inputs(cfg, self.seed, i)
+        lg, qd, kd, vd = _t(logits, dev), _t(q, dev), _t(kn, dev), _t(vn, dev)
+        eng.step_confidence(lg)
+        c_dev = eng.c.cpu().numpy().astype(np.float64)
+        bud_dev = eng.budget.cpu().numpy()
+        eng.step_attention(qd, kd, vd)
+        out = eng.out.float().cpu().numpy()
+        mass = eng.mass.cpu().numpy()
+        eng.step_ema_rank(t)
+        ema = eng.cache.ema.cpu().numpy()
+        if scores is not None:
+            eng.score.copy_(_t(scores, dev))
+        score = eng.score.cpu().numpy()
+        eng.step_compact(kd, vd)
+        eng.step_quantize(t)
+        torch.cuda.synchronize()
+        assert int(eng.cache.status.cpu()[0]) == 0, "device status set"
+        evicted = eng.evicted.cpu().numpy()
+        events = 0
+        c_ref = np.zeros(cfg.batch)
+        for b in range(cfg.batch):
+            c_ref[b] = O.confidence(logits[b])[0]
+            assert abs(c_dev[b] - c_ref[b]) <= ATOL, f"step {i} b={b}: confidence {c_dev[b]} vs {c_ref[b]}"
+        for (l, b) in self.pairs:
+            w = f"step {i} l={l} b={b}"
+            nl, nh = self.budgets(l)
+            N = O.budget(c_ref[b], pol.tau, nh, nl)
+            got_N = int(bud_dev[l if bud_dev.shape[0] > 1 else 0, b])
+            if got_N != N:
+                assert abs(c_ref[b] - pol.tau) <= ATOL, f"{w}: budget {got_N} vs {N}, c={c_ref[b]}"
+                self.band += 1
+                N = got_N
+            pre = self.orc[(l, b)]
+            n = pre.n
+            sg = None if scores is None else scores[l, b, :n]
+            r = O.step_one(pre, q[l, b], kn[l, b], vn[l, b], t, pol, N, score_given=sg)
+            assert rel_maxabs(out[l, b], r["o"]) <= OTOL, f"{w}: attention output"
+            m = mass[l, b, :, : n + 1].sum(0) / cfg.hq
+            assert np.abs(m - r["mass"]).max() <= ATOL, f"{w}: mass"
+            assert np.abs(ema[l, b, :n] - r["ema"]).max(initial=0) <= ATOL, f"{w}: EMA"
+            assert abs(ema[l, b, n] - r["a_new"]) <= ATOL, f"{w}: new-token EMA"
+            if scores is None:
+                assert np.abs(score[l, b, :n] - r["score"]).max(initial=0) <= ATOL, f"{w}: score"
+            snap = eng.cache.snapshot(l, b)
+            want_pos = r["cache"].pos
+            if not np.array_equal(snap["pos"].astype(np.int64), want_pos):
+                s = r["score"] if sg is None else sg
+                ev = np.sort(s[~r["keep"]])
+                kp = np.sort(s[: max(0, n - pol.protect)][r["keep"][: max(0, n - pol.protect)]])
+                gap = (kp[0] - ev[-1]) if len(ev) and len(kp) else float("nan")
+                raise AssertionError(f"{w}: survivors differ (boundary score gap {gap:.3e})")
+            assert evicted[l, b] == int((~r["keep"]).sum()), f"{w}: evicted count"
+            assert_state_equal(snap, r["cache"], what=w)
+            self.orc[(l, b)] = r["cache"]
+            events += int(evicted[l, b] > 0)
+        return events
+
+
+@pytest.mark.parametrize("name", list(TINY))
+def test_parity_tiny(name):
+    cfg = TINY[name]
+    steps = 70 if cfg.prefill == 0 else 24
+    print(f"[parity] {name} steps={steps}", flush=True)
+    run = Run(cfg, seed=11)
+    events = sum(run.step(i) for i in range(steps))
+    assert events > 0
+    assert run.band <= 1
+
+
+def test_parity_pyramid_budgets():
+    lo = (60, 52, 44)
+    hi = tuple(x // 2 for x in lo)
+    cfg = _cfg("pyr", 3, 2, 10, 2, 128, 600, 120, max(hi), max(lo), 8, 24,
+               layer_n_low=lo, layer_n_high=hi)
+    print("[parity] pyramid", flush=True)
+    run = Run(cfg, seed=5)
+    for i in range(12):
+        run.step(i)
+    n, _ = run.eng.cache.lengths()
+    for l in range(3):
+        assert (n[l] <= lo[l] + 1).all()
+
+
+def test_selection_with_tied_scores():
+    """Crafted scores with heavy ties (same array on both sides)."""
+    cfg = TINY["g5_d128"]
+    print("[parity] tied scores", flush=True)
+    run = Run(cfg, seed=4)
+    rng = np.random.default_rng(9)
+    for i in range(8):
+        s = (rng.integers(0, 3, size=(cfg.layers, cfg.batch, cfg.cap)) / 2.0).astype(np.float32)
+        run.step(i, scores=s)
+
+
+def test_confidence_closed_forms_and_flags():
+    import mixed_precision_attention_amd as M
+    dev = _dev()
+    V, B = 152064, 8
+    rng = np.random.default_rng(3)
+    z = np.zeros((B, V), np.float32)
+    z[0] = 1.25                                          # uniform
+    z[1] = -np.inf; z[1, 777] = 3.0                       # one-hot
+    z[2] = -np.inf; z[2, [5, 9, 100]] = 0.5               # 3-way tie
+    z[3] = rng.standard_normal(V) * 8
+    z[4] = rng.standard_normal(V) * 0.5
+    z[5] = rng.standard_normal(V); z[5, 17] = np.nan      # flagged
+    z[6] = -np.inf                                        # flagged
+    z[7] = rng.standard_normal(V); z[7, 3] = np.inf       # flagged
+    pol = M.make_policy(synth.Policy(n_high=1024, n_low=2048))
+    c = torch.zeros(B, device=dev)
+    bud = torch.zeros((1, B), dtype=torch.int32, device=dev)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = torch.zeros(M.engine.workspace_bytes(M._lib.WS_CONFIDENCE, batch=B, vocab=V),
+                     dtype=torch.uint8, device=dev)
+    M.confidence(_t(z, dev), pol, c, bud, st, ws)
+    torch.cuda.synchronize()
+    c = c.cpu().numpy()
+    bud = bud.cpu().numpy()[0]
+    assert abs(c[0] - (0.15 + 0.3 / V)) <= ATOL
+    assert abs(c[1] - 1.0) <= ATOL
+    assert abs(c[2] - (0.4 * (1 - np.log(3) / np.log(V)) + 0.15 + 0.1)) <= ATOL
+    for b in (3, 4):
+        assert abs(c[b] - O.confidence(z[b])[0]) <= ATOL
+    assert np.isnan(c[5:]).all() and (bud[5:] == 2048).all()
+    assert int(st.cpu()[0]) & M.STATUS_NONFINITE_LOGITS
+    for b in range(5):
+        assert bud[b] == O.budget(O.confidence(z[b])[0], 0.7, 1024, 2048)
+
+
+@pytest.mark.parametrize("V", [7, 4096, 4097, 50257])
+def test_confidence_ragged_vocab(V):
+    import mixed_precision_attention_amd as M
+    dev = _dev()
+    B = 5
+    rng = np.random.default_rng(V)
+    z = (rng.standard_normal((B, V + 3)) * rng.choice([0.5, 2, 8], size=(B, 1))).astype(np.float32)
+    pol = M.make_policy(synth.Policy())
+    c = torch.zeros(B, device=dev)
+    bud = torch.zeros((1, B), dtype=torch.int32, device=dev)
+    ws = torch.zeros(M.engine.workspace_bytes(M._lib.WS_CONFIDENCE, batch=B, vocab=V),
+                     dtype=torch.uint8, device=dev)
+    zt = _t(z, dev)[:, :V]   # row stride V+3 (ld > vocab)
+    M.confidence(zt, pol, c, bud, None, ws)
+    torch.cuda.synchronize()
+    for b in range(B):
+        assert abs(float(c[b]) - O.confidence(z[b, :V])[0]) <= ATOL
+
+
+def test_qwen32b_shape_two_layers():
+    cfg = synth.get_config("qwen32b").with_(layers=2)
+    print(f"[parity] qwen32b 2 layers cap={cfg.cap}", flush=True)
+    run = Run(cfg, seed=1, pairs=[(0, 0), (0, 5), (1, 3), (1, 7)], device_prefill=True)
+    for i in range(3):
+        run.step(i)
+
+
+def test_qwen32b_full_launch_sampled():
+    """All 64 layers x batch 8 in the benchmark's launch configuration;
+    three (layer, sequence) pairs checked against the oracle."""
+    cfg = synth.get_config("qwen32b")
+    print(f"[parity] qwen32b full cap={cfg.cap}", flush=True)
+    run = Run(cfg, seed=2, pairs=[(0, 0), (31, 4), (63, 7)], device_prefill=True)
+    for i in range(2):
+        run.step(i)
