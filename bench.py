@@ -1,0 +1,250 @@
+#!/usr/bin/env python3
+"""Throughput of the CONF-KV decode step on one MI355X.
+
+One step = the whole hot path over one batch: confidence + budget, decode
+attention with fused INT8 dequantisation and per-key mass, EMA + rank,
+eviction + compaction + append, FP16 -> INT8 window quantisation, for every
+layer and sequence. Workload: Qwen-32B shape (64 layers, 40 query / 8 KV
+heads, d 128), batch 8, 2048-token prefill, V = 152064, N_high/N_low =
+1024/2048, P = 64, W = 256; seeded synthetic inputs resident in HBM before
+the timed region.
+
+Byte accounting: the steps are deterministic, so an untimed pass from the
+same prefill records every step's cache lengths and row moves; the timed
+pass replays the same steps. Bytes are the algorithmic bytes of the method
+(INT8 codes 2*Hkv*d per token, FP16 rows 4*Hkv*d, scales, q/o, mass,
+metadata 16 B/token, moved rows read+write, quantised rows, logits).
+
+Prints one JSON line.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=48)
+    ap.add_argument("--config", default="qwen32b")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="CPU time budget of the oracle baseline sample (0 disables it)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after the run, one plain device copy of this size (counter scaling)")
+    return ap.parse_args()
+
+
+def step_bytes(cfg, n, n8, moved8, moved16, quantised):
+    """Algorithmic bytes of one step from the pre-step lengths [L, B]."""
+    H, d, Hq = cfg.hkv, cfg.d, cfg.hq
+    f = n - n8
+    attn = (H * d * (2 * n8 + 4 * (f + 1)) + 8 * H * d + 4 * Hq * d + 4 * (n + 1)).sum()
+    meta = (16 * n).sum()
+    comp = (2 * (moved8 * 2 * H * d + moved16 * 4 * H * d)).sum() + 8 * H * d * n.size
+    quant = 6 * H * d * quantised.sum()
+    conf = 4 * cfg.batch * cfg.vocab
+    return dict(attn=int(attn), meta=int(meta), compact=int(comp), quant=int(quant), conf=int(conf),
+                total=int(attn + meta + comp + quant + conf))
+
+
+def cpu_baseline(cfg, kp, vp, logits0, q0, kn0, vn0, budget_s):
+    """Oracle (fp64 numpy) on the first decode step after the prefill, over
+    as many (layer, sequence) pairs as fit the time budget; extrapolated to
+    the whole step."""
+    import numpy as np
+    from oracle import confk_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    pol = cfg.policy
+    t0 = time.perf_counter()
+    cs = [O.confidence(logits0[b])[0] for b in range(cfg.batch)]
+    t_conf = time.perf_counter() - t0
+    rng = np.random.default_rng(0)
+    pairs = [(int(l), int(b)) for l, b in zip(rng.integers(0, cfg.layers, 64), rng.integers(0, cfg.batch, 64))]
+    done, t_pairs = 0, 0.0
+    for (l, b) in pairs:
+        c = O.prefill(kp[l, b].cpu().numpy(), vp[l, b].cpu().numpy(), pol.window)
+        N = O.budget(cs[b], pol.tau, pol.n_high, pol.n_low)
+        t1 = time.perf_counter()
+        O.step_one(c, q0[l, b], kn0[l, b], vn0[l, b], cfg.prefill, pol, N)
+        t_pairs += time.perf_counter() - t1
+        done += 1
+        if t_pairs + t_conf >= budget_s:
+            break
+    per_step = t_conf + t_pairs / done * cfg.layers * cfg.batch
+    return dict(per_step_s=per_step, pairs=done, threads=threads)
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus N > 1 is not supported",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mixed_precision_attention_amd as M
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    cfg = synth.get_config(args.config)
+    pol = cfg.policy
+    K, Wm = args.steps, args.warmup
+    S = K + Wm
+
+    eng = M.DecodeEngine(cfg, dev)
+    kp, vp = synth.gen.prefill_kv_device(cfg, args.seed, dev)
+    inputs = []
+    for s in range(S):
+        lg = synth.gen.logits_device(cfg, args.seed, s, dev)
+        q, kn, vn = synth.gen.decode_inputs_device(cfg, args.seed, s, dev)
+        inputs.append((lg, q, kn, vn, cfg.prefill + s))
+    torch.cuda.synchronize()
+
+    # ---- untimed pass: per-step lengths and moves for the byte count
+    eng.prefill(kp, vp)
+    per_step = []
+    evict_frac = []
+    for s in range(S):
+        lg, q, kn, vn, t = inputs[s]
+        m0 = eng.cache.meta.cpu().numpy()
+        eng.step_confidence(lg)
+        eng.step_attention(q, kn, vn)
+        eng.step_ema_rank(t)
+        eng.step_compact(kn, vn)
+        m1 = eng.cache.meta.cpu().numpy()
+        eng.step_quantize(t)
+        m2 = eng.cache.meta.cpu().numpy()
+        evict_frac.append(float((m1[..., M.META_EVICTED] > 0).mean()))
+        per_step.append(step_bytes(
+            cfg, m0[..., M.META_N].astype(np.int64), m0[..., M.META_N8].astype(np.int64),
+            m1[..., M.META_MOVED].astype(np.int64), m1[..., M.META_MOVED16].astype(np.int64),
+            (m2[..., M.META_N8] - m1[..., M.META_N8]).astype(np.int64)))
+    torch.cuda.synchronize()
+    status = int(eng.cache.status.cpu()[0])
+    n_end = eng.cache.meta[..., M.META_N].float()
+    len_mean = float(n_end.mean())
+
+    # ---- timed pass: same steps from the same prefill
+    eng.prefill(kp, vp)
+    for s in range(Wm):
+        lg, q, kn, vn, t = inputs[s]
+        eng.step(lg, q, kn, vn, t)
+    torch.cuda.synchronize()
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    ev = [(E(), E(), E(), E()) for _ in range(K)]
+    start, stop = E(), E()
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(K):
+        lg, q, kn, vn, t = inputs[Wm + i]
+        a0, a1, c0, c1 = ev[i]
+        eng.step_confidence(lg)
+        a0.record(stream)
+        eng.step_attention(q, kn, vn)
+        a1.record(stream)
+        eng.step_ema_rank(t)
+        c0.record(stream)
+        eng.step_compact(kn, vn)
+        c1.record(stream)
+        eng.step_quantize(t)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    attn_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    comp_ms = [e[2].elapsed_time(e[3]) for e in ev]
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    timed = per_step[Wm:]
+    bytes_total = sum(p["total"] for p in timed)
+    attn_bytes = sum(p["attn"] for p in timed) / K
+    ms_per_step = total_ms / K
+    value = bytes_total / (total_ms * 1e-3) / 1e9
+    attn_avg_ms = sum(attn_ms) / K
+    achieved = attn_bytes / (attn_avg_ms * 1e-3) / 1e9
+    comp_avg_ms = sum(comp_ms) / K
+
+    out = {
+        "metric": "decode-step KV GB/s (% HBM peak) + steps/s, Qwen-32B-shape batch 8",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8+f16 (f32 accumulate)",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: {cfg.layers} layers, {cfg.hq}/{cfg.hkv} heads, d{cfg.d}, "
+                        f"batch {cfg.batch}, {cfg.prefill}-token prefill, V={cfg.vocab}, "
+                        f"N_high/N_low={pol.n_high}/{pol.n_low}, P={pol.protect}, W={pol.window}",
+            "layers": cfg.layers, "batch": cfg.batch, "hq": cfg.hq, "hkv": cfg.hkv, "d": cfg.d,
+            "prefill": cfg.prefill, "vocab": cfg.vocab, "parallelism": "single GPU",
+        },
+        "steps_per_s": round(1000.0 / ms_per_step, 2),
+        "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
+        "bytes_per_step": int(bytes_total / K),
+        "attn_ms": round(attn_avg_ms, 5),
+        "compact_ms": round(comp_avg_ms, 5),
+        "compact_share": round(comp_avg_ms / ms_per_step, 4),
+        "mean_len_end": round(len_mean, 1),
+        "eviction_frac": round(sum(evict_frac[Wm:]) / K, 4),
+        "status": status,
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel": "attn_decode_kernel<128>",
+            "bytes_per_launch": int(attn_bytes),
+        },
+    }
+    if args.cpu_seconds > 0:
+        lg0, q0, kn0, vn0, _ = inputs[0]
+        cb = cpu_baseline(cfg, kp, vp, lg0.cpu().numpy(), q0.cpu().numpy(), kn0.cpu().numpy(),
+                          vn0.cpu().numpy(), args.cpu_seconds)
+        step0 = per_step[0]["total"]
+        out["cpu_baseline"] = {
+            "value": round(step0 / cb["per_step_s"] / 1e9, 4),
+            "unit": "GB/s",
+            "cores": cb["threads"],
+            "kind": "oracle",
+            "sample": f"first decode step after the prefill: confidence of all {cfg.batch} rows plus "
+                      f"{cb['pairs']} of {cfg.layers * cfg.batch} (layer, sequence) pairs, "
+                      f"extrapolated to the whole step",
+            "steps_per_s": round(1.0 / cb["per_step_s"], 5),
+        }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -64,8 +64,9 @@ extern "C" {
 #define CONFK_META_CALIB 4   /* 1 once the INT8 scales are set                  */
 #define CONFK_META_SAT 5     /* INT8 codes clamped at +-127 so far              */
 #define CONFK_META_EVICTED 6 /* tokens evicted by the last confk_compact        */
-#define CONFK_META_MOVED 7   /* K/V rows moved by the last confk_compact        */
-#define CONFK_META_WORDS 8
+#define CONFK_META_MOVED 7   /* INT8 tokens moved by the last confk_compact     */
+#define CONFK_META_MOVED16 8 /* FP16 tokens moved by the last confk_compact     */
+#define CONFK_META_WORDS 16
 
 /* ---- confk_quantize modes ---------------------------------------------- */
 #define CONFK_QUANT_STEP 0    /* move the token that left the FP16 window     */

@@ -124,6 +124,7 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
       atomicOr(c.status, (uint32_t)CONFK_STATUS_CAPACITY);
       meta[CONFK_META_EVICTED] = 0;
       meta[CONFK_META_MOVED] = 0;
+      meta[CONFK_META_MOVED16] = 0;
       if (a.evicted_out) a.evicted_out[lb] = 0;
     }
     return;
@@ -280,7 +281,7 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
     __syncthreads();
   };
 
-  int moved = 0;
+  int moved8 = 0, moved16 = 0;
   if (k > 0) {
     // ------------------------------------------------- 3. metadata, ascending
     int have_w0 = -1;
@@ -387,7 +388,7 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
         }
         __syncthreads();
       }
-      moved += r.movers;
+      (is8 ? moved8 : moved16) += r.movers;
     }
   }
 
@@ -423,7 +424,8 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
     meta[CONFK_META_BASE8] = b8;
     meta[CONFK_META_BASE16] = b16;
     meta[CONFK_META_EVICTED] = k;
-    meta[CONFK_META_MOVED] = moved;
+    meta[CONFK_META_MOVED] = moved8;
+    meta[CONFK_META_MOVED16] = moved16;
     if (a.evicted_out) a.evicted_out[lb] = k;
   }
 }

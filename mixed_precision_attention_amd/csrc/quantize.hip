@@ -155,6 +155,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(QuantArgs a) {
       meta[CONFK_META_SAT] = 0;
       meta[CONFK_META_EVICTED] = 0;
       meta[CONFK_META_MOVED] = 0;
+      meta[CONFK_META_MOVED16] = 0;
       if (lb == 0) *c.status = 0u;
     }
   }
