@@ -122,6 +122,7 @@ def main():
     eng.prefill(kp, vp)
     per_step = []
     evict_frac = []
+    moved_rows = []
     for s in range(S):
         lg, q, kn, vn, t = inputs[s]
         m0 = eng.cache.meta.cpu().numpy()
@@ -133,6 +134,9 @@ def main():
         eng.step_quantize(t)
         m2 = eng.cache.meta.cpu().numpy()
         evict_frac.append(float((m1[..., M.META_EVICTED] > 0).mean()))
+        if s >= Wm:
+            ev_mask = m1[..., M.META_EVICTED] > 0
+            moved_rows.extend((m1[..., M.META_MOVED] + m1[..., M.META_MOVED16])[ev_mask].tolist())
         per_step.append(step_bytes(
             cfg, m0[..., M.META_N].astype(np.int64), m0[..., M.META_N8].astype(np.int64),
             m1[..., M.META_MOVED].astype(np.int64), m1[..., M.META_MOVED16].astype(np.int64),
@@ -216,6 +220,8 @@ def main():
         "compact_share": round(comp_avg_ms / ms_per_step, 4),
         "mean_len_end": round(len_mean, 1),
         "eviction_frac": round(sum(evict_frac[Wm:]) / K, 4),
+        "moved_rows_per_event": (round(float(np.mean(moved_rows)), 1) if moved_rows else 0.0),
+        "moved_rows_p90": (int(np.percentile(moved_rows, 90)) if moved_rows else 0),
         "status": status,
         "roofline": {
             "bound": "hbm",

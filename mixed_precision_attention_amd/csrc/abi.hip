@@ -82,6 +82,7 @@ int confk_confidence(const float* logits, int64_t ld, int32_t batch, int32_t voc
   a.batch = batch;
   a.vocab = vocab;
   a.nbl = nbl;
+  a.vec4 = (ld % 4 == 0) && (((uintptr_t)logits & 15) == 0);
   a.tau = pol->tau;
   a.w_h = pol->w_h;
   a.w_m = pol->w_m;

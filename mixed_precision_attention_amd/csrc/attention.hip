@@ -26,9 +26,15 @@
 // power of two into fp16's normal range), so the fp32 scores carry ~22 bits;
 // the probabilities fed to the second product are fp16.
 //
+// Memory pipeline: each wave walks every 4th 16-key tile of a region and
+// holds two tiles of raw K/V in registers, loading tile t+4 while tile t is
+// converted and multiplied. Tail rows are clamped to a valid row (their
+// scores are masked), so loads carry no branches.
+//
 // Mass: the log2-domain scores are kept in LDS (or a global spill area for
-// very long caches); once the waves' running maxima and normalisers are
-// merged, each key's mass sum_h 2^(s_h - M_h) / L_h is formed exactly.
+// caches too long for the LDS budget); once the waves' running maxima and
+// normalisers are merged, each key's mass sum_h 2^(s_h - M_h) / L_h is
+// formed exactly.
 #include "confk_internal.h"
 
 namespace confk {
@@ -45,6 +51,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kScoreLdsBytes = 24 * 1024;  // LDS budget for the score tile store
 
 // Two INT8 codes (bytes b0/b1 or b2/b3 of x = codes ^ 0x80808080) -> two fp16.
 // perm places each biased code under an 0x64 exponent byte: fp16 value
@@ -85,7 +92,6 @@ struct Tile {
 // Physical d of element j of chunk kc in the query/key operands of lane
 // group kg. INT8 rows: each lane reads 16 contiguous bytes per 64-byte half
 // of the row; FP16 rows: 8 contiguous halves per chunk.
-template <int D>
 __device__ __forceinline__ int d_int8(int kc, int kg) {
   return (kc >> 1) * 64 + 16 * kg + 8 * (kc & 1);
 }
@@ -102,7 +108,7 @@ __device__ __forceinline__ float build_q(const uint16_t* qrow, const float* ksca
   float mx = 0.f;
 #pragma unroll
   for (int kc = 0; kc < KC; ++kc) {
-    const int d0 = INT8 ? d_int8<D>(kc, kg) : d_fp16(kc, kg);
+    const int d0 = INT8 ? d_int8(kc, kg) : d_fp16(kc, kg);
     if (active) {
       const u32x4 raw = *reinterpret_cast<const u32x4*>(qrow + d0);
       const half8_t h = as_half8(raw);
@@ -170,8 +176,23 @@ __device__ __forceinline__ half4_t softmax_tile(float4_t s, SoftState& st, float
   return p;
 }
 
+// Raw registers of one 16-key INT8 tile of this lane.
 template <int D>
-__global__ __launch_bounds__(kThreads) void attn_decode_kernel(AttnArgs a) {
+struct Raw8 {
+  u32x4 k[Tile<D>::KU];         // K row r16: 16 bytes per 64-byte half
+  uint32_t v[4][Tile<D>::CB / 4];  // V rows 4kg+j: D/16 bytes at channel (D/16)*r16
+};
+
+// Raw registers of one 16-key FP16 tile of this lane.
+template <int D>
+struct Raw16 {
+  u32x4 k[Tile<D>::KC];            // K row r16: 8 halves per chunk
+  uint32_t v[4][Tile<D>::CB / 2];  // V rows 4kg+j: D/16 halves at channel (D/16)*r16
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
+void attn_decode_kernel(AttnArgs a) {
   constexpr int KC = Tile<D>::KC;
   constexpr int CB = Tile<D>::CB;
   constexpr int KU = Tile<D>::KU;
@@ -241,53 +262,38 @@ __global__ __launch_bounds__(kThreads) void attn_decode_kernel(AttnArgs a) {
   };
 
   // ------------------------------------------------------------ INT8 region
+  auto slot8 = [&](int i) {  // ring slot of INT8 logical index i (clamped to the region)
+    int s = base8 + min(i, n8 - 1);
+    return s >= c.cap ? s - c.cap : s;
+  };
+  auto load8 = [&](Raw8<D>& r, int t) {
+    const int i0 = t * 16;
+    const int8_t* krow = k8 + (size_t)slot8(i0 + r16) * D;
+#pragma unroll
+    for (int uu = 0; uu < KU; ++uu) r.k[uu] = *reinterpret_cast<const u32x4*>(krow + 64 * uu + 16 * kg);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int8_t* vrow = v8 + (size_t)slot8(i0 + 4 * kg + j) * D + (D / 16) * r16;
+      if constexpr (CB == 8) {
+        const u32x2 t2 = *reinterpret_cast<const u32x2*>(vrow);
+        r.v[j][0] = t2[0];
+        r.v[j][1] = t2[1];
+      } else {
+        r.v[j][0] = *reinterpret_cast<const uint32_t*>(vrow);
+      }
+    }
+  };
   if (nt8 > w) {
+    Raw8<D> ra, rb;
+    load8(ra, w);
     half8_t qhi[KC], qlo[KC];
     const float unscale = build_q<D, true>(qrow, ks, head_ok, kg, qhi, qlo);
-    for (int t = w; t < nt8; t += kWaves) {
+    auto tile8 = [&](const Raw8<D>& r, int t) {
       const int i0 = t * 16;
-      // K rows: lane reads key r16
-      u32x4 kx[KU];
-      {
-        const int i = i0 + r16;
-        if (i < n8) {
-          int slot = base8 + i;
-          if (slot >= c.cap) slot -= c.cap;
-          const int8_t* row = k8 + (size_t)slot * D;
-#pragma unroll
-          for (int uu = 0; uu < KU; ++uu)
-            kx[uu] = *reinterpret_cast<const u32x4*>(row + 64 * uu + 16 * kg);
-        } else {
-#pragma unroll
-          for (int uu = 0; uu < KU; ++uu) kx[uu] = (u32x4){0x80808080u, 0x80808080u, 0x80808080u, 0x80808080u};
-        }
-      }
-      // V rows: lane reads keys i0+4kg+j, channels [ (D/16)*r16, +D/16 )
-      uint32_t vx[4][CB / 4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = i0 + 4 * kg + j;
-        if (i < n8) {
-          int slot = base8 + i;
-          if (slot >= c.cap) slot -= c.cap;
-          const int8_t* row = v8 + (size_t)slot * D + (D / 16) * r16;
-          if constexpr (CB == 8) {
-            const u32x2 t2 = *reinterpret_cast<const u32x2*>(row);
-            vx[j][0] = t2[0];
-            vx[j][1] = t2[1];
-          } else {
-            vx[j][0] = *reinterpret_cast<const uint32_t*>(row);
-          }
-        } else {
-#pragma unroll
-          for (int z = 0; z < CB / 4; ++z) vx[j][z] = 0u;
-        }
-      }
-      // scores
       float4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        const u32x4 xw = kx[kc >> 1] ^ 0x80808080u;
+        const u32x4 xw = r.k[kc >> 1] ^ 0x80808080u;
         const int o = 2 * (kc & 1);
         u32x4 hv;
         hv[0] = codes_to_h2(xw[o], kSelLo);
@@ -305,15 +311,22 @@ __global__ __launch_bounds__(kThreads) void attn_decode_kernel(AttnArgs a) {
       }
       store_scores(i0, s);
       const half4_t pT = softmax_tile<CB>(s, st, acc);
-      // P.V
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
         const int wd = cb >> 2, bb = cb & 3;
         u32x2 av;
-        av[0] = code_pair_rows(vx[0][wd], vx[1][wd], bb);
-        av[1] = code_pair_rows(vx[2][wd], vx[3][wd], bb);
+        av[0] = code_pair_rows(r.v[0][wd], r.v[1][wd], bb);
+        av[1] = code_pair_rows(r.v[2][wd], r.v[3][wd], bb);
         acc[cb] = __builtin_amdgcn_mfma_f32_16x16x16f16(as_half4(av), pT, acc[cb], 0, 0, 0);
       }
+    };
+    for (int t = w; t < nt8; t += 2 * kWaves) {
+      const int t1 = t + kWaves;
+      if (t1 < nt8) load8(rb, t1);
+      tile8(ra, t);
+      if (t1 >= nt8) break;
+      if (t1 + kWaves < nt8) load8(ra, t1 + kWaves);
+      tile8(rb, t1);
     }
     // V scales of the INT8 part: channel of acc[cb][v] is CB*(4kg+v)+cb
 #pragma unroll
@@ -323,63 +336,42 @@ __global__ __launch_bounds__(kThreads) void attn_decode_kernel(AttnArgs a) {
   }
 
   // ------------------------------------------------------ FP16 region + new
+  auto row16 = [&](const uint16_t* ring, const uint16_t* nw, int jj) {  // FP16-local index jj
+    if (jj >= f) return nw;  // the new token (also the clamp target of tail rows)
+    int s = base16 + jj;
+    s = s >= c.cap16 ? s - c.cap16 : s;
+    return ring + (size_t)s * D;
+  };
+  auto load16 = [&](Raw16<D>& r, int t) {
+    const int j0 = t * 16;
+    const uint16_t* krow = row16(k16, kn, j0 + r16);
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) r.k[kc] = *reinterpret_cast<const u32x4*>(krow + d_fp16(kc, kg));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint16_t* vrow = row16(v16, vn, j0 + 4 * kg + j) + (D / 16) * r16;
+      if constexpr (CB == 8) {
+        const u32x4 t4 = *reinterpret_cast<const u32x4*>(vrow);
+#pragma unroll
+        for (int z = 0; z < 4; ++z) r.v[j][z] = t4[z];
+      } else {
+        const u32x2 t2 = *reinterpret_cast<const u32x2*>(vrow);
+        r.v[j][0] = t2[0];
+        r.v[j][1] = t2[1];
+      }
+    }
+  };
   if (nt16 > w) {
+    Raw16<D> ra, rb;
+    load16(ra, w);
     half8_t qhi[KC], qlo[KC];
     const float unscale = build_q<D, false>(qrow, nullptr, head_ok, kg, qhi, qlo);
-    for (int t = w; t < nt16; t += kWaves) {
-      const int j0 = t * 16;  // FP16-local index of the tile's first key
-      u32x4 kx[KC];
-      {
-        const int jj = j0 + r16;
-        const uint16_t* row = nullptr;
-        if (jj < f) {
-          int slot = base16 + jj;
-          if (slot >= c.cap16) slot -= c.cap16;
-          row = k16 + (size_t)slot * D;
-        } else if (jj == f) {
-          row = kn;
-        }
-        if (row) {
-#pragma unroll
-          for (int kc = 0; kc < KC; ++kc)
-            kx[kc] = *reinterpret_cast<const u32x4*>(row + d_fp16(kc, kg));
-        } else {
-#pragma unroll
-          for (int kc = 0; kc < KC; ++kc) kx[kc] = (u32x4){0u, 0u, 0u, 0u};
-        }
-      }
-      uint32_t vx[4][CB / 2];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int jj = j0 + 4 * kg + j;
-        const uint16_t* row = nullptr;
-        if (jj < f) {
-          int slot = base16 + jj;
-          if (slot >= c.cap16) slot -= c.cap16;
-          row = v16 + (size_t)slot * D;
-        } else if (jj == f) {
-          row = vn;
-        }
-        if (row) {
-          row += (D / 16) * r16;
-          if constexpr (CB == 8) {
-            const u32x4 t4 = *reinterpret_cast<const u32x4*>(row);
-#pragma unroll
-            for (int z = 0; z < 4; ++z) vx[j][z] = t4[z];
-          } else {
-            const u32x2 t2 = *reinterpret_cast<const u32x2*>(row);
-            vx[j][0] = t2[0];
-            vx[j][1] = t2[1];
-          }
-        } else {
-#pragma unroll
-          for (int z = 0; z < CB / 2; ++z) vx[j][z] = 0u;
-        }
-      }
+    auto tile16 = [&](const Raw16<D>& r, int t) {
+      const int j0 = t * 16;
       float4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        const half8_t ak = as_half8(kx[kc]);
+        const half8_t ak = as_half8(r.k[kc]);
         s = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, qhi[kc], s, 0, 0, 0);
         s = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, qlo[kc], s, 0, 0, 0);
       }
@@ -394,10 +386,18 @@ __global__ __launch_bounds__(kThreads) void attn_decode_kernel(AttnArgs a) {
       for (int cb = 0; cb < CB; ++cb) {
         const int wd = cb >> 1, hf = cb & 1;
         u32x2 av;
-        av[0] = half_pair_rows(vx[0][wd], vx[1][wd], hf);
-        av[1] = half_pair_rows(vx[2][wd], vx[3][wd], hf);
+        av[0] = half_pair_rows(r.v[0][wd], r.v[1][wd], hf);
+        av[1] = half_pair_rows(r.v[2][wd], r.v[3][wd], hf);
         acc[cb] = __builtin_amdgcn_mfma_f32_16x16x16f16(as_half4(av), pT, acc[cb], 0, 0, 0);
       }
+    };
+    for (int t = w; t < nt16; t += 2 * kWaves) {
+      const int t1 = t + kWaves;
+      if (t1 < nt16) load16(rb, t1);
+      tile16(ra, t);
+      if (t1 >= nt16) break;
+      if (t1 + kWaves < nt16) load16(ra, t1 + kWaves);
+      tile16(rb, t1);
     }
   }
 
@@ -468,8 +468,7 @@ static int score_slots(int cap) { return ((cap + 30 + 15) / 16) * 16; }
 
 int attention_plan_n_lds(int d, int g, int cap, int* spill_stride) {
   const int need = score_slots(cap);
-  const int budget = 40 * 1024;  // LDS bytes per workgroup for scores
-  int fit = (budget / (4 * g)) / 16 * 16;
+  int fit = (kScoreLdsBytes / (4 * g)) / 16 * 16;
   const int min_slots = (kWaves * d + 15) / 16 * 16;  // room for the output reduction
   if (fit < min_slots) fit = min_slots;
   if (need <= fit) {

@@ -21,19 +21,22 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kPerThread = 16;
 constexpr int kChunk = kThreads * kPerThread;
+constexpr float kLog2e = 1.4426950408889634f;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// e^d for d <= 0 through the hardware base-2 exponential.
+__device__ __forceinline__ float exp_neg(float d) { return exp2f(d * kLog2e); }
 
 struct RowState {
   float M, S, T, t1, t2;
   uint32_t flag;  // bit 0: NaN or +inf seen
 };
 
+// Inserts x into the two largest values t1 >= t2 of a multiset.
 __device__ __forceinline__ void top2_insert(float& t1, float& t2, float x) {
-  if (x > t1) {
-    t2 = t1;
-    t1 = x;
-  } else if (x > t2) {
-    t2 = x;
-  }
+  const float n2 = fmaxf(t2, fminf(t1, x));
+  t1 = fmaxf(t1, x);
+  t2 = n2;
 }
 
 __device__ __forceinline__ RowState merge(const RowState& a, const RowState& b) {
@@ -46,13 +49,13 @@ __device__ __forceinline__ RowState merge(const RowState& a, const RowState& b) 
   r.T = 0.f;
   if (a.S > 0.f) {
     const float d = a.M - r.M;
-    const float e = expf(d);
+    const float e = exp_neg(d);
     r.S += a.S * e;
     r.T += (a.T + d * a.S) * e;
   }
   if (b.S > 0.f) {
     const float d = b.M - r.M;
-    const float e = expf(d);
+    const float e = exp_neg(d);
     r.S += b.S * e;
     r.T += (b.T + d * b.S) * e;
   }
@@ -78,10 +81,28 @@ __global__ __launch_bounds__(kThreads) void conf_partial_kernel(ConfArgs a) {
   const int end = min(a.vocab, start + a.chunk);
 
   float x[kPerThread];
+  if (a.vec4) {
+    // 16-byte loads: thread t reads groups t, t+256, ... of 4 logits
 #pragma unroll
-  for (int k = 0; k < kPerThread; ++k) {
-    const int i = start + threadIdx.x + k * kThreads;
-    x[k] = (i < end) ? row[i] : -INFINITY;
+    for (int k = 0; k < kPerThread / 4; ++k) {
+      const int i = start + 4 * (threadIdx.x + k * kThreads);
+      if (i + 3 < end) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(row + i);
+        x[4 * k] = v[0];
+        x[4 * k + 1] = v[1];
+        x[4 * k + 2] = v[2];
+        x[4 * k + 3] = v[3];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[4 * k + e] = (i + e < end) ? row[i + e] : -INFINITY;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) {
+      const int i = start + threadIdx.x + k * kThreads;
+      x[k] = (i < end) ? row[i] : -INFINITY;
+    }
   }
   RowState s;
   s.M = -INFINITY;
@@ -106,7 +127,7 @@ __global__ __launch_bounds__(kThreads) void conf_partial_kernel(ConfArgs a) {
       const float v = x[k];
       if (v > -INFINITY && v < INFINITY) {  // finite (NaN fails both)
         const float d = v - s.M;
-        const float e = expf(d);
+        const float e = exp_neg(d);
         s.S += e;
         s.T += d * e;
       }
@@ -132,18 +153,20 @@ __global__ __launch_bounds__(kThreads) void conf_partial_kernel(ConfArgs a) {
   }
 }
 
+// One wave per row: lane i merges partials i, i+64, ... in order, then a
+// butterfly merge (commutative, so every lane ends with the same state).
 __global__ __launch_bounds__(64) void conf_final_kernel(ConfArgs a) {
-  const int b = blockIdx.x * 64 + threadIdx.x;
-  if (b >= a.batch) return;
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x;
   const float* p = a.partial + (int64_t)b * a.nchunks * 6;
   RowState r;
-  r.M = p[0];
-  r.S = p[1];
-  r.T = p[2];
-  r.t1 = p[3];
-  r.t2 = p[4];
-  r.flag = __builtin_bit_cast(uint32_t, p[5]);
-  for (int i = 1; i < a.nchunks; ++i) {
+  r.M = -INFINITY;
+  r.S = 0.f;
+  r.T = 0.f;
+  r.t1 = -INFINITY;
+  r.t2 = -INFINITY;
+  r.flag = 0;
+  for (int i = lane; i < a.nchunks; i += 64) {
     RowState q;
     q.M = p[6 * i + 0];
     q.S = p[6 * i + 1];
@@ -153,6 +176,9 @@ __global__ __launch_bounds__(64) void conf_final_kernel(ConfArgs a) {
     q.flag = __builtin_bit_cast(uint32_t, p[6 * i + 5]);
     r = merge(r, q);
   }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) r = merge(r, shfl_state(r, o));
+  if (lane != 0) return;
   float c;
   const bool bad = r.flag != 0 || !(r.M > -INFINITY);
   if (bad) {
@@ -189,7 +215,7 @@ hipError_t launch_confidence(const ConfArgs& in, hipStream_t s) {
   hipLaunchKernelGGL(conf_partial_kernel, dim3(a.nchunks, a.batch), dim3(kThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(conf_final_kernel, dim3((a.batch + 63) / 64), dim3(64), 0, s, a);
+  hipLaunchKernelGGL(conf_final_kernel, dim3(a.batch), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 

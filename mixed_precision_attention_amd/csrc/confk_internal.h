@@ -36,6 +36,7 @@ struct ConfArgs {
   const float* logits;
   int64_t ld;
   int32_t batch, vocab, chunk, nchunks, nbl;
+  int32_t vec4;  // rows are 16-byte aligned: vector loads
   float tau, w_h, w_m, w_p;
   int32_t n_high, n_low;
   const int32_t* layer_n_high;

@@ -8,13 +8,17 @@
 // the cached tokens, which are stored in ascending position order.
 //
 // One workgroup per (layer, sequence); ~16 bytes per token, memory-bound.
+// For up to kThreads * kPer tokens every thread issues all of its loads at
+// once and keeps the updated EMA and positions in registers for the score
+// pass, so the kernel costs one round trip to memory plus one barrier.
 #include "confk_internal.h"
 
 namespace confk {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
+constexpr int kPer = 8;
 
 __global__ __launch_bounds__(kThreads) void ema_rank_kernel(EmaArgs a) {
   const CacheView& c = a.c;
@@ -32,44 +36,102 @@ __global__ __launch_bounds__(kThreads) void ema_rank_kernel(EmaArgs a) {
   const float inv_hq = 1.f / (float)c.hq;
   const float lam = a.lambda;
   const float oml = 1.f - lam;
+  const int H = c.hkv;
 
   if (!meta_ok(n, meta[CONFK_META_N8], meta[CONFK_META_BASE8], meta[CONFK_META_BASE16], cap,
                c.cap16)) {  // no slot for the new token: flag, leave the state alone
     if (threadIdx.x == 0) atomicOr(c.status, (uint32_t)CONFK_STATUS_CAPACITY);
     return;
   }
+  __shared__ float red[kThreads / 64];
+  __shared__ int pend[2];
 
+  const bool fast = n <= kThreads * kPer;
+  float av[kPer];
+  int pv[kPer];
   float amax = 0.f;
-  for (int i = threadIdx.x; i < n; i += kThreads) {
-    float m = 0.f;
-    for (int j = 0; j < c.hkv; ++j) m += mass[(size_t)j * cap + i];
-    const float v = lam * ema[i] + oml * (m * inv_hq);
-    ema[i] = v;
-    amax = fmaxf(amax, v);
+  if (fast) {
+    float ms[kPer];
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      const int i = threadIdx.x + r * kThreads;
+      ms[r] = 0.f;
+      av[r] = 0.f;
+      pv[r] = 0;
+      if (i < n) {
+        av[r] = ema[i];
+        pv[r] = pos[i];
+      }
+    }
+    // four kv heads' partial masses per round trip, summed in head order
+    for (int j0 = 0; j0 < H; j0 += 4) {
+      float t4[4][kPer];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int r = 0; r < kPer; ++r) {
+          const int i = threadIdx.x + r * kThreads;
+          t4[q][r] = (j0 + q < H && i < n) ? mass[(size_t)(j0 + q) * cap + i] : 0.f;
+        }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int r = 0; r < kPer; ++r)
+          if (j0 + q < H) ms[r] += t4[q][r];
+    }
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      const int i = threadIdx.x + r * kThreads;
+      if (i < n) {
+        av[r] = lam * av[r] + oml * (ms[r] * inv_hq);
+        ema[i] = av[r];
+        amax = fmaxf(amax, av[r]);
+      }
+    }
+  } else {
+    for (int i = threadIdx.x; i < n; i += kThreads) {
+      float m = 0.f;
+      for (int j = 0; j < H; ++j) m += mass[(size_t)j * cap + i];
+      const float v = lam * ema[i] + oml * (m * inv_hq);
+      ema[i] = v;
+      amax = fmaxf(amax, v);
+    }
   }
   if (threadIdx.x == 0) {
     float m = 0.f;
-    for (int j = 0; j < c.hkv; ++j) m += mass[(size_t)j * cap + n];
+    for (int j = 0; j < H; ++j) m += mass[(size_t)j * cap + n];
     ema[n] = oml * (m * inv_hq);
+    pend[0] = n > 0 ? pos[0] : 0;
+    pend[1] = n > 0 ? pos[n - 1] : 0;
     pos[n] = a.t;
   }
   amax = wave_max(amax);
-  __shared__ float red[kThreads / 64];
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
   __syncthreads();
   amax = red[0];
+#pragma unroll
   for (int q = 1; q < kThreads / 64; ++q) amax = fmaxf(amax, red[q]);
   if (n == 0) return;
 
-  const int p0 = pos[0];
-  const int p1 = pos[n - 1];
+  const int p0 = pend[0];
+  const int p1 = pend[1];
   const float inv_a = amax > 0.f ? 1.f / amax : 0.f;
   const float inv_r = p1 > p0 ? 1.f / (float)(p1 - p0) : 0.f;
   const float alpha = a.alpha;
-  for (int i = threadIdx.x; i < n; i += kThreads) {
-    const float ah = ema[i] * inv_a;
-    const float rh = p1 > p0 ? (float)(pos[i] - p0) * inv_r : 1.f;
-    score[i] = alpha * ah + (1.f - alpha) * rh;
+  if (fast) {
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      const int i = threadIdx.x + r * kThreads;
+      if (i < n) {
+        const float rh = p1 > p0 ? (float)(pv[r] - p0) * inv_r : 1.f;
+        score[i] = alpha * (av[r] * inv_a) + (1.f - alpha) * rh;
+      }
+    }
+  } else {
+    for (int i = threadIdx.x; i < n; i += kThreads) {
+      const float rh = p1 > p0 ? (float)(pos[i] - p0) * inv_r : 1.f;
+      score[i] = alpha * (ema[i] * inv_a) + (1.f - alpha) * rh;
+    }
   }
 }
 

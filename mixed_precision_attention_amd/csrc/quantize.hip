@@ -31,7 +31,26 @@ __device__ __forceinline__ int8_t quant_code(float x, float s, int& sat) {
   return (int8_t)r;
 }
 
-// One workgroup per (layer, sequence); threads over (K|V, head, channel).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Codes of 8 consecutive channels (fp16 bits in h) under 8 scales.
+__device__ __forceinline__ u32x2 quant8(u32x4 h, const float* s, int& sat) {
+  u32x2 out = {0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint16_t bits = (uint16_t)(h[e >> 1] >> (16 * (e & 1)));
+    const int8_t q = quant_code(half_bits_to_float(bits), s[e], sat);
+    out[e >> 2] |= (uint32_t)(uint8_t)q << (8 * (e & 3));
+  }
+  return out;
+}
+
+// One workgroup per (layer, sequence); thread e handles 8 consecutive
+// channels of one (K|V, head) row. The oldest FP16 row and its scales are
+// fetched together with its position, so the common case costs two round
+// trips to memory.
 __global__ __launch_bounds__(kThreads) void quantize_step_kernel(QuantArgs a) {
   const CacheView& c = a.c;
   const int lb = blockIdx.x;
@@ -46,7 +65,7 @@ __global__ __launch_bounds__(kThreads) void quantize_step_kernel(QuantArgs a) {
   int calib = meta[CONFK_META_CALIB];
   const int32_t* pos = c.pos + (size_t)lbc * c.cap;
   const int H = c.hkv, D = c.d;
-  const int elems = 2 * H * D;
+  const int groups = 2 * H * D / 8;  // 8-channel groups over (K|V, head)
   // after the append the FP16 ring may hold cap16 tokens, so only check the
   // INT8 side and the ring bases here
   if (n < 0 || n8 < 0 || n8 > n || n > c.cap || n - n8 > c.cap16 || base8 < 0 || base8 >= c.cap ||
@@ -57,11 +76,27 @@ __global__ __launch_bounds__(kThreads) void quantize_step_kernel(QuantArgs a) {
   const int limit = a.t - a.window;
   int sat = 0;
 
-  while (n8 < n && pos[n8] <= limit) {
+  while (n8 < n) {
+    // the oldest FP16 token: its row (speculatively) and its position
+    u32x4 hv[4];
+    int hq_[4];
+    int cnt = 0;
+    for (int e = threadIdx.x; e < groups; e += kThreads, ++cnt) {
+      const int kv = e / (groups / 2);
+      const int r = e - kv * (groups / 2);
+      const int hh = (8 * r) / D;
+      const size_t hrow = (size_t)lbc * H + hh;
+      if (cnt < 4) {
+        hv[cnt] = *reinterpret_cast<const u32x4*>((kv ? c.v16 : c.k16) + (hrow * c.cap16 + base16) * D +
+                                                  (8 * r - hh * D));
+        hq_[cnt] = e;
+      }
+    }
+    if (pos[n8] > limit) break;  // uniform: every thread reads the same word
     const int f = n - n8;
     if (!calib) {
       // scales over every cached token (all FP16 while uncalibrated)
-      for (int e = threadIdx.x; e < elems; e += kThreads) {
+      for (int e = threadIdx.x; e < 2 * H * D; e += kThreads) {
         const int kv = e / (H * D);
         const int hd = e - kv * H * D;
         const int hh = hd / D, ch = hd - hh * D;
@@ -72,25 +107,38 @@ __global__ __launch_bounds__(kThreads) void quantize_step_kernel(QuantArgs a) {
           if (slot >= c.cap16) slot -= c.cap16;
           amax = fmaxf(amax, fabsf(half_bits_to_float(ring[(size_t)slot * D + ch])));
         }
-        float* sc = (kv ? c.vs : c.ks) + ((size_t)lbc * H + hh) * D;
-        sc[ch] = __fdiv_rn(amax, 127.f);
+        (kv ? c.vs : c.ks)[((size_t)lbc * H + hh) * D + ch] = __fdiv_rn(amax, 127.f);
       }
+      __syncthreads();  // scales written by other threads are read below
       calib = 1;
     }
     int dst = base8 + n8;
     if (dst >= c.cap) dst -= c.cap;
-    for (int e = threadIdx.x; e < elems; e += kThreads) {
-      const int kv = e / (H * D);
-      const int hd = e - kv * H * D;
-      const int hh = hd / D, ch = hd - hh * D;
+    int q = 0;
+    for (int e = threadIdx.x; e < groups; e += kThreads, ++q) {
+      const int kv = e / (groups / 2);
+      const int r = e - kv * (groups / 2);
+      const int hh = (8 * r) / D;
+      const int ch = 8 * r - hh * D;
       const size_t hrow = (size_t)lbc * H + hh;
-      const uint16_t* src = (kv ? c.v16 : c.k16) + (hrow * c.cap16 + base16) * D;
-      const float s = (kv ? c.vs : c.ks)[hrow * D + ch];
-      int8_t* q = (kv ? c.v8 : c.k8) + (hrow * c.cap + dst) * D;
-      q[ch] = quant_code(half_bits_to_float(src[ch]), s, sat);
+      const float* sp = (kv ? c.vs : c.ks) + hrow * D + ch;
+      float s8[8];
+      const f32x4 s0 = *reinterpret_cast<const f32x4*>(sp);
+      const f32x4 s1 = *reinterpret_cast<const f32x4*>(sp + 4);
+#pragma unroll
+      for (int z = 0; z < 4; ++z) {
+        s8[z] = s0[z];
+        s8[4 + z] = s1[z];
+      }
+      const u32x4 h = (q < 4 && hq_[q] == e)
+                          ? hv[q]
+                          : *reinterpret_cast<const u32x4*>((kv ? c.v16 : c.k16) +
+                                                            (hrow * c.cap16 + base16) * D + ch);
+      *reinterpret_cast<u32x2*>((kv ? c.v8 : c.k8) + (hrow * c.cap + dst) * D + ch) = quant8(h, s8, sat);
     }
     base16 = base16 + 1 == c.cap16 ? 0 : base16 + 1;
     ++n8;
+    __syncthreads();  // the next iteration reads the ring at the new base
   }
   sat = wave_sum_i(sat);
   __shared__ int red[kThreads / 64];
