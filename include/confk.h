@@ -75,6 +75,7 @@ extern "C" {
 /* ---- confk_workspace_size selectors ------------------------------------ */
 #define CONFK_WS_CONFIDENCE 0
 #define CONFK_WS_ATTENTION 1
+#define CONFK_WS_COMPACT 2
 
 /*
  * Policy (hyper-parameters of the review's "复现评估" section and the
@@ -197,13 +198,17 @@ int confk_ema_rank(const confk_cache* cache, int32_t layer0, int32_t nlayers, co
  *   score        fp32 [nlayers][B][cap] from confk_ema_rank
  *   k_new,v_new  fp16 [nlayers][B][hkv][d]
  *   evicted_out  int32 [nlayers][B] device or NULL: tokens evicted
+ *   ws           >= confk_workspace_size(CONFK_WS_COMPACT, ...) bytes: the
+ *                move plans (and, above 4096 tokens per sequence, metadata
+ *                staging); contents need no initialisation
  * Sets CONFK_STATUS_CAPACITY (and skips the append) if a sequence has no
- * free slot. Errors: INVALID_ARG, BUDGET (protect > n_low or > n_high).
+ * free slot. Errors: INVALID_ARG, BUDGET (protect > n_low or > n_high,
+ * capacity below n_low + 2, FP16 ring below window + 1), WORKSPACE.
  */
 int confk_compact(const confk_cache* cache, int32_t layer0, int32_t nlayers, const int32_t* budget,
                   int32_t budget_layer_stride, const float* score, const confk_policy* pol,
-                  const uint16_t* k_new, const uint16_t* v_new, int32_t* evicted_out,
-                  void* stream);
+                  const uint16_t* k_new, const uint16_t* v_new, int32_t* evicted_out, void* ws,
+                  size_t ws_bytes, void* stream);
 
 /*
  * confk_quantize -- FP16 -> INT8 storage per (head, channel).
@@ -227,8 +232,9 @@ int confk_quantize(const confk_cache* cache, int32_t layer0, int32_t nlayers, in
                    const uint16_t* v_src, int32_t n_src, void* stream);
 
 /* Workspace bytes needed by confk_confidence (which = CONFK_WS_CONFIDENCE;
- * uses batch, vocab) or confk_attn_decode (CONFK_WS_ATTENTION; uses the cache
- * dims and nlayers). Returns 0 when none is needed. */
+ * uses batch, vocab), confk_attn_decode (CONFK_WS_ATTENTION) or confk_compact
+ * (CONFK_WS_COMPACT; both use the cache dims and nlayers). Returns 0 when
+ * none is needed. */
 size_t confk_workspace_size(int32_t which, const confk_cache* cache, int32_t nlayers,
                             int32_t batch, int32_t vocab);
 

@@ -29,6 +29,7 @@ QUANT_STEP = 0
 QUANT_PREFILL = 1
 WS_CONFIDENCE = 0
 WS_ATTENTION = 1
+WS_COMPACT = 2
 
 EXPORTS = [
     "confk_confidence", "confk_attn_decode", "confk_ema_rank", "confk_compact",
@@ -81,7 +82,8 @@ def load():
     lib.confk_ema_rank.argtypes = [P(Cache), c_int32, c_int32, c_void_p, P(Policy), c_int32,
                                    c_void_p, c_void_p]
     lib.confk_compact.argtypes = [P(Cache), c_int32, c_int32, c_void_p, c_int32, c_void_p,
-                                  P(Policy), c_void_p, c_void_p, c_void_p, c_void_p]
+                                  P(Policy), c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                                  c_void_p]
     lib.confk_quantize.argtypes = [P(Cache), c_int32, c_int32, c_int32, P(Policy), c_int32,
                                    c_void_p, c_void_p, c_int32, c_void_p]
     lib.confk_workspace_size.argtypes = [c_int32, P(Cache), c_int32, c_int32, c_int32]

@@ -55,6 +55,10 @@ size_t confk_workspace_size(int32_t which, const confk_cache* cache, int32_t nla
     if (batch < 1 || vocab < 1) return 0;
     return confidence_ws_bytes(batch, vocab);
   }
+  if (which == CONFK_WS_COMPACT) {
+    if (!cache || nlayers < 1 || cache->cap < 2) return 0;
+    return compact_ws_bytes(nlayers, cache->batch, cache->cap);
+  }
   if (which == CONFK_WS_ATTENTION) {
     if (!cache || nlayers < 1 || cache->hkv < 1 || cache->hq % cache->hkv) return 0;
     const int g = cache->hq / cache->hkv;
@@ -143,7 +147,8 @@ int confk_ema_rank(const confk_cache* cache, int32_t layer0, int32_t nlayers, co
 
 int confk_compact(const confk_cache* cache, int32_t layer0, int32_t nlayers, const int32_t* budget,
                   int32_t budget_layer_stride, const float* score, const confk_policy* pol,
-                  const uint16_t* k_new, const uint16_t* v_new, int32_t* evicted_out, void* stream) {
+                  const uint16_t* k_new, const uint16_t* v_new, int32_t* evicted_out, void* ws,
+                  size_t ws_bytes, void* stream) {
   if (!cache_ok(cache) || !layers_ok(cache, layer0, nlayers)) return CONFK_ERR_INVALID_ARG;
   if (!budget || !score || !k_new || !v_new || !policy_ok(pol)) return CONFK_ERR_INVALID_ARG;
   if (budget_layer_stride != 0 && budget_layer_stride != cache->batch) return CONFK_ERR_INVALID_ARG;
@@ -151,7 +156,11 @@ int confk_compact(const confk_cache* cache, int32_t layer0, int32_t nlayers, con
   if (pol->protect > pol->n_high || pol->protect > pol->n_low) return CONFK_ERR_BUDGET;
   if (pol->n_low + 1 > cache->cap - 1 || pol->n_high + 1 > cache->cap - 1) return CONFK_ERR_BUDGET;
   if (pol->window + 1 > cache->cap16) return CONFK_ERR_BUDGET;
+  const size_t need = compact_ws_bytes(nlayers, cache->batch, cache->cap);
+  if (!ws || ws_bytes < need) return CONFK_ERR_WORKSPACE;
   CompactArgs a{};
+  a.plan = (int32_t*)ws;
+  a.stage = (int32_t*)((char*)ws + compact_plan_bytes(nlayers, cache->batch, cache->cap));
   a.c = view_of(cache);
   a.layer0 = layer0;
   a.nl = nlayers;

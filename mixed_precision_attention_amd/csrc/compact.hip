@@ -7,26 +7,30 @@
 // (Algorithm 1): if |C_l| > N evict the lowest-ranked unprotected tokens and
 // compact the survivors; step 13 appends the new K/V in FP16.
 //
-// One workgroup per (layer, sequence); thread t owns a contiguous run of
-// logical indices. For caches of up to 4096 tokens the run's scores are read
-// once into registers; longer caches re-read them from memory.
-//  1. k = n - N tokens leave, chosen among the n - P oldest. A 4-pass radix
-//     select over order-preserving uint32 images of the fp32 scores finds the
-//     k-th smallest score T; every candidate below T leaves, plus the oldest
-//     ties at T (a prefix count in position order), which makes the evicted
-//     set unique: the k smallest (score, position) pairs.
-//  2. One block scan gives each survivor its new logical index; the survivor
-//     list (new index -> old index) is kept in LDS.
-//  3. EMA / position metadata are rewritten densely in place.
-//  4. K/V rows move inside their rings. Each region (INT8 ring, FP16 ring)
-//     is packed toward the end that moves fewer rows: keep the base and
-//     shift the survivors after the first hole down, or advance the base and
-//     shift the survivors before the last hole up. Evictions mostly hit old
-//     tokens, so usually only a few rows move. Moves go in rounds (read all
-//     rows of a round, barrier, write them) in an order that never
-//     overwrites an unread source.
-//  5. The new token's K/V rows are written to the FP16 ring.
-// Steps without eviction only append.
+// Two kernels.
+//
+// Plan (one workgroup per (layer, sequence)); thread t owns a contiguous run
+// of logical indices:
+//  1. k = n - N tokens leave, chosen among the n - P oldest: exactly the k
+//     smallest 64-bit keys (order-preserving image of the fp32 score, logical
+//     index); the index is position order, so equal scores evict the older
+//     token first. The k-th key is found from a 1024-bucket histogram of the
+//     monotone bucket floor(score * 1024) (clamped), then by ranking the few
+//     keys of the boundary bucket; a radix select on the score bits covers
+//     crowded buckets and long caches.
+//  2. Ballot bit-plane scans give each survivor its new logical index and
+//     each region (INT8 ring, FP16 ring) its eviction count and first / last
+//     hole, behind one barrier.
+//  3. EMA / position metadata are rewritten densely in place (every thread
+//     read its run before the first barrier).
+//  4. Each region is packed toward the end that moves fewer rows: keep the
+//     base and shift the survivors after the first hole down, or advance the
+//     base and shift the survivors before the last hole up. The movers'
+//     sources go to a plan in the workspace.
+// Move (one workgroup per (layer, sequence, kv head, K|V) ring): the planned
+// rows move in rounds (read all rows of a round, barrier, write them) in an
+// order that never overwrites an unread source; then the new token's row is
+// written to the FP16 ring.
 #include "confk_internal.h"
 
 namespace confk {
@@ -35,111 +39,141 @@ namespace {
 
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
-constexpr int kWin = 8192;                // survivor-list entries held in LDS at once
-constexpr int kMetaPer = kWin / kThreads;  // metadata entries per thread per window
-constexpr int kRegs = 8;                  // 16-byte row pieces per thread per move round
-constexpr int kRegKeys = 8;               // scores per thread kept in registers
+constexpr int kRegKeys = 8;    // indices per thread held in registers
+constexpr int kBuckets = 1024;
+constexpr int kRankMax = 64;   // boundary-bucket keys ranked by one wave
+constexpr int kHdr = 16;       // plan header words per (layer, sequence)
+constexpr int kMoveThreads = 256;
+constexpr int kMoveRegs = 4;   // 16-byte pieces per thread per round
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// plan header words
+enum { H_MOV8 = 0, H_LEFT8, H_E8, H_JLO8, H_MOV16, H_LEFT16, H_E16, H_JLO16, H_BASE8, H_BASE16,
+       H_APPEND };
+
+// Order-preserving uint32 image of an fp32 score; NaN sorts above +inf
+// (0xFFFFFFFF stays free as the "not a candidate" key).
 __device__ __forceinline__ uint32_t ord_bits(float f) {
+  if (f != f) return 0xFFFFFFFEu;
   const uint32_t u = __builtin_bit_cast(uint32_t, f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-constexpr int kSmallK = 32;  // evictions up to this count use the minima select
+// Monotone (non-decreasing) bucket of a score; NaN goes to the top.
+__device__ __forceinline__ int bucket_of(float s) {
+  if (!(s >= 0.f)) return s < 0.f ? 0 : kBuckets - 1;
+  const float x = s * (float)kBuckets;
+  return x >= (float)(kBuckets - 1) ? kBuckets - 1 : (int)x;
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int lane = threadIdx.x & 63;
+  return lane ? (~0ull >> (64 - lane)) : 0ull;
+}
+
+// Wave exclusive prefix and total of small non-negative counts (< 16).
+__device__ __forceinline__ int wave_prefix16(int x, int& total) {
+  const uint64_t lt = lanemask_lt();
+  int pre = 0, tot = 0;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const uint64_t m = __ballot((x >> b) & 1);
+    pre += __popcll(m & lt) << b;
+    tot += __popcll(m) << b;
+  }
+  total = tot;
+  return pre;
+}
 
 struct Shared {
-  int tmp[4][kWaves];
-  uint32_t hist[256];
-  uint32_t sel_digit, sel_before;
-  uint64_t wk[kWaves][kSmallK];  // each wave's smallest keys
+  uint32_t hist[kBuckets];
+  int wsum[3][kWaves];  // per-wave keeps, e8, e16
+  int wfirst[2][kWaves], wlast[2][kWaves];
+  uint64_t rank_keys[kRankMax];
+  int rank_n;
+  int sel_bucket, sel_below, sel_crowded;
   uint64_t kth;
+  uint32_t sel_digit, sel_before;
 };
 
-// Exclusive block scan of x[0..3] at once; totals in tot[0..3].
-__device__ __forceinline__ void block_scan4(const int* x, int* excl, int* tot, Shared& sh) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int incl[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    incl[q] = x[q];
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(incl[q], o, 64);
-      if (lane >= o) incl[q] += y;
-    }
-    if (lane == 63) sh.tmp[q][w] = incl[q];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    int base = 0, t = 0;
-#pragma unroll
-    for (int z = 0; z < kWaves; ++z) {
-      const int v = sh.tmp[q][z];
-      base += (z < w) ? v : 0;
-      t += v;
-    }
-    excl[q] = base + incl[q] - x[q];
-    tot[q] = t;
-  }
-  __syncthreads();
-}
-
-// Block minimum of x[0..3] (maxima are passed negated).
-__device__ __forceinline__ void block_min4(int* x, Shared& sh) {
-  const int w = threadIdx.x >> 6;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x[q] = min(x[q], __shfl_xor(x[q], o, 64));
-    if ((threadIdx.x & 63) == 0) sh.tmp[q][w] = x[q];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    int r = sh.tmp[q][0];
-#pragma unroll
-    for (int z = 1; z < kWaves; ++z) r = min(r, sh.tmp[q][z]);
-    x[q] = r;
-  }
-  __syncthreads();
-}
-
 struct Region {
-  int rs, m;     // first logical index, tokens before the step
-  int e;         // evicted
-  int first_ev;  // logical index of the first / last evicted token
-  int last_ev;
-  int js;        // new logical index of the region's first survivor
-  bool left;     // pack toward the base (true) or toward the end (false)
-  int movers;
+  int rs, m, e, first_ev, last_ev;
+  int left, movers, jlo;
 };
 
 __device__ __forceinline__ void plan_region(Region& r) {
-  if (r.e == 0) {
-    r.left = true;
-    r.movers = 0;
-    return;
-  }
+  r.left = 1;
+  r.movers = 0;
+  r.jlo = 0;
+  if (r.e == 0) return;
   const int mk = r.m - r.e;                           // survivors
   const int cost_l = mk - (r.first_ev - r.rs);        // survivors after the first hole
   const int cost_r = (r.last_ev - r.rs) - (r.e - 1);  // survivors before the last hole
   r.left = cost_l <= cost_r;
   r.movers = r.left ? cost_l : cost_r;
+  r.jlo = r.left ? (r.first_ev - r.rs) : 0;
+}
+
+// Radix select of the kk-th smallest 32-bit key among the candidates; leaves
+// in kk how many keys equal to the result are selected.
+template <bool REG, typename KeyAt>
+__device__ uint32_t radix_select(int& kk, int cnt, int lo, int ncand, const uint32_t* kreg,
+                                 KeyAt key_at, Shared& sh) {
+  uint32_t prefix = 0, mask = 0;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    if (threadIdx.x < 256) sh.hist[threadIdx.x] = 0;
+    __syncthreads();
+    if constexpr (REG) {
+#pragma unroll
+      for (int j = 0; j < kRegKeys; ++j)
+        if (j < cnt && lo + j < ncand && (kreg[j] & mask) == prefix)
+          atomicAdd(&sh.hist[(kreg[j] >> shift) & 255u], 1u);
+    } else {
+      for (int j = 0; j < cnt; ++j) {
+        const uint32_t key = key_at(j);
+        if (lo + j < ncand && (key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      const int lane = threadIdx.x;
+      const uint32_t h0 = sh.hist[4 * lane], h1 = sh.hist[4 * lane + 1], h2 = sh.hist[4 * lane + 2],
+                     h3 = sh.hist[4 * lane + 3];
+      const int s = (int)(h0 + h1 + h2 + h3);
+      int incl = s;
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+      }
+      const int excl = incl - s;
+      if (excl < kk && kk <= incl) {
+        const int c0 = excl + (int)h0, c1 = c0 + (int)h1, c2 = c1 + (int)h2;
+        const int q = c0 >= kk ? 0 : (c1 >= kk ? 1 : (c2 >= kk ? 2 : 3));
+        sh.sel_digit = (uint32_t)(4 * lane + q);
+        sh.sel_before = (uint32_t)(q == 0 ? excl : (q == 1 ? c0 : (q == 2 ? c1 : c2)));
+      }
+    }
+    __syncthreads();
+    prefix |= sh.sel_digit << shift;
+    mask |= 0xFFu << shift;
+    kk -= (int)sh.sel_before;
+  }
+  return prefix;
 }
 
 template <bool REG>
-__global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
+__global__ __launch_bounds__(kThreads) void compact_plan_kernel(CompactArgs a) {
   const CacheView& c = a.c;
   const int lb = blockIdx.x;
   const int l = lb / c.B;
   const int b = lb - l * c.B;
   const int lbc = (a.layer0 + l) * c.B + b;
   const int cap = c.cap;
-  const int H = c.hkv, D = c.d;
   int32_t* meta = c.meta + lbc * CONFK_META_WORDS;
+  int32_t* hdr = a.plan + (size_t)lb * (kHdr + 2 * (size_t)cap);
+  int32_t* src8 = hdr + kHdr;
+  int32_t* src16 = src8 + cap;
   const int n = meta[CONFK_META_N];
   const int n8 = meta[CONFK_META_N8];
   const int base8 = meta[CONFK_META_BASE8];
@@ -149,20 +183,19 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
   float* ema = c.ema + (size_t)lbc * cap;
   int32_t* pos = c.pos + (size_t)lbc * cap;
   const float* score = a.score + (size_t)lb * cap;
-
-  extern __shared__ int lds_i[];
-  int* S = lds_i;                                // [kWin] survivor list window
-  uint32_t* evbits = (uint32_t*)(lds_i + kWin);  // [(cap + 31) / 32] eviction flags
   __shared__ Shared sh;
 
   const int nn = n + 1;  // tokens incl. the new one
   const int f = n - n8;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   if (!meta_ok(n, n8, base8, base16, cap, c.cap16)) {  // no room: flag, leave the cache as it is
     if (threadIdx.x == 0) {
       atomicOr(c.status, (uint32_t)CONFK_STATUS_CAPACITY);
       meta[CONFK_META_EVICTED] = 0;
       meta[CONFK_META_MOVED] = 0;
       meta[CONFK_META_MOVED16] = 0;
+      hdr[H_MOV8] = hdr[H_MOV16] = 0;
+      hdr[H_APPEND] = -1;
       if (a.evicted_out) a.evicted_out[lb] = 0;
     }
     return;
@@ -170,353 +203,280 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
   const int k = n > N ? n - N : 0;
   const int ncand = n - P;  // candidates: logical [0, ncand)
 
-  // the new token's rows: 16-byte pieces over (K|V, head, d); each thread's
-  // first piece is read now, the rest (large head counts only) at the append
-  const int half_pieces = H * D / 8;
-  auto app_src = [&](int e) {
-    const int kv = e / half_pieces, r = e - kv * half_pieces;
-    return reinterpret_cast<const u32x4*>((kv ? a.v_new : a.k_new) + (size_t)lb * H * D + r * 8);
-  };
-  u32x4 app = {0u, 0u, 0u, 0u};
-  if ((int)threadIdx.x < 2 * half_pieces) app = *app_src(threadIdx.x);
+  if (k == 0) {  // nothing leaves: the new token (metadata slot n) is appended
+    if (threadIdx.x == 0) {
+      hdr[H_MOV8] = hdr[H_MOV16] = 0;
+      int slot = base16 + f;
+      hdr[H_APPEND] = slot >= c.cap16 ? slot - c.cap16 : slot;
+      meta[CONFK_META_N] = nn;
+      meta[CONFK_META_EVICTED] = 0;
+      meta[CONFK_META_MOVED] = 0;
+      meta[CONFK_META_MOVED16] = 0;
+      if (a.evicted_out) a.evicted_out[lb] = 0;
+    }
+    return;
+  }
 
-  int n8n = n8, fn = f, b8 = base8, b16 = base16, nkeep = nn, moved8 = 0, moved16 = 0;
-  if (k > 0) {
-    const int chunk = (nn + kThreads - 1) / kThreads;
-    const int lo = min(nn, (int)threadIdx.x * chunk);
-    const int cnt = min(nn, lo + chunk) - lo;
-    uint32_t kreg[REG ? kRegKeys : 1];
-    if constexpr (REG) {
+  const int chunk = (nn + kThreads - 1) / kThreads;
+  const int lo = min(nn, (int)threadIdx.x * chunk);
+  const int cnt = min(nn, lo + chunk) - lo;
+  // this thread's run: score keys, EMA and positions (read before any write)
+  uint32_t kreg[REG ? kRegKeys : 1];
+  float ereg[REG ? kRegKeys : 1];
+  int preg[REG ? kRegKeys : 1];
+  int bk[REG ? kRegKeys : 1];
+  if constexpr (REG) {
 #pragma unroll
-      for (int j = 0; j < kRegKeys; ++j) {
-        const int i = lo + j;
-        kreg[j] = (j < cnt && i < ncand) ? ord_bits(score[i]) : 0xFFFFFFFFu;
+    for (int j = 0; j < kRegKeys; ++j) {
+      const int i = lo + j;
+      const bool in = j < cnt;
+      const bool cand = in && i < ncand;
+      const float s = cand ? score[i] : 0.f;
+      kreg[j] = cand ? ord_bits(s) : 0xFFFFFFFFu;
+      bk[j] = cand ? bucket_of(s) : kBuckets;
+      ereg[j] = in ? ema[i] : 0.f;
+      preg[j] = in ? pos[i] : 0;
+    }
+  }
+  auto key_at = [&](int j) -> uint32_t {
+    if constexpr (REG) {
+      return kreg[j];
+    } else {
+      const int i = lo + j;
+      return i < ncand ? ord_bits(score[i]) : 0xFFFFFFFFu;
+    }
+  };
+
+  // ---------------------------------------------------------- 1. select
+  // T64: the k-th smallest (key, index); every candidate at or below leaves.
+  uint64_t T64 = 0;
+  bool use_radix = !REG;
+  if constexpr (REG) {
+    for (int i = threadIdx.x; i < kBuckets; i += kThreads) sh.hist[i] = 0;
+    if (threadIdx.x == 0) sh.rank_n = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kRegKeys; ++j)
+      if (bk[j] < kBuckets) atomicAdd(&sh.hist[bk[j]], 1u);
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      constexpr int per = kBuckets / 64;
+      int hsum = 0;
+      uint32_t hv[per];
+#pragma unroll
+      for (int q = 0; q < per; ++q) {
+        hv[q] = sh.hist[per * lane + q];
+        hsum += (int)hv[q];
+      }
+      int incl = hsum;
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+      }
+      const int excl = incl - hsum;
+      if (excl < k && k <= incl) {
+        int run = excl, bsel = per * lane, below = excl;
+        bool found = false;
+#pragma unroll
+        for (int q = 0; q < per; ++q) {
+          if (!found && run + (int)hv[q] >= k) {
+            found = true;
+            bsel = per * lane + q;
+            below = run;
+          }
+          run += (int)hv[q];
+        }
+        sh.sel_bucket = bsel;
+        sh.sel_below = below;
+        sh.sel_crowded = (int)sh.hist[bsel] > kRankMax;
       }
     }
-    auto key_at = [&](int j) -> uint32_t {
-      if constexpr (REG) {
-        return kreg[j];
-      } else {
-        const int i = lo + j;
-        return i < ncand ? ord_bits(score[i]) : 0xFFFFFFFFu;
-      }
-    };
-    for (int i = threadIdx.x; i < (nn + 31) / 32; i += kThreads) evbits[i] = 0u;
-
-    // ------------------------------------------------------ 1. select
-    // Small k (register path): the k smallest 64-bit keys (score bits, index)
-    // are found exactly by k rounds of wave minima per wave, then k rounds
-    // over the waves' candidates; no atomics. Otherwise a 4-pass radix select
-    // on the score bits, with ties at the threshold resolved by index.
-    const bool small = REG && k <= kSmallK;
-    uint64_t T64 = 0;
-    uint32_t T = 0;
-    int kk = k;
-    if (small) {
-      uint64_t k64[REG ? kRegKeys : 1];
+    __syncthreads();
+    const int bsel = sh.sel_bucket;
+    if (!sh.sel_crowded) {
 #pragma unroll
-      for (int j = 0; j < (REG ? kRegKeys : 1); ++j) {
-        const int i = lo + j;
-        k64[j] = (j < cnt && i < ncand) ? (((uint64_t)key_at(j) << 32) | (uint32_t)i) : ~0ull;
-      }
-      const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-      for (int r = 0; r < k; ++r) {
-        uint64_t m = ~0ull;
-#pragma unroll
-        for (int j = 0; j < (REG ? kRegKeys : 1); ++j) m = min(m, k64[j]);
-        uint64_t wmin = m;
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-          const uint64_t y = __shfl_xor(wmin, o, 64);
-          wmin = min(wmin, y);
-        }
-        if (lane == 0) sh.wk[w][r] = wmin;
-#pragma unroll
-        for (int j = 0; j < (REG ? kRegKeys : 1); ++j)
-          if (k64[j] == wmin) k64[j] = ~0ull;  // keys are unique: only the owner matches
-      }
+      for (int j = 0; j < kRegKeys; ++j)
+        if (bk[j] == bsel) sh.rank_keys[atomicAdd(&sh.rank_n, 1)] = ((uint64_t)kreg[j] << 32) | (uint32_t)(lo + j);
       __syncthreads();
       if (threadIdx.x < 64) {
-        // the waves' k smallest hold the block's k smallest
-        uint64_t v[(kWaves * kSmallK + 63) / 64];
-#pragma unroll
-        for (int q = 0; q < (kWaves * kSmallK + 63) / 64; ++q) {
-          const int e = lane + 64 * q;
-          const int ww = e / kSmallK, rr = e - ww * kSmallK;
-          v[q] = (ww < kWaves && rr < k) ? sh.wk[ww][rr] : ~0ull;
+        // rank the boundary bucket's keys; the (k - below)-th smallest is T64
+        const int m = sh.rank_n;
+        const int want = k - sh.sel_below - 1;
+        if (lane < m) {
+          const uint64_t mine = sh.rank_keys[lane];
+          int rank = 0;
+          for (int q = 0; q < m; ++q) rank += sh.rank_keys[q] < mine ? 1 : 0;
+          if (rank == want) sh.kth = mine;
         }
-        uint64_t kth = ~0ull;
-        for (int r = 0; r < k; ++r) {
-          uint64_t m = ~0ull;
-#pragma unroll
-          for (int q = 0; q < (kWaves * kSmallK + 63) / 64; ++q) m = min(m, v[q]);
-#pragma unroll
-          for (int o = 32; o > 0; o >>= 1) {
-            const uint64_t y = __shfl_xor(m, o, 64);
-            m = min(m, y);
-          }
-          kth = m;
-#pragma unroll
-          for (int q = 0; q < (kWaves * kSmallK + 63) / 64; ++q)
-            if (v[q] == m) v[q] = ~0ull;
-        }
-        if (lane == 0) sh.kth = kth;
       }
       __syncthreads();
       T64 = sh.kth;
     } else {
-      uint32_t prefix = 0, mask = 0;
-      for (int shift = 24; shift >= 0; shift -= 8) {
-        if (threadIdx.x < 256) sh.hist[threadIdx.x] = 0;
-        __syncthreads();
-        if constexpr (REG) {
-#pragma unroll
-          for (int j = 0; j < kRegKeys; ++j)
-            if (j < cnt && lo + j < ncand && (kreg[j] & mask) == prefix)
-              atomicAdd(&sh.hist[(kreg[j] >> shift) & 255u], 1u);
-        } else {
-          for (int j = 0; j < cnt; ++j) {
-            const uint32_t key = key_at(j);
-            if (lo + j < ncand && (key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
-          }
-        }
-        __syncthreads();
-        if (threadIdx.x < 64) {
-          const int lane = threadIdx.x;
-          const uint32_t h0 = sh.hist[4 * lane], h1 = sh.hist[4 * lane + 1],
-                         h2 = sh.hist[4 * lane + 2], h3 = sh.hist[4 * lane + 3];
-          const int s = (int)(h0 + h1 + h2 + h3);
-          int incl = s;
-          for (int o = 1; o < 64; o <<= 1) {
-            const int y = __shfl_up(incl, o, 64);
-            if (lane >= o) incl += y;
-          }
-          const int excl = incl - s;
-          if (excl < kk && kk <= incl) {
-            // first of the lane's 4 bins whose running count reaches kk
-            const int c0 = excl + (int)h0, c1 = c0 + (int)h1, c2 = c1 + (int)h2;
-            const int q = c0 >= kk ? 0 : (c1 >= kk ? 1 : (c2 >= kk ? 2 : 3));
-            sh.sel_digit = (uint32_t)(4 * lane + q);
-            sh.sel_before = (uint32_t)(q == 0 ? excl : (q == 1 ? c0 : (q == 2 ? c1 : c2)));
-          }
-        }
-        __syncthreads();
-        prefix |= sh.sel_digit << shift;
-        mask |= 0xFFu << shift;
-        kk -= (int)sh.sel_before;
-      }
-      T = prefix;  // the kk oldest ties at T leave
+      use_radix = true;
     }
-
-    // ------------------------------------------- 2. flags, scans, regions
-    const int jmax = REG ? kRegKeys : cnt;  // constant trip count keeps kreg in registers
-    int x4[4] = {0, 0, 0, 0}, ex4[4], tot4[4];
-    if (!small) {
+  }
+  if (use_radix) {
+    int kk = k;
+    const uint32_t T = radix_select<REG>(kk, cnt, lo, ncand, kreg, key_at, sh);
+    // the kk-th smallest index among the keys equal to T: runs are contiguous
+    // in index order, so a block scan of tie counts locates it
+    int ties = 0;
+    if constexpr (REG) {
 #pragma unroll
-      for (int j = 0; j < jmax; ++j)
-        if (j < cnt) x4[0] += (lo + j < ncand && key_at(j) == T) ? 1 : 0;
-      block_scan4(x4, ex4, tot4, sh);
+      for (int j = 0; j < kRegKeys; ++j) ties += (j < cnt && lo + j < ncand && kreg[j] == T) ? 1 : 0;
+    } else {
+      for (int j = 0; j < cnt; ++j) ties += (lo + j < ncand && key_at(j) == T) ? 1 : 0;
     }
-    int keeps = 0, e8 = 0, e16 = 0;
-    int mm[4] = {INT32_MAX, INT32_MAX, INT32_MAX, INT32_MAX};  // first8, -last8, first16, -last16
-    {
-      int tie_run = small ? 0 : ex4[0];
-#pragma unroll
-      for (int j = 0; j < jmax; ++j) {
-        if (j >= cnt) break;
-        const int i = lo + j;
-        bool ev = false;
-        if (i < ncand) {
-          const uint32_t key = key_at(j);
-          if (small) {
-            ev = (((uint64_t)key << 32) | (uint32_t)i) <= T64;
-          } else if (key < T) {
-            ev = true;
-          } else if (key == T) {
-            ev = tie_run < kk;
-            ++tie_run;
-          }
-        }
-        if (ev) {
-          atomicOr(&evbits[i >> 5], 1u << (i & 31));
-          if (i < n8) {
-            ++e8;
-            mm[0] = min(mm[0], i);
-            mm[1] = min(mm[1], -i);
-          } else {
-            ++e16;
-            mm[2] = min(mm[2], i);
-            mm[3] = min(mm[3], -i);
-          }
-        } else {
-          ++keeps;
-        }
-      }
+    int incl = ties;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += y;
     }
-    x4[0] = keeps;
-    x4[1] = e8;
-    x4[2] = e16;
-    x4[3] = 0;
-    block_scan4(x4, ex4, tot4, sh);  // its barriers also publish evbits
-    const int keep_base = ex4[0];
-    nkeep = tot4[0];
-    block_min4(mm, sh);
-    Region r8{0, n8, tot4[1], mm[0], -mm[1], 0, true, 0};
-    Region r16{n8, f, tot4[2], mm[2], -mm[3], n8 - tot4[1], true, 0};
-    plan_region(r8);
-    plan_region(r16);
-
-    // survivor list for new logical indices [w0, w0 + kWin)
-    int have_w0 = -1;
-    auto build_window = [&](int w0) {
-      __syncthreads();
-      int jn = keep_base;
+    if (lane == 63) sh.wsum[0][w] = incl;
+    __syncthreads();
+    int before = incl - ties;
+    for (int q = 0; q < w; ++q) before += sh.wsum[0][q];
+    if (ties > 0 && before < kk && kk <= before + ties) {
+      int run = before;
       for (int j = 0; j < cnt; ++j) {
-        const int i = lo + j;
-        if (!((evbits[i >> 5] >> (i & 31)) & 1u)) {
-          if (jn >= w0 && jn < w0 + kWin) S[jn - w0] = i;
-          ++jn;
-        }
-      }
-      __syncthreads();
-      have_w0 = w0;
-    };
-
-    // ------------------------------------------------ 3. metadata, ascending
-    for (int w0 = 0; w0 < nkeep; w0 += kWin) {
-      build_window(w0);
-      const int wend = min(nkeep, w0 + kWin);
-      float ev_[kMetaPer];
-      int pv_[kMetaPer];
-#pragma unroll
-      for (int r = 0; r < kMetaPer; ++r) {
-        const int j = w0 + threadIdx.x + r * kThreads;
-        if (j < wend) {
-          const int i = S[j - w0];
-          ev_[r] = ema[i];
-          pv_[r] = pos[i];
-        }
-      }
-      __syncthreads();
-#pragma unroll
-      for (int r = 0; r < kMetaPer; ++r) {
-        const int j = w0 + threadIdx.x + r * kThreads;
-        if (j < wend) {
-          ema[j] = ev_[r];
-          pos[j] = pv_[r];
+        if (lo + j < ncand && key_at(j) == T) {
+          if (++run == kk) sh.kth = ((uint64_t)T << 32) | (uint32_t)(lo + j);
         }
       }
     }
+    __syncthreads();
+    T64 = sh.kth;
+  }
 
-    // ------------------------------------------------------ 4. K/V rows
-    auto move_region = [&](const Region& r, const bool is8) {
-      if (r.movers == 0) return;
-      const int C = is8 ? cap : c.cap16;
-      const int base = is8 ? base8 : base16;
-      const int rowbytes = is8 ? D : 2 * D;  // per head, K or V
-      const int pieces_h = rowbytes / 16;    // 16-byte pieces per head row
-      const int pieces = 2 * H * pieces_h;   // per token (K and V, all heads)
-      const int per_round = max(1, (kRegs * kThreads) / pieces);
-      unsigned char* kb = is8 ? (unsigned char*)c.k8 : (unsigned char*)c.k16;
-      unsigned char* vb = is8 ? (unsigned char*)c.v8 : (unsigned char*)c.v16;
-      const size_t head_stride = (size_t)C * rowbytes;  // bytes per (l, b, head) ring
-      const size_t lb_off = (size_t)lbc * H * head_stride;
-      const int mk = r.m - r.e;
-      const int jlo = r.left ? (r.first_ev - r.rs) : 0;  // region-local new indices
-      const int jhi = r.left ? mk : r.movers;            // exclusive
-      const int nrounds = (jhi - jlo + per_round - 1) / per_round;
-      // round rr covers region-local new indices [ja, jb): ascending when
-      // packing toward the base, descending otherwise
-      auto bounds = [&](int rr, int& ja, int& jb) {
-        if (r.left) {
-          ja = jlo + rr * per_round;
-          jb = min(jhi, ja + per_round);
-        } else {
-          jb = jhi - rr * per_round;
-          ja = max(jlo, jb - per_round);
-        }
-      };
-      // row piece uu of round [ja, ...): pointer to its (l, b, head) ring and
-      // the source / destination slots
-      auto piece = [&](int uu, int ja, int& slot_src, int& slot_dst) -> unsigned char* {
-        const int mv = uu / pieces;
-        const int rem = uu - mv * pieces;
-        const int kv = rem / (H * pieces_h);
-        const int rem2 = rem - kv * H * pieces_h;
-        const int hh = rem2 / pieces_h;
-        const int pc = rem2 - hh * pieces_h;
-        const int jl = ja + mv;
-        int s0 = base + (S[r.js + jl - have_w0] - r.rs);
-        if (s0 >= C) s0 -= C;
-        int s1 = base + (r.left ? jl : jl + r.e);
-        if (s1 >= C) s1 -= C;
-        slot_src = s0;
-        slot_dst = s1;
-        return (kv ? vb : kb) + lb_off + hh * head_stride + pc * 16;
-      };
-      // Round rr+1 reads only slots that round rr does not write (its sources
-      // lie beyond round rr's destinations in the packing direction), so the
-      // loads of the next round are issued right after the stores of this
-      // one; a wait plus barrier then orders them before the next stores.
-      u32x4 buf[kRegs];
-      int ja, jb;
-      bounds(0, ja, jb);
-      {
-        const int ga = r.js + ja, gb = r.js + jb;
-        if (have_w0 < 0 || ga < have_w0 || gb > have_w0 + kWin) build_window(max(0, min(ga, nkeep - kWin)));
+  // ------------------------------------------- 2. flags, scans, regions
+  auto leaves = [&](int j) -> bool {
+    const int i = lo + j;
+    return i < ncand && ((((uint64_t)key_at(j)) << 32) | (uint32_t)i) <= T64;
+  };
+  uint32_t evm = 0;  // bit j: index lo + j leaves (register path)
+  int keeps = 0, e8 = 0, e16 = 0;
+  int f8 = INT32_MAX, l8 = -1, f16 = INT32_MAX, l16 = -1;
+  auto tally = [&](int j) {
+    const int i = lo + j;
+    if (leaves(j)) {
+      if (j < 32) evm |= 1u << j;
+      if (i < n8) {
+        ++e8;
+        f8 = min(f8, i);
+        l8 = max(l8, i);
+      } else {
+        ++e16;
+        f16 = min(f16, i);
+        l16 = max(l16, i);
       }
+    } else {
+      ++keeps;
+    }
+  };
+  if constexpr (REG) {
 #pragma unroll
-      for (int q = 0; q < kRegs; ++q) {
-        const int uu = threadIdx.x + q * kThreads;
-        if (uu < (jb - ja) * pieces) {
-          int ss, sd;
-          unsigned char* p = piece(uu, ja, ss, sd);
-          buf[q] = *reinterpret_cast<const u32x4*>(p + (size_t)ss * rowbytes);
-        }
-      }
-      for (int rr = 0; rr < nrounds; ++rr) {
-        // stores of round rr (destinations from the current window)
+    for (int j = 0; j < kRegKeys; ++j)
+      if (j < cnt) tally(j);
+  } else {
+    for (int j = 0; j < cnt; ++j) tally(j);
+  }
+  int tk, t8, t16, pre_keep;
+  if constexpr (REG) {  // counts of at most kRegKeys: bit-plane ballots
+    pre_keep = wave_prefix16(keeps, tk);
+    wave_prefix16(e8, t8);
+    wave_prefix16(e16, t16);
+  } else {
+    int incl = keeps;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += y;
+    }
+    pre_keep = incl - keeps;
+    tk = __shfl(incl, 63, 64);
+    t8 = e8;
+    t16 = e16;
+    for (int o = 32; o > 0; o >>= 1) {
+      t8 += __shfl_xor(t8, o, 64);
+      t16 += __shfl_xor(t16, o, 64);
+    }
+  }
+  // first / last holes: runs are contiguous, so the lowest (highest) lane
+  // with a hole holds the wave's first (last)
+  const uint64_t h8 = __ballot(e8 > 0), h16 = __ballot(e16 > 0);
+  const int wf8 = h8 ? __shfl(f8, __ffsll((unsigned long long)h8) - 1, 64) : INT32_MAX;
+  const int wl8 = h8 ? __shfl(l8, 63 - __clzll((long long)h8), 64) : -1;
+  const int wf16 = h16 ? __shfl(f16, __ffsll((unsigned long long)h16) - 1, 64) : INT32_MAX;
+  const int wl16 = h16 ? __shfl(l16, 63 - __clzll((long long)h16), 64) : -1;
+  __syncthreads();  // the select's shared values are no longer read
+  if (lane == 0) {
+    sh.wsum[0][w] = tk;
+    sh.wsum[1][w] = t8;
+    sh.wsum[2][w] = t16;
+    sh.wfirst[0][w] = wf8;
+    sh.wlast[0][w] = wl8;
+    sh.wfirst[1][w] = wf16;
+    sh.wlast[1][w] = wl16;
+  }
+  __syncthreads();
+  int keep_base = pre_keep, nkeep = 0;
+  Region r8{0, n8, 0, INT32_MAX, -1, 1, 0, 0}, r16{n8, f, 0, INT32_MAX, -1, 1, 0, 0};
 #pragma unroll
-        for (int q = 0; q < kRegs; ++q) {
-          const int uu = threadIdx.x + q * kThreads;
-          if (uu < (jb - ja) * pieces) {
-            int ss, sd;
-            unsigned char* p = piece(uu, ja, ss, sd);
-            *reinterpret_cast<u32x4*>(p + (size_t)sd * rowbytes) = buf[q];
-          }
-        }
-        if (rr + 1 < nrounds) {
-          int na, nb;
-          bounds(rr + 1, na, nb);
-          const int ga = r.js + na, gb = r.js + nb;
-          if (ga < have_w0 || gb > have_w0 + kWin) {
-            // the survivor list moves on: finish this round first
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            build_window(max(0, min(ga, nkeep - kWin)));
-          }
-#pragma unroll
-          for (int q = 0; q < kRegs; ++q) {
-            const int uu = threadIdx.x + q * kThreads;
-            if (uu < (nb - na) * pieces) {
-              int ss, sd;
-              unsigned char* p = piece(uu, na, ss, sd);
-              buf[q] = *reinterpret_cast<const u32x4*>(p + (size_t)ss * rowbytes);
-            }
-          }
-          ja = na;
-          jb = nb;
-        }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-      }
-    };
-    move_region(r8, true);
-    move_region(r16, false);
-    moved8 = r8.movers;
-    moved16 = r16.movers;
+  for (int q = 0; q < kWaves; ++q) {
+    keep_base += q < w ? sh.wsum[0][q] : 0;
+    nkeep += sh.wsum[0][q];
+    r8.e += sh.wsum[1][q];
+    r16.e += sh.wsum[2][q];
+    r8.first_ev = min(r8.first_ev, sh.wfirst[0][q]);
+    r8.last_ev = max(r8.last_ev, sh.wlast[0][q]);
+    r16.first_ev = min(r16.first_ev, sh.wfirst[1][q]);
+    r16.last_ev = max(r16.last_ev, sh.wlast[1][q]);
+  }
+  plan_region(r8);
+  plan_region(r16);
+  const int js16 = n8 - r8.e;  // new logical index of the first FP16 survivor
 
-    n8n = n8 - r8.e;
-    fn = f - r16.e;
+  // ------------------------------------- 3. metadata and 4. move plan
+  auto emit = [&](int i, int jn, float ev_, int pv_) {
+    ema[jn] = ev_;
+    pos[jn] = pv_;
+    if (i < n8) {
+      if (jn >= r8.jlo && jn < r8.jlo + r8.movers) src8[jn - r8.jlo] = i;
+    } else if (i < n) {
+      const int j = jn - js16;  // region-local new index
+      if (j >= r16.jlo && j < r16.jlo + r16.movers) src16[j - r16.jlo] = i - n8;
+    }
+  };
+  if constexpr (REG) {
+    int jn = keep_base;
+#pragma unroll
+    for (int j = 0; j < kRegKeys; ++j)
+      if (j < cnt && !((evm >> j) & 1u)) emit(lo + j, jn++, ereg[j], preg[j]);
+  } else {
+    // long caches: survivors' metadata goes through a staging area; every
+    // read of a run precedes the barrier, every in-place write follows it
+    float* se = reinterpret_cast<float*>(a.stage + (size_t)lb * 2 * cap);
+    int32_t* sp = a.stage + (size_t)lb * 2 * cap + cap;
+    int jn = keep_base;
+    for (int j = 0; j < cnt; ++j) {
+      if (!leaves(j)) {
+        se[jn] = ema[lo + j];
+        sp[jn] = pos[lo + j];
+        ++jn;
+      }
+    }
+    __syncthreads();
+    jn = keep_base;
+    for (int j = 0; j < cnt; ++j) {
+      if (!leaves(j)) {
+        emit(lo + j, jn, se[jn], sp[jn]);
+        ++jn;
+      }
+    }
+  }
+
+  // ------------------------------------------------------------ header
+  if (threadIdx.x == 0) {
+    int b8 = base8, b16 = base16;
     if (!r8.left) {
       b8 += r8.e;
       if (b8 >= cap) b8 -= cap;
@@ -525,41 +485,154 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
       b16 += r16.e;
       if (b16 >= c.cap16) b16 -= c.cap16;
     }
-  }
-
-  // ------------------------------------------------- 5. append + header
-  {
-    int slot = b16 + fn;
-    if (slot >= c.cap16) slot -= c.cap16;
-    for (int e = threadIdx.x; e < 2 * half_pieces; e += kThreads) {
-      const int kv = e / half_pieces, r = e - kv * half_pieces;
-      const int hh = (r * 8) / D, ch = (r * 8) - hh * D;
-      uint16_t* dst = (kv ? c.v16 : c.k16) + (((size_t)lbc * H + hh) * c.cap16 + slot) * D + ch;
-      *reinterpret_cast<u32x4*>(dst) = e == (int)threadIdx.x ? app : *app_src(e);
-    }
-  }
-  if (threadIdx.x == 0) {
+    hdr[H_MOV8] = r8.movers;
+    hdr[H_LEFT8] = r8.left;
+    hdr[H_E8] = r8.e;
+    hdr[H_JLO8] = r8.jlo;
+    hdr[H_MOV16] = r16.movers;
+    hdr[H_LEFT16] = r16.left;
+    hdr[H_E16] = r16.e;
+    hdr[H_JLO16] = r16.jlo;
+    hdr[H_BASE8] = base8;
+    hdr[H_BASE16] = base16;
+    const int slot = b16 + (f - r16.e);
+    hdr[H_APPEND] = slot >= c.cap16 ? slot - c.cap16 : slot;
     meta[CONFK_META_N] = nkeep;
-    meta[CONFK_META_N8] = n8n;
+    meta[CONFK_META_N8] = n8 - r8.e;
     meta[CONFK_META_BASE8] = b8;
     meta[CONFK_META_BASE16] = b16;
     meta[CONFK_META_EVICTED] = k;
-    meta[CONFK_META_MOVED] = moved8;
-    meta[CONFK_META_MOVED16] = moved16;
+    meta[CONFK_META_MOVED] = r8.movers;
+    meta[CONFK_META_MOVED16] = r16.movers;
     if (a.evicted_out) a.evicted_out[lb] = k;
+  }
+}
+
+// One workgroup per (layer, sequence, kv head, K|V): planned row moves of the
+// head's INT8 and FP16 rings, then the new token's row.
+__global__ __launch_bounds__(kMoveThreads) void compact_move_kernel(CompactArgs a) {
+  const CacheView& c = a.c;
+  const int lb = blockIdx.x;
+  const int hh = blockIdx.y;
+  const int kv = blockIdx.z;
+  const int l = lb / c.B;
+  const int b = lb - l * c.B;
+  const int lbc = (a.layer0 + l) * c.B + b;
+  const int H = c.hkv, D = c.d;
+  const int cap = c.cap;
+  const int32_t* hdr = a.plan + (size_t)lb * (kHdr + 2 * (size_t)cap);
+  const size_t hrow = (size_t)lbc * H + hh;
+  // the new token's row, read early (D halves)
+  const uint16_t* nsrc = (kv ? a.v_new : a.k_new) + ((size_t)lb * H + hh) * D;
+  const int npieces = D / 8;
+  u32x4 nrow = {0u, 0u, 0u, 0u};
+  if ((int)threadIdx.x < npieces) nrow = *reinterpret_cast<const u32x4*>(nsrc + threadIdx.x * 8);
+  const int mov8 = hdr[H_MOV8], mov16 = hdr[H_MOV16];
+  const int append = hdr[H_APPEND];
+  if (append < 0) return;  // the plan flagged a capacity error
+
+  for (int region = 0; region < 2; ++region) {
+    const bool is8 = region == 0;
+    const int movers = is8 ? mov8 : mov16;
+    if (movers == 0) continue;
+    const int left = hdr[is8 ? H_LEFT8 : H_LEFT16];
+    const int e = hdr[is8 ? H_E8 : H_E16];
+    const int jlo = hdr[is8 ? H_JLO8 : H_JLO16];
+    const int base = hdr[is8 ? H_BASE8 : H_BASE16];
+    const int32_t* src = hdr + kHdr + (is8 ? 0 : cap);
+    const int C = is8 ? cap : c.cap16;
+    const int rowbytes = is8 ? D : 2 * D;
+    const int pieces = rowbytes / 16;
+    unsigned char* ring = is8 ? (unsigned char*)((kv ? c.v8 : c.k8) + hrow * cap * D)
+                              : (unsigned char*)((kv ? c.v16 : c.k16) + hrow * c.cap16 * D);
+    const int per_round = max(1, kMoveRegs * kMoveThreads / pieces);
+    const int nrounds = (movers + per_round - 1) / per_round;
+    // round order: ascending movers when packing toward the base, descending
+    // otherwise; round r+1 never reads what round r writes
+    auto round_range = [&](int rr, int& ma, int& mb) {
+      if (left) {
+        ma = rr * per_round;
+        mb = min(movers, ma + per_round);
+      } else {
+        mb = movers - rr * per_round;
+        ma = max(0, mb - per_round);
+      }
+    };
+    u32x4 buf[kMoveRegs];
+    int ma, mb;
+    round_range(0, ma, mb);
+#pragma unroll
+    for (int q = 0; q < kMoveRegs; ++q) {
+      const int u = threadIdx.x + q * kMoveThreads;
+      if (u < (mb - ma) * pieces) {
+        const int mv = ma + u / pieces, pc = u % pieces;
+        int s = base + src[mv];
+        if (s >= C) s -= C;
+        buf[q] = *reinterpret_cast<const u32x4*>(ring + (size_t)s * rowbytes + pc * 16);
+      }
+    }
+    for (int rr = 0; rr < nrounds; ++rr) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();  // every source of this round has been read
+#pragma unroll
+      for (int q = 0; q < kMoveRegs; ++q) {
+        const int u = threadIdx.x + q * kMoveThreads;
+        if (u < (mb - ma) * pieces) {
+          const int mv = ma + u / pieces, pc = u % pieces;
+          const int j = jlo + mv;
+          int d = base + (left ? j : j + e);
+          if (d >= C) d -= C;
+          *reinterpret_cast<u32x4*>(ring + (size_t)d * rowbytes + pc * 16) = buf[q];
+        }
+      }
+      if (rr + 1 < nrounds) {
+        round_range(rr + 1, ma, mb);
+#pragma unroll
+        for (int q = 0; q < kMoveRegs; ++q) {
+          const int u = threadIdx.x + q * kMoveThreads;
+          if (u < (mb - ma) * pieces) {
+            const int mv = ma + u / pieces, pc = u % pieces;
+            int s = base + src[mv];
+            if (s >= C) s -= C;
+            buf[q] = *reinterpret_cast<const u32x4*>(ring + (size_t)s * rowbytes + pc * 16);
+          }
+        }
+      }
+    }
+  }
+  // append (after this ring's moves: the slot may have been a source)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if ((int)threadIdx.x < npieces) {
+    uint16_t* dst = (kv ? c.v16 : c.k16) + (hrow * c.cap16 + append) * D + threadIdx.x * 8;
+    *reinterpret_cast<u32x4*>(dst) = nrow;
   }
 }
 
 }  // namespace
 
+size_t compact_ws_bytes(int nlayers, int batch, int cap) {
+  // plan: header + two source lists per (layer, sequence); staging of the
+  // long-cache path: EMA and positions per (layer, sequence)
+  const size_t plan = (size_t)nlayers * batch * (kHdr + 2 * (size_t)cap) * 4;
+  const size_t stage = cap > kRegKeys * kThreads ? (size_t)nlayers * batch * 2 * (size_t)cap * 4 : 0;
+  return plan + stage;
+}
+
+size_t compact_plan_bytes(int nlayers, int batch, int cap) {
+  return (size_t)nlayers * batch * (kHdr + 2 * (size_t)cap) * 4;
+}
+
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
-  const int lds = (kWin + (a.c.cap + 32) / 32 + 1) * 4;
   const int blocks = a.nl * a.c.B;
   if (a.c.cap <= kRegKeys * kThreads) {
-    hipLaunchKernelGGL(compact_kernel<true>, dim3(blocks), dim3(kThreads), lds, s, a);
+    hipLaunchKernelGGL(compact_plan_kernel<true>, dim3(blocks), dim3(kThreads), 0, s, a);
   } else {
-    hipLaunchKernelGGL(compact_kernel<false>, dim3(blocks), dim3(kThreads), lds, s, a);
+    hipLaunchKernelGGL(compact_plan_kernel<false>, dim3(blocks), dim3(kThreads), 0, s, a);
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(compact_move_kernel, dim3(blocks, a.c.hkv, 2), dim3(kMoveThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -71,6 +71,8 @@ struct EmaArgs {
 struct CompactArgs {
   CacheView c;
   int32_t layer0, nl, budget_stride, protect;
+  int32_t* plan;   // workspace: per-(layer, sequence) move plans
+  int32_t* stage;  // workspace: metadata staging (caches above 4096 tokens)
   const int32_t* budget;
   const float* score;
   const uint16_t* k_new;
@@ -95,6 +97,8 @@ int attention_lds_bytes(int d, int g, int n_lds);
 int attention_plan_n_lds(int d, int g, int cap, int* spill_stride);
 hipError_t launch_ema_rank(const EmaArgs& a, hipStream_t s);
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
+size_t compact_ws_bytes(int nlayers, int batch, int cap);
+size_t compact_plan_bytes(int nlayers, int batch, int cap);
 hipError_t launch_quantize_step(const QuantArgs& a, hipStream_t s);
 hipError_t launch_prefill(const QuantArgs& a, hipStream_t s);
 

@@ -110,13 +110,13 @@ def ema_rank(cache, mass, pol, t, score, layer0=0, nlayers=None):
         cache.ref(), layer0, nl, _p(mass), ctypes.byref(pol), int(t), _p(score), _stream()))
 
 
-def compact(cache, budget, budget_stride, score, pol, k_new, v_new, evicted=None, layer0=0,
+def compact(cache, budget, budget_stride, score, pol, k_new, v_new, ws, evicted=None, layer0=0,
             nlayers=None):
     lib = L.load()
     nl = cache.layers - layer0 if nlayers is None else nlayers
     L.check("confk_compact", lib.confk_compact(
         cache.ref(), layer0, nl, _p(budget), int(budget_stride), _p(score), ctypes.byref(pol),
-        _p(k_new), _p(v_new), _p(evicted), _stream()))
+        _p(k_new), _p(v_new), _p(evicted), _p(ws), ws.numel() * ws.element_size(), _stream()))
 
 
 def quantize(cache, pol, t, mode=L.QUANT_STEP, k_src=None, v_src=None, n_src=0, layer0=0,
@@ -158,6 +158,8 @@ class DecodeEngine:
         self.conf_ws = torch.zeros(max(cws, 4), dtype=torch.uint8, device=device)
         aws = workspace_bytes(L.WS_ATTENTION, self.cache, nlayers=Lr)
         self.attn_ws = torch.zeros(aws, dtype=torch.uint8, device=device) if aws else None
+        kws = workspace_bytes(L.WS_COMPACT, self.cache, nlayers=Lr)
+        self.compact_ws = torch.zeros(kws, dtype=torch.uint8, device=device)
         self.out = torch.zeros((Lr, B, cfg.hq, cfg.d), dtype=torch.float16, device=device)
         self.mass = torch.zeros((Lr, B, cfg.hkv, cfg.cap), dtype=torch.float32, device=device)
         self.score = torch.zeros((Lr, B, cfg.cap), dtype=torch.float32, device=device)
@@ -181,7 +183,7 @@ class DecodeEngine:
 
     def step_compact(self, k_new, v_new):
         compact(self.cache, self.budget, self.budget_stride, self.score, self.pol, k_new, v_new,
-                self.evicted)
+                self.compact_ws, self.evicted)
 
     def step_quantize(self, t):
         quantize(self.cache, self.pol, t)

@@ -115,8 +115,12 @@ def test_attention_workspace_needed_only_for_long_caches(lib):
 def test_compact_quantize_ema_validation(lib):
     c = _fake_cache(cap=100, cap16=65)
     pol = _pol()
-    cp = lambda cc, p, stride=0: lib.confk_compact(  # noqa: E731
-        ctypes.byref(cc), 0, 2, FAKE, stride, FAKE, ctypes.byref(p), FAKE, FAKE, None, None)
+    wsb = lib.confk_workspace_size(M._lib.WS_COMPACT, ctypes.byref(c), 2, 0, 0)
+    assert wsb == 2 * 3 * (16 + 2 * 100) * 4
+    cp = lambda cc, p, stride=0, ws=FAKE, n=wsb: lib.confk_compact(  # noqa: E731
+        ctypes.byref(cc), 0, 2, FAKE, stride, FAKE, ctypes.byref(p), FAKE, FAKE, None, ws, n, None)
+    assert cp(c, _pol(), ws=None) == M.ERR_WORKSPACE
+    assert cp(c, _pol(), n=wsb - 1) == M.ERR_WORKSPACE
     assert cp(c, _pol(protect=30)) == M.ERR_BUDGET             # P > N_high
     assert cp(c, _pol(n_low=99)) == M.ERR_BUDGET               # no slot for N_low + 1 + new
     assert cp(c, _pol(window=64), stride=5) == M.ERR_INVALID_ARG

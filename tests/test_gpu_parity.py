@@ -184,6 +184,17 @@ def test_parity_pyramid_budgets():
         assert (n[l] <= lo[l] + 1).all()
 
 
+def test_parity_long_cache_path():
+    """Capacity above 4096 tokens: compaction re-reads scores from memory and
+    stages metadata; the first step evicts thousands of tokens."""
+    cfg = _cfg("long", 1, 2, 5, 1, 128, 900, 5000, 600, 1200, 16, 64)
+    assert cfg.cap > 4096
+    print("[parity] long cache", flush=True)
+    run = Run(cfg, seed=8)
+    events = sum(run.step(i) for i in range(6))
+    assert events > 0
+
+
 def test_selection_with_tied_scores():
     """Crafted scores with heavy ties (same array on both sides)."""
     cfg = TINY["g5_d128"]
