@@ -436,14 +436,17 @@ __global__ __launch_bounds__(kThreads) void compact_plan_kernel(CompactArgs a) {
   const int js16 = n8 - r8.e;  // new logical index of the first FP16 survivor
 
   // ------------------------------------- 3. metadata and 4. move plan
+  // plan entries are stored in move order: ascending new index when packing
+  // toward the base, descending otherwise
   auto emit = [&](int i, int jn, float ev_, int pv_) {
     ema[jn] = ev_;
     pos[jn] = pv_;
     if (i < n8) {
-      if (jn >= r8.jlo && jn < r8.jlo + r8.movers) src8[jn - r8.jlo] = i;
+      const int m = jn - r8.jlo;
+      if (m >= 0 && m < r8.movers) src8[r8.left ? m : r8.movers - 1 - m] = i;
     } else if (i < n) {
-      const int j = jn - js16;  // region-local new index
-      if (j >= r16.jlo && j < r16.jlo + r16.movers) src16[j - r16.jlo] = i - n8;
+      const int m = jn - js16 - r16.jlo;  // region-local new index minus the first mover's
+      if (m >= 0 && m < r16.movers) src16[r16.left ? m : r16.movers - 1 - m] = i - n8;
     }
   };
   if constexpr (REG) {
@@ -509,8 +512,13 @@ __global__ __launch_bounds__(kThreads) void compact_plan_kernel(CompactArgs a) {
 }
 
 // One workgroup per (layer, sequence, kv head, K|V): planned row moves of the
-// head's INT8 and FP16 rings, then the new token's row.
+// head's INT8 and FP16 rings, then the new token's row. The plan header, the
+// first round of both rings' source lists and the new row are read in one
+// round trip, the first round's rows in a second; one barrier separates all
+// reads from all writes. Rings whose movers exceed one round continue in
+// further rounds (read, barrier, write), in plan order.
 __global__ __launch_bounds__(kMoveThreads) void compact_move_kernel(CompactArgs a) {
+  typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
   const CacheView& c = a.c;
   const int lb = blockIdx.x;
   const int hh = blockIdx.y;
@@ -521,89 +529,110 @@ __global__ __launch_bounds__(kMoveThreads) void compact_move_kernel(CompactArgs 
   const int H = c.hkv, D = c.d;
   const int cap = c.cap;
   const int32_t* hdr = a.plan + (size_t)lb * (kHdr + 2 * (size_t)cap);
+  const int32_t* src8 = hdr + kHdr;
+  const int32_t* src16 = src8 + cap;
   const size_t hrow = (size_t)lbc * H + hh;
-  // the new token's row, read early (D halves)
+  const int p8 = D / 16, p16 = D / 8;  // 16-byte pieces per row
+  const int per8 = kMoveRegs * kMoveThreads / p8, per16 = kMoveRegs * kMoveThreads / p16;
+
+  // round trip 1: header, first-round sources (speculative), new row
+  const i32x4 hA = reinterpret_cast<const i32x4*>(hdr)[0];
+  const i32x4 hB = reinterpret_cast<const i32x4*>(hdr)[1];
+  const i32x4 hC = reinterpret_cast<const i32x4*>(hdr)[2];
+  int s8[kMoveRegs], s16[kMoveRegs];
+#pragma unroll
+  for (int q = 0; q < kMoveRegs; ++q) {
+    const int u = threadIdx.x + q * kMoveThreads;
+    const int m8 = u / p8, m16 = u / p16;
+    s8[q] = m8 < min(per8, cap) ? src8[m8] : 0;
+    s16[q] = m16 < min(per16, cap) ? src16[m16] : 0;
+  }
   const uint16_t* nsrc = (kv ? a.v_new : a.k_new) + ((size_t)lb * H + hh) * D;
-  const int npieces = D / 8;
   u32x4 nrow = {0u, 0u, 0u, 0u};
-  if ((int)threadIdx.x < npieces) nrow = *reinterpret_cast<const u32x4*>(nsrc + threadIdx.x * 8);
-  const int mov8 = hdr[H_MOV8], mov16 = hdr[H_MOV16];
-  const int append = hdr[H_APPEND];
+  if ((int)threadIdx.x < p16) nrow = *reinterpret_cast<const u32x4*>(nsrc + threadIdx.x * 8);
+  const int mov8 = hA[H_MOV8], left8 = hA[H_LEFT8], e8 = hA[H_E8], jlo8 = hA[H_JLO8];
+  const int mov16 = hB[H_MOV16 - 4], left16 = hB[H_LEFT16 - 4], e16 = hB[H_E16 - 4],
+            jlo16 = hB[H_JLO16 - 4];
+  const int base8 = hC[H_BASE8 - 8], base16 = hC[H_BASE16 - 8], append = hC[H_APPEND - 8];
   if (append < 0) return;  // the plan flagged a capacity error
 
-  for (int region = 0; region < 2; ++region) {
-    const bool is8 = region == 0;
-    const int movers = is8 ? mov8 : mov16;
-    if (movers == 0) continue;
-    const int left = hdr[is8 ? H_LEFT8 : H_LEFT16];
-    const int e = hdr[is8 ? H_E8 : H_E16];
-    const int jlo = hdr[is8 ? H_JLO8 : H_JLO16];
-    const int base = hdr[is8 ? H_BASE8 : H_BASE16];
-    const int32_t* src = hdr + kHdr + (is8 ? 0 : cap);
-    const int C = is8 ? cap : c.cap16;
-    const int rowbytes = is8 ? D : 2 * D;
-    const int pieces = rowbytes / 16;
-    unsigned char* ring = is8 ? (unsigned char*)((kv ? c.v8 : c.k8) + hrow * cap * D)
-                              : (unsigned char*)((kv ? c.v16 : c.k16) + hrow * c.cap16 * D);
-    const int per_round = max(1, kMoveRegs * kMoveThreads / pieces);
-    const int nrounds = (movers + per_round - 1) / per_round;
-    // round order: ascending movers when packing toward the base, descending
-    // otherwise; round r+1 never reads what round r writes
-    auto round_range = [&](int rr, int& ma, int& mb) {
-      if (left) {
-        ma = rr * per_round;
-        mb = min(movers, ma + per_round);
-      } else {
-        mb = movers - rr * per_round;
-        ma = max(0, mb - per_round);
-      }
-    };
-    u32x4 buf[kMoveRegs];
-    int ma, mb;
-    round_range(0, ma, mb);
+  unsigned char* ring8 = (unsigned char*)((kv ? c.v8 : c.k8) + hrow * cap * D);
+  unsigned char* ring16 = (unsigned char*)((kv ? c.v16 : c.k16) + hrow * c.cap16 * D);
+  // mover m (plan order) -> destination slot
+  auto dst_slot = [](int m, int movers, int left, int e, int jlo, int base, int C) {
+    const int j = jlo + (left ? m : movers - 1 - m);
+    int d = base + (left ? j : j + e);
+    return d >= C ? d - C : d;
+  };
+
+  // round trip 2: the first round's rows of both rings
+  const int n8r = min(mov8, per8), n16r = min(mov16, per16);
+  u32x4 b8[kMoveRegs], b16[kMoveRegs];
 #pragma unroll
-    for (int q = 0; q < kMoveRegs; ++q) {
-      const int u = threadIdx.x + q * kMoveThreads;
-      if (u < (mb - ma) * pieces) {
-        const int mv = ma + u / pieces, pc = u % pieces;
-        int s = base + src[mv];
-        if (s >= C) s -= C;
-        buf[q] = *reinterpret_cast<const u32x4*>(ring + (size_t)s * rowbytes + pc * 16);
-      }
+  for (int q = 0; q < kMoveRegs; ++q) {
+    const int u = threadIdx.x + q * kMoveThreads;
+    if (u / p8 < n8r) {
+      int sl = base8 + s8[q];
+      if (sl >= cap) sl -= cap;
+      b8[q] = *reinterpret_cast<const u32x4*>(ring8 + (size_t)sl * D + (u % p8) * 16);
     }
-    for (int rr = 0; rr < nrounds; ++rr) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();  // every source of this round has been read
+    if (u / p16 < n16r) {
+      int sl = base16 + s16[q];
+      if (sl >= c.cap16) sl -= c.cap16;
+      b16[q] = *reinterpret_cast<const u32x4*>(ring16 + (size_t)sl * 2 * D + (u % p16) * 16);
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();  // every source of the first round has been read
+#pragma unroll
+  for (int q = 0; q < kMoveRegs; ++q) {
+    const int u = threadIdx.x + q * kMoveThreads;
+    if (u / p8 < n8r) {
+      const int d = dst_slot(u / p8, mov8, left8, e8, jlo8, base8, cap);
+      *reinterpret_cast<u32x4*>(ring8 + (size_t)d * D + (u % p8) * 16) = b8[q];
+    }
+    if (u / p16 < n16r) {
+      const int d = dst_slot(u / p16, mov16, left16, e16, jlo16, base16, c.cap16);
+      *reinterpret_cast<u32x4*>(ring16 + (size_t)d * 2 * D + (u % p16) * 16) = b16[q];
+    }
+  }
+
+  // further rounds (large evictions): sources of round r+1 lie beyond round
+  // r's destinations in the packing direction
+  auto rounds = [&](unsigned char* ring, int rowbytes, int pieces, int per, int movers, int left,
+                    int e, int jlo, int base, int C, const int32_t* src) {
+    for (int m0 = per; m0 < movers; m0 += per) {
+      const int mend = min(movers, m0 + per);
+      u32x4 buf[kMoveRegs];
 #pragma unroll
       for (int q = 0; q < kMoveRegs; ++q) {
         const int u = threadIdx.x + q * kMoveThreads;
-        if (u < (mb - ma) * pieces) {
-          const int mv = ma + u / pieces, pc = u % pieces;
-          const int j = jlo + mv;
-          int d = base + (left ? j : j + e);
-          if (d >= C) d -= C;
-          *reinterpret_cast<u32x4*>(ring + (size_t)d * rowbytes + pc * 16) = buf[q];
+        const int m = m0 + u / pieces;
+        if (m < mend) {
+          int sl = base + src[m];
+          if (sl >= C) sl -= C;
+          buf[q] = *reinterpret_cast<const u32x4*>(ring + (size_t)sl * rowbytes + (u % pieces) * 16);
         }
       }
-      if (rr + 1 < nrounds) {
-        round_range(rr + 1, ma, mb);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
 #pragma unroll
-        for (int q = 0; q < kMoveRegs; ++q) {
-          const int u = threadIdx.x + q * kMoveThreads;
-          if (u < (mb - ma) * pieces) {
-            const int mv = ma + u / pieces, pc = u % pieces;
-            int s = base + src[mv];
-            if (s >= C) s -= C;
-            buf[q] = *reinterpret_cast<const u32x4*>(ring + (size_t)s * rowbytes + pc * 16);
-          }
+      for (int q = 0; q < kMoveRegs; ++q) {
+        const int u = threadIdx.x + q * kMoveThreads;
+        const int m = m0 + u / pieces;
+        if (m < mend) {
+          const int d = dst_slot(m, movers, left, e, jlo, base, C);
+          *reinterpret_cast<u32x4*>(ring + (size_t)d * rowbytes + (u % pieces) * 16) = buf[q];
         }
       }
     }
-  }
-  // append (after this ring's moves: the slot may have been a source)
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  if ((int)threadIdx.x < npieces) {
+  };
+  if (mov8 > per8) rounds(ring8, D, p8, per8, mov8, left8, e8, jlo8, base8, cap, src8);
+  if (mov16 > per16) rounds(ring16, 2 * D, p16, per16, mov16, left16, e16, jlo16, base16, c.cap16, src16);
+
+  // append: every FP16 source has been read (barrier above), and the slot is
+  // not a destination
+  if ((int)threadIdx.x < p16) {
     uint16_t* dst = (kv ? c.v16 : c.k16) + (hrow * c.cap16 + append) * D + threadIdx.x * 8;
     *reinterpret_cast<u32x4*>(dst) = nrow;
   }

@@ -63,21 +63,21 @@ __global__ __launch_bounds__(kThreads) void ema_rank_kernel(EmaArgs a) {
         pv[r] = pos[i];
       }
     }
-    // four kv heads' partial masses per round trip, summed in head order
-    for (int j0 = 0; j0 < H; j0 += 4) {
-      float t4[4][kPer];
+    // eight kv heads' partial masses per round trip, summed in head order
+    for (int j0 = 0; j0 < H; j0 += 8) {
+      float t8[8][kPer];
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+      for (int q = 0; q < 8; ++q)
 #pragma unroll
         for (int r = 0; r < kPer; ++r) {
           const int i = threadIdx.x + r * kThreads;
-          t4[q][r] = (j0 + q < H && i < n) ? mass[(size_t)(j0 + q) * cap + i] : 0.f;
+          t8[q][r] = (j0 + q < H && i < n) ? mass[(size_t)(j0 + q) * cap + i] : 0.f;
         }
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+      for (int q = 0; q < 8; ++q)
 #pragma unroll
         for (int r = 0; r < kPer; ++r)
-          if (j0 + q < H) ms[r] += t4[q][r];
+          if (j0 + q < H) ms[r] += t8[q][r];
     }
 #pragma unroll
     for (int r = 0; r < kPer; ++r) {

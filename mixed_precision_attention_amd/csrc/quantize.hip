@@ -77,8 +77,12 @@ __global__ __launch_bounds__(kThreads) void quantize_step_kernel(QuantArgs a) {
   int sat = 0;
 
   while (n8 < n) {
-    // the oldest FP16 token: its row (speculatively) and its position
+    // the oldest FP16 token's position, the next one's, and (speculatively)
+    // the row and its scales: one round trip in the common case
+    const int p_first = pos[n8];
+    const int p_next = n8 + 1 < n ? pos[n8 + 1] : INT32_MAX;
     u32x4 hv[4];
+    f32x4 sv[4][2];
     int hq_[4];
     int cnt = 0;
     for (int e = threadIdx.x; e < groups; e += kThreads, ++cnt) {
@@ -89,11 +93,15 @@ __global__ __launch_bounds__(kThreads) void quantize_step_kernel(QuantArgs a) {
       if (cnt < 4) {
         hv[cnt] = *reinterpret_cast<const u32x4*>((kv ? c.v16 : c.k16) + (hrow * c.cap16 + base16) * D +
                                                   (8 * r - hh * D));
+        const float* sp = (kv ? c.vs : c.ks) + hrow * D + (8 * r - hh * D);
+        sv[cnt][0] = *reinterpret_cast<const f32x4*>(sp);
+        sv[cnt][1] = *reinterpret_cast<const f32x4*>(sp + 4);
         hq_[cnt] = e;
       }
     }
-    if (pos[n8] > limit) break;  // uniform: every thread reads the same word
+    if (p_first > limit) break;  // uniform: every thread reads the same word
     const int f = n - n8;
+    const bool fresh_scales = !calib;
     if (!calib) {
       // scales over every cached token (all FP16 while uncalibrated)
       for (int e = threadIdx.x; e < 2 * H * D; e += kThreads) {
@@ -121,24 +129,32 @@ __global__ __launch_bounds__(kThreads) void quantize_step_kernel(QuantArgs a) {
       const int hh = (8 * r) / D;
       const int ch = 8 * r - hh * D;
       const size_t hrow = (size_t)lbc * H + hh;
-      const float* sp = (kv ? c.vs : c.ks) + hrow * D + ch;
+      const bool pre = q < 4 && hq_[q] == e;
       float s8[8];
-      const f32x4 s0 = *reinterpret_cast<const f32x4*>(sp);
-      const f32x4 s1 = *reinterpret_cast<const f32x4*>(sp + 4);
+      if (pre && !fresh_scales) {
 #pragma unroll
-      for (int z = 0; z < 4; ++z) {
-        s8[z] = s0[z];
-        s8[4 + z] = s1[z];
+        for (int z = 0; z < 4; ++z) {
+          s8[z] = sv[q][0][z];
+          s8[4 + z] = sv[q][1][z];
+        }
+      } else {
+        const float* sp = (kv ? c.vs : c.ks) + hrow * D + ch;
+        const f32x4 s0 = *reinterpret_cast<const f32x4*>(sp);
+        const f32x4 s1 = *reinterpret_cast<const f32x4*>(sp + 4);
+#pragma unroll
+        for (int z = 0; z < 4; ++z) {
+          s8[z] = s0[z];
+          s8[4 + z] = s1[z];
+        }
       }
-      const u32x4 h = (q < 4 && hq_[q] == e)
-                          ? hv[q]
+      const u32x4 h = pre ? hv[q]
                           : *reinterpret_cast<const u32x4*>((kv ? c.v16 : c.k16) +
                                                             (hrow * c.cap16 + base16) * D + ch);
       *reinterpret_cast<u32x2*>((kv ? c.v8 : c.k8) + (hrow * c.cap + dst) * D + ch) = quant8(h, s8, sat);
     }
     base16 = base16 + 1 == c.cap16 ? 0 : base16 + 1;
     ++n8;
-    __syncthreads();  // the next iteration reads the ring at the new base
+    if (p_next > limit) break;  // the next FP16 token stays FP16 (uniform)
   }
   sat = wave_sum_i(sat);
   __shared__ int red[kThreads / 64];
