@@ -131,10 +131,8 @@ typedef struct confk_cache {
  *   status        uint32 [1] device or NULL; NaN / +inf / all -inf logits
  *                 set CONFK_STATUS_NONFINITE_LOGITS, give c = NaN and the
  *                 loose budget
- *   ws            >= confk_workspace_size(CONFK_WS_CONFIDENCE, ...) bytes,
- *                 zero-filled before its first use with this batch and
- *                 vocab; every call leaves it ready for the next (its last
- *                 words count chunk arrivals per row and return to zero)
+ *   ws            >= confk_workspace_size(CONFK_WS_CONFIDENCE, ...) bytes
+ *                 (per-chunk partial reductions; no initialisation needed)
  * Errors: INVALID_ARG (null, batch < 1, vocab < 2, ld < vocab, nbl < 1,
  * only one of the layer arrays given), WORKSPACE.
  */

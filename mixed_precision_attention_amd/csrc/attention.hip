@@ -26,13 +26,16 @@
 // power of two into fp16's normal range), so the fp32 scores carry ~22 bits;
 // the probabilities fed to the second product are fp16.
 //
-// Memory pipeline: each wave walks every 4th 16-key tile of a region and
-// holds two tiles of raw K/V in registers, loading tile t+4 while tile t is
-// converted and multiplied. Tail rows are clamped to a valid row (their
-// scores are masked), so loads carry no branches.
+// Memory pipeline: each wave walks every 4th 16-key tile of a region. In the
+// INT8 region it holds three tiles of raw codes in registers (two loads in
+// flight while one tile is converted and multiplied), in the FP16 region two.
+// The query, K scales and V scales are staged once in LDS, so switching
+// regions costs no memory round trip, and the first FP16 tiles are requested
+// before the FP16 query operands are built. Tail rows are clamped to a valid
+// row (their scores are masked), so loads carry no branches.
 //
-// Mass: the log2-domain scores are kept in LDS (or a global spill area for
-// caches too long for the LDS budget); once the waves' running maxima and
+// Mass: the log2-domain scores are kept in LDS (or, in a separate kernel
+// instance, partly in a global spill area for// caches too long for the LDS budget); once the waves' running maxima and
 // normalisers are merged, each key's mass sum_h 2^(s_h - M_h) / L_h is
 // formed exactly.
 #include "confk_internal.h"
@@ -51,7 +54,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kScoreLdsBytes = 24 * 1024;  // LDS budget for the score tile store
+constexpr int kScoreLdsBytes = 48 * 1024;  // LDS budget for the score store (3 groups per CU)
 
 // Two INT8 codes (bytes b0/b1 or b2/b3 of x = codes ^ 0x80808080) -> two fp16.
 // perm places each biased code under an 0x64 exponent byte: fp16 value
@@ -98,7 +101,8 @@ __device__ __forceinline__ int d_int8(int kc, int kg) {
 __device__ __forceinline__ int d_fp16(int kc, int kg) { return 32 * kc + 8 * kg; }
 
 // Builds the hi/lo fp16 query operands of this lane (head hh, group kg) for
-// one key region; returns the power-of-two factor that undoes the scaling.
+// one key region from the LDS copy of the query (and K scales); returns the
+// power-of-two factor that undoes the scaling.
 template <int D, bool INT8>
 __device__ __forceinline__ float build_q(const uint16_t* qrow, const float* kscale, bool active,
                                          int kg, half8_t* qhi, half8_t* qlo) {
@@ -110,8 +114,7 @@ __device__ __forceinline__ float build_q(const uint16_t* qrow, const float* ksca
   for (int kc = 0; kc < KC; ++kc) {
     const int d0 = INT8 ? d_int8(kc, kg) : d_fp16(kc, kg);
     if (active) {
-      const u32x4 raw = *reinterpret_cast<const u32x4*>(qrow + d0);
-      const half8_t h = as_half8(raw);
+      const half8_t h = as_half8(*reinterpret_cast<const u32x4*>(qrow + d0));
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         float v = (float)h[j] * cq;
@@ -158,7 +161,7 @@ __device__ __forceinline__ half4_t softmax_tile(float4_t s, SoftState& st, float
   tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
   const float mnew = fmaxf(st.m, tmax);
   if (__any(mnew > st.m)) {
-    const float corr = exp2f(st.m - mnew);
+    const float corr = __builtin_amdgcn_exp2f(st.m - mnew);
     st.l *= corr;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) acc[cb] *= corr;
@@ -168,7 +171,7 @@ __device__ __forceinline__ half4_t softmax_tile(float4_t s, SoftState& st, float
   float lsum = 0.f;
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-    const float e = exp2f(s[v] - mnew);
+    const float e = __builtin_amdgcn_exp2f(s[v] - mnew);
     lsum += e;
     p[v] = (_Float16)e;
   }
@@ -179,7 +182,7 @@ __device__ __forceinline__ half4_t softmax_tile(float4_t s, SoftState& st, float
 // Raw registers of one 16-key INT8 tile of this lane.
 template <int D>
 struct Raw8 {
-  u32x4 k[Tile<D>::KU];         // K row r16: 16 bytes per 64-byte half
+  u32x4 k[Tile<D>::KU];            // K row r16: 16 bytes per 64-byte half
   uint32_t v[4][Tile<D>::CB / 4];  // V rows 4kg+j: D/16 bytes at channel (D/16)*r16
 };
 
@@ -190,7 +193,18 @@ struct Raw16 {
   uint32_t v[4][Tile<D>::CB / 2];  // V rows 4kg+j: D/16 halves at channel (D/16)*r16
 };
 
-template <int D>
+// LDS layout: scores [g][n_lds] fp32 (later the per-wave output reduction
+// [kWaves][g][D] fp32), then the query [g][D] fp16, K scales [D], V scales [D].
+__host__ __device__ __forceinline__ int score_area_floats(int d, int g, int n_lds) {
+  const int sc = g * n_lds;
+  const int red = kWaves * g * d;
+  return sc > red ? sc : red;
+}
+
+// SPILL: scores past the LDS budget go to global memory. Kept out of the
+// common instance because global stores in the tile loop make the load
+// counter unusable for partial waits (stores complete out of order).
+template <int D, bool SPILL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
 void attn_decode_kernel(AttnArgs a) {
   constexpr int KC = Tile<D>::KC;
@@ -228,23 +242,23 @@ void attn_decode_kernel(AttnArgs a) {
   const int8_t* v8 = c.v8 + hrow * c.cap * D;
   const uint16_t* k16 = c.k16 + hrow * c.cap16 * D;
   const uint16_t* v16 = c.v16 + hrow * c.cap16 * D;
-  const float* ks = c.ks + hrow * D;
-  const float* vs = c.vs + hrow * D;
   const size_t qoff = ((size_t)lb * c.hq + (size_t)h * g) * D;
-  const uint16_t* qb = a.q + qoff;
   const uint16_t* kn = a.k_new + ((size_t)lb * H + h) * D;
   const uint16_t* vn = a.v_new + ((size_t)lb * H + h) * D;
-  float* spill = a.spill ? a.spill + (size_t)u * g * a.spill_stride : nullptr;
+  float* spill = SPILL ? a.spill + (size_t)u * g * a.spill_stride : nullptr;
 
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index (uniform)
   const int r16 = lane & 15;
   const int kg = lane >> 4;
   const bool head_ok = r16 < g;
-  const uint16_t* qrow = qb + (size_t)r16 * D;
 
-  float* sc = lds;  // [g][n_lds]
   const int n_lds = a.n_lds;
+  float* sc = lds;  // [g][n_lds]
+  uint16_t* q_lds = reinterpret_cast<uint16_t*>(lds + score_area_floats(D, g, n_lds));  // [g][D]
+  float* ks_lds = reinterpret_cast<float*>(q_lds + g * D);                               // [D]
+  float* vs_lds = ks_lds + D;                                                            // [D]
+  const uint16_t* qrow = q_lds + (size_t)(head_ok ? r16 : 0) * D;
 
   float4_t acc[CB];
 #pragma unroll
@@ -254,16 +268,16 @@ void attn_decode_kernel(AttnArgs a) {
   auto store_scores = [&](int p0, float4_t s) {
     if (!head_ok) return;
     const int p = p0 + 4 * kg;
-    if (p0 < n_lds) {
+    if (!SPILL || p0 < n_lds) {
       *reinterpret_cast<float4_t*>(sc + (size_t)r16 * n_lds + p) = s;
     } else {
       *reinterpret_cast<float4_t*>(spill + (size_t)r16 * a.spill_stride + p) = s;
     }
   };
 
-  // ------------------------------------------------------------ INT8 region
+  // ------------------------------------------------------------ tile loads
   auto slot8 = [&](int i) {  // ring slot of INT8 logical index i (clamped to the region)
-    int s = base8 + min(i, n8 - 1);
+    int s = base8 + min(i, max(n8 - 1, 0));
     return s >= c.cap ? s - c.cap : s;
   };
   auto load8 = [&](Raw8<D>& r, int t) {
@@ -283,59 +297,6 @@ void attn_decode_kernel(AttnArgs a) {
       }
     }
   };
-  if (nt8 > w) {
-    Raw8<D> ra, rb;
-    load8(ra, w);
-    half8_t qhi[KC], qlo[KC];
-    const float unscale = build_q<D, true>(qrow, ks, head_ok, kg, qhi, qlo);
-    auto tile8 = [&](const Raw8<D>& r, int t) {
-      const int i0 = t * 16;
-      float4_t s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        const u32x4 xw = r.k[kc >> 1] ^ 0x80808080u;
-        const int o = 2 * (kc & 1);
-        u32x4 hv;
-        hv[0] = codes_to_h2(xw[o], kSelLo);
-        hv[1] = codes_to_h2(xw[o], kSelHi);
-        hv[2] = codes_to_h2(xw[o + 1], kSelLo);
-        hv[3] = codes_to_h2(xw[o + 1], kSelHi);
-        const half8_t ak = as_half8(hv);
-        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, qhi[kc], s, 0, 0, 0);
-        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, qlo[kc], s, 0, 0, 0);
-      }
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int i = i0 + 4 * kg + v;
-        s[v] = !head_ok ? 0.f : (i < n8 ? s[v] * unscale : -INFINITY);
-      }
-      store_scores(i0, s);
-      const half4_t pT = softmax_tile<CB>(s, st, acc);
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        const int wd = cb >> 2, bb = cb & 3;
-        u32x2 av;
-        av[0] = code_pair_rows(r.v[0][wd], r.v[1][wd], bb);
-        av[1] = code_pair_rows(r.v[2][wd], r.v[3][wd], bb);
-        acc[cb] = __builtin_amdgcn_mfma_f32_16x16x16f16(as_half4(av), pT, acc[cb], 0, 0, 0);
-      }
-    };
-    for (int t = w; t < nt8; t += 2 * kWaves) {
-      const int t1 = t + kWaves;
-      if (t1 < nt8) load8(rb, t1);
-      tile8(ra, t);
-      if (t1 >= nt8) break;
-      if (t1 + kWaves < nt8) load8(ra, t1 + kWaves);
-      tile8(rb, t1);
-    }
-    // V scales of the INT8 part: channel of acc[cb][v] is CB*(4kg+v)+cb
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) acc[cb][v] *= vs[CB * (4 * kg + v) + cb];
-  }
-
-  // ------------------------------------------------------ FP16 region + new
   auto row16 = [&](const uint16_t* ring, const uint16_t* nw, int jj) {  // FP16-local index jj
     if (jj >= f) return nw;  // the new token (also the clamp target of tail rows)
     int s = base16 + jj;
@@ -361,9 +322,113 @@ void attn_decode_kernel(AttnArgs a) {
       }
     }
   };
-  if (nt16 > w) {
-    Raw16<D> ra, rb;
-    load16(ra, w);
+
+  // ------------------------------------------------------------ prologue
+  // The query and the K/V scales (at most 2 x 256 16-byte pieces) are fetched
+  // first, then this wave's first INT8 tiles, then the pieces go to LDS: the
+  // tile loads stay in flight across the barrier.
+  const int qp = g * D / 8;          // 16-byte pieces of the query block
+  const int npieces = qp + D / 2;    // + K scales, V scales
+  const u32x4* qsrc4 = reinterpret_cast<const u32x4*>(a.q + qoff);
+  const u32x4* ks4 = reinterpret_cast<const u32x4*>(c.ks + hrow * D);
+  const u32x4* vs4 = reinterpret_cast<const u32x4*>(c.vs + hrow * D);
+  u32x4 piece[2];
+#pragma unroll
+  for (int z = 0; z < 2; ++z) {  // unconditional loads (spare threads re-read piece 0)
+    const int e = threadIdx.x + z * kThreads;
+    const u32x4* src = e < qp             ? qsrc4 + e
+                       : e < qp + D / 4   ? ks4 + (e - qp)
+                       : e < npieces      ? vs4 + (e - qp - D / 4)
+                                          : qsrc4;
+    piece[z] = *src;
+  }
+  const bool has8 = nt8 > w;  // this wave has INT8 tiles (uniform per wave)
+  const int last8 = max(nt8 - 1, 0);
+  Raw8<D> ra8, rb8, rc8;
+  // Loads past the region are clamped to its last tile (rows are read, never
+  // used; an empty region reads its ring's first slot), so no load below is
+  // conditional and the load counter allows partial waits everywhere.
+  load8(ra8, min(w, last8));
+  load8(rb8, min(w + kWaves, last8));
+#pragma unroll
+  for (int z = 0; z < 2; ++z) {
+    const int e = threadIdx.x + z * kThreads;
+    if (e < qp) {
+      reinterpret_cast<u32x4*>(q_lds)[e] = piece[z];
+    } else if (e < npieces) {
+      reinterpret_cast<u32x4*>(ks_lds)[e - qp] = piece[z];
+    }
+  }
+  __syncthreads();
+
+  // ------------------------------------------------------------ INT8 region
+  if (has8) {
+    half8_t qhi[KC], qlo[KC];
+    const float unscale = build_q<D, true>(qrow, ks_lds, head_ok, kg, qhi, qlo);
+    auto tile8 = [&](const Raw8<D>& r, int t) {
+      const int i0 = t * 16;
+      float4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const u32x4 xw = r.k[kc >> 1] ^ 0x80808080u;
+        const int o = 2 * (kc & 1);
+        u32x4 hv;
+        hv[0] = codes_to_h2(xw[o], kSelLo);
+        hv[1] = codes_to_h2(xw[o], kSelHi);
+        hv[2] = codes_to_h2(xw[o + 1], kSelLo);
+        hv[3] = codes_to_h2(xw[o + 1], kSelHi);
+        const half8_t ak = as_half8(hv);
+        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, qhi[kc], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, qlo[kc], s, 0, 0, 0);
+      }
+      s *= unscale;  // padded heads have zero queries and so zero scores
+      if (i0 + 16 > n8) {  // tail tile (uniform)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (head_ok && i0 + 4 * kg + v >= n8) s[v] = -INFINITY;
+      }
+      store_scores(i0, s);
+      const half4_t pT = softmax_tile<CB>(s, st, acc);
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const int wd = cb >> 2, bb = cb & 3;
+        u32x2 av;
+        av[0] = code_pair_rows(r.v[0][wd], r.v[1][wd], bb);
+        av[1] = code_pair_rows(r.v[2][wd], r.v[3][wd], bb);
+        acc[cb] = __builtin_amdgcn_mfma_f32_16x16x16f16(as_half4(av), pT, acc[cb], 0, 0, 0);
+      }
+    };
+    // three tiles in registers: two loads in flight while one is computed.
+    // This wave's tiles are t_j = w + 4j, j < m8; the loop has one exit and
+    // the remaining 0-2 tiles (already loaded) follow it.
+    const int m8 = (nt8 - w + kWaves - 1) / kWaves;
+    int j = 0;
+    for (; j + 3 <= m8; j += 3) {
+      const int t = w + kWaves * j;
+      load8(rc8, t + 2 * kWaves);
+      tile8(ra8, t);
+      load8(ra8, min(t + 3 * kWaves, last8));
+      tile8(rb8, t + kWaves);
+      load8(rb8, min(t + 4 * kWaves, last8));
+      tile8(rc8, t + 2 * kWaves);
+    }
+    if (j < m8) tile8(ra8, w + kWaves * j);
+    if (j + 1 < m8) tile8(rb8, w + kWaves * (j + 1));
+  }
+
+  // ------------------------------------------------------ FP16 region + new
+  const bool has16 = nt16 > w;
+  const int last16 = nt16 - 1;  // nt16 >= 1: the new token is always there
+  Raw16<D> ra, rb;
+  load16(ra, min(w, last16));
+  if (has8) {
+    // V scales of the INT8 part: channel of acc[cb][v] is CB*(4kg+v)+cb
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[cb][v] *= vs_lds[CB * (4 * kg + v) + cb];
+  }
+  if (has16) {
     half8_t qhi[KC], qlo[KC];
     const float unscale = build_q<D, false>(qrow, nullptr, head_ok, kg, qhi, qlo);
     auto tile16 = [&](const Raw16<D>& r, int t) {
@@ -375,10 +440,11 @@ void attn_decode_kernel(AttnArgs a) {
         s = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, qhi[kc], s, 0, 0, 0);
         s = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, qlo[kc], s, 0, 0, 0);
       }
+      s *= unscale;
+      if (j0 + 16 > f + 1) {  // tail tile (uniform)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int jj = j0 + 4 * kg + v;
-        s[v] = !head_ok ? 0.f : (jj <= f ? s[v] * unscale : -INFINITY);
+        for (int v = 0; v < 4; ++v)
+          if (head_ok && j0 + 4 * kg + v > f) s[v] = -INFINITY;
       }
       store_scores(p16 + j0, s);
       const half4_t pT = softmax_tile<CB>(s, st, acc);
@@ -391,14 +457,16 @@ void attn_decode_kernel(AttnArgs a) {
         acc[cb] = __builtin_amdgcn_mfma_f32_16x16x16f16(as_half4(av), pT, acc[cb], 0, 0, 0);
       }
     };
-    for (int t = w; t < nt16; t += 2 * kWaves) {
-      const int t1 = t + kWaves;
-      if (t1 < nt16) load16(rb, t1);
+    const int m16 = (nt16 - w + kWaves - 1) / kWaves;
+    int j = 0;
+    for (; j + 2 <= m16; j += 2) {
+      const int t = w + kWaves * j;
+      load16(rb, t + kWaves);
       tile16(ra, t);
-      if (t1 >= nt16) break;
-      if (t1 + kWaves < nt16) load16(ra, t1 + kWaves);
-      tile16(rb, t1);
+      load16(ra, min(t + 2 * kWaves, last16));
+      tile16(rb, t + kWaves);
     }
+    if (j < m16) tile16(ra, w + kWaves * j);
   }
 
   // -------------------------------------------------------------- merge
@@ -428,7 +496,7 @@ void attn_decode_kernel(AttnArgs a) {
     const int p = i < n8 ? i : p16 + (i - n8);
     float sum = 0.f;
     for (int hh = 0; hh < g; ++hh) {
-      const float s = p < n_lds ? sc[(size_t)hh * n_lds + p] : spill[(size_t)hh * a.spill_stride + p];
+      const float s = (!SPILL || p < n_lds) ? sc[(size_t)hh * n_lds + p] : spill[(size_t)hh * a.spill_stride + p];
       sum += exp2f(s - Mh[hh]) * iL[hh];
     }
     mout[i] = sum;
@@ -458,9 +526,8 @@ void attn_decode_kernel(AttnArgs a) {
 }  // namespace
 
 int attention_lds_bytes(int d, int g, int n_lds) {
-  const int sc = g * n_lds;
-  const int red = kWaves * g * d;
-  return 4 * (sc > red ? sc : red);
+  // scores / output reduction, the query, K and V scales
+  return 4 * score_area_floats(d, g, n_lds) + 2 * g * d + 8 * d;
 }
 
 // Score slots per head: padded INT8 tiles + padded FP16 tiles (incl. new).
@@ -481,10 +548,13 @@ int attention_plan_n_lds(int d, int g, int cap, int* spill_stride) {
 
 hipError_t launch_attention(const AttnArgs& a, int lds_bytes, hipStream_t s) {
   const int units = a.nl * a.c.B * a.c.hkv;
+  const dim3 grid(units), block(kThreads);
   if (a.c.d == 128) {
-    hipLaunchKernelGGL(attn_decode_kernel<128>, dim3(units), dim3(kThreads), lds_bytes, s, a);
+    if (a.spill) hipLaunchKernelGGL((attn_decode_kernel<128, true>), grid, block, lds_bytes, s, a);
+    else hipLaunchKernelGGL((attn_decode_kernel<128, false>), grid, block, lds_bytes, s, a);
   } else {
-    hipLaunchKernelGGL(attn_decode_kernel<64>, dim3(units), dim3(kThreads), lds_bytes, s, a);
+    if (a.spill) hipLaunchKernelGGL((attn_decode_kernel<64, true>), grid, block, lds_bytes, s, a);
+    else hipLaunchKernelGGL((attn_decode_kernel<64, false>), grid, block, lds_bytes, s, a);
   }
   return hipGetLastError();
 }

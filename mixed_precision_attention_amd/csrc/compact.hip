@@ -27,10 +27,12 @@
 //     base and shift the survivors after the first hole down, or advance the
 //     base and shift the survivors before the last hole up. The movers'
 //     sources go to a plan in the workspace.
-// Move (one workgroup per (layer, sequence, kv head, K|V) ring): the planned
-// rows move in rounds (read all rows of a round, barrier, write them) in an
-// order that never overwrites an unread source; then the new token's row is
-// written to the FP16 ring.
+// Move (one wave per (layer, sequence, kv head, K|V) ring): the planned rows
+// move in rounds (read all rows of a round, wait, write them) in an order that
+// never overwrites an unread source; then the new token's row is written to
+// the FP16 ring.
+#include <type_traits>
+
 #include "confk_internal.h"
 
 namespace confk {
@@ -43,8 +45,8 @@ constexpr int kRegKeys = 8;    // indices per thread held in registers
 constexpr int kBuckets = 1024;
 constexpr int kRankMax = 64;   // boundary-bucket keys ranked by one wave
 constexpr int kHdr = 16;       // plan header words per (layer, sequence)
-constexpr int kMoveThreads = 256;
-constexpr int kMoveRegs = 4;   // 16-byte pieces per thread per round
+constexpr int kMoveRegs8 = 8;   // 16-byte pieces per lane per round, INT8 ring
+constexpr int kMoveRegs16 = 4;  // 16-byte pieces per lane per round, FP16 ring
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -511,45 +513,44 @@ __global__ __launch_bounds__(kThreads) void compact_plan_kernel(CompactArgs a) {
   }
 }
 
-// One workgroup per (layer, sequence, kv head, K|V): planned row moves of the
+// One wave per (layer, sequence, kv head, K|V): planned row moves of the
 // head's INT8 and FP16 rings, then the new token's row. The plan header, the
-// first round of both rings' source lists and the new row are read in one
-// round trip, the first round's rows in a second; one barrier separates all
-// reads from all writes. Rings whose movers exceed one round continue in
-// further rounds (read, barrier, write), in plan order.
-__global__ __launch_bounds__(kMoveThreads) void compact_move_kernel(CompactArgs a) {
+// source indices of the first rounds (one row per lane) and the new row are
+// read in one round trip, the rows in a second; a wave orders its own loads
+// before its stores with a counter wait, so no barrier is needed. Rounds of
+// one ring follow plan order: round r+1 reads only slots beyond round r's
+// destinations in the packing direction.
+template <int D>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(6)))
+void compact_move_kernel(CompactArgs a) {
   typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
   const CacheView& c = a.c;
+  const int lane = threadIdx.x;
   const int lb = blockIdx.x;
   const int hh = blockIdx.y;
   const int kv = blockIdx.z;
   const int l = lb / c.B;
   const int b = lb - l * c.B;
   const int lbc = (a.layer0 + l) * c.B + b;
-  const int H = c.hkv, D = c.d;
+  const int H = c.hkv;
   const int cap = c.cap;
   const int32_t* hdr = a.plan + (size_t)lb * (kHdr + 2 * (size_t)cap);
   const int32_t* src8 = hdr + kHdr;
   const int32_t* src16 = src8 + cap;
   const size_t hrow = (size_t)lbc * H + hh;
-  const int p8 = D / 16, p16 = D / 8;  // 16-byte pieces per row
-  const int per8 = kMoveRegs * kMoveThreads / p8, per16 = kMoveRegs * kMoveThreads / p16;
+  constexpr int p8 = D / 16, p16 = D / 8;  // 16-byte pieces per row
+  constexpr int per8 = kMoveRegs8 * 64 / p8 < 64 ? kMoveRegs8 * 64 / p8 : 64;
+  constexpr int per16 = kMoveRegs16 * 64 / p16 < 64 ? kMoveRegs16 * 64 / p16 : 64;
 
-  // round trip 1: header, first-round sources (speculative), new row
+  // round trip 1: header, first-round source indices (speculative), new row
   const i32x4 hA = reinterpret_cast<const i32x4*>(hdr)[0];
   const i32x4 hB = reinterpret_cast<const i32x4*>(hdr)[1];
   const i32x4 hC = reinterpret_cast<const i32x4*>(hdr)[2];
-  int s8[kMoveRegs], s16[kMoveRegs];
-#pragma unroll
-  for (int q = 0; q < kMoveRegs; ++q) {
-    const int u = threadIdx.x + q * kMoveThreads;
-    const int m8 = u / p8, m16 = u / p16;
-    s8[q] = m8 < min(per8, cap) ? src8[m8] : 0;
-    s16[q] = m16 < min(per16, cap) ? src16[m16] : 0;
-  }
+  const int sl8 = lane < min(per8, cap) ? src8[lane] : 0;
+  const int sl16 = lane < min(per16, cap) ? src16[lane] : 0;
   const uint16_t* nsrc = (kv ? a.v_new : a.k_new) + ((size_t)lb * H + hh) * D;
   u32x4 nrow = {0u, 0u, 0u, 0u};
-  if ((int)threadIdx.x < p16) nrow = *reinterpret_cast<const u32x4*>(nsrc + threadIdx.x * 8);
+  if (lane < p16) nrow = *reinterpret_cast<const u32x4*>(nsrc + lane * 8);
   const int mov8 = hA[H_MOV8], left8 = hA[H_LEFT8], e8 = hA[H_E8], jlo8 = hA[H_JLO8];
   const int mov16 = hB[H_MOV16 - 4], left16 = hB[H_LEFT16 - 4], e16 = hB[H_E16 - 4],
             jlo16 = hB[H_JLO16 - 4];
@@ -564,76 +565,48 @@ __global__ __launch_bounds__(kMoveThreads) void compact_move_kernel(CompactArgs 
     int d = base + (left ? j : j + e);
     return d >= C ? d - C : d;
   };
+  auto src_slot = [](int s, int base, int C) {
+    int v = base + s;
+    return v >= C ? v - C : v;
+  };
 
-  // round trip 2: the first round's rows of both rings
-  const int n8r = min(mov8, per8), n16r = min(mov16, per16);
-  u32x4 b8[kMoveRegs], b16[kMoveRegs];
-#pragma unroll
-  for (int q = 0; q < kMoveRegs; ++q) {
-    const int u = threadIdx.x + q * kMoveThreads;
-    if (u / p8 < n8r) {
-      int sl = base8 + s8[q];
-      if (sl >= cap) sl -= cap;
-      b8[q] = *reinterpret_cast<const u32x4*>(ring8 + (size_t)sl * D + (u % p8) * 16);
-    }
-    if (u / p16 < n16r) {
-      int sl = base16 + s16[q];
-      if (sl >= c.cap16) sl -= c.cap16;
-      b16[q] = *reinterpret_cast<const u32x4*>(ring16 + (size_t)sl * 2 * D + (u % p16) * 16);
-    }
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();  // every source of the first round has been read
-#pragma unroll
-  for (int q = 0; q < kMoveRegs; ++q) {
-    const int u = threadIdx.x + q * kMoveThreads;
-    if (u / p8 < n8r) {
-      const int d = dst_slot(u / p8, mov8, left8, e8, jlo8, base8, cap);
-      *reinterpret_cast<u32x4*>(ring8 + (size_t)d * D + (u % p8) * 16) = b8[q];
-    }
-    if (u / p16 < n16r) {
-      const int d = dst_slot(u / p16, mov16, left16, e16, jlo16, base16, c.cap16);
-      *reinterpret_cast<u32x4*>(ring16 + (size_t)d * 2 * D + (u % p16) * 16) = b16[q];
-    }
-  }
-
-  // further rounds (large evictions): sources of round r+1 lie beyond round
-  // r's destinations in the packing direction
-  auto rounds = [&](unsigned char* ring, int rowbytes, int pieces, int per, int movers, int left,
-                    int e, int jlo, int base, int C, const int32_t* src) {
-    for (int m0 = per; m0 < movers; m0 += per) {
+  // round trip 2 onwards: rounds of each ring in plan order
+  auto rounds = [&](auto nregs_c, auto pieces_c, unsigned char* ring, int rowbytes, int per, int movers,
+                    int left, int e, int jlo, int base, int C, const int32_t* src, int sl0) {
+    constexpr int NR = decltype(nregs_c)::value;
+    constexpr int pieces = decltype(pieces_c)::value;
+    for (int m0 = 0; m0 < movers; m0 += per) {
       const int mend = min(movers, m0 + per);
-      u32x4 buf[kMoveRegs];
+      const int sl = m0 == 0 ? sl0 : (m0 + lane < mend ? src[m0 + lane] : 0);
+      u32x4 buf[NR];
 #pragma unroll
-      for (int q = 0; q < kMoveRegs; ++q) {
-        const int u = threadIdx.x + q * kMoveThreads;
-        const int m = m0 + u / pieces;
-        if (m < mend) {
-          int sl = base + src[m];
-          if (sl >= C) sl -= C;
-          buf[q] = *reinterpret_cast<const u32x4*>(ring + (size_t)sl * rowbytes + (u % pieces) * 16);
-        }
+      for (int q = 0; q < NR; ++q) {
+        const int u = lane + 64 * q, r = u / pieces;
+        const int s = __shfl(sl, r & 63, 64);
+        if (m0 + r < mend)
+          buf[q] = *reinterpret_cast<const u32x4*>(
+              ring + (uint32_t)(src_slot(s, base, C) * rowbytes + (u % pieces) * 16));
       }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
 #pragma unroll
-      for (int q = 0; q < kMoveRegs; ++q) {
-        const int u = threadIdx.x + q * kMoveThreads;
-        const int m = m0 + u / pieces;
-        if (m < mend) {
-          const int d = dst_slot(m, movers, left, e, jlo, base, C);
-          *reinterpret_cast<u32x4*>(ring + (size_t)d * rowbytes + (u % pieces) * 16) = buf[q];
+      for (int q = 0; q < NR; ++q) {
+        const int u = lane + 64 * q, r = u / pieces;
+        if (m0 + r < mend) {
+          const int d = dst_slot(m0 + r, movers, left, e, jlo, base, C);
+          *reinterpret_cast<u32x4*>(ring + (uint32_t)(d * rowbytes + (u % pieces) * 16)) = buf[q];
         }
       }
     }
   };
-  if (mov8 > per8) rounds(ring8, D, p8, per8, mov8, left8, e8, jlo8, base8, cap, src8);
-  if (mov16 > per16) rounds(ring16, 2 * D, p16, per16, mov16, left16, e16, jlo16, base16, c.cap16, src16);
+  rounds(std::integral_constant<int, kMoveRegs8>{}, std::integral_constant<int, p8>{}, ring8, D, per8, mov8,
+         left8, e8, jlo8, base8, cap, src8, sl8);
+  rounds(std::integral_constant<int, kMoveRegs16>{}, std::integral_constant<int, p16>{}, ring16, 2 * D, per16,
+         mov16, left16, e16, jlo16, base16, c.cap16, src16, sl16);
 
-  // append: every FP16 source has been read (barrier above), and the slot is
-  // not a destination
-  if ((int)threadIdx.x < p16) {
-    uint16_t* dst = (kv ? c.v16 : c.k16) + (hrow * c.cap16 + append) * D + threadIdx.x * 8;
+  // append: every FP16 source has been read (the waits above), and the slot
+  // is not a destination
+  if (lane < p16) {
+    uint16_t* dst = (kv ? c.v16 : c.k16) + (hrow * c.cap16 + append) * D + lane * 8;
     *reinterpret_cast<u32x4*>(dst) = nrow;
   }
 }
@@ -661,7 +634,11 @@ hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(compact_move_kernel, dim3(blocks, a.c.hkv, 2), dim3(kMoveThreads), 0, s, a);
+  if (a.c.d == 128) {
+    hipLaunchKernelGGL(compact_move_kernel<128>, dim3(blocks, a.c.hkv, 2), dim3(64), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(compact_move_kernel<64>, dim3(blocks, a.c.hkv, 2), dim3(64), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -10,8 +10,8 @@
 // and the states merge associatively; from the merged row state
 //   H = ln S - T/S,   p1 = 1/S,   ln p1 - ln p2 = top1 - top2.
 // Rows are split over many workgroups (HBM-bound: each logit is read once);
-// the workgroup that finishes a row's last chunk merges the per-chunk states
-// in a fixed order, so the result does not depend on scheduling.
+// a second tiny kernel merges the per-chunk states in a fixed order, so the
+// result does not depend on scheduling.
 #include "confk_internal.h"
 
 namespace confk {
@@ -140,7 +140,6 @@ __global__ __launch_bounds__(kThreads) void conf_partial_kernel(ConfArgs a) {
   const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) red[w] = s;
   __syncthreads();
-  __shared__ int is_last;
   if (threadIdx.x == 0) {
     RowState r = red[0];
     for (int i = 1; i < kThreads / 64; ++i) r = merge(r, red[i]);
@@ -151,16 +150,13 @@ __global__ __launch_bounds__(kThreads) void conf_partial_kernel(ConfArgs a) {
     p[3] = r.t1;
     p[4] = r.t2;
     p[5] = __builtin_bit_cast(float, r.flag);
-    __threadfence();  // the partial is visible before the count
-    is_last = atomicAdd(&a.counter[b], 1u) == (uint32_t)(a.nchunks - 1);
   }
-  __syncthreads();
-  if (!is_last || threadIdx.x >= 64) return;
-  // The row's last chunk to finish merges all partials: lane i takes
-  // partials i, i+64, ... in order, then a butterfly merge (commutative, so
-  // every lane ends with the same state; the result does not depend on which
-  // block finished last).
-  __threadfence();
+}
+
+// One wave per row: lane i merges partials i, i+64, ... in order, then a
+// butterfly merge (commutative, so every lane ends with the same state).
+__global__ __launch_bounds__(64) void conf_final_kernel(ConfArgs a) {
+  const int b = blockIdx.x;
   const int lane = threadIdx.x;
   const float* p = a.partial + (int64_t)b * a.nchunks * 6;
   RowState r;
@@ -183,7 +179,6 @@ __global__ __launch_bounds__(kThreads) void conf_partial_kernel(ConfArgs a) {
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) r = merge(r, shfl_state(r, o));
   if (lane != 0) return;
-  a.counter[b] = 0u;  // ready for the next call
   float c;
   const bool bad = r.flag != 0 || !(r.M > -INFINITY);
   if (bad) {
@@ -208,19 +203,19 @@ __global__ __launch_bounds__(kThreads) void conf_partial_kernel(ConfArgs a) {
 
 }  // namespace
 
-// Workspace: per-chunk partial states, then one arrival counter per row
-// (zero before the first call; every call leaves it zero).
 size_t confidence_ws_bytes(int32_t batch, int32_t vocab) {
   const int nchunks = (vocab + kChunk - 1) / kChunk;
-  return (size_t)batch * nchunks * 6 * sizeof(float) + (size_t)batch * sizeof(uint32_t);
+  return (size_t)batch * nchunks * 6 * sizeof(float);
 }
 
 hipError_t launch_confidence(const ConfArgs& in, hipStream_t s) {
   ConfArgs a = in;
   a.chunk = kChunk;
   a.nchunks = (a.vocab + kChunk - 1) / kChunk;
-  a.counter = reinterpret_cast<uint32_t*>(a.partial + (size_t)a.batch * a.nchunks * 6);
   hipLaunchKernelGGL(conf_partial_kernel, dim3(a.nchunks, a.batch), dim3(kThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(conf_final_kernel, dim3(a.batch), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 

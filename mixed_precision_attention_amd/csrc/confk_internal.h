@@ -41,8 +41,7 @@ struct ConfArgs {
   int32_t n_high, n_low;
   const int32_t* layer_n_high;
   const int32_t* layer_n_low;
-  float* partial;     // [batch][nchunks][6]
-  uint32_t* counter;  // [batch] chunk arrivals per row
+  float* partial;  // [batch][nchunks][6]
   float* c_out;
   int32_t* budget_out;
   uint32_t* status;

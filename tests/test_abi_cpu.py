@@ -109,7 +109,7 @@ def test_attention_workspace_needed_only_for_long_caches(lib):
     assert need > 0
     assert lib.confk_attn_decode(ctypes.byref(big), 0, 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 4,
                                  None) == M.ERR_WORKSPACE
-    assert lib.confk_workspace_size(M._lib.WS_CONFIDENCE, None, 0, 8, 152064) == 8 * 38 * 6 * 4 + 8 * 4
+    assert lib.confk_workspace_size(M._lib.WS_CONFIDENCE, None, 0, 8, 152064) == 8 * 38 * 6 * 4
 
 
 def test_compact_quantize_ema_validation(lib):
