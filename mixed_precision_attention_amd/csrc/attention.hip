@@ -51,7 +51,15 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 4;
+// Waves per workgroup (one workgroup per (layer, sequence, kv head)) and the
+// target waves per SIMD; the register budget follows from the latter.
+#ifndef CONFK_ATTN_WAVES
+#define CONFK_ATTN_WAVES 4
+#endif
+#ifndef CONFK_ATTN_OCCUPANCY
+#define CONFK_ATTN_OCCUPANCY 3
+#endif
+constexpr int kWaves = CONFK_ATTN_WAVES;
 constexpr int kThreads = kWaves * 64;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kScoreLdsBytes = 48 * 1024;  // LDS budget for the score store (3 groups per CU)
@@ -153,12 +161,30 @@ struct SoftState {
   float l;  // partial normaliser over this lane's keys
 };
 
-// Online-softmax update for one 16-key tile; returns P^T operand.
+// max without NaN canonicalisation (operands are finite scores or -inf)
+__device__ __forceinline__ float fmax_raw(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
+// Max over the four lanes {l, l^16, l^32, l^48} (the 16 keys of a tile for
+// one head): two cross-row swaps, no LDS round trip.
+__device__ __forceinline__ float tile_max(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const float y = fmax_raw(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t v = __float_as_uint(y);
+  const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return fmax_raw(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Online-softmax update for one 16-key tile of raw scores s (true score =
+// s * unscale, log2 units); returns the P^T operand.
 template <int CB>
-__device__ __forceinline__ half4_t softmax_tile(float4_t s, SoftState& st, float4_t* acc) {
-  float tmax = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+__device__ __forceinline__ half4_t softmax_tile(float4_t s, float unscale, SoftState& st,
+                                                float4_t* acc) {
+  const float tmax = tile_max(fmax_raw(fmax_raw(s[0], s[1]), fmax_raw(s[2], s[3]))) * unscale;
   const float mnew = fmaxf(st.m, tmax);
   if (__any(mnew > st.m)) {
     const float corr = __builtin_amdgcn_exp2f(st.m - mnew);
@@ -171,7 +197,7 @@ __device__ __forceinline__ half4_t softmax_tile(float4_t s, SoftState& st, float
   float lsum = 0.f;
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-    const float e = __builtin_amdgcn_exp2f(s[v] - mnew);
+    const float e = __builtin_amdgcn_exp2f(fmaf(s[v], unscale, -mnew));
     lsum += e;
     p[v] = (_Float16)e;
   }
@@ -205,7 +231,7 @@ __host__ __device__ __forceinline__ int score_area_floats(int d, int g, int n_ld
 // common instance because global stores in the tile loop make the load
 // counter unusable for partial waits (stores complete out of order).
 template <int D, bool SPILL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(CONFK_ATTN_OCCUPANCY)))
 void attn_decode_kernel(AttnArgs a) {
   constexpr int KC = Tile<D>::KC;
   constexpr int CB = Tile<D>::CB;
@@ -264,6 +290,9 @@ void attn_decode_kernel(AttnArgs a) {
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) acc[cb] = (float4_t){0.f, 0.f, 0.f, 0.f};
   SoftState st{-INFINITY, 0.f};
+  // Stored scores are raw products; usc[0] / usc[1] turn INT8 / FP16 region
+  // scores into log2 units.
+  __shared__ float usc[2];
 
   auto store_scores = [&](int p0, float4_t s) {
     if (!head_ok) return;
@@ -276,26 +305,41 @@ void attn_decode_kernel(AttnArgs a) {
   };
 
   // ------------------------------------------------------------ tile loads
-  auto slot8 = [&](int i) {  // ring slot of INT8 logical index i (clamped to the region)
-    int s = base8 + min(i, max(n8 - 1, 0));
-    return s >= c.cap ? s - c.cap : s;
-  };
-  auto load8 = [&](Raw8<D>& r, int t) {
-    const int i0 = t * 16;
-    const int8_t* krow = k8 + (size_t)slot8(i0 + r16) * D;
+  // INT8 rows: running ring slots of this lane's K row and first V row in
+  // the next tile this wave loads (tiles w, w+kWaves, ... in order). Loads
+  // past the region repeat the wave's last tile (cache hits), so the
+  // pipelined loops below need no conditional loads. 32-bit byte offsets
+  // from the uniform ring base.
+  const int last8 = max(nt8 - 1, 0);
+  const uint32_t cap = (uint32_t)c.cap;
+  auto wrap = [&](uint32_t x) { return min(x, x - cap); };  // x < 2 cap
+  const uint32_t step8 = (uint32_t)(16 * kWaves) % cap;
+  uint32_t vinc[4];
 #pragma unroll
-    for (int uu = 0; uu < KU; ++uu) r.k[uu] = *reinterpret_cast<const u32x4*>(krow + 64 * uu + 16 * kg);
+  for (int j = 0; j < 4; ++j) vinc[j] = (uint32_t)j % cap;
+  int tnext = min(w, last8);  // tile of the next load (uniform)
+  uint32_t sk = (uint32_t)((base8 + 16 * tnext + r16) % c.cap);
+  uint32_t sv = (uint32_t)((base8 + 16 * tnext + 4 * kg) % c.cap);
+  auto load8 = [&](Raw8<D>& r) {
+    const uint32_t ko = sk * D + 16 * kg;
+#pragma unroll
+    for (int uu = 0; uu < KU; ++uu) r.k[uu] = *reinterpret_cast<const u32x4*>(k8 + ko + 64 * uu);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int8_t* vrow = v8 + (size_t)slot8(i0 + 4 * kg + j) * D + (D / 16) * r16;
+      const uint32_t vo = wrap(sv + vinc[j]) * D + (D / 16) * r16;
       if constexpr (CB == 8) {
-        const u32x2 t2 = *reinterpret_cast<const u32x2*>(vrow);
+        const u32x2 t2 = *reinterpret_cast<const u32x2*>(v8 + vo);
         r.v[j][0] = t2[0];
         r.v[j][1] = t2[1];
       } else {
-        r.v[j][0] = *reinterpret_cast<const uint32_t*>(vrow);
+        r.v[j][0] = *reinterpret_cast<const uint32_t*>(v8 + vo);
       }
     }
+    const bool adv = tnext + kWaves <= last8;
+    const uint32_t by = adv ? step8 : 0u;
+    tnext += adv ? kWaves : 0;
+    sk = wrap(sk + by);
+    sv = wrap(sv + by);
   };
   auto row16 = [&](const uint16_t* ring, const uint16_t* nw, int jj) {  // FP16-local index jj
     if (jj >= f) return nw;  // the new token (also the clamp target of tail rows)
@@ -343,13 +387,12 @@ void attn_decode_kernel(AttnArgs a) {
     piece[z] = *src;
   }
   const bool has8 = nt8 > w;  // this wave has INT8 tiles (uniform per wave)
-  const int last8 = max(nt8 - 1, 0);
   Raw8<D> ra8, rb8, rc8;
   // Loads past the region are clamped to its last tile (rows are read, never
   // used; an empty region reads its ring's first slot), so no load below is
   // conditional and the load counter allows partial waits everywhere.
-  load8(ra8, min(w, last8));
-  load8(rb8, min(w + kWaves, last8));
+  load8(ra8);
+  load8(rb8);
 #pragma unroll
   for (int z = 0; z < 2; ++z) {
     const int e = threadIdx.x + z * kThreads;
@@ -365,6 +408,7 @@ void attn_decode_kernel(AttnArgs a) {
   if (has8) {
     half8_t qhi[KC], qlo[KC];
     const float unscale = build_q<D, true>(qrow, ks_lds, head_ok, kg, qhi, qlo);
+    if (w == 0) usc[0] = unscale;  // every wave computes the same factor
     auto tile8 = [&](const Raw8<D>& r, int t) {
       const int i0 = t * 16;
       float4_t s = {0.f, 0.f, 0.f, 0.f};
@@ -381,14 +425,13 @@ void attn_decode_kernel(AttnArgs a) {
         s = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, qhi[kc], s, 0, 0, 0);
         s = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, qlo[kc], s, 0, 0, 0);
       }
-      s *= unscale;  // padded heads have zero queries and so zero scores
       if (i0 + 16 > n8) {  // tail tile (uniform)
 #pragma unroll
         for (int v = 0; v < 4; ++v)
           if (head_ok && i0 + 4 * kg + v >= n8) s[v] = -INFINITY;
       }
       store_scores(i0, s);
-      const half4_t pT = softmax_tile<CB>(s, st, acc);
+      const half4_t pT = softmax_tile<CB>(s, unscale, st, acc);
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
         const int wd = cb >> 2, bb = cb & 3;
@@ -405,11 +448,11 @@ void attn_decode_kernel(AttnArgs a) {
     int j = 0;
     for (; j + 3 <= m8; j += 3) {
       const int t = w + kWaves * j;
-      load8(rc8, t + 2 * kWaves);
+      load8(rc8);
       tile8(ra8, t);
-      load8(ra8, min(t + 3 * kWaves, last8));
+      load8(ra8);
       tile8(rb8, t + kWaves);
-      load8(rb8, min(t + 4 * kWaves, last8));
+      load8(rb8);
       tile8(rc8, t + 2 * kWaves);
     }
     if (j < m8) tile8(ra8, w + kWaves * j);
@@ -431,6 +474,7 @@ void attn_decode_kernel(AttnArgs a) {
   if (has16) {
     half8_t qhi[KC], qlo[KC];
     const float unscale = build_q<D, false>(qrow, nullptr, head_ok, kg, qhi, qlo);
+    if (w == 0) usc[1] = unscale;
     auto tile16 = [&](const Raw16<D>& r, int t) {
       const int j0 = t * 16;
       float4_t s = {0.f, 0.f, 0.f, 0.f};
@@ -440,14 +484,13 @@ void attn_decode_kernel(AttnArgs a) {
         s = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, qhi[kc], s, 0, 0, 0);
         s = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, qlo[kc], s, 0, 0, 0);
       }
-      s *= unscale;
       if (j0 + 16 > f + 1) {  // tail tile (uniform)
 #pragma unroll
         for (int v = 0; v < 4; ++v)
           if (head_ok && j0 + 4 * kg + v > f) s[v] = -INFINITY;
       }
       store_scores(p16 + j0, s);
-      const half4_t pT = softmax_tile<CB>(s, st, acc);
+      const half4_t pT = softmax_tile<CB>(s, unscale, st, acc);
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
         const int wd = cb >> 1, hf = cb & 1;
@@ -494,10 +537,11 @@ void attn_decode_kernel(AttnArgs a) {
   float* mout = a.mass + ((size_t)lb * H + h) * c.cap;
   for (int i = threadIdx.x; i < nk; i += kThreads) {
     const int p = i < n8 ? i : p16 + (i - n8);
+    const float u = i < n8 ? usc[0] : usc[1];
     float sum = 0.f;
     for (int hh = 0; hh < g; ++hh) {
       const float s = (!SPILL || p < n_lds) ? sc[(size_t)hh * n_lds + p] : spill[(size_t)hh * a.spill_stride + p];
-      sum += exp2f(s - Mh[hh]) * iL[hh];
+      sum += exp2f(fmaf(s, u, -Mh[hh])) * iL[hh];
     }
     mout[i] = sum;
   }
