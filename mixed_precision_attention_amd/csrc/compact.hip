@@ -45,8 +45,7 @@ constexpr int kRegKeys = 8;    // indices per thread held in registers
 constexpr int kBuckets = 1024;
 constexpr int kRankMax = 64;   // boundary-bucket keys ranked by one wave
 constexpr int kHdr = 16;       // plan header words per (layer, sequence)
-constexpr int kMoveRegs8 = 8;   // 16-byte pieces per lane per round, INT8 ring
-constexpr int kMoveRegs16 = 4;  // 16-byte pieces per lane per round, FP16 ring
+constexpr int kMoveRegs = 8;  // 16-byte pieces per lane per move round
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -513,102 +512,116 @@ __global__ __launch_bounds__(kThreads) void compact_plan_kernel(CompactArgs a) {
   }
 }
 
-// One wave per (layer, sequence, kv head, K|V): planned row moves of the
-// head's INT8 and FP16 rings, then the new token's row. The plan header, the
-// source indices of the first rounds (one row per lane) and the new row are
-// read in one round trip, the rows in a second; a wave orders its own loads
-// before its stores with a counter wait, so no barrier is needed. Rounds of
-// one ring follow plan order: round r+1 reads only slots beyond round r's
+template <int D, int LGP, int NW>
+__device__ __forceinline__ void ring_rounds(unsigned char* ringk, unsigned char* ringv, int C, int movers,
+                                            int left, int e, int jlo, int base, const int32_t* src, int* sv,
+                                            bool have) {
+  constexpr int NR = D == 128 ? kMoveRegs : kMoveRegs - 2;  // 16-byte pieces per lane per ring per round
+  constexpr int ROWS = (NR * 64) >> LGP;                    // rows per round
+  constexpr int ROWB = 16 << LGP;                           // bytes per row
+  const int lane = threadIdx.x;
+  int win = have ? 0 : -64 * NW;  // first mover of the source window held in sv (64 * NW movers)
+  for (int m0 = 0; m0 < movers; m0 += ROWS) {
+    if (m0 >= win + 64 * NW) {  // next source window (uniform)
+      win = m0;
+#pragma unroll
+      for (int q = 0; q < NW; ++q) sv[q] = win + lane + 64 * q < movers ? src[win + lane + 64 * q] : 0;
+    }
+    u32x4 bk[NR], bv[NR];
+#pragma unroll
+    for (int q = 0; q < NR; ++q) {
+      const int u = lane + 64 * q;
+      const int r = m0 + (u >> LGP);  // mover of this piece
+      int sel = sv[0];
+#pragma unroll
+      for (int z = 1; z < NW; ++z) sel = ((r - win) >> 6) == z ? sv[z] : sel;  // uniform for a given q
+      const int sidx = __shfl(sel, r & 63, 64);
+      if (r < movers) {
+        int ss = base + sidx;
+        ss = ss >= C ? ss - C : ss;
+        const uint32_t o = (uint32_t)ss * ROWB + (u & ((1 << LGP) - 1)) * 16;
+        bk[q] = *reinterpret_cast<const u32x4*>(ringk + o);
+        bv[q] = *reinterpret_cast<const u32x4*>(ringv + o);
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int q = 0; q < NR; ++q) {
+      const int u = lane + 64 * q;
+      const int r = m0 + (u >> LGP);
+      if (r < movers) {
+        const int j = jlo + (left ? r : movers - 1 - r);
+        int ds = base + (left ? j : j + e);
+        ds = ds >= C ? ds - C : ds;
+        const uint32_t o = (uint32_t)ds * ROWB + (u & ((1 << LGP) - 1)) * 16;
+        *reinterpret_cast<u32x4*>(ringk + o) = bk[q];
+        *reinterpret_cast<u32x4*>(ringv + o) = bv[q];
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ unsigned char* uniform_ptr(const void* p) {
+  const uint64_t rp = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)rp);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(rp >> 32));
+  return (unsigned char*)(((uint64_t)hi << 32) | lo);
+}
+
+// One wave per (layer, sequence, kv head): the planned moves of that head's
+// K and V INT8 rings, then of its FP16 rings, then the append. Round trip 1
+// reads the plan header, the first 256 INT8 movers' source indices
+// (speculatively) and the new token's K and V rows; round trip 2 reads the
+// first round's rows (64 INT8 / 32 FP16 rows of each ring at d = 128), which
+// are then written; longer plans take more rounds. A wave orders its own
+// loads before its stores with a counter wait, so no barrier is needed.
+// Rounds follow plan order: round r+1 reads only slots beyond round r's
 // destinations in the packing direction.
 template <int D>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(6)))
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4)))
 void compact_move_kernel(CompactArgs a) {
   typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+  constexpr int L8 = D == 128 ? 3 : 2, L16 = L8 + 1;  // log2 of 16-byte pieces per row
+  constexpr int P16 = D / 8;
   const CacheView& c = a.c;
   const int lane = threadIdx.x;
   const int lb = blockIdx.x;
   const int hh = blockIdx.y;
-  const int kv = blockIdx.z;
   const int l = lb / c.B;
   const int b = lb - l * c.B;
   const int lbc = (a.layer0 + l) * c.B + b;
   const int H = c.hkv;
-  const int cap = c.cap;
+  const int cap = c.cap, cap16 = c.cap16;
   const int32_t* hdr = a.plan + (size_t)lb * (kHdr + 2 * (size_t)cap);
   const int32_t* src8 = hdr + kHdr;
   const int32_t* src16 = src8 + cap;
   const size_t hrow = (size_t)lbc * H + hh;
-  constexpr int p8 = D / 16, p16 = D / 8;  // 16-byte pieces per row
-  constexpr int per8 = kMoveRegs8 * 64 / p8 < 64 ? kMoveRegs8 * 64 / p8 : 64;
-  constexpr int per16 = kMoveRegs16 * 64 / p16 < 64 ? kMoveRegs16 * 64 / p16 : 64;
 
-  // round trip 1: header, first-round source indices (speculative), new row
-  const i32x4 hA = reinterpret_cast<const i32x4*>(hdr)[0];
-  const i32x4 hB = reinterpret_cast<const i32x4*>(hdr)[1];
-  const i32x4 hC = reinterpret_cast<const i32x4*>(hdr)[2];
-  const int sl8 = lane < min(per8, cap) ? src8[lane] : 0;
-  const int sl16 = lane < min(per16, cap) ? src16[lane] : 0;
-  const uint16_t* nsrc = (kv ? a.v_new : a.k_new) + ((size_t)lb * H + hh) * D;
+  // round trip 1
+  const i32x4 hA = reinterpret_cast<const i32x4*>(hdr)[0];  // MOV8, LEFT8, E8, JLO8
+  const i32x4 hB = reinterpret_cast<const i32x4*>(hdr)[1];  // MOV16, LEFT16, E16, JLO16
+  const i32x4 hC = reinterpret_cast<const i32x4*>(hdr)[2];  // BASE8, BASE16, APPEND
+  int sv8[4], sv16[1] = {0};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) sv8[q] = lane + 64 * q < cap ? src8[lane + 64 * q] : 0;
+  const int nkv = lane / P16;  // lanes [0, P16): K piece, [P16, 2 P16): V piece of the new row
   u32x4 nrow = {0u, 0u, 0u, 0u};
-  if (lane < p16) nrow = *reinterpret_cast<const u32x4*>(nsrc + lane * 8);
-  const int mov8 = hA[H_MOV8], left8 = hA[H_LEFT8], e8 = hA[H_E8], jlo8 = hA[H_JLO8];
-  const int mov16 = hB[H_MOV16 - 4], left16 = hB[H_LEFT16 - 4], e16 = hB[H_E16 - 4],
-            jlo16 = hB[H_JLO16 - 4];
-  const int base8 = hC[H_BASE8 - 8], base16 = hC[H_BASE16 - 8], append = hC[H_APPEND - 8];
+  if (lane < 2 * P16)
+    nrow = *reinterpret_cast<const u32x4*>((nkv ? a.v_new : a.k_new) + ((size_t)lb * H + hh) * D +
+                                           (lane - nkv * P16) * 8);
+  const int append = hC[2];
   if (append < 0) return;  // the plan flagged a capacity error
 
-  unsigned char* ring8 = (unsigned char*)((kv ? c.v8 : c.k8) + hrow * cap * D);
-  unsigned char* ring16 = (unsigned char*)((kv ? c.v16 : c.k16) + hrow * c.cap16 * D);
-  // mover m (plan order) -> destination slot
-  auto dst_slot = [](int m, int movers, int left, int e, int jlo, int base, int C) {
-    const int j = jlo + (left ? m : movers - 1 - m);
-    int d = base + (left ? j : j + e);
-    return d >= C ? d - C : d;
-  };
-  auto src_slot = [](int s, int base, int C) {
-    int v = base + s;
-    return v >= C ? v - C : v;
-  };
-
-  // round trip 2 onwards: rounds of each ring in plan order
-  auto rounds = [&](auto nregs_c, auto pieces_c, unsigned char* ring, int rowbytes, int per, int movers,
-                    int left, int e, int jlo, int base, int C, const int32_t* src, int sl0) {
-    constexpr int NR = decltype(nregs_c)::value;
-    constexpr int pieces = decltype(pieces_c)::value;
-    for (int m0 = 0; m0 < movers; m0 += per) {
-      const int mend = min(movers, m0 + per);
-      const int sl = m0 == 0 ? sl0 : (m0 + lane < mend ? src[m0 + lane] : 0);
-      u32x4 buf[NR];
-#pragma unroll
-      for (int q = 0; q < NR; ++q) {
-        const int u = lane + 64 * q, r = u / pieces;
-        const int s = __shfl(sl, r & 63, 64);
-        if (m0 + r < mend)
-          buf[q] = *reinterpret_cast<const u32x4*>(
-              ring + (uint32_t)(src_slot(s, base, C) * rowbytes + (u % pieces) * 16));
-      }
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-#pragma unroll
-      for (int q = 0; q < NR; ++q) {
-        const int u = lane + 64 * q, r = u / pieces;
-        if (m0 + r < mend) {
-          const int d = dst_slot(m0 + r, movers, left, e, jlo, base, C);
-          *reinterpret_cast<u32x4*>(ring + (uint32_t)(d * rowbytes + (u % pieces) * 16)) = buf[q];
-        }
-      }
-    }
-  };
-  rounds(std::integral_constant<int, kMoveRegs8>{}, std::integral_constant<int, p8>{}, ring8, D, per8, mov8,
-         left8, e8, jlo8, base8, cap, src8, sl8);
-  rounds(std::integral_constant<int, kMoveRegs16>{}, std::integral_constant<int, p16>{}, ring16, 2 * D, per16,
-         mov16, left16, e16, jlo16, base16, c.cap16, src16, sl16);
+  ring_rounds<D, L8, 4>(uniform_ptr(c.k8 + hrow * cap * D), uniform_ptr(c.v8 + hrow * cap * D), cap, hA[0],
+                        hA[1], hA[2], hA[3], hC[0], src8, sv8, true);
+  unsigned char* k16 = uniform_ptr(c.k16 + hrow * cap16 * D);
+  unsigned char* v16 = uniform_ptr(c.v16 + hrow * cap16 * D);
+  ring_rounds<D, L16, 1>(k16, v16, cap16, hB[0], hB[1], hB[2], hB[3], hC[1], src16, sv16, false);
 
   // append: every FP16 source has been read (the waits above), and the slot
   // is not a destination
-  if (lane < p16) {
-    uint16_t* dst = (kv ? c.v16 : c.k16) + (hrow * c.cap16 + append) * D + lane * 8;
-    *reinterpret_cast<u32x4*>(dst) = nrow;
-  }
+  if (lane < 2 * P16)
+    *reinterpret_cast<u32x4*>((nkv ? v16 : k16) + (uint32_t)append * (2 * D) + (lane - nkv * P16) * 16) = nrow;
 }
 
 }  // namespace
@@ -635,9 +648,9 @@ hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.c.d == 128) {
-    hipLaunchKernelGGL(compact_move_kernel<128>, dim3(blocks, a.c.hkv, 2), dim3(64), 0, s, a);
+    hipLaunchKernelGGL(compact_move_kernel<128>, dim3(blocks, a.c.hkv), dim3(64), 0, s, a);
   } else {
-    hipLaunchKernelGGL(compact_move_kernel<64>, dim3(blocks, a.c.hkv, 2), dim3(64), 0, s, a);
+    hipLaunchKernelGGL(compact_move_kernel<64>, dim3(blocks, a.c.hkv), dim3(64), 0, s, a);
   }
   return hipGetLastError();
 }

@@ -137,8 +137,15 @@ def workspace_bytes(which, cache=None, nlayers=0, batch=0, vocab=0):
 class DecodeEngine:
     """Buffers of one decode step for a workload config, and the step itself."""
 
-    def __init__(self, cfg, device="cuda"):
+    def __init__(self, cfg, device="cuda", overlap=False):
         self.cfg = cfg
+        # overlap=True: confidence reads only the logits and feeds only the
+        # compaction, so step() may run it on a second stream (default
+        # priority) beside the attention launch. Off by default: in a model the
+        # logits of a step come out of that step's forward pass, after its
+        # attention.
+        self.side = torch.cuda.Stream(device=device) if overlap else None
+        self.conf_done = torch.cuda.Event() if overlap else None
         self.pol = make_policy(cfg.policy)
         self.cache = DeviceCache.for_config(cfg, device)
         Lr, B = cfg.layers, cfg.batch
@@ -189,8 +196,17 @@ class DecodeEngine:
         quantize(self.cache, self.pol, t)
 
     def step(self, logits, q, k_new, v_new, t):
-        self.step_confidence(logits)
+        if self.side is None:
+            self.step_confidence(logits)
+        else:
+            main = torch.cuda.current_stream()
+            self.side.wait_stream(main)  # the logits, and the previous step's use of the budget
+            with torch.cuda.stream(self.side):
+                self.step_confidence(logits)
+            self.conf_done.record(self.side)
         self.step_attention(q, k_new, v_new)
         self.step_ema_rank(t)
+        if self.side is not None:
+            torch.cuda.current_stream().wait_event(self.conf_done)
         self.step_compact(k_new, v_new)
         self.step_quantize(t)

@@ -195,6 +195,17 @@ def test_parity_long_cache_path():
     assert events > 0
 
 
+def test_parity_plan_and_move_kernels_path():
+    """Capacity between the single-kernel limit (2560 slots) and 4096: the
+    plan kernel selects from registers and a second kernel moves the rows."""
+    cfg = _cfg("mid", 1, 2, 5, 1, 128, 700, 3000, 500, 1000, 16, 64)
+    assert 2560 < cfg.cap <= 4096
+    print("[parity] plan + move kernels", flush=True)
+    run = Run(cfg, seed=6)
+    events = sum(run.step(i) for i in range(6))
+    assert events > 0
+
+
 def test_selection_with_tied_scores():
     """Crafted scores with heavy ties (same array on both sides)."""
     cfg = TINY["g5_d128"]
@@ -276,3 +287,41 @@ def test_qwen32b_full_launch_sampled():
     run = Run(cfg, seed=2, pairs=[(0, 0), (31, 4), (63, 7)], device_prefill=True)
     for i in range(2):
         run.step(i)
+
+
+def test_parity_many_heads_multi_round_moves():
+    """16 kv heads of d128 and a large first eviction: the compaction moves
+    take several rounds of the single-kernel path."""
+    cfg = _cfg("h16_d128", 1, 2, 16, 16, 128, 400, 600, 96, 200, 16, 48)
+    print("[parity] h16_d128 multi-round moves", flush=True)
+    run = Run(cfg, seed=5)
+    events = sum(run.step(i) for i in range(6))
+    assert events > 0
+
+
+def test_overlapped_step_matches_serial():
+    """DecodeEngine.step (confidence on a second stream) leaves exactly the
+    state of the five calls issued one after another on one stream."""
+    import mixed_precision_attention_amd as M
+    dev = _dev()
+    cfg = TINY["g5_d128"]
+    kp, vp = synth.prefill_kv(cfg, 3)
+    engs = [M.DecodeEngine(cfg, dev, overlap=True), M.DecodeEngine(cfg, dev, overlap=False)]
+    for e in engs:
+        e.prefill(_t(kp, dev), _t(vp, dev))
+    for i in range(20):
+        logits, q, kn, vn, t = _inputs(cfg, 3, i)
+        lg, qd, kd, vd = _t(logits, dev), _t(q, dev), _t(kn, dev), _t(vn, dev)
+        engs[0].step(lg, qd, kd, vd, t)
+        e = engs[1]
+        e.step_confidence(lg)
+        e.step_attention(qd, kd, vd)
+        e.step_ema_rank(t)
+        e.step_compact(kd, vd)
+        e.step_quantize(t)
+    torch.cuda.synchronize()
+    a, b = engs
+    for name in ("meta", "k8", "v8", "k16", "v16", "kscale", "vscale", "ema", "pos", "status"):
+        assert torch.equal(getattr(a.cache, name), getattr(b.cache, name)), name
+    for name in ("c", "budget", "out", "mass", "score"):
+        assert torch.equal(getattr(a, name), getattr(b, name)), name
