@@ -28,6 +28,23 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "attn_decode_qwen32b_b8_traffic.md")
+
+
+def counted_traffic():
+    """HBM bytes per attention launch from the committed counter summary, or
+    None when the summary is missing or the attention source has changed
+    since the counters were taken."""
+    import hashlib
+    try:
+        line = [l for l in open(TRAFFIC_SUMMARY) if l.startswith("traffic-json:")][-1]
+        rec = json.loads(line.split(":", 1)[1])
+        src = open(os.path.join(ROOT, rec["source"]), "rb").read()
+    except (OSError, IndexError, ValueError, KeyError):
+        return None
+    if hashlib.sha256(src).hexdigest() != rec["source_sha256"]:
+        return None
+    return int(rec["traffic_bytes_per_launch"])
 
 
 def parse():
@@ -241,7 +258,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": counted_traffic(),
             "kernel": "attn_decode_kernel<128>",
             "bytes_per_launch": int(attn_bytes),
         },
