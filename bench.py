@@ -31,10 +31,10 @@ HBM_PEAK_GBS = 8000.0
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "attn_decode_qwen32b_b8_traffic.md")
 
 
-def counted_traffic():
+def counted_traffic(workload):
     """HBM bytes per attention launch from the committed counter summary, or
-    None when the summary is missing or the attention source has changed
-    since the counters were taken."""
+    None when the summary is missing, covers another workload, or the
+    attention source has changed since the counters were taken."""
     import hashlib
     try:
         line = [l for l in open(TRAFFIC_SUMMARY) if l.startswith("traffic-json:")][-1]
@@ -42,7 +42,7 @@ def counted_traffic():
         src = open(os.path.join(ROOT, rec["source"]), "rb").read()
     except (OSError, IndexError, ValueError, KeyError):
         return None
-    if hashlib.sha256(src).hexdigest() != rec["source_sha256"]:
+    if hashlib.sha256(src).hexdigest() != rec["source_sha256"] or rec.get("workload") != workload:
         return None
     return int(rec["traffic_bytes_per_launch"])
 
@@ -62,14 +62,16 @@ def parse():
 
 
 def step_bytes(cfg, n, n8, moved8, moved16, quantised):
-    """Algorithmic bytes of one step from the pre-step lengths [L, B]."""
+    """Algorithmic bytes of one step from the pre-step lengths [L, B]. The
+    full-cache comparison run moves K/V, q/o and the appended row only."""
     H, d, Hq = cfg.hkv, cfg.d, cfg.hq
     f = n - n8
-    attn = (H * d * (2 * n8 + 4 * (f + 1)) + 8 * H * d + 4 * Hq * d + 4 * (n + 1)).sum()
-    meta = (16 * n).sum()
+    full = cfg.mode == "full_kv"
+    attn = (H * d * (2 * n8 + 4 * (f + 1)) + 8 * H * d * (n8 > 0) + 4 * Hq * d + (0 if full else 4 * (n + 1))).sum()
+    meta = 0 if full else (16 * n).sum()
     comp = (2 * (moved8 * 2 * H * d + moved16 * 4 * H * d)).sum() + 8 * H * d * n.size
     quant = 6 * H * d * quantised.sum()
-    conf = 4 * cfg.batch * cfg.vocab
+    conf = 0 if full else 4 * cfg.batch * cfg.vocab
     return dict(attn=int(attn), meta=int(meta), compact=int(comp), quant=int(quant), conf=int(conf),
                 total=int(attn + meta + comp + quant + conf))
 
@@ -140,16 +142,21 @@ def main():
     per_step = []
     evict_frac = []
     moved_rows = []
+    full = cfg.mode == "full_kv"
     for s in range(S):
         lg, q, kn, vn, t = inputs[s]
         m0 = eng.cache.meta.cpu().numpy()
-        eng.step_confidence(lg)
-        eng.step_attention(q, kn, vn)
-        eng.step_ema_rank(t)
-        eng.step_compact(kn, vn)
-        m1 = eng.cache.meta.cpu().numpy()
-        eng.step_quantize(t)
-        m2 = eng.cache.meta.cpu().numpy()
+        if full:
+            eng.step(lg, q, kn, vn, t)
+            m1 = m2 = eng.cache.meta.cpu().numpy()
+        else:
+            eng.step_confidence(lg)
+            eng.step_attention(q, kn, vn)
+            eng.step_ema_rank(t)
+            eng.step_compact(kn, vn)
+            m1 = eng.cache.meta.cpu().numpy()
+            eng.step_quantize(t)
+            m2 = eng.cache.meta.cpu().numpy()
         evict_frac.append(float((m1[..., M.META_EVICTED] > 0).mean()))
         if s >= Wm:
             ev_mask = m1[..., M.META_EVICTED] > 0
@@ -192,15 +199,21 @@ def main():
     for i in range(K):
         lg, q, kn, vn, t = inputs[Wm + i]
         a0, a1, c0, c1 = ev[i]
-        eng.step_confidence(lg)
+        if not full:
+            eng.step_confidence(lg)
         a0.record(stream)
-        eng.step_attention(q, kn, vn)
+        if full:
+            M.engine.attn_decode(eng.cache, q, kn, vn, eng.out, None, None)
+        else:
+            eng.step_attention(q, kn, vn)
         a1.record(stream)
-        eng.step_ema_rank(t)
+        if not full:
+            eng.step_ema_rank(t)
         c0.record(stream)
         eng.step_compact(kn, vn)
         c1.record(stream)
-        eng.step_quantize(t)
+        if not full:
+            eng.step_quantize(t)
     torch.cuda.synchronize()
     attn_ms = [e[0].elapsed_time(e[1]) for e in ev]
     comp_ms = [e[2].elapsed_time(e[3]) for e in ev]
@@ -237,7 +250,8 @@ def main():
         "config": {
             "workload": f"{cfg.name}: {cfg.layers} layers, {cfg.hq}/{cfg.hkv} heads, d{cfg.d}, "
                         f"batch {cfg.batch}, {cfg.prefill}-token prefill, V={cfg.vocab}, "
-                        f"N_high/N_low={pol.n_high}/{pol.n_low}, P={pol.protect}, W={pol.window}",
+                        f"N_high/N_low={pol.n_high}/{pol.n_low}, P={pol.protect}, W={pol.window}, "
+                        f"alpha={pol.alpha}" + (", full FP16 cache (comparison run)" if full else ""),
             "layers": cfg.layers, "batch": cfg.batch, "hq": cfg.hq, "hkv": cfg.hkv, "d": cfg.d,
             "prefill": cfg.prefill, "vocab": cfg.vocab, "parallelism": "single GPU",
         },
@@ -258,8 +272,8 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": counted_traffic(),
-            "kernel": "attn_decode_kernel<128>",
+            "traffic": counted_traffic(cfg.name),
+            "kernel": "attn_decode_kernel<128, false, false>" if full else "attn_decode_kernel<128, false, true>",
             "bytes_per_launch": int(attn_bytes),
         },
     }

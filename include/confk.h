@@ -156,7 +156,8 @@ int confk_confidence(const float* logits, int64_t ld, int32_t batch, int32_t voc
  *   out           fp16 [nlayers][B][hq][d]
  *   mass          fp32 [nlayers][B][hkv][cap]: mass[..][j][i] = sum over the
  *                 query heads of kv head j of P_h,i, for i = 0..n (the
- *                 per-key mean over all query heads is sum_j / hq)
+ *                 per-key mean over all query heads is sum_j / hq); or NULL
+ *                 when the caller needs only the output (no workspace then)
  *   ws            >= confk_workspace_size(CONFK_WS_ATTENTION, ...) bytes
  *                 (score spill for caches too long for on-chip memory)
  * Layers layer0 .. layer0+nlayers-1 of the cache are processed; tensor

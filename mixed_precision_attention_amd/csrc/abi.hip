@@ -106,11 +106,11 @@ int confk_attn_decode(const confk_cache* cache, int32_t layer0, int32_t nlayers,
                       const uint16_t* k_new, const uint16_t* v_new, uint16_t* out, float* mass,
                       void* ws, size_t ws_bytes, void* stream) {
   if (!cache_ok(cache) || !layers_ok(cache, layer0, nlayers)) return CONFK_ERR_INVALID_ARG;
-  if (!q || !k_new || !v_new || !out || !mass) return CONFK_ERR_INVALID_ARG;
+  if (!q || !k_new || !v_new || !out) return CONFK_ERR_INVALID_ARG;
   const int g = cache->hq / cache->hkv;
   if ((cache->d != 64 && cache->d != 128) || g > 16) return CONFK_ERR_UNSUPPORTED;
   int stride = 0;
-  const int n_lds = attention_plan_n_lds(cache->d, g, cache->cap, &stride);
+  const int n_lds = mass ? attention_plan_n_lds(cache->d, g, cache->cap, &stride) : 0;
   const size_t need = (size_t)nlayers * cache->batch * cache->hkv * g * (size_t)stride * sizeof(float);
   if (need && (!ws || ws_bytes < need)) return CONFK_ERR_WORKSPACE;
   AttnArgs a{};

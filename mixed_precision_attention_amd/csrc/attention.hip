@@ -230,7 +230,9 @@ __host__ __device__ __forceinline__ int score_area_floats(int d, int g, int n_ld
 // SPILL: scores past the LDS budget go to global memory. Kept out of the
 // common instance because global stores in the tile loop make the load
 // counter unusable for partial waits (stores complete out of order).
-template <int D, bool SPILL>
+// MASS = false: no per-key mass (no score store; for callers that only need
+// the attention output, e.g. a full-cache baseline).
+template <int D, bool SPILL, bool MASS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(CONFK_ATTN_OCCUPANCY)))
 void attn_decode_kernel(AttnArgs a) {
   constexpr int KC = Tile<D>::KC;
@@ -295,7 +297,7 @@ void attn_decode_kernel(AttnArgs a) {
   __shared__ float usc[2];
 
   auto store_scores = [&](int p0, float4_t s) {
-    if (!head_ok) return;
+    if (!MASS || !head_ok) return;
     const int p = p0 + 4 * kg;
     if (!SPILL || p0 < n_lds) {
       *reinterpret_cast<float4_t*>(sc + (size_t)r16 * n_lds + p) = s;
@@ -535,7 +537,7 @@ void attn_decode_kernel(AttnArgs a) {
 
   // per-key mass (summed over this kv head's query heads)
   float* mout = a.mass + ((size_t)lb * H + h) * c.cap;
-  for (int i = threadIdx.x; i < nk; i += kThreads) {
+  for (int i = threadIdx.x; MASS && i < nk; i += kThreads) {
     const int p = i < n8 ? i : p16 + (i - n8);
     const float u = i < n8 ? usc[0] : usc[1];
     float sum = 0.f;
@@ -594,11 +596,13 @@ hipError_t launch_attention(const AttnArgs& a, int lds_bytes, hipStream_t s) {
   const int units = a.nl * a.c.B * a.c.hkv;
   const dim3 grid(units), block(kThreads);
   if (a.c.d == 128) {
-    if (a.spill) hipLaunchKernelGGL((attn_decode_kernel<128, true>), grid, block, lds_bytes, s, a);
-    else hipLaunchKernelGGL((attn_decode_kernel<128, false>), grid, block, lds_bytes, s, a);
+    if (!a.mass) hipLaunchKernelGGL((attn_decode_kernel<128, false, false>), grid, block, lds_bytes, s, a);
+    else if (a.spill) hipLaunchKernelGGL((attn_decode_kernel<128, true, true>), grid, block, lds_bytes, s, a);
+    else hipLaunchKernelGGL((attn_decode_kernel<128, false, true>), grid, block, lds_bytes, s, a);
   } else {
-    if (a.spill) hipLaunchKernelGGL((attn_decode_kernel<64, true>), grid, block, lds_bytes, s, a);
-    else hipLaunchKernelGGL((attn_decode_kernel<64, false>), grid, block, lds_bytes, s, a);
+    if (!a.mass) hipLaunchKernelGGL((attn_decode_kernel<64, false, false>), grid, block, lds_bytes, s, a);
+    else if (a.spill) hipLaunchKernelGGL((attn_decode_kernel<64, true, true>), grid, block, lds_bytes, s, a);
+    else hipLaunchKernelGGL((attn_decode_kernel<64, false, true>), grid, block, lds_bytes, s, a);
   }
   return hipGetLastError();
 }

@@ -171,6 +171,8 @@ class DecodeEngine:
         self.mass = torch.zeros((Lr, B, cfg.hkv, cfg.cap), dtype=torch.float32, device=device)
         self.score = torch.zeros((Lr, B, cfg.cap), dtype=torch.float32, device=device)
         self.evicted = torch.zeros((Lr, B), dtype=torch.int32, device=device)
+        if cfg.mode == "full_kv":
+            self.budget.fill_(cfg.policy.n_low)
 
     def prefill(self, k_src, v_src):
         """k_src, v_src fp16 [L, B, Hkv, L0, d] on the device (L0 may be 0)."""
@@ -196,6 +198,12 @@ class DecodeEngine:
         quantize(self.cache, self.pol, t)
 
     def step(self, logits, q, k_new, v_new, t):
+        if self.cfg.mode == "full_kv":
+            # comparison run: attention output only, then the append (the
+            # budget covers every token, so nothing is evicted or quantised)
+            attn_decode(self.cache, q, k_new, v_new, self.out, None, None)
+            self.step_compact(k_new, v_new)
+            return
         if self.side is None:
             self.step_confidence(logits)
         else:

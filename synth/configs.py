@@ -41,6 +41,9 @@ class Config:
     # per-layer budgets (CONF-KV-L); None means uniform budgets
     layer_n_low: Optional[Tuple[int, ...]] = None
     layer_n_high: Optional[Tuple[int, ...]] = None
+    # "confkv": the method; "full_kv": comparison run keeping every token in
+    # FP16 (attention output only, then the append)
+    mode: str = "confkv"
 
     @property
     def cap(self) -> int:
@@ -95,6 +98,17 @@ CONFIGS = {
         name="qwen32b", layers=64, batch=8, hq=40, hkv=8, d=128, vocab=152064,
         prefill=2048, steps=4096,
         policy=Policy(n_high=1024, n_low=2048, protect=64, window=256)),
+    # Comparison runs on the Qwen-32B shape: every token kept in FP16 (the
+    # window covers the whole run, the budget is never exceeded) ...
+    "qwen32b_fullkv": Config(
+        name="qwen32b_fullkv", layers=64, batch=8, hq=40, hkv=8, d=128, vocab=152064,
+        prefill=2048, steps=2048,
+        policy=Policy(n_high=4094, n_low=4094, protect=64, window=4094), mode="full_kv"),
+    # ... and a sliding window of the newest 512 tokens (recency-only rank)
+    "qwen32b_sw512": Config(
+        name="qwen32b_sw512", layers=64, batch=8, hq=40, hkv=8, d=128, vocab=152064,
+        prefill=2048, steps=4096,
+        policy=Policy(alpha=0.0, n_high=512, n_low=512, protect=64, window=256)),
     # Long-context pyramid (CONF-KV-L), Qwen-32B layer shape, batch 1
     "qwen32b_pyramid": Config(
         name="qwen32b_pyramid", layers=64, batch=1, hq=40, hkv=8, d=128, vocab=152064,

@@ -325,3 +325,30 @@ def test_overlapped_step_matches_serial():
         assert torch.equal(getattr(a.cache, name), getattr(b.cache, name)), name
     for name in ("c", "budget", "out", "mass", "score"):
         assert torch.equal(getattr(a, name), getattr(b, name)), name
+
+
+def test_attention_without_mass_gives_the_same_output():
+    """mass = NULL (no score store, no mass pass) gives the same output to the
+    attention tolerance (the compiler may order the arithmetic differently)."""
+    import mixed_precision_attention_amd as M
+    dev = _dev()
+    cfg = TINY["g5_d128"]
+    kp, vp = synth.prefill_kv(cfg, 3)
+    eng = M.DecodeEngine(cfg, dev)
+    eng.prefill(_t(kp, dev), _t(vp, dev))
+    for i in range(3):
+        logits, q, kn, vn, t = _inputs(cfg, 3, i)
+        lg, qd, kd, vd = _t(logits, dev), _t(q, dev), _t(kn, dev), _t(vn, dev)
+        eng.step_confidence(lg)
+        eng.step_attention(qd, kd, vd)
+        with_mass = eng.out.clone()
+        M.engine.attn_decode(eng.cache, qd, kd, vd, eng.out, None, None)
+        torch.cuda.synchronize()
+        for l in range(cfg.layers):
+            for b in range(cfg.batch):
+                got = eng.out[l, b].float().cpu().numpy()
+                ref = with_mass[l, b].float().cpu().numpy()
+                assert rel_maxabs(got, ref) <= OTOL / 2, f"step {i} l={l} b={b}"
+        eng.step_ema_rank(t)
+        eng.step_compact(kd, vd)
+        eng.step_quantize(t)
