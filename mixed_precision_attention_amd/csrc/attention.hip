@@ -219,11 +219,19 @@ struct Raw16 {
   uint32_t v[4][Tile<D>::CB / 2];  // V rows 4kg+j: D/16 halves at channel (D/16)*r16
 };
 
-// LDS layout: scores [g][n_lds] fp32 (later the per-wave output reduction
-// [kWaves][g][D] fp32), then the query [g][D] fp16, K scales [D], V scales [D].
+// Output reduction rows: lane (head r16, group kg) holds d/4 consecutive
+// channels; each such block is padded by 4 floats and a head's row spans
+// 4 blocks, so the 64 lanes of a wave spread over all LDS banks.
+__host__ __device__ constexpr int red_block(int d) { return d / 4 + 4; }
+__host__ __device__ constexpr int red_row(int d) { return 4 * red_block(d); }
+
+// LDS layout: scores [g][n_lds] fp32 (n_lds = 4 mod 32, so the heads' rows
+// fall on different banks; later the per-wave output reduction
+// [kWaves][g][red_row] fp32), then the query [g][D] fp16, K scales [D],
+// V scales [D].
 __host__ __device__ __forceinline__ int score_area_floats(int d, int g, int n_lds) {
   const int sc = g * n_lds;
-  const int red = kWaves * g * d;
+  const int red = kWaves * g * red_row(d);
   return sc > red ? sc : red;
 }
 
@@ -299,7 +307,7 @@ void attn_decode_kernel(AttnArgs a) {
   auto store_scores = [&](int p0, float4_t s) {
     if (!MASS || !head_ok) return;
     const int p = p0 + 4 * kg;
-    if (!SPILL || p0 < n_lds) {
+    if (!SPILL || p0 + 16 <= n_lds) {  // whole tiles stay in LDS (n_lds is not a multiple of 16)
       *reinterpret_cast<float4_t*>(sc + (size_t)r16 * n_lds + p) = s;
     } else {
       *reinterpret_cast<float4_t*>(spill + (size_t)r16 * a.spill_stride + p) = s;
@@ -537,34 +545,72 @@ void attn_decode_kernel(AttnArgs a) {
 
   // per-key mass (summed over this kv head's query heads)
   float* mout = a.mass + ((size_t)lb * H + h) * c.cap;
-  for (int i = threadIdx.x; MASS && i < nk; i += kThreads) {
-    const int p = i < n8 ? i : p16 + (i - n8);
-    const float u = i < n8 ? usc[0] : usc[1];
-    float sum = 0.f;
-    for (int hh = 0; hh < g; ++hh) {
-      const float s = (!SPILL || p < n_lds) ? sc[(size_t)hh * n_lds + p] : spill[(size_t)hh * a.spill_stride + p];
-      sum += exp2f(fmaf(s, u, -Mh[hh])) * iL[hh];
+  if constexpr (MASS && !SPILL) {
+    // groups of 4 slots (both regions start 16-aligned; slots past a region
+    // hold masked scores and are not written out); all heads' scores of a
+    // group are fetched before the exponentials
+    const int q8 = (n8 + 3) >> 2, q16 = (f + 1 + 3) >> 2;
+    for (int gi = threadIdx.x; gi < q8 + q16; gi += kThreads) {
+      const bool r8 = gi < q8;
+      const int slot = r8 ? 4 * gi : p16 + 4 * (gi - q8);
+      const int i0 = r8 ? 4 * gi : n8 + 4 * (gi - q8);
+      const int lim = r8 ? n8 : nk;
+      const float u = usc[r8 ? 0 : 1];
+      float4_t sv[16];
+#pragma unroll
+      for (int hh = 0; hh < 16; ++hh)
+        if (hh < g) sv[hh] = *reinterpret_cast<const float4_t*>(sc + (size_t)hh * n_lds + slot);
+      float4_t sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int hh = 0; hh < 16; ++hh) {
+        if (hh < g) {
+          const float m = Mh[hh], il = iL[hh];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) sum[v] += __builtin_amdgcn_exp2f(fmaf(sv[hh][v], u, -m)) * il;
+        }
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        if (i0 + v < lim) mout[i0 + v] = sum[v];
     }
-    mout[i] = sum;
+  } else if constexpr (MASS) {
+    for (int i = threadIdx.x; i < nk; i += kThreads) {
+      const int p = i < n8 ? i : p16 + (i - n8);
+      const float u = i < n8 ? usc[0] : usc[1];
+      float sum = 0.f;
+      for (int hh = 0; hh < g; ++hh) {
+        const float s = (p | 15) < n_lds ? sc[(size_t)hh * n_lds + p] : spill[(size_t)hh * a.spill_stride + p];
+        sum += exp2f(fmaf(s, u, -Mh[hh])) * iL[hh];
+      }
+      mout[i] = sum;
+    }
   }
   __syncthreads();
 
-  // output: scale each wave's accumulator to the merged normaliser, sum waves
-  float* red = lds;  // [kWaves][g][D], aliases the score area
+  // output: scale each wave's accumulator to the merged normaliser, sum waves.
+  // Channel of acc[cb][v] is CB*(4kg+v)+cb: lane block kg, offset CB*v+cb.
+  constexpr int RB = red_block(D), RR = red_row(D);
+  float* red = lds;  // [kWaves][g][RR], aliases the score area
   if (head_ok) {
     const float fct = (wl[w][r16] > 0.f) ? exp2f(st.m - Mh[r16]) * iL[r16] : 0.f;
-    float* dst = red + ((size_t)w * g + r16) * D;
+    float* dst = red + ((size_t)w * g + r16) * RR + kg * RB;
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
+    for (int v = 0; v < 4; ++v)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) dst[CB * (4 * kg + v) + cb] = acc[cb][v] * fct;
+      for (int hf = 0; hf < CB / 4; ++hf) {
+        const float4_t x = {acc[4 * hf][v] * fct, acc[4 * hf + 1][v] * fct, acc[4 * hf + 2][v] * fct,
+                            acc[4 * hf + 3][v] * fct};
+        *reinterpret_cast<float4_t*>(dst + CB * v + 4 * hf) = x;
+      }
   }
   __syncthreads();
   uint16_t* ob = a.out + qoff;
   for (int idx = threadIdx.x; idx < g * D; idx += kThreads) {
+    const int hh = idx / D, ch = idx - hh * D;
+    const int off = hh * RR + (ch / (D / 4)) * RB + ch % (D / 4);
     float o = 0.f;
 #pragma unroll
-    for (int q = 0; q < kWaves; ++q) o += red[(size_t)q * g * D + idx];
+    for (int q = 0; q < kWaves; ++q) o += red[(size_t)q * g * RR + off];
     ob[idx] = float_to_half_bits(o);
   }
 }
@@ -579,14 +625,18 @@ int attention_lds_bytes(int d, int g, int n_lds) {
 // Score slots per head: padded INT8 tiles + padded FP16 tiles (incl. new).
 static int score_slots(int cap) { return ((cap + 30 + 15) / 16) * 16; }
 
+// Row length of the LDS score store: a multiple of 4 floats that is 4 mod 32
+// (bank spread across heads).
+static int bank_pad(int x) { return (x + 31) / 32 * 32 + 4; }
+
 int attention_plan_n_lds(int d, int g, int cap, int* spill_stride) {
   const int need = score_slots(cap);
-  int fit = (kScoreLdsBytes / (4 * g)) / 16 * 16;
-  const int min_slots = (kWaves * d + 15) / 16 * 16;  // room for the output reduction
+  int fit = bank_pad(kScoreLdsBytes / (4 * g) - 36);
+  const int min_slots = bank_pad(kWaves * red_row(d));  // room for the output reduction
   if (fit < min_slots) fit = min_slots;
-  if (need <= fit) {
+  if (bank_pad(need) <= fit) {
     *spill_stride = 0;
-    return need;
+    return bank_pad(need);
   }
   *spill_stride = need;
   return fit;
