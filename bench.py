@@ -218,6 +218,17 @@ def main():
     attn_ms = [e[0].elapsed_time(e[1]) for e in ev]
     comp_ms = [e[2].elapsed_time(e[3]) for e in ev]
 
+    retention = None
+    if cfg.plant_depths:  # planted keys still cached after the timed steps, per depth
+        planted = synth.gen.plant_positions(cfg)
+        pos = eng.cache.pos.cpu().numpy()
+        nlen = eng.cache.meta[..., M.META_N].cpu().numpy()
+        kept = np.array([[planted[b] in pos[l, b, : nlen[l, b]] for b in range(cfg.batch)]
+                         for l in range(cfg.layers)])
+        retention = {"depths": list(cfg.plant_depths), "positions": planted.tolist(),
+                     "kept_layers_per_depth": kept.sum(axis=0).tolist(), "layers": cfg.layers,
+                     "all_kept": bool(kept.all())}
+
     if args.calib_copy_mib:
         n = args.calib_copy_mib << 20
         src = torch.ones(n, dtype=torch.uint8, device=dev)
@@ -277,6 +288,8 @@ def main():
             "bytes_per_launch": int(attn_bytes),
         },
     }
+    if retention is not None:
+        out["retention"] = retention
     if args.cpu_seconds > 0:
         lg0, q0, kn0, vn0, _ = inputs[0]
         cb = cpu_baseline(cfg, kp, vp, lg0.cpu().numpy(), q0.cpu().numpy(), kn0.cpu().numpy(),

@@ -44,6 +44,13 @@ class Config:
     # "confkv": the method; "full_kv": comparison run keeping every token in
     # FP16 (attention output only, then the append)
     mode: str = "confkv"
+    # planted key (a stand-in for needle retrieval): sequence b holds, at
+    # position round(plant_depths[b] * prefill), the key plant_beta * u in
+    # every layer and kv head (u a seeded unit vector per layer and kv head),
+    # and every decode query is plant_gamma * u plus N(0, 1) noise
+    plant_depths: Tuple[float, ...] = ()
+    plant_beta: float = 0.0
+    plant_gamma: float = 0.0
 
     @property
     def cap(self) -> int:
@@ -109,6 +116,14 @@ CONFIGS = {
         name="qwen32b_sw512", layers=64, batch=8, hq=40, hkv=8, d=128, vocab=152064,
         prefill=2048, steps=4096,
         policy=Policy(alpha=0.0, n_high=512, n_low=512, protect=64, window=256)),
+    # Long-context pyramid with one planted key per sequence at depths
+    # 10/30/50/70/90 % of the prefill (five sequences, one per depth)
+    "qwen32b_niah": Config(
+        name="qwen32b_niah", layers=64, batch=5, hq=40, hkv=8, d=128, vocab=152064,
+        prefill=32768, steps=512,
+        policy=Policy(n_high=_PYR_HI[0], n_low=_PYR_LO[0], protect=64, window=256),
+        layer_n_low=_PYR_LO, layer_n_high=_PYR_HI,
+        plant_depths=(0.1, 0.3, 0.5, 0.7, 0.9), plant_beta=2.0 * 128 ** 0.5, plant_gamma=4.0),
     # Long-context pyramid (CONF-KV-L), Qwen-32B layer shape, batch 1
     "qwen32b_pyramid": Config(
         name="qwen32b_pyramid", layers=64, batch=1, hq=40, hkv=8, d=128, vocab=152064,

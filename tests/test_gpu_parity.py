@@ -352,3 +352,24 @@ def test_attention_without_mass_gives_the_same_output():
         eng.step_ema_rank(t)
         eng.step_compact(kd, vd)
         eng.step_quantize(t)
+
+
+def test_long_context_pyramid_retains_planted_keys():
+    """Long-context pyramid at the Qwen-32B layer shape: a 32768-token prefill,
+    the budgets of the first and last layer (4096 and 1024 loose), one planted
+    key per sequence at 10/30/50/70/90 % depth that the decode queries align
+    with. Sampled pairs follow the oracle; every planted key is kept."""
+    base = synth.get_config("qwen32b_niah")
+    cfg = base.with_(layers=2, layer_n_low=(base.layer_n_low[0], base.layer_n_low[-1]),
+                     layer_n_high=(base.layer_n_high[0], base.layer_n_high[-1]))
+    print(f"[parity] long-context pyramid cap={cfg.cap}", flush=True)
+    run = Run(cfg, seed=3, pairs=[(0, 0), (1, 2), (1, 4)])
+    planted = synth.gen.plant_positions(cfg)
+    for i in range(3):
+        run.step(i)
+        pos = run.eng.cache.pos.cpu().numpy()
+        n, _ = run.eng.cache.lengths()
+        for l in range(cfg.layers):
+            assert (n[l] <= cfg.layer_n_low[l] + 1).all()
+            for b in range(cfg.batch):
+                assert planted[b] in pos[l, b, : n[l, b]], f"step {i} l={l} b={b}: planted key evicted"
