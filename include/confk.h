@@ -131,15 +131,27 @@ typedef struct confk_cache {
  *   status        uint32 [1] device or NULL; NaN / +inf / all -inf logits
  *                 set CONFK_STATUS_NONFINITE_LOGITS, give c = NaN and the
  *                 loose budget
+ *   token_out     int32 [batch] device or NULL: the next token x_{t+1}
+ *                 (review Algorithm 1, step 13), chosen in the same pass.
+ *                 temperature = 0: greedy, the smallest index among the
+ *                 largest logits. temperature > 0: the smallest index i whose
+ *                 cumulative weight sum_{j<=i} e^(z_j/temperature) (index
+ *                 order) exceeds uniform[b] times the total, i.e. sampling
+ *                 from softmax(z / temperature) by inversion. -1 for flagged
+ *                 rows.
+ *   uniform       fp32 [batch] device, each in [0, 1): the caller's random
+ *                 draw per row (read only when temperature > 0)
  *   ws            >= confk_workspace_size(CONFK_WS_CONFIDENCE, ...) bytes
  *                 (per-chunk partial reductions; no initialisation needed)
  * Errors: INVALID_ARG (null, batch < 1, vocab < 2, ld < vocab, nbl < 1,
- * only one of the layer arrays given), WORKSPACE.
+ * only one of the layer arrays given, temperature negative, NaN or +inf,
+ * token_out with temperature > 0 but no uniform), WORKSPACE.
  */
 int confk_confidence(const float* logits, int64_t ld, int32_t batch, int32_t vocab,
                      const confk_policy* pol, const int32_t* layer_n_high,
                      const int32_t* layer_n_low, int32_t nbl, float* c_out,
-                     int32_t* budget_out, uint32_t* status, void* ws, size_t ws_bytes,
+                     int32_t* budget_out, uint32_t* status, const float* uniform,
+                     float temperature, int32_t* token_out, void* ws, size_t ws_bytes,
                      void* stream);
 
 /*

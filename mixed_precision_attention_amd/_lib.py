@@ -76,7 +76,7 @@ def load():
     P = ctypes.POINTER
     lib.confk_confidence.argtypes = [c_void_p, c_int64, c_int32, c_int32, P(Policy), c_void_p,
                                      c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
-                                     c_size_t, c_void_p]
+                                     c_float, c_void_p, c_void_p, c_size_t, c_void_p]
     lib.confk_attn_decode.argtypes = [P(Cache), c_int32, c_int32, c_void_p, c_void_p, c_void_p,
                                       c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
     lib.confk_ema_rank.argtypes = [P(Cache), c_int32, c_int32, c_void_p, P(Policy), c_int32,

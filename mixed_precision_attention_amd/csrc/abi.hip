@@ -72,8 +72,11 @@ size_t confk_workspace_size(int32_t which, const confk_cache* cache, int32_t nla
 int confk_confidence(const float* logits, int64_t ld, int32_t batch, int32_t vocab,
                      const confk_policy* pol, const int32_t* layer_n_high,
                      const int32_t* layer_n_low, int32_t nbl, float* c_out, int32_t* budget_out,
-                     uint32_t* status, void* ws, size_t ws_bytes, void* stream) {
+                     uint32_t* status, const float* uniform, float temperature, int32_t* token_out,
+                     void* ws, size_t ws_bytes, void* stream) {
   if (!logits || !c_out || !budget_out || !pol) return CONFK_ERR_INVALID_ARG;
+  if (!(temperature >= 0.f) || temperature == INFINITY) return CONFK_ERR_INVALID_ARG;
+  if (token_out && temperature > 0.f && !uniform) return CONFK_ERR_INVALID_ARG;
   if (batch < 1 || vocab < 2 || ld < vocab || nbl < 1) return CONFK_ERR_INVALID_ARG;
   if ((layer_n_high == nullptr) != (layer_n_low == nullptr)) return CONFK_ERR_INVALID_ARG;
   if (!layer_n_high && nbl != 1) return CONFK_ERR_INVALID_ARG;
@@ -98,6 +101,9 @@ int confk_confidence(const float* logits, int64_t ld, int32_t batch, int32_t voc
   a.partial = (float*)ws;
   a.c_out = c_out;
   a.budget_out = budget_out;
+  a.token_out = token_out;
+  a.uniform = uniform;
+  a.inv_temp = (token_out && temperature > 0.f) ? 1.f / temperature : 0.f;
   a.status = status;
   return launch_status(launch_confidence(a, (hipStream_t)stream));
 }

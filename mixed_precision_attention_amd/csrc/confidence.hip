@@ -12,6 +12,14 @@
 // Rows are split over many workgroups (HBM-bound: each logit is read once);
 // a second tiny kernel merges the per-chunk states in a fixed order, so the
 // result does not depend on scheduling.
+//
+// Next-token choice (review Algorithm 1, step 13, the sampling of x_{t+1}),
+// fused into the same pass: the state also carries the index of top1
+// (greedy: the smallest index among equal maxima) and, for temperature
+// sampling, S_T = sum e^((z-M)/T). The final kernel draws by inversion with
+// the caller's uniform number u: the smallest index whose cumulative weight in
+// index order exceeds u * S_T, found chunk by chunk and then inside the one
+// chunk where the cumulative weight crosses.
 #include "confk_internal.h"
 
 namespace confk {
@@ -30,7 +38,10 @@ __device__ __forceinline__ float exp_neg(float d) { return exp2f(d * kLog2e); }
 struct RowState {
   float M, S, T, t1, t2;
   uint32_t flag;  // bit 0: NaN or +inf seen
+  float ST;       // sum e^((z-M)/temp), sampling only
+  int32_t i1;     // index of t1 (smallest among equal maxima)
 };
+constexpr int kRec = 8;  // floats per partial record
 
 // Inserts x into the two largest values t1 >= t2 of a multiset.
 __device__ __forceinline__ void top2_insert(float& t1, float& t2, float x) {
@@ -39,25 +50,30 @@ __device__ __forceinline__ void top2_insert(float& t1, float& t2, float x) {
   t2 = n2;
 }
 
-__device__ __forceinline__ RowState merge(const RowState& a, const RowState& b) {
+// inv_t: 1 / temperature for sampling, 0 when S_T is not needed
+__device__ __forceinline__ RowState merge(const RowState& a, const RowState& b, float inv_t) {
   RowState r;
   r.M = fmaxf(a.M, b.M);
   r.flag = a.flag | b.flag;
   r.t1 = fmaxf(a.t1, b.t1);
   r.t2 = fmaxf(fminf(a.t1, b.t1), fmaxf(a.t2, b.t2));
+  r.i1 = a.t1 > b.t1 ? a.i1 : (b.t1 > a.t1 ? b.i1 : min(a.i1, b.i1));
   r.S = 0.f;
   r.T = 0.f;
+  r.ST = 0.f;
   if (a.S > 0.f) {
     const float d = a.M - r.M;
     const float e = exp_neg(d);
     r.S += a.S * e;
     r.T += (a.T + d * a.S) * e;
+    if (inv_t > 0.f) r.ST += a.ST * exp_neg(d * inv_t);
   }
   if (b.S > 0.f) {
     const float d = b.M - r.M;
     const float e = exp_neg(d);
     r.S += b.S * e;
     r.T += (b.T + d * b.S) * e;
+    if (inv_t > 0.f) r.ST += b.ST * exp_neg(d * inv_t);
   }
   return r;
 }
@@ -70,6 +86,8 @@ __device__ __forceinline__ RowState shfl_state(const RowState& s, int o) {
   r.t1 = __shfl_xor(s.t1, o, 64);
   r.t2 = __shfl_xor(s.t2, o, 64);
   r.flag = (uint32_t)__shfl_xor((int)s.flag, o, 64);
+  r.ST = __shfl_xor(s.ST, o, 64);
+  r.i1 = __shfl_xor(s.i1, o, 64);
   return r;
 }
 
@@ -104,11 +122,17 @@ __global__ __launch_bounds__(kThreads) void conf_partial_kernel(ConfArgs a) {
       x[k] = (i < end) ? row[i] : -INFINITY;
     }
   }
+  // logical index of x[k]
+  auto idx = [&](int k) {
+    return a.vec4 ? start + 4 * (threadIdx.x + (k >> 2) * kThreads) + (k & 3) : start + threadIdx.x + k * kThreads;
+  };
+  const float inv_t = a.inv_temp;
   RowState s;
   s.M = -INFINITY;
   s.t1 = -INFINITY;
   s.t2 = -INFINITY;
   s.flag = 0;
+  s.i1 = INT32_MAX;
 #pragma unroll
   for (int k = 0; k < kPerThread; ++k) {
     const float v = x[k];
@@ -116,11 +140,13 @@ __global__ __launch_bounds__(kThreads) void conf_partial_kernel(ConfArgs a) {
       s.flag = 1;
     } else {
       s.M = fmaxf(s.M, v);
+      if (v > s.t1 || (v == s.t1 && v > -INFINITY && idx(k) < s.i1)) s.i1 = idx(k);
       top2_insert(s.t1, s.t2, v);
     }
   }
   s.S = 0.f;
   s.T = 0.f;
+  s.ST = 0.f;
   if (s.M > -INFINITY) {
 #pragma unroll
     for (int k = 0; k < kPerThread; ++k) {
@@ -130,26 +156,29 @@ __global__ __launch_bounds__(kThreads) void conf_partial_kernel(ConfArgs a) {
         const float e = exp_neg(d);
         s.S += e;
         s.T += d * e;
+        if (inv_t > 0.f) s.ST += exp_neg(d * inv_t);
       }
     }
   }
   // wave reduction
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) s = merge(s, shfl_state(s, o));
+  for (int o = 1; o < 64; o <<= 1) s = merge(s, shfl_state(s, o), inv_t);
   __shared__ RowState red[kThreads / 64];
   const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) red[w] = s;
   __syncthreads();
   if (threadIdx.x == 0) {
     RowState r = red[0];
-    for (int i = 1; i < kThreads / 64; ++i) r = merge(r, red[i]);
-    float* p = a.partial + ((int64_t)b * a.nchunks + chunk) * 6;
+    for (int i = 1; i < kThreads / 64; ++i) r = merge(r, red[i], inv_t);
+    float* p = a.partial + ((int64_t)b * a.nchunks + chunk) * kRec;
     p[0] = r.M;
     p[1] = r.S;
     p[2] = r.T;
     p[3] = r.t1;
     p[4] = r.t2;
     p[5] = __builtin_bit_cast(float, r.flag);
+    p[6] = r.ST;
+    p[7] = __builtin_bit_cast(float, r.i1);
   }
 }
 
@@ -158,7 +187,20 @@ __global__ __launch_bounds__(kThreads) void conf_partial_kernel(ConfArgs a) {
 __global__ __launch_bounds__(64) void conf_final_kernel(ConfArgs a) {
   const int b = blockIdx.x;
   const int lane = threadIdx.x;
-  const float* p = a.partial + (int64_t)b * a.nchunks * 6;
+  const float* p = a.partial + (int64_t)b * a.nchunks * kRec;
+  const float inv_t = a.inv_temp;
+  auto load = [&](int i) {
+    RowState q;
+    q.M = p[kRec * i + 0];
+    q.S = p[kRec * i + 1];
+    q.T = p[kRec * i + 2];
+    q.t1 = p[kRec * i + 3];
+    q.t2 = p[kRec * i + 4];
+    q.flag = __builtin_bit_cast(uint32_t, p[kRec * i + 5]);
+    q.ST = p[kRec * i + 6];
+    q.i1 = __builtin_bit_cast(int32_t, p[kRec * i + 7]);
+    return q;
+  };
   RowState r;
   r.M = -INFINITY;
   r.S = 0.f;
@@ -166,21 +208,88 @@ __global__ __launch_bounds__(64) void conf_final_kernel(ConfArgs a) {
   r.t1 = -INFINITY;
   r.t2 = -INFINITY;
   r.flag = 0;
-  for (int i = lane; i < a.nchunks; i += 64) {
-    RowState q;
-    q.M = p[6 * i + 0];
-    q.S = p[6 * i + 1];
-    q.T = p[6 * i + 2];
-    q.t1 = p[6 * i + 3];
-    q.t2 = p[6 * i + 4];
-    q.flag = __builtin_bit_cast(uint32_t, p[6 * i + 5]);
-    r = merge(r, q);
-  }
+  r.ST = 0.f;
+  r.i1 = INT32_MAX;
+  for (int i = lane; i < a.nchunks; i += 64) r = merge(r, load(i), inv_t);
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) r = merge(r, shfl_state(r, o));
+  for (int o = 1; o < 64; o <<= 1) r = merge(r, shfl_state(r, o), inv_t);
+  const bool bad = r.flag != 0 || !(r.M > -INFINITY);
+
+  if (a.token_out) {  // next-token choice (uniform per row)
+    int tok = -1;
+    if (!bad && !(inv_t > 0.f)) {
+      tok = r.i1;  // greedy
+    } else if (!bad) {
+      // chunk weights e^((M_c - M)/T) S_T,c in chunk order; lane holds
+      // chunks lane, lane+64, ... (ascending), the wave scans them in order
+      const float target = a.uniform[b] * r.ST;
+      float run = 0.f;  // weight of all chunks before this lane's current group
+      int cstar = -1;
+      float before = 0.f;
+      for (int c0 = 0; c0 < a.nchunks && cstar < 0; c0 += 64) {
+        const int ci = c0 + lane;
+        float wgt = 0.f;
+        if (ci < a.nchunks) {
+          const RowState q = load(ci);
+          if (q.S > 0.f) wgt = q.ST * exp_neg((q.M - r.M) * inv_t);
+        }
+        float incl = wgt;
+        for (int o = 1; o < 64; o <<= 1) {
+          const float yv = __shfl_up(incl, o, 64);
+          if (lane >= o) incl += yv;
+        }
+        const bool cross = ci < a.nchunks && run + incl > target;
+        const uint64_t m = __ballot(cross);
+        if (m) {
+          const int src = __ffsll((unsigned long long)m) - 1;
+          cstar = c0 + src;
+          before = run + __shfl(incl - wgt, src, 64);
+        }
+        run += __shfl(incl, 63, 64);
+      }
+      // rounding left the target at the total: the last chunk's last element
+      const bool past_end = cstar < 0;
+      if (past_end) cstar = a.nchunks - 1;
+      // inside chunk cstar: lane L sums elements [start + L*per, +per) in order
+      const float* row = a.logits + (int64_t)b * a.ld;
+      const int start = cstar * a.chunk;
+      const int end = min(a.vocab, start + a.chunk);
+      const int per = (a.chunk + 63) / 64;
+      const int lo = start + lane * per, hi = min(end, lo + per);
+      float wsum = 0.f;
+      for (int i = lo; i < hi; ++i) {
+        const float v = row[i];
+        if (v > -INFINITY) wsum += exp_neg((v - r.M) * inv_t);
+      }
+      float incl = wsum;
+      for (int o = 1; o < 64; o <<= 1) {
+        const float yv = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += yv;
+      }
+      const float t2 = past_end ? INFINITY : target - before;
+      const uint64_t m = __ballot(lo < hi && incl > t2);
+      const int src = m ? __ffsll((unsigned long long)m) - 1 : 63 - __clzll((long long)__ballot(lo < hi));
+      float acc = __shfl(incl - wsum, src, 64);
+      if (lane == src) {
+        tok = hi - 1;  // rounding: the lane's last element
+        for (int i = lo; i < hi; ++i) {
+          const float v = row[i];
+          if (v > -INFINITY) {
+            acc += exp_neg((v - r.M) * inv_t);
+            if (acc > t2) {
+              tok = i;
+              break;
+            }
+          }
+        }
+      }
+      tok = __shfl(tok, src, 64);
+    }
+    if (lane == 0) a.token_out[b] = tok;
+  }
+
   if (lane != 0) return;
   float c;
-  const bool bad = r.flag != 0 || !(r.M > -INFINITY);
   if (bad) {
     c = __builtin_nanf("");
     if (a.status) atomicOr(a.status, (uint32_t)CONFK_STATUS_NONFINITE_LOGITS);
@@ -205,7 +314,7 @@ __global__ __launch_bounds__(64) void conf_final_kernel(ConfArgs a) {
 
 size_t confidence_ws_bytes(int32_t batch, int32_t vocab) {
   const int nchunks = (vocab + kChunk - 1) / kChunk;
-  return (size_t)batch * nchunks * 6 * sizeof(float);
+  return (size_t)batch * nchunks * kRec * sizeof(float);
 }
 
 hipError_t launch_confidence(const ConfArgs& in, hipStream_t s) {

@@ -41,10 +41,13 @@ struct ConfArgs {
   int32_t n_high, n_low;
   const int32_t* layer_n_high;
   const int32_t* layer_n_low;
-  float* partial;  // [batch][nchunks][6]
+  float* partial;  // [batch][nchunks][8]
   float* c_out;
   int32_t* budget_out;
   uint32_t* status;
+  const float* uniform;  // [batch] in [0, 1): temperature sampling
+  float inv_temp;        // 1 / temperature, 0 for greedy or no choice
+  int32_t* token_out;    // [batch] or null
 };
 
 struct AttnArgs {

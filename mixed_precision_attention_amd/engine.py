@@ -85,13 +85,15 @@ class DeviceCache:
 
 # ------------------------------------------------------------------ calls
 
-def confidence(logits, pol, c_out, budget_out, status, ws, layer_n_high=None, layer_n_low=None):
+def confidence(logits, pol, c_out, budget_out, status, ws, layer_n_high=None, layer_n_low=None,
+               token_out=None, temperature=0.0, uniform=None):
     lib = L.load()
     nbl = 1 if layer_n_high is None else int(layer_n_high.numel())
     L.check("confk_confidence", lib.confk_confidence(
         _p(logits), logits.stride(0), logits.shape[0], logits.shape[1], ctypes.byref(pol),
         _p(layer_n_high), _p(layer_n_low), nbl, _p(c_out), _p(budget_out), _p(status),
-        _p(ws), ws.numel() * ws.element_size(), _stream()))
+        _p(uniform), float(temperature), _p(token_out), _p(ws), ws.numel() * ws.element_size(),
+        _stream()))
 
 
 def attn_decode(cache, q, k_new, v_new, out, mass, ws, layer0=0, nlayers=None):
@@ -171,6 +173,7 @@ class DecodeEngine:
         self.mass = torch.zeros((Lr, B, cfg.hkv, cfg.cap), dtype=torch.float32, device=device)
         self.score = torch.zeros((Lr, B, cfg.cap), dtype=torch.float32, device=device)
         self.evicted = torch.zeros((Lr, B), dtype=torch.int32, device=device)
+        self.token = torch.zeros(B, dtype=torch.int32, device=device)
         if cfg.mode == "full_kv":
             self.budget.fill_(cfg.policy.n_low)
 
@@ -180,9 +183,13 @@ class DecodeEngine:
         quantize(self.cache, self.pol, 0, L.QUANT_PREFILL, k_src, v_src, n_src)
 
     # the five calls of one step, in the order of the method
-    def step_confidence(self, logits):
+    def step_confidence(self, logits, temperature=None, uniform=None):
+        """Confidence and budgets; with temperature given (0 = greedy) also the
+        next token of every sequence into self.token, in the same pass."""
         confidence(logits, self.pol, self.c, self.budget, self.cache.status, self.conf_ws,
-                   self.layer_n_high, self.layer_n_low)
+                   self.layer_n_high, self.layer_n_low,
+                   token_out=None if temperature is None else self.token,
+                   temperature=0.0 if temperature is None else temperature, uniform=uniform)
 
     def step_attention(self, q, k_new, v_new):
         attn_decode(self.cache, q, k_new, v_new, self.out, self.mass, self.attn_ws)

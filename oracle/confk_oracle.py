@@ -73,6 +73,36 @@ def confidence(logits, w_h=0.4, w_m=0.3, w_p=0.3):
     return float(c), 0, dict(H_hat=float(H_hat), m=float(m), sig=float(sig), p1=float(p1))
 
 
+def next_token(logits, temperature=0.0, u=0.0):
+    """Next token x_{t+1} (review Algorithm 1, step 13).
+
+    temperature 0: greedy, the smallest index among the largest logits.
+    temperature > 0: sampling from softmax(z / temperature) by inversion with
+    the uniform draw u in [0, 1): the smallest index i (index order) whose
+    cumulative probability sum_{j<=i} p_j exceeds u. Reading: the pages name
+    the sampling step without fixing a rule; inversion in index order with a
+    caller-supplied uniform is the plain reading that makes the draw
+    reproducible. Returns -1 for flagged rows (as the confidence does).
+    """
+    z = np.asarray(logits, dtype=np.float64)
+    if z.shape[0] < 2 or np.isnan(z).any() or np.isposinf(z).any() or np.isneginf(z).all():
+        return -1
+    if temperature == 0:
+        return int(np.flatnonzero(z == z.max())[0])
+    w = np.exp((z - z.max()) / temperature)
+    cdf = np.cumsum(w / w.sum())
+    return int(min(np.searchsorted(cdf, u, side="right"), z.shape[0] - 1))
+
+
+def token_interval(logits, temperature, i):
+    """Cumulative probability before and through token i under
+    softmax(z / temperature): a draw u picks i exactly when lo <= u < hi."""
+    z = np.asarray(logits, dtype=np.float64)
+    w = np.exp((z - z.max()) / temperature)
+    p = w / w.sum()
+    return float(p[:i].sum()), float(p[: i + 1].sum())
+
+
 def budget(c, tau, n_high, n_low):
     """Tight budget N_high when c >= tau (confident), loose N_low otherwise ([S]; [R2]).
 

@@ -67,13 +67,15 @@ FAKE = ctypes.c_void_p(0x1000)
 
 def test_confidence_validation(lib):
     pol = _pol()
-    ok_args = dict(logits=FAKE, ld=10, batch=2, vocab=10, nbl=1, ws=FAKE, wsb=1 << 20)
+    ok_args = dict(logits=FAKE, ld=10, batch=2, vocab=10, nbl=1, ws=FAKE, wsb=1 << 20, uniform=None,
+                   temperature=0.0, token=None)
 
     def call(**kw):
         a = dict(ok_args)
         a.update(kw)
         return lib.confk_confidence(a["logits"], a["ld"], a["batch"], a["vocab"], ctypes.byref(pol),
-                                    None, None, a["nbl"], FAKE, FAKE, None, a["ws"], a["wsb"], None)
+                                    None, None, a["nbl"], FAKE, FAKE, None, a["uniform"], a["temperature"],
+                                    a["token"], a["ws"], a["wsb"], None)
     assert call(logits=None) == M.ERR_INVALID_ARG
     assert call(vocab=1) == M.ERR_INVALID_ARG
     assert call(ld=5) == M.ERR_INVALID_ARG
@@ -81,8 +83,12 @@ def test_confidence_validation(lib):
     assert call(nbl=2) == M.ERR_INVALID_ARG          # per-layer count without arrays
     assert call(ws=None) == M.ERR_WORKSPACE
     assert call(wsb=4) == M.ERR_WORKSPACE
+    assert call(temperature=-1.0) == M.ERR_INVALID_ARG
+    assert call(temperature=float("nan")) == M.ERR_INVALID_ARG
+    assert call(temperature=float("inf")) == M.ERR_INVALID_ARG
+    assert call(temperature=0.8, token=FAKE) == M.ERR_INVALID_ARG   # sampling needs uniforms
     assert lib.confk_confidence(FAKE, 10, 2, 10, ctypes.byref(pol), FAKE, None, 2, FAKE, FAKE, None,
-                                FAKE, 1 << 20, None) == M.ERR_INVALID_ARG
+                                None, 0.0, None, FAKE, 1 << 20, None) == M.ERR_INVALID_ARG
 
 
 def test_attention_validation(lib):
@@ -109,7 +115,7 @@ def test_attention_workspace_needed_only_for_long_caches(lib):
     assert need > 0
     assert lib.confk_attn_decode(ctypes.byref(big), 0, 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 4,
                                  None) == M.ERR_WORKSPACE
-    assert lib.confk_workspace_size(M._lib.WS_CONFIDENCE, None, 0, 8, 152064) == 8 * 38 * 6 * 4
+    assert lib.confk_workspace_size(M._lib.WS_CONFIDENCE, None, 0, 8, 152064) == 8 * 38 * 8 * 4
 
 
 def test_compact_quantize_ema_validation(lib):

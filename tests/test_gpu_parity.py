@@ -373,3 +373,76 @@ def test_long_context_pyramid_retains_planted_keys():
             assert (n[l] <= cfg.layer_n_low[l] + 1).all()
             for b in range(cfg.batch):
                 assert planted[b] in pos[l, b, : n[l, b]], f"step {i} l={l} b={b}: planted key evicted"
+
+
+def _conf_buffers(dev, B, V):
+    import mixed_precision_attention_amd as M
+    pol = M.engine.make_policy(synth.Policy(n_high=1024, n_low=2048))
+    c = torch.zeros(B, dtype=torch.float32, device=dev)
+    bud = torch.zeros((1, B), dtype=torch.int32, device=dev)
+    tok = torch.zeros(B, dtype=torch.int32, device=dev)
+    ws = torch.zeros(M.engine.workspace_bytes(M._lib.WS_CONFIDENCE, batch=B, vocab=V), dtype=torch.uint8,
+                     device=dev)
+    return pol, c, bud, tok, ws
+
+
+def test_next_token_greedy_and_sampled():
+    """Step-13 choice fused into the confidence pass: greedy equals the
+    oracle's (smallest index among the largest logits, ties crafted); a
+    tempered draw is a token whose cumulative-probability interval holds u
+    (to fp32 summation error)."""
+    import mixed_precision_attention_amd as M
+    dev = _dev()
+    for V, ld in ((152064, 152064), (5003, 5008), (1000, 1003)):
+        B = 8
+        rng = np.random.default_rng(V)
+        z = np.zeros((B, ld), np.float32)
+        z[:, :V] = rng.standard_normal((B, V)).astype(np.float32) * np.array([0.5, 2, 8, 8, 2, 0.5, 8, 8])[:, None]
+        z[3, [7, V - 2]] = z[3, :V].max() + 1.0        # tied maxima: the smaller index wins
+        z[6, : V // 2] = -np.inf                        # a block of impossible tokens
+        zt = _t(z, dev)[:, :V]
+        pol, c, bud, tok, ws = _conf_buffers(dev, B, V)
+        M.confidence(zt, pol, c, bud, None, ws, token_out=tok, temperature=0.0)
+        torch.cuda.synchronize()
+        for b in range(B):
+            assert int(tok[b]) == O.next_token(z[b, :V], 0.0), f"V={V} b={b} greedy"
+        for T in (0.5, 1.0, 2.0):
+            u = rng.random(B).astype(np.float32)
+            M.confidence(zt, pol, c, bud, None, ws, token_out=tok, temperature=T, uniform=_t(u, dev))
+            torch.cuda.synchronize()
+            for b in range(B):
+                i = int(tok[b])
+                assert 0 <= i < V and np.isfinite(z[b, i]), f"V={V} T={T} b={b}: token {i}"
+                lo, hi = O.token_interval(z[b, :V], T, i)
+                assert lo - 5e-5 <= float(u[b]) <= hi + 5e-5, f"V={V} T={T} b={b}: u={u[b]} not in [{lo}, {hi}]"
+                assert abs(float(c[b]) - O.confidence(z[b, :V])[0]) <= ATOL
+
+
+def test_next_token_temperature_sweep():
+    """The confidence is computed on the untempered distribution; the higher
+    the sampling temperature, the less often a confident step emits the token
+    the confidence describes (its argmax). Rows follow the workload's logit
+    mix (scales 0.5 / 2 / 8)."""
+    import mixed_precision_attention_amd as M
+    dev = _dev()
+    cfg = synth.get_config("gpt2_layer")
+    V, B, steps = cfg.vocab, cfg.batch, 96
+    pol, c, bud, tok, ws = _conf_buffers(dev, B, V)
+    rng = np.random.default_rng(23)
+    rates = {}
+    for T in (0.0, 0.5, 1.0, 1.5):
+        hit = n = 0
+        for s in range(steps):
+            z = synth.logits_for_step(cfg, 31, s)
+            u = rng.random(B).astype(np.float32)
+            M.confidence(_t(z, dev), pol, c, bud, None, ws, token_out=tok, temperature=T, uniform=_t(u, dev))
+            torch.cuda.synchronize()
+            for b in range(B):
+                if float(c[b]) >= 0.7:
+                    n += 1
+                    hit += int(tok[b]) == O.next_token(z[b], 0.0)
+        rates[T] = hit / max(n, 1)
+    print("[sweep] argmax rate of confident steps by temperature:", rates, flush=True)
+    assert rates[0.0] == 1.0
+    assert rates[0.5] >= rates[1.0] >= rates[1.5]
+    assert rates[1.5] < 0.9

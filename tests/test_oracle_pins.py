@@ -460,3 +460,48 @@ def test_ema_of_retained_token_follows_closed_recurrence():
     j = int(np.flatnonzero(caches[0][0].pos == tracked)[0])
     want = sum((1 - pol.lam) * pol.lam ** (len(hist) - 1 - k) * hist[k] for k in range(len(hist)))
     assert abs(caches[0][0].ema[j] - want) < 1e-15
+
+
+# ---------------------------------------------------------------- next token
+
+def test_next_token_greedy_smallest_index_among_ties():
+    z = np.array([0.5, 2.0, -1.0, 2.0, 1.9], np.float32)
+    assert O.next_token(z, 0.0) == 1
+    z2 = np.array([-np.inf, 3.0, 3.0], np.float32)
+    assert O.next_token(z2, 0.0) == 1
+    assert O.next_token(np.array([np.nan, 1.0], np.float32), 0.0) == -1
+
+
+def test_next_token_two_level_closed_form():
+    # p = (1/4, 3/4) at temperature 1; (1, sqrt 3)/(1 + sqrt 3) at temperature 2
+    z = np.array([0.0, np.log(3.0)])
+    assert O.next_token(z, 1.0, 0.0) == 0
+    assert O.next_token(z, 1.0, 0.2499) == 0
+    assert O.next_token(z, 1.0, 0.2501) == 1
+    p0 = 1.0 / (1.0 + np.sqrt(3.0))
+    assert O.next_token(z, 2.0, p0 - 1e-6) == 0
+    assert O.next_token(z, 2.0, p0 + 1e-6) == 1
+    lo, hi = O.token_interval(z, 2.0, 1)
+    assert abs(lo - p0) < 1e-12 and abs(hi - 1.0) < 1e-12
+
+
+def test_next_token_frequencies_match_tempered_softmax():
+    rng = np.random.default_rng(17)
+    z = rng.standard_normal(12) * 1.5
+    z[4] = -np.inf                       # never drawn
+    T = 0.7
+    p = np.exp((z - z.max()) / T)
+    p /= p.sum()
+    us = rng.random(20000)
+    counts = np.bincount([O.next_token(z, T, u) for u in us], minlength=12)
+    assert counts[4] == 0
+    sd = np.sqrt(p * (1 - p) / len(us))
+    assert np.all(np.abs(counts / len(us) - p) <= 4.5 * sd + 1e-12)
+
+
+def test_next_token_low_temperature_approaches_greedy():
+    rng = np.random.default_rng(5)
+    z = rng.standard_normal(50)
+    g = O.next_token(z, 0.0)
+    for u in (0.01, 0.5, 0.99):
+        assert O.next_token(z, 1e-3, u) == g
