@@ -262,7 +262,8 @@ def main():
             "workload": f"{cfg.name}: {cfg.layers} layers, {cfg.hq}/{cfg.hkv} heads, d{cfg.d}, "
                         f"batch {cfg.batch}, {cfg.prefill}-token prefill, V={cfg.vocab}, "
                         f"N_high/N_low={pol.n_high}/{pol.n_low}, P={pol.protect}, W={pol.window}, "
-                        f"alpha={pol.alpha}" + (", full FP16 cache (comparison run)" if full else ""),
+                        f"alpha={pol.alpha}" + (", full FP16 cache (comparison run)" if full else "")
+                        + (f", block eviction B={pol.block}" if pol.block else ""),
             "layers": cfg.layers, "batch": cfg.batch, "hq": cfg.hq, "hkv": cfg.hkv, "d": cfg.d,
             "prefill": cfg.prefill, "vocab": cfg.vocab, "parallelism": "single GPU",
         },

@@ -83,10 +83,18 @@ extern "C" {
  * tight budget taken when c >= tau, n_low the loose budget, protect (P) the
  * newest tokens never evicted, window (W) the FP16 window, alpha the rank
  * mix, lambda the EMA decay, (w_h, w_m, w_p) the confidence weights.
+ * block: 0 for the method's token eviction; B >= 16 evicts whole blocks of B
+ * consecutive cached tokens instead (the coarse, block-level eviction the
+ * review's "局限与改进" and "独立分析的弱点" sections name as the way to fit
+ * paged serving layouts; block score and grouping are this library's
+ * reading, the pages fix neither): the candidates are
+ * grouped into blocks of B from the oldest (a trailing partial block is kept),
+ * a block ranks by the largest score of its tokens, and the ceil((n-N)/B)
+ * lowest-ranked blocks leave (the older block first among equals).
  */
 typedef struct confk_policy {
   float tau, alpha, lambda, w_h, w_m, w_p;
-  int32_t n_high, n_low, protect, window;
+  int32_t n_high, n_low, protect, window, block;
 } confk_policy;
 
 /*
@@ -215,9 +223,11 @@ int confk_ema_rank(const confk_cache* cache, int32_t layer0, int32_t nlayers, co
  *   ws           >= confk_workspace_size(CONFK_WS_COMPACT, ...) bytes: the
  *                move plans (and, above 4096 tokens per sequence, metadata
  *                staging); contents need no initialisation
+ * With pol->block = B > 0, whole blocks of B tokens leave (see confk_policy).
  * Sets CONFK_STATUS_CAPACITY (and skips the append) if a sequence has no
  * free slot. Errors: INVALID_ARG, BUDGET (protect > n_low or > n_high,
- * capacity below n_low + 2, FP16 ring below window + 1), WORKSPACE.
+ * capacity below n_low + 2, FP16 ring below window + 1), UNSUPPORTED (more
+ * than 512 blocks per sequence), WORKSPACE.
  */
 int confk_compact(const confk_cache* cache, int32_t layer0, int32_t nlayers, const int32_t* budget,
                   int32_t budget_layer_stride, const float* score, const confk_policy* pol,

@@ -42,6 +42,7 @@ class Policy(ctypes.Structure):
         ("tau", c_float), ("alpha", c_float), ("lambda_", c_float),
         ("w_h", c_float), ("w_m", c_float), ("w_p", c_float),
         ("n_high", c_int32), ("n_low", c_int32), ("protect", c_int32), ("window", c_int32),
+        ("block", c_int32),
     ]
 
 

@@ -26,6 +26,7 @@ bool policy_ok(const confk_policy* p) {
   if (!p) return false;
   if (p->n_high < 1 || p->n_low < 1 || p->protect < 0 || p->window < 1) return false;
   if (!(p->lambda >= 0.f && p->lambda <= 1.f) || !(p->alpha >= 0.f && p->alpha <= 1.f)) return false;
+  if (p->block != 0 && p->block < 16) return false;
   return true;
 }
 
@@ -162,6 +163,7 @@ int confk_compact(const confk_cache* cache, int32_t layer0, int32_t nlayers, con
   if (pol->protect > pol->n_high || pol->protect > pol->n_low) return CONFK_ERR_BUDGET;
   if (pol->n_low + 1 > cache->cap - 1 || pol->n_high + 1 > cache->cap - 1) return CONFK_ERR_BUDGET;
   if (pol->window + 1 > cache->cap16) return CONFK_ERR_BUDGET;
+  if (pol->block > 0 && cache->cap / pol->block > kMaxEvictBlocks) return CONFK_ERR_UNSUPPORTED;
   const size_t need = compact_ws_bytes(nlayers, cache->batch, cache->cap);
   if (!ws || ws_bytes < need) return CONFK_ERR_WORKSPACE;
   CompactArgs a{};
@@ -172,6 +174,7 @@ int confk_compact(const confk_cache* cache, int32_t layer0, int32_t nlayers, con
   a.nl = nlayers;
   a.budget_stride = budget_layer_stride;
   a.protect = pol->protect;
+  a.block = pol->block;
   a.budget = budget;
   a.score = score;
   a.k_new = k_new;

@@ -18,6 +18,9 @@
 //     monotone bucket floor(score * 1024) (clamped), then by ranking the few
 //     keys of the boundary bucket; a radix select on the score bits covers
 //     crowded buckets and long caches.
+//     Block eviction (B > 0) takes kb = min(full blocks, ceil(k / B)) whole
+//     blocks of B consecutive candidates instead, the blocks with the
+//     smallest (largest key in the block, block index), so k = kb * B.
 //  2. Ballot bit-plane scans give each survivor its new logical index and
 //     each region (INT8 ring, FP16 ring) its eviction count and first / last
 //     hole, behind one barrier.
@@ -45,6 +48,7 @@ constexpr int kRegKeys = 8;    // indices per thread held in registers
 constexpr int kBuckets = 1024;
 constexpr int kRankMax = 64;   // boundary-bucket keys ranked by one wave
 constexpr int kHdr = 16;       // plan header words per (layer, sequence)
+static_assert(2 * kMaxEvictBlocks <= kBuckets, "block keys and flags share the histogram");
 constexpr int kMoveRegs = 8;  // 16-byte pieces per lane per move round
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -163,7 +167,7 @@ __device__ uint32_t radix_select(int& kk, int cnt, int lo, int ncand, const uint
   return prefix;
 }
 
-template <bool REG>
+template <bool REG, bool BLOCK>
 __global__ __launch_bounds__(kThreads) void compact_plan_kernel(CompactArgs a) {
   const CacheView& c = a.c;
   const int lb = blockIdx.x;
@@ -201,8 +205,15 @@ __global__ __launch_bounds__(kThreads) void compact_plan_kernel(CompactArgs a) {
     }
     return;
   }
-  const int k = n > N ? n - N : 0;
+  int k = n > N ? n - N : 0;
   const int ncand = n - P;  // candidates: logical [0, ncand)
+  const int B = BLOCK ? a.block : 0;  // block eviction: whole blocks of B candidates
+  int nb = 0, kb = 0;       // full candidate blocks; blocks that leave
+  if (BLOCK && k > 0) {
+    nb = ncand / B;
+    kb = min(nb, (k + B - 1) / B);
+    k = kb * B;
+  }
 
   if (k == 0) {  // nothing leaves: the new token (metadata slot n) is appended
     if (threadIdx.x == 0) {
@@ -250,9 +261,47 @@ __global__ __launch_bounds__(kThreads) void compact_plan_kernel(CompactArgs a) {
 
   // ---------------------------------------------------------- 1. select
   // T64: the k-th smallest (key, index); every candidate at or below leaves.
+  // Block eviction instead marks the kb blocks with the smallest (largest
+  // key in the block, block index) in bsel.
   uint64_t T64 = 0;
-  bool use_radix = !REG;
-  if constexpr (REG) {
+  uint32_t* const bmax = sh.hist;                    // [nb] block keys
+  uint32_t* const bsel = sh.hist + kMaxEvictBlocks;  // [nb] 1: the block leaves
+  bool use_radix = !REG && !BLOCK;
+  if constexpr (BLOCK) {
+    for (int q = threadIdx.x; q < nb; q += kThreads) bmax[q] = 0u;  // below every key
+    __syncthreads();
+    const int span = nb * B;
+    int cur = -1;
+    uint32_t run = 0;
+    auto fold = [&](int j) {
+      const int i = lo + j;
+      if (i < span) {
+        const int q = i / B;
+        if (q != cur) {
+          if (cur >= 0) atomicMax(&bmax[cur], run);
+          cur = q;
+          run = 0u;
+        }
+        run = max(run, key_at(j));
+      }
+    };
+    if constexpr (REG) {
+#pragma unroll
+      for (int j = 0; j < kRegKeys; ++j)
+        if (j < cnt) fold(j);
+    } else {
+      for (int j = 0; j < cnt; ++j) fold(j);
+    }
+    if (cur >= 0) atomicMax(&bmax[cur], run);
+    __syncthreads();
+    for (int q = threadIdx.x; q < nb; q += kThreads) {
+      const uint64_t mine = ((uint64_t)bmax[q] << 32) | (uint32_t)q;
+      int rank = 0;
+      for (int z = 0; z < nb; ++z) rank += (((uint64_t)bmax[z] << 32) | (uint32_t)z) < mine ? 1 : 0;
+      bsel[q] = rank < kb ? 1u : 0u;
+    }
+    __syncthreads();
+  } else if constexpr (REG) {
     for (int i = threadIdx.x; i < kBuckets; i += kThreads) sh.hist[i] = 0;
     if (threadIdx.x == 0) sh.rank_n = 0;
     __syncthreads();
@@ -352,6 +401,7 @@ __global__ __launch_bounds__(kThreads) void compact_plan_kernel(CompactArgs a) {
   // ------------------------------------------- 2. flags, scans, regions
   auto leaves = [&](int j) -> bool {
     const int i = lo + j;
+    if constexpr (BLOCK) return i < nb * B && bsel[i / B] != 0u;
     return i < ncand && ((((uint64_t)key_at(j)) << 32) | (uint32_t)i) <= T64;
   };
   uint32_t evm = 0;  // bit j: index lo + j leaves (register path)
@@ -408,7 +458,7 @@ __global__ __launch_bounds__(kThreads) void compact_plan_kernel(CompactArgs a) {
   const int wl8 = h8 ? __shfl(l8, 63 - __clzll((long long)h8), 64) : -1;
   const int wf16 = h16 ? __shfl(f16, __ffsll((unsigned long long)h16) - 1, 64) : INT32_MAX;
   const int wl16 = h16 ? __shfl(l16, 63 - __clzll((long long)h16), 64) : -1;
-  __syncthreads();  // the select's shared values are no longer read
+  __syncthreads();  // the select's shared values other than bsel are no longer read
   if (lane == 0) {
     sh.wsum[0][w] = tk;
     sh.wsum[1][w] = t8;
@@ -640,10 +690,17 @@ size_t compact_plan_bytes(int nlayers, int batch, int cap) {
 
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
   const int blocks = a.nl * a.c.B;
-  if (a.c.cap <= kRegKeys * kThreads) {
-    hipLaunchKernelGGL(compact_plan_kernel<true>, dim3(blocks), dim3(kThreads), 0, s, a);
+  const bool reg = a.c.cap <= kRegKeys * kThreads;
+  if (a.block > 0) {
+    if (reg)
+      hipLaunchKernelGGL((compact_plan_kernel<true, true>), dim3(blocks), dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((compact_plan_kernel<false, true>), dim3(blocks), dim3(kThreads), 0, s, a);
   } else {
-    hipLaunchKernelGGL(compact_plan_kernel<false>, dim3(blocks), dim3(kThreads), 0, s, a);
+    if (reg)
+      hipLaunchKernelGGL((compact_plan_kernel<true, false>), dim3(blocks), dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((compact_plan_kernel<false, false>), dim3(blocks), dim3(kThreads), 0, s, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -19,7 +19,9 @@
 // sampling, S_T = sum e^((z-M)/T). The final kernel draws by inversion with
 // the caller's uniform number u: the smallest index whose cumulative weight in
 // index order exceeds u * S_T, found chunk by chunk and then inside the one
-// chunk where the cumulative weight crosses.
+// chunk where the cumulative weight crosses. The kernels are instantiated per
+// kind of choice (none, greedy, sampling), so each carries only the state it
+// needs.
 #include "confk_internal.h"
 
 namespace confk {
@@ -43,6 +45,9 @@ struct RowState {
 };
 constexpr int kRec = 8;  // floats per partial record
 
+// kind of next-token choice made in the pass
+enum { kNoChoice = 0, kGreedy = 1, kSample = 2 };
+
 // Inserts x into the two largest values t1 >= t2 of a multiset.
 __device__ __forceinline__ void top2_insert(float& t1, float& t2, float x) {
   const float n2 = fmaxf(t2, fminf(t1, x));
@@ -50,14 +55,18 @@ __device__ __forceinline__ void top2_insert(float& t1, float& t2, float x) {
   t2 = n2;
 }
 
-// inv_t: 1 / temperature for sampling, 0 when S_T is not needed
+// inv_t: 1 / temperature (sampling only)
+template <int CH>
 __device__ __forceinline__ RowState merge(const RowState& a, const RowState& b, float inv_t) {
   RowState r;
   r.M = fmaxf(a.M, b.M);
   r.flag = a.flag | b.flag;
   r.t1 = fmaxf(a.t1, b.t1);
   r.t2 = fmaxf(fminf(a.t1, b.t1), fmaxf(a.t2, b.t2));
-  r.i1 = a.t1 > b.t1 ? a.i1 : (b.t1 > a.t1 ? b.i1 : min(a.i1, b.i1));
+  if constexpr (CH == kGreedy)
+    r.i1 = a.t1 > b.t1 ? a.i1 : (b.t1 > a.t1 ? b.i1 : min(a.i1, b.i1));
+  else
+    r.i1 = INT32_MAX;
   r.S = 0.f;
   r.T = 0.f;
   r.ST = 0.f;
@@ -66,18 +75,19 @@ __device__ __forceinline__ RowState merge(const RowState& a, const RowState& b, 
     const float e = exp_neg(d);
     r.S += a.S * e;
     r.T += (a.T + d * a.S) * e;
-    if (inv_t > 0.f) r.ST += a.ST * exp_neg(d * inv_t);
+    if constexpr (CH == kSample) r.ST += a.ST * exp_neg(d * inv_t);
   }
   if (b.S > 0.f) {
     const float d = b.M - r.M;
     const float e = exp_neg(d);
     r.S += b.S * e;
     r.T += (b.T + d * b.S) * e;
-    if (inv_t > 0.f) r.ST += b.ST * exp_neg(d * inv_t);
+    if constexpr (CH == kSample) r.ST += b.ST * exp_neg(d * inv_t);
   }
   return r;
 }
 
+template <int CH>
 __device__ __forceinline__ RowState shfl_state(const RowState& s, int o) {
   RowState r;
   r.M = __shfl_xor(s.M, o, 64);
@@ -86,11 +96,12 @@ __device__ __forceinline__ RowState shfl_state(const RowState& s, int o) {
   r.t1 = __shfl_xor(s.t1, o, 64);
   r.t2 = __shfl_xor(s.t2, o, 64);
   r.flag = (uint32_t)__shfl_xor((int)s.flag, o, 64);
-  r.ST = __shfl_xor(s.ST, o, 64);
-  r.i1 = __shfl_xor(s.i1, o, 64);
+  r.ST = CH == kSample ? __shfl_xor(s.ST, o, 64) : 0.f;
+  r.i1 = CH == kGreedy ? __shfl_xor(s.i1, o, 64) : INT32_MAX;
   return r;
 }
 
+template <int CH>
 __global__ __launch_bounds__(kThreads) void conf_partial_kernel(ConfArgs a) {
   const int b = blockIdx.y;
   const int chunk = blockIdx.x;
@@ -122,7 +133,7 @@ __global__ __launch_bounds__(kThreads) void conf_partial_kernel(ConfArgs a) {
       x[k] = (i < end) ? row[i] : -INFINITY;
     }
   }
-  // logical index of x[k]
+  // logical index of x[k], ascending in k
   auto idx = [&](int k) {
     return a.vec4 ? start + 4 * (threadIdx.x + (k >> 2) * kThreads) + (k & 3) : start + threadIdx.x + k * kThreads;
   };
@@ -140,7 +151,8 @@ __global__ __launch_bounds__(kThreads) void conf_partial_kernel(ConfArgs a) {
       s.flag = 1;
     } else {
       s.M = fmaxf(s.M, v);
-      if (v > s.t1 || (v == s.t1 && v > -INFINITY && idx(k) < s.i1)) s.i1 = idx(k);
+      if constexpr (CH == kGreedy)
+        if (v > s.t1) s.i1 = idx(k);  // strict: the first of equal maxima stays
       top2_insert(s.t1, s.t2, v);
     }
   }
@@ -156,20 +168,20 @@ __global__ __launch_bounds__(kThreads) void conf_partial_kernel(ConfArgs a) {
         const float e = exp_neg(d);
         s.S += e;
         s.T += d * e;
-        if (inv_t > 0.f) s.ST += exp_neg(d * inv_t);
+        if constexpr (CH == kSample) s.ST += exp_neg(d * inv_t);
       }
     }
   }
   // wave reduction
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) s = merge(s, shfl_state(s, o), inv_t);
+  for (int o = 1; o < 64; o <<= 1) s = merge<CH>(s, shfl_state<CH>(s, o), inv_t);
   __shared__ RowState red[kThreads / 64];
   const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) red[w] = s;
   __syncthreads();
   if (threadIdx.x == 0) {
     RowState r = red[0];
-    for (int i = 1; i < kThreads / 64; ++i) r = merge(r, red[i], inv_t);
+    for (int i = 1; i < kThreads / 64; ++i) r = merge<CH>(r, red[i], inv_t);
     float* p = a.partial + ((int64_t)b * a.nchunks + chunk) * kRec;
     p[0] = r.M;
     p[1] = r.S;
@@ -184,6 +196,7 @@ __global__ __launch_bounds__(kThreads) void conf_partial_kernel(ConfArgs a) {
 
 // One wave per row: lane i merges partials i, i+64, ... in order, then a
 // butterfly merge (commutative, so every lane ends with the same state).
+template <int CH>
 __global__ __launch_bounds__(64) void conf_final_kernel(ConfArgs a) {
   const int b = blockIdx.x;
   const int lane = threadIdx.x;
@@ -210,15 +223,15 @@ __global__ __launch_bounds__(64) void conf_final_kernel(ConfArgs a) {
   r.flag = 0;
   r.ST = 0.f;
   r.i1 = INT32_MAX;
-  for (int i = lane; i < a.nchunks; i += 64) r = merge(r, load(i), inv_t);
+  for (int i = lane; i < a.nchunks; i += 64) r = merge<CH>(r, load(i), inv_t);
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) r = merge(r, shfl_state(r, o), inv_t);
+  for (int o = 1; o < 64; o <<= 1) r = merge<CH>(r, shfl_state<CH>(r, o), inv_t);
   const bool bad = r.flag != 0 || !(r.M > -INFINITY);
 
-  if (a.token_out) {  // next-token choice (uniform per row)
+  if constexpr (CH != kNoChoice) {  // next-token choice (uniform per row)
     int tok = -1;
-    if (!bad && !(inv_t > 0.f)) {
-      tok = r.i1;  // greedy
+    if constexpr (CH == kGreedy) {
+      if (!bad) tok = r.i1;
     } else if (!bad) {
       // chunk weights e^((M_c - M)/T) S_T,c in chunk order; lane holds
       // chunks lane, lane+64, ... (ascending), the wave scans them in order
@@ -321,10 +334,17 @@ hipError_t launch_confidence(const ConfArgs& in, hipStream_t s) {
   ConfArgs a = in;
   a.chunk = kChunk;
   a.nchunks = (a.vocab + kChunk - 1) / kChunk;
-  hipLaunchKernelGGL(conf_partial_kernel, dim3(a.nchunks, a.batch), dim3(kThreads), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(conf_final_kernel, dim3(a.batch), dim3(64), 0, s, a);
+  const dim3 grid(a.nchunks, a.batch);
+  if (!a.token_out) {
+    hipLaunchKernelGGL(conf_partial_kernel<kNoChoice>, grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(conf_final_kernel<kNoChoice>, dim3(a.batch), dim3(64), 0, s, a);
+  } else if (a.inv_temp > 0.f) {
+    hipLaunchKernelGGL(conf_partial_kernel<kSample>, grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(conf_final_kernel<kSample>, dim3(a.batch), dim3(64), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(conf_partial_kernel<kGreedy>, grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(conf_final_kernel<kGreedy>, dim3(a.batch), dim3(64), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -71,9 +71,12 @@ struct EmaArgs {
   float* score;
 };
 
+constexpr int kMaxEvictBlocks = 512;  // blocks per sequence in block eviction
+
 struct CompactArgs {
   CacheView c;
   int32_t layer0, nl, budget_stride, protect;
+  int32_t block;  // 0: token eviction; B: whole blocks of B tokens
   int32_t* plan;   // workspace: per-(layer, sequence) move plans
   int32_t* stage;  // workspace: metadata staging (caches above 4096 tokens)
   const int32_t* budget;

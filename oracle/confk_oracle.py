@@ -231,23 +231,42 @@ def rank_scores(a, pos, alpha):
 # Eviction and compaction  ([S] Token-Ranking und Eviktion; [R3] steps 5-11)
 # ---------------------------------------------------------------------------
 
-def select_keep(s, pos, N, P):
+def select_keep(s, pos, N, P, block=0):
     """Keep mask after budget eviction of one (layer, sequence).
 
     If n <= N nothing is evicted. Otherwise exactly k = n - N tokens are
     evicted: those with the smallest (s, pos) among all tokens except the P
     newest positions, which are always kept. Reading: equal scores evict the
     older token first.
+
+    block = B > 0 is the coarse variant that the review's sections on
+    limitations ("局限与改进", "独立分析的弱点") name for paged layouts:
+    whole blocks of B position-consecutive candidates leave. Reading: the
+    candidates are cut into blocks from the oldest, a trailing partial block
+    stays, a block's score is the largest score among its tokens, and
+    min(full blocks, ceil(k / B)) blocks with the smallest (block score,
+    block order) leave, so the kept count may fall below N by less than B
+    (or stay above it when too few full blocks exist).
     """
     n = len(s)
     if N < P:
         raise ValueError("budget below the protected window")
+    if block < 0:
+        raise ValueError("negative block size")
     keep = np.ones(n, dtype=bool)
     if n <= N:
         return keep
     k = n - N
     order_by_pos = np.argsort(pos, kind="stable")
     cand = order_by_pos[: max(0, n - P)]
+    if block > 0:
+        blocks = [cand[j * block:(j + 1) * block] for j in range(len(cand) // block)]
+        kb = min(len(blocks), -(-k // block))
+        ranked = sorted(range(len(blocks)),
+                        key=lambda j: (max(float(s[i]) for i in blocks[j]), j))
+        for j in ranked[:kb]:
+            keep[blocks[j]] = False
+        return keep
     key = sorted(cand.tolist(), key=lambda i: (float(s[i]), int(pos[i])))
     keep[np.asarray(key[:k], dtype=np.int64)] = False
     return keep
@@ -395,7 +414,7 @@ def step_one(cache, q, k_new, v_new, t, pol, N, score_given=None):
     a, a_new = ema_update(cache.ema, m, pol.lam)
     s = rank_scores(a, cache.pos, pol.alpha)
     s_sel = s if score_given is None else np.asarray(score_given, np.float64)
-    kp = select_keep(s_sel, cache.pos, N, pol.protect)
+    kp = select_keep(s_sel, cache.pos, N, pol.protect, getattr(pol, "block", 0))
     c1 = cache.copy()
     c1.ema = a
     c1 = compact(c1, kp)

@@ -21,6 +21,7 @@ class Policy:
     n_low: int = 512
     protect: int = 32
     window: int = 64
+    block: int = 0     # 0: token eviction; B: whole blocks of B tokens
 
 
 @dataclass(frozen=True)
@@ -116,6 +117,12 @@ CONFIGS = {
         name="qwen32b_sw512", layers=64, batch=8, hq=40, hkv=8, d=128, vocab=152064,
         prefill=2048, steps=4096,
         policy=Policy(alpha=0.0, n_high=512, n_low=512, protect=64, window=256)),
+    # The Qwen-32B workload with block eviction: whole blocks of 128 tokens
+    # leave (coarse eviction for paged layouts), same budgets
+    "qwen32b_block128": Config(
+        name="qwen32b_block128", layers=64, batch=8, hq=40, hkv=8, d=128, vocab=152064,
+        prefill=2048, steps=4096,
+        policy=Policy(n_high=1024, n_low=2048, protect=64, window=256, block=128)),
     # Long-context pyramid with one planted key per sequence at depths
     # 10/30/50/70/90 % of the prefill (five sequences, one per depth)
     "qwen32b_niah": Config(

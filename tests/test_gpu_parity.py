@@ -217,6 +217,45 @@ def test_selection_with_tied_scores():
         run.step(i, scores=s)
 
 
+def _block_cfg(cfg, block):
+    from dataclasses import replace
+    return cfg.with_(name=f"{cfg.name}_block{block}", policy=replace(cfg.policy, block=block))
+
+
+@pytest.mark.parametrize("case", ["regs", "long"])
+def test_parity_block_eviction(case):
+    """Whole blocks leave (block eviction): survivors, counts and every cache
+    byte against the oracle, on the register-held plan path and on the long
+    cache path (capacity above 4096)."""
+    if case == "regs":
+        cfg = _block_cfg(_cfg("blk", 2, 2, 10, 2, 128, 700, 400, 96, 200, 16, 48), 16)
+        steps = 40
+    else:
+        cfg = _block_cfg(_cfg("blk_long", 1, 2, 5, 1, 128, 900, 5000, 600, 1200, 16, 64), 32)
+        assert cfg.cap > 4096
+        steps = 40
+    print(f"[parity] {cfg.name} steps={steps}", flush=True)
+    run = Run(cfg, seed=12)
+    events = sum(run.step(i) for i in range(steps))
+    ev = run.eng.evicted.cpu().numpy()
+    assert events > 2 and np.all(ev % cfg.policy.block == 0)
+
+
+def test_block_eviction_with_tied_block_maxima():
+    """Crafted scores whose block maxima tie across blocks (same array on both
+    sides): the older block leaves first, bit-exactly as in the oracle."""
+    cfg = _block_cfg(TINY["g5_d128"], 16)
+    print("[parity] tied block maxima", flush=True)
+    run = Run(cfg, seed=4)
+    rng = np.random.default_rng(19)
+    nblk = cfg.cap // 16 + 1
+    for i in range(24):
+        top = rng.integers(0, 3, size=(cfg.layers, cfg.batch, nblk)) / 2.0
+        s = np.repeat(top, 16, axis=2)[:, :, : cfg.cap]
+        s = s - 0.25 * rng.integers(0, 2, size=s.shape)   # most blocks keep their top value
+        run.step(i, scores=s.astype(np.float32))
+
+
 def test_confidence_closed_forms_and_flags():
     import mixed_precision_attention_amd as M
     dev = _dev()

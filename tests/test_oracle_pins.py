@@ -343,6 +343,94 @@ def test_select_all_equal_evicts_oldest():
     assert np.array_equal(np.flatnonzero(~keep), np.arange(10))
 
 
+# ---- block eviction (the review's limitation sections: coarse eviction for
+# paged layouts). Block grouping and the block score are readings; the pins
+# below fix them by hand-worked cases, reduction to token eviction and a
+# brute-force characterisation.
+
+def test_select_block_hand_worked():
+    # 12 tokens, P = 2 protected, B = 3: full candidate blocks {0,1,2},
+    # {3,4,5}, {6,7,8}; token 9 is a partial block and stays. N = 7 -> k = 5
+    # -> ceil(5/3) = 2 blocks leave. Block maxima 0.9, 0.5, 0.4: the last two
+    # leave (a mean would drop block 0 instead of block 1, a min blocks 0, 2).
+    s = np.array([0.1, 0.9, 0.1, 0.5, 0.5, 0.5, 0.2, 0.3, 0.4, 0.0, 0.0, 0.0])
+    pos = np.arange(100, 112)
+    keep = O.select_keep(s, pos, 7, 2, block=3)
+    assert np.flatnonzero(~keep).tolist() == [3, 4, 5, 6, 7, 8]
+    # equal block maxima: the older block leaves first
+    s2 = np.array([0.5, 0.2, 0.1, 0.5, 0.1, 0.1, 0.7, 0.7, 0.7, 0.0, 0.0, 0.0])
+    keep = O.select_keep(s2, pos, 9, 2, block=3)        # k = 3 -> one block
+    assert np.flatnonzero(~keep).tolist() == [0, 1, 2]
+    # too few full blocks: every full block leaves, the count stays above N
+    keep = O.select_keep(s, pos, 2, 2, block=3)         # k = 10 -> 4 blocks wanted, 3 exist
+    assert np.flatnonzero(keep).tolist() == [9, 10, 11]
+
+
+def test_select_block_of_one_is_token_eviction():
+    rng = np.random.default_rng(21)
+    for _ in range(200):
+        n = int(rng.integers(1, 60))
+        P = int(rng.integers(0, n + 1))
+        N = int(rng.integers(P, n + 3))
+        s = rng.integers(0, 5, n) / 4.0                  # many ties
+        pos = np.sort(rng.choice(1000, n, replace=False))
+        perm = rng.permutation(n)                        # order must not matter
+        a = O.select_keep(s[perm], pos[perm], N, P, block=1)
+        b = O.select_keep(s[perm], pos[perm], N, P)
+        assert np.array_equal(a, b)
+
+
+def _brute_force_block_evict(s, pos, N, P, B):
+    n = len(s)
+    if n <= N:
+        return set()
+    rank = np.empty(n, np.int64)
+    rank[np.argsort(pos)] = np.arange(n)                 # 0 = oldest
+    nfull = (n - P) // B
+    members = {j: [i for i in range(n) if rank[i] // B == j] for j in range(nfull)}
+    score = {j: max(s[i] for i in members[j]) for j in members}
+    kb = min(nfull, (n - N + B - 1) // B)
+    found = []
+    for E in itertools.combinations(range(nfull), kb):
+        rest = [j for j in range(nfull) if j not in E]
+        if all((score[e], e) < (score[r], r) for e in E for r in rest):
+            found.append({i for e in E for i in members[e]})
+    assert len(found) == 1
+    return found[0]
+
+
+def test_select_block_brute_force():
+    rng = np.random.default_rng(22)
+    for _ in range(300):
+        B = int(rng.integers(1, 5))
+        n = int(rng.integers(1, 25))
+        P = int(rng.integers(0, n + 1))
+        N = int(rng.integers(P, n + 2))
+        s = rng.integers(0, 4, n) / 4.0
+        pos = rng.choice(500, n, replace=False)          # unsorted positions
+        keep = O.select_keep(s, pos, N, P, block=B)
+        assert set(np.flatnonzero(~keep).tolist()) == _brute_force_block_evict(s, pos, N, P, B)
+
+
+def test_select_block_recency_and_counts():
+    rng = np.random.default_rng(23)
+    n, P, B = 700, 32, 16
+    pos = np.sort(rng.choice(50_000, n, replace=False))
+    for N in (100, 333, 600, 668, 699):
+        k = n - N
+        nfull = (n - P) // B
+        kb = min(nfull, -(-k // B))
+        # recency scores (alpha = 0): the oldest kb blocks leave
+        keep = O.select_keep(O.rank_scores(rng.random(n), pos, 0.0), pos, N, P, block=B)
+        assert np.array_equal(np.flatnonzero(~keep), np.arange(kb * B))
+        keep = O.select_keep(rng.random(n), pos, N, P, block=B)
+        assert (~keep).sum() == kb * B and keep[-P:].all()
+        assert N - B < keep.sum() <= N
+        assert keep[nfull * B:].all()                    # partial block and protected stay
+        ev = np.flatnonzero(~keep)
+        assert np.all(ev.reshape(-1, B) % B == np.arange(B)) and np.all(np.diff(ev.reshape(-1, B)) == 1)
+
+
 def test_compact_and_append_preserve_rows():
     rng = np.random.default_rng(10)
     k = rng.standard_normal((12, 2, 4)); v = rng.standard_normal((12, 2, 4))
