@@ -562,22 +562,21 @@ __global__ __launch_bounds__(kThreads) void compact_plan_kernel(CompactArgs a) {
   }
 }
 
-template <int D, int LGP, int NW>
-__device__ __forceinline__ void ring_rounds(unsigned char* ringk, unsigned char* ringv, int C, int movers,
-                                            int left, int e, int jlo, int base, const int32_t* src, int* sv,
-                                            bool have) {
-  constexpr int NR = D == 128 ? kMoveRegs : kMoveRegs - 2;  // 16-byte pieces per lane per ring per round
-  constexpr int ROWS = (NR * 64) >> LGP;                    // rows per round
-  constexpr int ROWB = 16 << LGP;                           // bytes per row
-  const int lane = threadIdx.x;
+template <int D, int LGP, int NW, int NR>
+__device__ __forceinline__ void ring_rounds(unsigned char* ring, int C, int movers, int left, int e, int jlo,
+                                            int base, const int32_t* src, int* sv, bool have) {
+  constexpr int ROWS = (NR * 64) >> LGP;  // rows per round
+  constexpr int ROWB = 16 << LGP;         // bytes per row
+  static_assert(ROWS <= 64 * NW, "a round's movers must fit one source window");
+  const int lane = threadIdx.x & 63;
   int win = have ? 0 : -64 * NW;  // first mover of the source window held in sv (64 * NW movers)
   for (int m0 = 0; m0 < movers; m0 += ROWS) {
-    if (m0 >= win + 64 * NW) {  // next source window (uniform)
+    if (m0 + ROWS > win + 64 * NW) {  // the round leaves the window: reload it from m0 (uniform)
       win = m0;
 #pragma unroll
       for (int q = 0; q < NW; ++q) sv[q] = win + lane + 64 * q < movers ? src[win + lane + 64 * q] : 0;
     }
-    u32x4 bk[NR], bv[NR];
+    u32x4 bk[NR];
 #pragma unroll
     for (int q = 0; q < NR; ++q) {
       const int u = lane + 64 * q;
@@ -585,13 +584,11 @@ __device__ __forceinline__ void ring_rounds(unsigned char* ringk, unsigned char*
       int sel = sv[0];
 #pragma unroll
       for (int z = 1; z < NW; ++z) sel = ((r - win) >> 6) == z ? sv[z] : sel;  // uniform for a given q
-      const int sidx = __shfl(sel, r & 63, 64);
+      const int sidx = __shfl(sel, (r - win) & 63, 64);
       if (r < movers) {
         int ss = base + sidx;
         ss = ss >= C ? ss - C : ss;
-        const uint32_t o = (uint32_t)ss * ROWB + (u & ((1 << LGP) - 1)) * 16;
-        bk[q] = *reinterpret_cast<const u32x4*>(ringk + o);
-        bv[q] = *reinterpret_cast<const u32x4*>(ringv + o);
+        bk[q] = *reinterpret_cast<const u32x4*>(ring + (uint32_t)ss * ROWB + (u & ((1 << LGP) - 1)) * 16);
       }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -603,9 +600,7 @@ __device__ __forceinline__ void ring_rounds(unsigned char* ringk, unsigned char*
         const int j = jlo + (left ? r : movers - 1 - r);
         int ds = base + (left ? j : j + e);
         ds = ds >= C ? ds - C : ds;
-        const uint32_t o = (uint32_t)ds * ROWB + (u & ((1 << LGP) - 1)) * 16;
-        *reinterpret_cast<u32x4*>(ringk + o) = bk[q];
-        *reinterpret_cast<u32x4*>(ringv + o) = bv[q];
+        *reinterpret_cast<u32x4*>(ring + (uint32_t)ds * ROWB + (u & ((1 << LGP) - 1)) * 16) = bk[q];
       }
     }
   }
@@ -618,23 +613,25 @@ __device__ __forceinline__ unsigned char* uniform_ptr(const void* p) {
   return (unsigned char*)(((uint64_t)hi << 32) | lo);
 }
 
-// One wave per (layer, sequence, kv head): the planned moves of that head's
-// K and V INT8 rings, then of its FP16 rings, then the append. Round trip 1
-// reads the plan header, the first 256 INT8 movers' source indices
-// (speculatively) and the new token's K and V rows; round trip 2 reads the
-// first round's rows (64 INT8 / 32 FP16 rows of each ring at d = 128), which
-// are then written; longer plans take more rounds. A wave orders its own
-// loads before its stores with a counter wait, so no barrier is needed.
-// Rounds follow plan order: round r+1 reads only slots beyond round r's
-// destinations in the packing direction.
+// One workgroup of two waves per (layer, sequence, kv head): wave 0 moves the
+// K rings, wave 1 the V rings (planned INT8 moves, then FP16 moves, then the
+// append of the new token's row). Round trip 1 reads the plan header, the
+// first 256 INT8 movers' source indices (speculatively) and the new row;
+// round trip 2 reads the first round's rows (128 INT8 / 64 FP16 rows at
+// d = 128), which are then written; longer plans take more rounds. A wave
+// orders its own loads before its stores with a counter wait, so no barrier
+// is needed. Rounds follow plan order: round r+1 reads only slots beyond
+// round r's destinations in the packing direction.
 template <int D>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4)))
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(4)))
 void compact_move_kernel(CompactArgs a) {
   typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
   constexpr int L8 = D == 128 ? 3 : 2, L16 = L8 + 1;  // log2 of 16-byte pieces per row
   constexpr int P16 = D / 8;
+  constexpr int NR = D == 128 ? 2 * kMoveRegs : 2 * kMoveRegs - 4;  // pieces per lane per round
   const CacheView& c = a.c;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int kv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // 0: K, 1: V
   const int lb = blockIdx.x;
   const int hh = blockIdx.y;
   const int l = lb / c.B;
@@ -651,27 +648,23 @@ void compact_move_kernel(CompactArgs a) {
   const i32x4 hA = reinterpret_cast<const i32x4*>(hdr)[0];  // MOV8, LEFT8, E8, JLO8
   const i32x4 hB = reinterpret_cast<const i32x4*>(hdr)[1];  // MOV16, LEFT16, E16, JLO16
   const i32x4 hC = reinterpret_cast<const i32x4*>(hdr)[2];  // BASE8, BASE16, APPEND
-  int sv8[4], sv16[1] = {0};
+  constexpr int NW16 = D == 128 ? 1 : 2;  // FP16 source window: 64 * NW16 movers
+  int sv8[4], sv16[NW16] = {};
 #pragma unroll
   for (int q = 0; q < 4; ++q) sv8[q] = lane + 64 * q < cap ? src8[lane + 64 * q] : 0;
-  const int nkv = lane / P16;  // lanes [0, P16): K piece, [P16, 2 P16): V piece of the new row
   u32x4 nrow = {0u, 0u, 0u, 0u};
-  if (lane < 2 * P16)
-    nrow = *reinterpret_cast<const u32x4*>((nkv ? a.v_new : a.k_new) + ((size_t)lb * H + hh) * D +
-                                           (lane - nkv * P16) * 8);
+  if (lane < P16) nrow = *reinterpret_cast<const u32x4*>((kv ? a.v_new : a.k_new) + ((size_t)lb * H + hh) * D + lane * 8);
   const int append = hC[2];
   if (append < 0) return;  // the plan flagged a capacity error
 
-  ring_rounds<D, L8, 4>(uniform_ptr(c.k8 + hrow * cap * D), uniform_ptr(c.v8 + hrow * cap * D), cap, hA[0],
-                        hA[1], hA[2], hA[3], hC[0], src8, sv8, true);
-  unsigned char* k16 = uniform_ptr(c.k16 + hrow * cap16 * D);
-  unsigned char* v16 = uniform_ptr(c.v16 + hrow * cap16 * D);
-  ring_rounds<D, L16, 1>(k16, v16, cap16, hB[0], hB[1], hB[2], hB[3], hC[1], src16, sv16, false);
+  ring_rounds<D, L8, 4, NR>(uniform_ptr((kv ? c.v8 : c.k8) + hrow * cap * D), cap, hA[0], hA[1], hA[2], hA[3],
+                            hC[0], src8, sv8, true);
+  unsigned char* r16 = uniform_ptr((kv ? c.v16 : c.k16) + hrow * cap16 * D);
+  ring_rounds<D, L16, NW16, NR>(r16, cap16, hB[0], hB[1], hB[2], hB[3], hC[1], src16, sv16, false);
 
   // append: every FP16 source has been read (the waits above), and the slot
   // is not a destination
-  if (lane < 2 * P16)
-    *reinterpret_cast<u32x4*>((nkv ? v16 : k16) + (uint32_t)append * (2 * D) + (lane - nkv * P16) * 16) = nrow;
+  if (lane < P16) *reinterpret_cast<u32x4*>(r16 + (uint32_t)append * (2 * D) + lane * 16) = nrow;
 }
 
 }  // namespace
@@ -705,9 +698,9 @@ hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.c.d == 128) {
-    hipLaunchKernelGGL(compact_move_kernel<128>, dim3(blocks, a.c.hkv), dim3(64), 0, s, a);
+    hipLaunchKernelGGL(compact_move_kernel<128>, dim3(blocks, a.c.hkv), dim3(128), 0, s, a);
   } else {
-    hipLaunchKernelGGL(compact_move_kernel<64>, dim3(blocks, a.c.hkv), dim3(64), 0, s, a);
+    hipLaunchKernelGGL(compact_move_kernel<64>, dim3(blocks, a.c.hkv), dim3(128), 0, s, a);
   }
   return hipGetLastError();
 }

@@ -338,6 +338,25 @@ def test_parity_many_heads_multi_round_moves():
     assert events > 0
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_many_movers_in_both_rings(d):
+    """Crafted uniform scores scatter the evictions over the whole cache, so
+    one step moves several hundred INT8 rows and about a hundred FP16 rows
+    per ring: several move rounds and source-window reloads in each ring."""
+    import mixed_precision_attention_amd as M
+    hq, hkv = (4, 4) if d == 64 else (10, 2)
+    cfg = _cfg(f"many_movers_d{d}", 1, 2, hq, hkv, d, 500, 1200, 600, 900, 16, 200)
+    print(f"[parity] many movers d{d}", flush=True)
+    run = Run(cfg, seed=13)
+    rng = np.random.default_rng(31)
+    for i in range(3):
+        s = rng.random((cfg.layers, cfg.batch, cfg.cap)).astype(np.float32)
+        run.step(i, scores=s)
+        if i == 0:
+            meta = run.eng.cache.meta.cpu().numpy()
+            assert meta[..., M.META_MOVED].max() > 256 and meta[..., M.META_MOVED16].max() > 64
+
+
 def test_overlapped_step_matches_serial():
     """DecodeEngine.step (confidence on a second stream) leaves exactly the
     state of the five calls issued one after another on one stream."""
