@@ -93,6 +93,14 @@ __device__ __forceinline__ uint32_t half_pair_rows(uint32_t row0w, uint32_t row1
 __device__ __forceinline__ half8_t as_half8(u32x4 v) { return __builtin_bit_cast(half8_t, v); }
 __device__ __forceinline__ half4_t as_half4(u32x2 v) { return __builtin_bit_cast(half4_t, v); }
 
+// V rows are read once per step, each load instruction covering whole 128-byte
+// lines: non-temporal (streaming) loads, measured 3% faster for the kernel.
+// K loads stay cached: in the matrix-core operand layout one instruction reads
+// half of each of 16 rows and the next one the other half, which then hits.
+// Streaming the mass stores, or the K loads, was measured slower.
+template <typename T>
+__device__ __forceinline__ T stream_load(const T* p) { return __builtin_nontemporal_load(p); }
+
 template <int D>
 struct Tile {
   static constexpr int KC = D / 32;  // 16x16x32 chunks along d
@@ -338,11 +346,11 @@ void attn_decode_kernel(AttnArgs a) {
     for (int j = 0; j < 4; ++j) {
       const uint32_t vo = wrap(sv + vinc[j]) * D + (D / 16) * r16;
       if constexpr (CB == 8) {
-        const u32x2 t2 = *reinterpret_cast<const u32x2*>(v8 + vo);
+        const u32x2 t2 = stream_load(reinterpret_cast<const u32x2*>(v8 + vo));
         r.v[j][0] = t2[0];
         r.v[j][1] = t2[1];
       } else {
-        r.v[j][0] = *reinterpret_cast<const uint32_t*>(v8 + vo);
+        r.v[j][0] = stream_load(reinterpret_cast<const uint32_t*>(v8 + vo));
       }
     }
     const bool adv = tnext + kWaves <= last8;
@@ -366,11 +374,11 @@ void attn_decode_kernel(AttnArgs a) {
     for (int j = 0; j < 4; ++j) {
       const uint16_t* vrow = row16(v16, vn, j0 + 4 * kg + j) + (D / 16) * r16;
       if constexpr (CB == 8) {
-        const u32x4 t4 = *reinterpret_cast<const u32x4*>(vrow);
+        const u32x4 t4 = stream_load(reinterpret_cast<const u32x4*>(vrow));
 #pragma unroll
         for (int z = 0; z < 4; ++z) r.v[j][z] = t4[z];
       } else {
-        const u32x2 t2 = *reinterpret_cast<const u32x2*>(vrow);
+        const u32x2 t2 = stream_load(reinterpret_cast<const u32x2*>(vrow));
         r.v[j][0] = t2[0];
         r.v[j][1] = t2[1];
       }
@@ -397,12 +405,14 @@ void attn_decode_kernel(AttnArgs a) {
     piece[z] = *src;
   }
   const bool has8 = nt8 > w;  // this wave has INT8 tiles (uniform per wave)
+  // This wave's INT8 tiles are t_j = w + 4j, j < m8. Each is loaded exactly
+  // once: the loops below are peeled so that no load reaches past the last
+  // tile, and the loads inside a loop body are unconditional, so the load
+  // counter allows partial waits there.
+  const int m8 = (nt8 - w + kWaves - 1) / kWaves;
   Raw8<D> ra8, rb8, rc8;
-  // Loads past the region are clamped to its last tile (rows are read, never
-  // used; an empty region reads its ring's first slot), so no load below is
-  // conditional and the load counter allows partial waits everywhere.
-  load8(ra8);
-  load8(rb8);
+  if (m8 >= 1) load8(ra8);
+  if (m8 >= 2) load8(rb8);
 #pragma unroll
   for (int z = 0; z < 2; ++z) {
     const int e = threadIdx.x + z * kThreads;
@@ -452,11 +462,10 @@ void attn_decode_kernel(AttnArgs a) {
       }
     };
     // three tiles in registers: two loads in flight while one is computed.
-    // This wave's tiles are t_j = w + 4j, j < m8; the loop has one exit and
-    // the remaining 0-2 tiles (already loaded) follow it.
-    const int m8 = (nt8 - w + kWaves - 1) / kWaves;
+    // ra8 / rb8 hold tiles j, j+1 at the top of the loop, which runs while
+    // tiles j+2..j+4 exist; the last 0-4 tiles follow it.
     int j = 0;
-    for (; j + 3 <= m8; j += 3) {
+    for (; j + 5 <= m8; j += 3) {
       const int t = w + kWaves * j;
       load8(rc8);
       tile8(ra8, t);
@@ -465,15 +474,24 @@ void attn_decode_kernel(AttnArgs a) {
       load8(rb8);
       tile8(rc8, t + 2 * kWaves);
     }
-    if (j < m8) tile8(ra8, w + kWaves * j);
-    if (j + 1 < m8) tile8(rb8, w + kWaves * (j + 1));
+    const int rest = m8 - j, t = w + kWaves * j;
+    if (rest >= 3) {
+      load8(rc8);
+      tile8(ra8, t);
+      if (rest == 4) load8(ra8);
+      tile8(rb8, t + kWaves);
+      tile8(rc8, t + 2 * kWaves);
+      if (rest == 4) tile8(ra8, t + 3 * kWaves);
+    } else {
+      tile8(ra8, t);
+      if (rest == 2) tile8(rb8, t + kWaves);
+    }
   }
 
   // ------------------------------------------------------ FP16 region + new
   const bool has16 = nt16 > w;
-  const int last16 = nt16 - 1;  // nt16 >= 1: the new token is always there
   Raw16<D> ra, rb;
-  load16(ra, min(w, last16));
+  if (has16) load16(ra, w);
   if (has8) {
     // V scales of the INT8 part: channel of acc[cb][v] is CB*(4kg+v)+cb
 #pragma unroll
@@ -510,16 +528,24 @@ void attn_decode_kernel(AttnArgs a) {
         acc[cb] = __builtin_amdgcn_mfma_f32_16x16x16f16(as_half4(av), pT, acc[cb], 0, 0, 0);
       }
     };
+    // two tiles in registers; the loop runs while a third tile remains, so
+    // no load reaches past this wave's last tile
     const int m16 = (nt16 - w + kWaves - 1) / kWaves;
     int j = 0;
-    for (; j + 2 <= m16; j += 2) {
+    for (; j + 2 < m16; j += 2) {
       const int t = w + kWaves * j;
       load16(rb, t + kWaves);
       tile16(ra, t);
-      load16(ra, min(t + 2 * kWaves, last16));
+      load16(ra, t + 2 * kWaves);
       tile16(rb, t + kWaves);
     }
-    if (j < m16) tile16(ra, w + kWaves * j);
+    if (j + 1 < m16) {
+      load16(rb, w + kWaves * (j + 1));
+      tile16(ra, w + kWaves * j);
+      tile16(rb, w + kWaves * (j + 1));
+    } else {
+      tile16(ra, w + kWaves * j);
+    }
   }
 
   // -------------------------------------------------------------- merge

@@ -49,7 +49,15 @@ constexpr int kBuckets = 1024;
 constexpr int kRankMax = 64;   // boundary-bucket keys ranked by one wave
 constexpr int kHdr = 16;       // plan header words per (layer, sequence)
 static_assert(2 * kMaxEvictBlocks <= kBuckets, "block keys and flags share the histogram");
-constexpr int kMoveRegs = 8;  // 16-byte pieces per lane per move round
+// 16-byte pieces per lane per move round (d = 128; d = 64 takes 4 fewer) and
+// the move kernel's waves per SIMD: compile-time tuning knobs
+#ifndef CONFK_MOVE_PIECES
+#define CONFK_MOVE_PIECES 16
+#endif
+#ifndef CONFK_MOVE_OCCUPANCY
+#define CONFK_MOVE_OCCUPANCY 4
+#endif
+constexpr int kMovePieces = CONFK_MOVE_PIECES;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -623,12 +631,12 @@ __device__ __forceinline__ unsigned char* uniform_ptr(const void* p) {
 // is needed. Rounds follow plan order: round r+1 reads only slots beyond
 // round r's destinations in the packing direction.
 template <int D>
-__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(4)))
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(CONFK_MOVE_OCCUPANCY)))
 void compact_move_kernel(CompactArgs a) {
   typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
   constexpr int L8 = D == 128 ? 3 : 2, L16 = L8 + 1;  // log2 of 16-byte pieces per row
   constexpr int P16 = D / 8;
-  constexpr int NR = D == 128 ? 2 * kMoveRegs : 2 * kMoveRegs - 4;  // pieces per lane per round
+  constexpr int NR = D == 128 ? kMovePieces : kMovePieces - 4;  // pieces per lane per round
   const CacheView& c = a.c;
   const int lane = threadIdx.x & 63;
   const int kv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // 0: K, 1: V
@@ -648,16 +656,19 @@ void compact_move_kernel(CompactArgs a) {
   const i32x4 hA = reinterpret_cast<const i32x4*>(hdr)[0];  // MOV8, LEFT8, E8, JLO8
   const i32x4 hB = reinterpret_cast<const i32x4*>(hdr)[1];  // MOV16, LEFT16, E16, JLO16
   const i32x4 hC = reinterpret_cast<const i32x4*>(hdr)[2];  // BASE8, BASE16, APPEND
-  constexpr int NW16 = D == 128 ? 1 : 2;  // FP16 source window: 64 * NW16 movers
-  int sv8[4], sv16[NW16] = {};
+  // source windows (64 * NW movers) cover at least one round; the INT8 one
+  // is read speculatively with the header and covers 256 movers or more
+  constexpr int NW8 = ((NR * 64 >> L8) + 63) / 64 > 4 ? ((NR * 64 >> L8) + 63) / 64 : 4;
+  constexpr int NW16 = ((NR * 64 >> L16) + 63) / 64;
+  int sv8[NW8], sv16[NW16] = {};
 #pragma unroll
-  for (int q = 0; q < 4; ++q) sv8[q] = lane + 64 * q < cap ? src8[lane + 64 * q] : 0;
+  for (int q = 0; q < NW8; ++q) sv8[q] = lane + 64 * q < cap ? src8[lane + 64 * q] : 0;
   u32x4 nrow = {0u, 0u, 0u, 0u};
   if (lane < P16) nrow = *reinterpret_cast<const u32x4*>((kv ? a.v_new : a.k_new) + ((size_t)lb * H + hh) * D + lane * 8);
   const int append = hC[2];
   if (append < 0) return;  // the plan flagged a capacity error
 
-  ring_rounds<D, L8, 4, NR>(uniform_ptr((kv ? c.v8 : c.k8) + hrow * cap * D), cap, hA[0], hA[1], hA[2], hA[3],
+  ring_rounds<D, L8, NW8, NR>(uniform_ptr((kv ? c.v8 : c.k8) + hrow * cap * D), cap, hA[0], hA[1], hA[2], hA[3],
                             hC[0], src8, sv8, true);
   unsigned char* r16 = uniform_ptr((kv ? c.v16 : c.k16) + hrow * cap16 * D);
   ring_rounds<D, L16, NW16, NR>(r16, cap16, hB[0], hB[1], hB[2], hB[3], hC[1], src16, sv16, false);
@@ -697,10 +708,11 @@ hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  const dim3 mgrid(blocks, a.c.hkv), mblock(128);
   if (a.c.d == 128) {
-    hipLaunchKernelGGL(compact_move_kernel<128>, dim3(blocks, a.c.hkv), dim3(128), 0, s, a);
+    hipLaunchKernelGGL(compact_move_kernel<128>, mgrid, mblock, 0, s, a);
   } else {
-    hipLaunchKernelGGL(compact_move_kernel<64>, dim3(blocks, a.c.hkv), dim3(128), 0, s, a);
+    hipLaunchKernelGGL(compact_move_kernel<64>, mgrid, mblock, 0, s, a);
   }
   return hipGetLastError();
 }
