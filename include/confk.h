@@ -99,8 +99,9 @@ typedef struct confk_policy {
 
 /*
  * Cache of L layers x B sequences with Hkv kv heads of dimension d.
- * Per (layer l, sequence b) the retained tokens are ordered by position; the
- * oldest meta[N8] are INT8 and the rest FP16. Logical token i < n8 lives in
+ * Per (layer l, sequence b) the first meta[N8] logical tokens are INT8 (the
+ * oldest; in position order until token eviction fills holes, see
+ * confk_compact) and the rest FP16, in position order. Logical token i < n8 lives in
  * INT8 ring slot (base8 + i) % cap, logical token i >= n8 in FP16 ring slot
  * (base16 + i - n8) % cap16. ema and pos are dense in logical order.
  * Layouts (row-major):
@@ -206,15 +207,18 @@ int confk_ema_rank(const confk_cache* cache, int32_t layer0, int32_t nlayers, co
                    const confk_policy* pol, int32_t t, float* score, void* stream);
 
 /*
- * confk_compact -- budget eviction, stable compaction and append.
+ * confk_compact -- budget eviction, compaction and append.
  * Summary "Methodik" (Token-Ranking und Eviktion; zusammenhaengende
  * Komprimierung without indirection tables); review Algorithm 1 steps 5-11
  * and 13. Per (layer, sequence) with n tokens and budget N: if n > N, the
  * k = n - N tokens with the smallest (score, position) among all but the
- * newest `protect` tokens are evicted; survivors keep their order, the new
- * token (slot n metadata from confk_ema_rank, K/V from k_new/v_new) is
- * appended as FP16. Rows move only as far as needed: each region (INT8,
- * FP16) is packed toward whichever end moves fewer rows.
+ * newest `protect` tokens are evicted and the survivors are packed densely;
+ * the new token (slot n metadata from confk_ema_rank, K/V from k_new/v_new)
+ * is appended as FP16. The FP16 part keeps position order, packed toward
+ * whichever end moves fewer rows. The INT8 part: with token eviction, the
+ * surviving INT8 tokens at or beyond its new length fill the holes below it,
+ * in slot order (the fewest moves; the INT8 part is then no longer in
+ * position order); with block eviction it is packed like the FP16 part.
  *   budget       int32, entry for (l, b) at budget[l * budget_layer_stride + b]
  *                (stride 0: one budget per sequence; stride B: per layer)
  *   score        fp32 [nlayers][B][cap] from confk_ema_rank
@@ -226,8 +230,9 @@ int confk_ema_rank(const confk_cache* cache, int32_t layer0, int32_t nlayers, co
  * With pol->block = B > 0, whole blocks of B tokens leave (see confk_policy).
  * Sets CONFK_STATUS_CAPACITY (and skips the append) if a sequence has no
  * free slot. Errors: INVALID_ARG, BUDGET (protect > n_low or > n_high,
- * capacity below n_low + 2, FP16 ring below window + 1), UNSUPPORTED (more
- * than 512 blocks per sequence), WORKSPACE.
+ * capacity below n_low + 2, FP16 ring below window + 1, protect > window
+ * with token eviction), UNSUPPORTED (more than 512 blocks per sequence;
+ * block eviction with d other than 64 or 128), WORKSPACE.
  */
 int confk_compact(const confk_cache* cache, int32_t layer0, int32_t nlayers, const int32_t* budget,
                   int32_t budget_layer_stride, const float* score, const confk_policy* pol,

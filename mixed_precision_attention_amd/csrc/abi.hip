@@ -163,7 +163,10 @@ int confk_compact(const confk_cache* cache, int32_t layer0, int32_t nlayers, con
   if (pol->protect > pol->n_high || pol->protect > pol->n_low) return CONFK_ERR_BUDGET;
   if (pol->n_low + 1 > cache->cap - 1 || pol->n_high + 1 > cache->cap - 1) return CONFK_ERR_BUDGET;
   if (pol->window + 1 > cache->cap16) return CONFK_ERR_BUDGET;
+  // token eviction reorders the INT8 part: the newest P tokens must be FP16
+  if (pol->block == 0 && pol->protect > pol->window) return CONFK_ERR_BUDGET;
   if (pol->block > 0 && cache->cap / pol->block > kMaxEvictBlocks) return CONFK_ERR_UNSUPPORTED;
+  if (pol->block > 0 && cache->d != 64 && cache->d != 128) return CONFK_ERR_UNSUPPORTED;
   const size_t need = compact_ws_bytes(nlayers, cache->batch, cache->cap);
   if (!ws || ws_bytes < need) return CONFK_ERR_WORKSPACE;
   CompactArgs a{};

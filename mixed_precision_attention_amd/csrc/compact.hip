@@ -1,4 +1,4 @@
-// Budget eviction, stable compaction and append of the new token.
+// Budget eviction, compaction and append of the new token.
 //
 // CONF-KV summary, "Methodik: CONF-KV": tokens are ranked by the composite
 // score, the newest P are never evicted (Token-Ranking und Eviktion), and
@@ -7,33 +7,34 @@
 // (Algorithm 1): if |C_l| > N evict the lowest-ranked unprotected tokens and
 // compact the survivors; step 13 appends the new K/V in FP16.
 //
-// Two kernels.
-//
-// Plan (one workgroup per (layer, sequence)); thread t owns a contiguous run
-// of logical indices:
-//  1. k = n - N tokens leave, chosen among the n - P oldest: exactly the k
-//     smallest 64-bit keys (order-preserving image of the fp32 score, logical
-//     index); the index is position order, so equal scores evict the older
+// Plan kernel, one workgroup per (layer, sequence); thread t owns a contiguous
+// run of logical indices:
+//  1. k = n - N tokens leave, chosen among all but the newest P (the last P
+//     logical entries): exactly the k smallest 64-bit keys (order-preserving
+//     image of the fp32 score, position), so equal scores evict the older
 //     token first. The k-th key is found from a 1024-bucket histogram of the
 //     monotone bucket floor(score * 1024) (clamped), then by ranking the few
-//     keys of the boundary bucket; a radix select on the score bits covers
-//     crowded buckets and long caches.
+//     keys of the boundary bucket; radix selects on the score bits and then
+//     on the tied positions cover crowded buckets and long caches.
 //     Block eviction (B > 0) takes kb = min(full blocks, ceil(k / B)) whole
 //     blocks of B consecutive candidates instead, the blocks with the
 //     smallest (largest key in the block, block index), so k = kb * B.
 //  2. Ballot bit-plane scans give each survivor its new logical index and
 //     each region (INT8 ring, FP16 ring) its eviction count and first / last
-//     hole, behind one barrier.
-//  3. EMA / position metadata are rewritten densely in place (every thread
-//     read its run before the first barrier).
-//  4. Each region is packed toward the end that moves fewer rows: keep the
-//     base and shift the survivors after the first hole down, or advance the
-//     base and shift the survivors before the last hole up. The movers'
-//     sources go to a plan in the workspace.
-// Move (one wave per (layer, sequence, kv head, K|V) ring): the planned rows
-// move in rounds (read all rows of a round, wait, write them) in an order that
-// never overwrites an unread source; then the new token's row is written to
-// the FP16 ring.
+//     hole.
+//  3. Token eviction does everything in this kernel: the surviving INT8
+//     tokens at or beyond the new INT8 length fill the holes below it (slot
+//     order; sources and destinations are disjoint, so the rows move in one
+//     pass), the FP16 part is packed toward the end that moves fewer rows
+//     (keep the base and shift the survivors after the first hole down, or
+//     advance the base and shift the survivors before the last hole up), and
+//     the new token's rows are appended. EMA / position metadata are
+//     rewritten in place after a barrier that follows every read.
+//  4. Block eviction packs both regions that way and leaves the moves to:
+// Move kernel (one wave per (layer, sequence, kv head, K|V) ring): the
+// planned rows move in rounds (read all rows of a round, wait, write them) in
+// an order that never overwrites an unread source; then the new token's row
+// is written to the FP16 ring.
 #include <type_traits>
 
 #include "confk_internal.h"
@@ -102,6 +103,7 @@ __device__ __forceinline__ int wave_prefix16(int x, int& total) {
 struct Shared {
   uint32_t hist[kBuckets];
   int wsum[3][kWaves];  // per-wave keeps, e8, e16
+  int wfill[2][kWaves];  // per-wave INT8 holes and tails
   int wfirst[2][kWaves], wlast[2][kWaves];
   uint64_t rank_keys[kRankMax];
   int rank_n;
@@ -109,6 +111,18 @@ struct Shared {
   uint64_t kth;
   uint32_t sel_digit, sel_before;
 };
+
+// Tails' metadata and the fill lists of register-held runs (fewer than
+// n8 / 2 <= kFillMax holes when n < kRegKeys * kThreads).
+constexpr int kFillMax = kRegKeys * kThreads / 2;
+struct FillShared {
+  float e[kFillMax];
+  int32_t p[kFillMax], i[kFillMax], h[kFillMax];
+};
+
+// Workspace words per (layer, sequence) for long caches: staged metadata of
+// the survivors (EMA, position, old index) and the fill lists.
+__host__ __device__ constexpr size_t stage_words(int cap) { return 5 * (size_t)cap + 8; }
 
 struct Region {
   int rs, m, e, first_ev, last_ev;
@@ -128,25 +142,27 @@ __device__ __forceinline__ void plan_region(Region& r) {
   r.jlo = r.left ? (r.first_ev - r.rs) : 0;
 }
 
-// Radix select of the kk-th smallest 32-bit key among the candidates; leaves
-// in kk how many keys equal to the result are selected.
-template <bool REG, typename KeyAt>
-__device__ uint32_t radix_select(int& kk, int cnt, int lo, int ncand, const uint32_t* kreg,
-                                 KeyAt key_at, Shared& sh) {
+// Radix select of the kk-th smallest value val(j) among this workgroup's
+// entries with part(j) (j < cnt of each thread's run); leaves in kk how many
+// entries equal to the result are selected.
+template <bool REG, typename Part, typename Val>
+__device__ uint32_t radix_select(int& kk, int cnt, Part part, Val val, Shared& sh) {
   uint32_t prefix = 0, mask = 0;
   for (int shift = 24; shift >= 0; shift -= 8) {
     if (threadIdx.x < 256) sh.hist[threadIdx.x] = 0;
     __syncthreads();
+    auto count = [&](int j) {
+      if (part(j)) {
+        const uint32_t x = val(j);
+        if ((x & mask) == prefix) atomicAdd(&sh.hist[(x >> shift) & 255u], 1u);
+      }
+    };
     if constexpr (REG) {
 #pragma unroll
       for (int j = 0; j < kRegKeys; ++j)
-        if (j < cnt && lo + j < ncand && (kreg[j] & mask) == prefix)
-          atomicAdd(&sh.hist[(kreg[j] >> shift) & 255u], 1u);
+        if (j < cnt) count(j);
     } else {
-      for (int j = 0; j < cnt; ++j) {
-        const uint32_t key = key_at(j);
-        if (lo + j < ncand && (key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
-      }
+      for (int j = 0; j < cnt; ++j) count(j);
     }
     __syncthreads();
     if (threadIdx.x < 64) {
@@ -197,6 +213,20 @@ __global__ __launch_bounds__(kThreads) void compact_plan_kernel(CompactArgs a) {
   int32_t* pos = c.pos + (size_t)lbc * cap;
   const float* score = a.score + (size_t)lb * cap;
   __shared__ Shared sh;
+  __shared__ std::conditional_t<REG && !BLOCK, FillShared, char> fsh;
+  // the new token's K and V rows into the FP16 rings at `slot`
+  auto append_rows = [&](int slot) {
+    const int H = c.hkv, d = c.d, p16 = d >> 3, rp16 = 2 * H * p16;
+    const size_t ring16 = (size_t)c.cap16 * 2 * d;
+    unsigned char* k16b = reinterpret_cast<unsigned char*>(c.k16) + (size_t)lbc * H * ring16;
+    unsigned char* v16b = reinterpret_cast<unsigned char*>(c.v16) + (size_t)lbc * H * ring16;
+    for (int q = threadIdx.x; q < rp16; q += kThreads) {
+      const int ring = q / p16, pc = q - ring * p16, h = ring >> 1;
+      const uint16_t* src = ((ring & 1) ? a.v_new : a.k_new) + ((size_t)lb * H + h) * d + pc * 8;
+      unsigned char* dst = ((ring & 1) ? v16b : k16b) + (size_t)h * ring16 + (size_t)slot * 2 * d + pc * 16;
+      *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+    }
+  };
 
   const int nn = n + 1;  // tokens incl. the new one
   const int f = n - n8;
@@ -224,10 +254,14 @@ __global__ __launch_bounds__(kThreads) void compact_plan_kernel(CompactArgs a) {
   }
 
   if (k == 0) {  // nothing leaves: the new token (metadata slot n) is appended
+    int slot = base16 + f;
+    slot = slot >= c.cap16 ? slot - c.cap16 : slot;
+    if constexpr (!BLOCK) append_rows(slot);
     if (threadIdx.x == 0) {
-      hdr[H_MOV8] = hdr[H_MOV16] = 0;
-      int slot = base16 + f;
-      hdr[H_APPEND] = slot >= c.cap16 ? slot - c.cap16 : slot;
+      if constexpr (BLOCK) {
+        hdr[H_MOV8] = hdr[H_MOV16] = 0;
+        hdr[H_APPEND] = slot;
+      }
       meta[CONFK_META_N] = nn;
       meta[CONFK_META_EVICTED] = 0;
       meta[CONFK_META_MOVED] = 0;
@@ -266,9 +300,18 @@ __global__ __launch_bounds__(kThreads) void compact_plan_kernel(CompactArgs a) {
       return i < ncand ? ord_bits(score[i]) : 0xFFFFFFFFu;
     }
   };
+  // position of logical index lo + j (the non-register form reads memory,
+  // valid until the metadata is rewritten in place)
+  auto pos_at = [&](int j) -> uint32_t {
+    if constexpr (REG) {
+      return (uint32_t)preg[j];
+    } else {
+      return (uint32_t)pos[lo + j];
+    }
+  };
 
   // ---------------------------------------------------------- 1. select
-  // T64: the k-th smallest (key, index); every candidate at or below leaves.
+  // T64: the k-th smallest (key, position); every candidate at or below leaves.
   // Block eviction instead marks the kb blocks with the smallest (largest
   // key in the block, block index) in bsel.
   uint64_t T64 = 0;
@@ -354,7 +397,7 @@ __global__ __launch_bounds__(kThreads) void compact_plan_kernel(CompactArgs a) {
     if (!sh.sel_crowded) {
 #pragma unroll
       for (int j = 0; j < kRegKeys; ++j)
-        if (bk[j] == bsel) sh.rank_keys[atomicAdd(&sh.rank_n, 1)] = ((uint64_t)kreg[j] << 32) | (uint32_t)(lo + j);
+        if (bk[j] == bsel) sh.rank_keys[atomicAdd(&sh.rank_n, 1)] = ((uint64_t)kreg[j] << 32) | (uint32_t)preg[j];
       __syncthreads();
       if (threadIdx.x < 64) {
         // rank the boundary bucket's keys; the (k - below)-th smallest is T64
@@ -374,43 +417,21 @@ __global__ __launch_bounds__(kThreads) void compact_plan_kernel(CompactArgs a) {
     }
   }
   if (use_radix) {
+    // the k-th smallest key T, then the kk-th smallest position among the
+    // candidates whose key is T (positions are unique)
     int kk = k;
-    const uint32_t T = radix_select<REG>(kk, cnt, lo, ncand, kreg, key_at, sh);
-    // the kk-th smallest index among the keys equal to T: runs are contiguous
-    // in index order, so a block scan of tie counts locates it
-    int ties = 0;
-    if constexpr (REG) {
-#pragma unroll
-      for (int j = 0; j < kRegKeys; ++j) ties += (j < cnt && lo + j < ncand && kreg[j] == T) ? 1 : 0;
-    } else {
-      for (int j = 0; j < cnt; ++j) ties += (lo + j < ncand && key_at(j) == T) ? 1 : 0;
-    }
-    int incl = ties;
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += y;
-    }
-    if (lane == 63) sh.wsum[0][w] = incl;
-    __syncthreads();
-    int before = incl - ties;
-    for (int q = 0; q < w; ++q) before += sh.wsum[0][q];
-    if (ties > 0 && before < kk && kk <= before + ties) {
-      int run = before;
-      for (int j = 0; j < cnt; ++j) {
-        if (lo + j < ncand && key_at(j) == T) {
-          if (++run == kk) sh.kth = ((uint64_t)T << 32) | (uint32_t)(lo + j);
-        }
-      }
-    }
-    __syncthreads();
-    T64 = sh.kth;
+    auto cand = [&](int j) { return lo + j < ncand; };
+    const uint32_t T = radix_select<REG>(kk, cnt, cand, key_at, sh);
+    auto tied = [&](int j) { return lo + j < ncand && key_at(j) == T; };
+    const uint32_t Tp = radix_select<REG>(kk, cnt, tied, pos_at, sh);
+    T64 = ((uint64_t)T << 32) | Tp;
   }
 
   // ------------------------------------------- 2. flags, scans, regions
   auto leaves = [&](int j) -> bool {
     const int i = lo + j;
     if constexpr (BLOCK) return i < nb * B && bsel[i / B] != 0u;
-    return i < ncand && ((((uint64_t)key_at(j)) << 32) | (uint32_t)i) <= T64;
+    return i < ncand && ((((uint64_t)key_at(j)) << 32) | pos_at(j)) <= T64;
   };
   uint32_t evm = 0;  // bit j: index lo + j leaves (register path)
   int keeps = 0, e8 = 0, e16 = 0;
@@ -494,79 +515,305 @@ __global__ __launch_bounds__(kThreads) void compact_plan_kernel(CompactArgs a) {
   plan_region(r16);
   const int js16 = n8 - r8.e;  // new logical index of the first FP16 survivor
 
-  // ------------------------------------- 3. metadata and 4. move plan
-  // plan entries are stored in move order: ascending new index when packing
-  // toward the base, descending otherwise
-  auto emit = [&](int i, int jn, float ev_, int pv_) {
-    ema[jn] = ev_;
-    pos[jn] = pv_;
-    if (i < n8) {
-      const int m = jn - r8.jlo;
-      if (m >= 0 && m < r8.movers) src8[r8.left ? m : r8.movers - 1 - m] = i;
-    } else if (i < n) {
-      const int m = jn - js16 - r16.jlo;  // region-local new index minus the first mover's
-      if (m >= 0 && m < r16.movers) src16[r16.left ? m : r16.movers - 1 - m] = i - n8;
+  if constexpr (BLOCK) {
+    // ------------------------ block eviction: stable packing, moves planned
+
+    // ------------------------------------- 3. metadata and 4. move plan
+    // plan entries are stored in move order: ascending new index when packing
+    // toward the base, descending otherwise
+    auto emit = [&](int i, int jn, float ev_, int pv_) {
+      ema[jn] = ev_;
+      pos[jn] = pv_;
+      if (i < n8) {
+        const int m = jn - r8.jlo;
+        if (m >= 0 && m < r8.movers) src8[r8.left ? m : r8.movers - 1 - m] = i;
+      } else if (i < n) {
+        const int m = jn - js16 - r16.jlo;  // region-local new index minus the first mover's
+        if (m >= 0 && m < r16.movers) src16[r16.left ? m : r16.movers - 1 - m] = i - n8;
+      }
+    };
+    if constexpr (REG) {
+      int jn = keep_base;
+  #pragma unroll
+      for (int j = 0; j < kRegKeys; ++j)
+        if (j < cnt && !((evm >> j) & 1u)) emit(lo + j, jn++, ereg[j], preg[j]);
+    } else {
+      // long caches: survivors' metadata goes through a staging area; every
+      // read of a run precedes the barrier, every in-place write follows it
+      float* se = reinterpret_cast<float*>(a.stage + (size_t)lb * stage_words(cap));
+      int32_t* sp = a.stage + (size_t)lb * stage_words(cap) + cap;
+      int jn = keep_base;
+      for (int j = 0; j < cnt; ++j) {
+        if (!leaves(j)) {
+          se[jn] = ema[lo + j];
+          sp[jn] = pos[lo + j];
+          ++jn;
+        }
+      }
+      __syncthreads();
+      jn = keep_base;
+      for (int j = 0; j < cnt; ++j) {
+        if (!leaves(j)) {
+          emit(lo + j, jn, se[jn], sp[jn]);
+          ++jn;
+        }
+      }
     }
-  };
-  if constexpr (REG) {
-    int jn = keep_base;
-#pragma unroll
-    for (int j = 0; j < kRegKeys; ++j)
-      if (j < cnt && !((evm >> j) & 1u)) emit(lo + j, jn++, ereg[j], preg[j]);
+
+    // ------------------------------------------------------------ header
+    if (threadIdx.x == 0) {
+      int b8 = base8, b16 = base16;
+      if (!r8.left) {
+        b8 += r8.e;
+        if (b8 >= cap) b8 -= cap;
+      }
+      if (!r16.left) {
+        b16 += r16.e;
+        if (b16 >= c.cap16) b16 -= c.cap16;
+      }
+      hdr[H_MOV8] = r8.movers;
+      hdr[H_LEFT8] = r8.left;
+      hdr[H_E8] = r8.e;
+      hdr[H_JLO8] = r8.jlo;
+      hdr[H_MOV16] = r16.movers;
+      hdr[H_LEFT16] = r16.left;
+      hdr[H_E16] = r16.e;
+      hdr[H_JLO16] = r16.jlo;
+      hdr[H_BASE8] = base8;
+      hdr[H_BASE16] = base16;
+      const int slot = b16 + (f - r16.e);
+      hdr[H_APPEND] = slot >= c.cap16 ? slot - c.cap16 : slot;
+      meta[CONFK_META_N] = nkeep;
+      meta[CONFK_META_N8] = n8 - r8.e;
+      meta[CONFK_META_BASE8] = b8;
+      meta[CONFK_META_BASE16] = b16;
+      meta[CONFK_META_EVICTED] = k;
+      meta[CONFK_META_MOVED] = r8.movers;
+      meta[CONFK_META_MOVED16] = r16.movers;
+      if (a.evicted_out) a.evicted_out[lb] = k;
+    }
   } else {
-    // long caches: survivors' metadata goes through a staging area; every
-    // read of a run precedes the barrier, every in-place write follows it
-    float* se = reinterpret_cast<float*>(a.stage + (size_t)lb * 2 * cap);
-    int32_t* sp = a.stage + (size_t)lb * 2 * cap + cap;
-    int jn = keep_base;
-    for (int j = 0; j < cnt; ++j) {
-      if (!leaves(j)) {
-        se[jn] = ema[lo + j];
-        sp[jn] = pos[lo + j];
-        ++jn;
+    // ------------- token eviction: INT8 hole filling, FP16 packing, append
+    // Holes are the evicted INT8 entries below the new INT8 length m8, tails
+    // the surviving INT8 entries at or beyond it; the r-th tail (slot order)
+    // moves to the r-th hole. Tails and holes are disjoint slots, so those
+    // moves need no ordering. The FP16 part is packed stably as planned above.
+    const int m8 = js16;
+    int nh = 0, nt = 0;
+    auto hole_tail = [&](int j, bool lv) {
+      const int i = lo + j;
+      if (i < n8) {
+        nh += (lv && i < m8) ? 1 : 0;
+        nt += (!lv && i >= m8) ? 1 : 0;
+      }
+    };
+    if constexpr (REG) {
+#pragma unroll
+      for (int j = 0; j < kRegKeys; ++j)
+        if (j < cnt) hole_tail(j, (evm >> j) & 1u);
+    } else {
+      for (int j = 0; j < cnt; ++j) hole_tail(j, leaves(j));
+    }
+    int hbase, tbase, nholes = 0;  // this thread's first hole and tail rank; holes in all
+    {
+      int th, tt;
+      if constexpr (REG) {
+        hbase = wave_prefix16(nh, th);
+        tbase = wave_prefix16(nt, tt);
+      } else {
+        int ih = nh, it = nt;
+        for (int o = 1; o < 64; o <<= 1) {
+          const int yh = __shfl_up(ih, o, 64), yt = __shfl_up(it, o, 64);
+          if (lane >= o) {
+            ih += yh;
+            it += yt;
+          }
+        }
+        hbase = ih - nh;
+        tbase = it - nt;
+        th = __shfl(ih, 63, 64);
+        tt = __shfl(it, 63, 64);
+      }
+      if (lane == 0) {
+        sh.wfill[0][w] = th;
+        sh.wfill[1][w] = tt;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < kWaves; ++q) {
+        hbase += q < w ? sh.wfill[0][q] : 0;
+        tbase += q < w ? sh.wfill[1][q] : 0;
+        nholes += sh.wfill[0][q];
+      }
+    }
+    // fill lists and the tails' metadata: LDS for register-held runs, the
+    // workspace otherwise (where the FP16 survivors' metadata is staged too:
+    // every read of the metadata precedes the barrier, every write follows)
+    int32_t* st = a.stage + (size_t)lb * stage_words(cap);
+    const int half = (cap + 1) / 2;
+    float* tse;
+    int32_t *tsp, *tsi, *hd;
+    if constexpr (REG) {
+      tse = fsh.e;
+      tsp = fsh.p;
+      tsi = fsh.i;
+      hd = fsh.h;
+    } else {
+      tse = reinterpret_cast<float*>(st + 3 * cap);
+      tsp = st + 3 * cap + half;
+      tsi = st + 3 * cap + 2 * half;
+      hd = st + 3 * cap + 3 * half;
+    }
+    auto emit16 = [&](int i, int jn, float ev_, int pv_) {  // FP16 survivor or the new token
+      ema[jn] = ev_;
+      pos[jn] = pv_;
+      if (i < n) {
+        const int m = jn - m8 - r16.jlo;
+        if (m >= 0 && m < r16.movers) src16[r16.left ? m : r16.movers - 1 - m] = i - n8;
+      }
+    };
+    if constexpr (REG) {
+      int h = hbase, t = tbase, jn = keep_base;
+#pragma unroll
+      for (int j = 0; j < kRegKeys; ++j) {
+        if (j < cnt) {
+          const int i = lo + j;
+          if (!((evm >> j) & 1u)) {
+            if (i >= n8) {
+              emit16(i, jn, ereg[j], preg[j]);
+            } else if (i >= m8) {
+              tse[t] = ereg[j];
+              tsp[t] = preg[j];
+              tsi[t] = i;
+              ++t;
+            }
+            ++jn;
+          } else if (i < m8) {
+            hd[h++] = i;
+          }
+        }
+      }
+    } else {
+      float* se = reinterpret_cast<float*>(st);
+      int32_t* sp = st + cap;
+      int32_t* si = st + 2 * cap;
+      int h = hbase, t = tbase, jn = keep_base;
+      for (int j = 0; j < cnt; ++j) {
+        const int i = lo + j;
+        if (!leaves(j)) {
+          if (i >= n8) {
+            se[jn] = ema[i];
+            sp[jn] = pos[i];
+            si[jn] = i;
+          } else if (i >= m8) {
+            tse[t] = ema[i];
+            tsp[t] = pos[i];
+            tsi[t] = i;
+            ++t;
+          }
+          ++jn;
+        } else if (i < m8) {
+          hd[h++] = i;
+        }
       }
     }
     __syncthreads();
-    jn = keep_base;
-    for (int j = 0; j < cnt; ++j) {
-      if (!leaves(j)) {
-        emit(lo + j, jn, se[jn], sp[jn]);
-        ++jn;
-      }
+    // each hole takes its tail's metadata
+    for (int r = hbase; r < hbase + nh; ++r) {
+      const int i = hd[r];
+      ema[i] = tse[r];
+      pos[i] = tsp[r];
     }
-  }
+    if constexpr (!REG) {
+      float* se = reinterpret_cast<float*>(st);
+      int32_t* sp = st + cap;
+      int32_t* si = st + 2 * cap;
+      for (int jn = max(keep_base, m8); jn < keep_base + keeps; ++jn) emit16(si[jn], jn, se[jn], sp[jn]);
+    }
+    __syncthreads();  // fill lists and FP16 movers are complete
 
-  // ------------------------------------------------------------ header
-  if (threadIdx.x == 0) {
-    int b8 = base8, b16 = base16;
-    if (!r8.left) {
-      b8 += r8.e;
-      if (b8 >= cap) b8 -= cap;
+    // ---- the moves: all 512 threads, 16-byte pieces, consecutive threads
+    // on consecutive pieces of a row
+    const int H = c.hkv, d = c.d;
+    const int p8 = d >> 4, rp8 = 2 * H * p8;   // pieces per INT8 row; per moved token
+    const int p16 = d >> 3, rp16 = 2 * H * p16;  // same for FP16 rows
+    const size_t ring8 = (size_t)cap * d, ring16 = (size_t)c.cap16 * 2 * d;  // bytes per ring
+    unsigned char* k8b = reinterpret_cast<unsigned char*>(c.k8) + (size_t)lbc * H * ring8;
+    unsigned char* v8b = reinterpret_cast<unsigned char*>(c.v8) + (size_t)lbc * H * ring8;
+    unsigned char* k16b = reinterpret_cast<unsigned char*>(c.k16) + (size_t)lbc * H * ring16;
+    unsigned char* v16b = reinterpret_cast<unsigned char*>(c.v16) + (size_t)lbc * H * ring16;
+    const int tot8 = nholes * rp8;
+    for (int q0 = threadIdx.x; q0 < tot8; q0 += 4 * kThreads) {
+      u32x4 v[4];
+      unsigned char* dp[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int q = q0 + u * kThreads;
+        dp[u] = nullptr;
+        if (q < tot8) {
+          const int r = q / rp8, rem = q - r * rp8;
+          const int ring = rem / p8, pc = rem - ring * p8;
+          unsigned char* rb = ((ring & 1) ? v8b : k8b) + (size_t)(ring >> 1) * ring8 + pc * 16;
+          int ss = base8 + tsi[r], ds = base8 + hd[r];
+          ss = ss >= cap ? ss - cap : ss;
+          ds = ds >= cap ? ds - cap : ds;
+          v[u] = *reinterpret_cast<const u32x4*>(rb + (size_t)ss * d);
+          dp[u] = rb + (size_t)ds * d;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (dp[u]) *reinterpret_cast<u32x4*>(dp[u]) = v[u];
     }
+    // FP16 packing in plan order: a round reads all of its rows, waits, and
+    // writes them; round r+1 reads only slots beyond round r's destinations
+    const int mv16 = r16.movers, C16 = c.cap16;
+    const int rows16 = max(1, 4 * kThreads / rp16);
+    for (int m0 = 0; m0 < mv16; m0 += rows16) {
+      const int tot = min(rows16, mv16 - m0) * rp16;
+      u32x4 v[4];
+      unsigned char* dp[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int q = threadIdx.x + u * kThreads;
+        dp[u] = nullptr;
+        if (q < tot) {
+          const int rr = m0 + q / rp16, rem = q % rp16;
+          const int ring = rem / p16, pc = rem - ring * p16;
+          unsigned char* rb = ((ring & 1) ? v16b : k16b) + (size_t)(ring >> 1) * ring16 + pc * 16;
+          const int j = r16.jlo + (r16.left ? rr : mv16 - 1 - rr);
+          int ss = base16 + src16[rr], ds = base16 + (r16.left ? j : j + r16.e);
+          ss = ss >= C16 ? ss - C16 : ss;
+          ds = ds >= C16 ? ds - C16 : ds;
+          v[u] = *reinterpret_cast<const u32x4*>(rb + (size_t)ss * 2 * d);
+          dp[u] = rb + (size_t)ds * 2 * d;
+        }
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (dp[u]) *reinterpret_cast<u32x4*>(dp[u]) = v[u];
+    }
+    int b16 = base16;
     if (!r16.left) {
       b16 += r16.e;
-      if (b16 >= c.cap16) b16 -= c.cap16;
+      if (b16 >= C16) b16 -= C16;
     }
-    hdr[H_MOV8] = r8.movers;
-    hdr[H_LEFT8] = r8.left;
-    hdr[H_E8] = r8.e;
-    hdr[H_JLO8] = r8.jlo;
-    hdr[H_MOV16] = r16.movers;
-    hdr[H_LEFT16] = r16.left;
-    hdr[H_E16] = r16.e;
-    hdr[H_JLO16] = r16.jlo;
-    hdr[H_BASE8] = base8;
-    hdr[H_BASE16] = base16;
-    const int slot = b16 + (f - r16.e);
-    hdr[H_APPEND] = slot >= c.cap16 ? slot - c.cap16 : slot;
-    meta[CONFK_META_N] = nkeep;
-    meta[CONFK_META_N8] = n8 - r8.e;
-    meta[CONFK_META_BASE8] = b8;
-    meta[CONFK_META_BASE16] = b16;
-    meta[CONFK_META_EVICTED] = k;
-    meta[CONFK_META_MOVED] = r8.movers;
-    meta[CONFK_META_MOVED16] = r16.movers;
-    if (a.evicted_out) a.evicted_out[lb] = k;
+    int slot = b16 + (f - r16.e);
+    slot = slot >= C16 ? slot - C16 : slot;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // every FP16 source has been read before the append slot is written
+    append_rows(slot);
+    if (threadIdx.x == 0) {
+      meta[CONFK_META_N] = nkeep;
+      meta[CONFK_META_N8] = m8;
+      meta[CONFK_META_BASE16] = b16;
+      meta[CONFK_META_EVICTED] = k;
+      meta[CONFK_META_MOVED] = nholes;
+      meta[CONFK_META_MOVED16] = mv16;
+      if (a.evicted_out) a.evicted_out[lb] = k;
+    }
   }
 }
 
@@ -684,7 +931,7 @@ size_t compact_ws_bytes(int nlayers, int batch, int cap) {
   // plan: header + two source lists per (layer, sequence); staging of the
   // long-cache path: EMA and positions per (layer, sequence)
   const size_t plan = (size_t)nlayers * batch * (kHdr + 2 * (size_t)cap) * 4;
-  const size_t stage = cap > kRegKeys * kThreads ? (size_t)nlayers * batch * 2 * (size_t)cap * 4 : 0;
+  const size_t stage = cap > kRegKeys * kThreads ? (size_t)nlayers * batch * stage_words(cap) * 4 : 0;
   return plan + stage;
 }
 
@@ -695,17 +942,17 @@ size_t compact_plan_bytes(int nlayers, int batch, int cap) {
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
   const int blocks = a.nl * a.c.B;
   const bool reg = a.c.cap <= kRegKeys * kThreads;
-  if (a.block > 0) {
-    if (reg)
-      hipLaunchKernelGGL((compact_plan_kernel<true, true>), dim3(blocks), dim3(kThreads), 0, s, a);
-    else
-      hipLaunchKernelGGL((compact_plan_kernel<false, true>), dim3(blocks), dim3(kThreads), 0, s, a);
-  } else {
+  if (a.block == 0) {  // token eviction: one kernel plans, fills, packs and appends
     if (reg)
       hipLaunchKernelGGL((compact_plan_kernel<true, false>), dim3(blocks), dim3(kThreads), 0, s, a);
     else
       hipLaunchKernelGGL((compact_plan_kernel<false, false>), dim3(blocks), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
   }
+  if (reg)
+    hipLaunchKernelGGL((compact_plan_kernel<true, true>), dim3(blocks), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((compact_plan_kernel<false, true>), dim3(blocks), dim3(kThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 mgrid(blocks, a.c.hkv), mblock(128);

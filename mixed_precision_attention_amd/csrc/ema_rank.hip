@@ -5,7 +5,8 @@
 // by s_i = alpha a^_i + (1 - alpha) r^_i (normalised EMA mass and normalised
 // recency). Abar_i is the mean over all query heads of the softmax weight of
 // key i; a^ = a / max a and r^ = (pos - pos_min) / (pos_max - pos_min) over
-// the cached tokens, which are stored in ascending position order.
+// the cached tokens (position extremes reduced here: compaction may reorder
+// the INT8 part).
 //
 // One workgroup per (layer, sequence); ~16 bytes per token, memory-bound.
 // For up to kThreads * kPer tokens every thread issues all of its loads at
@@ -44,12 +45,13 @@ __global__ __launch_bounds__(kThreads) void ema_rank_kernel(EmaArgs a) {
     return;
   }
   __shared__ float red[kThreads / 64];
-  __shared__ int pend[2];
+  __shared__ int redp[2][kThreads / 64];
 
   const bool fast = n <= kThreads * kPer;
   float av[kPer];
   int pv[kPer];
   float amax = 0.f;
+  int pmin = INT32_MAX, pmax = INT32_MIN;
   if (fast) {
     float ms[kPer];
 #pragma unroll
@@ -86,6 +88,8 @@ __global__ __launch_bounds__(kThreads) void ema_rank_kernel(EmaArgs a) {
         av[r] = lam * av[r] + oml * (ms[r] * inv_hq);
         ema[i] = av[r];
         amax = fmaxf(amax, av[r]);
+        pmin = min(pmin, pv[r]);
+        pmax = max(pmax, pv[r]);
       }
     }
   } else {
@@ -95,26 +99,38 @@ __global__ __launch_bounds__(kThreads) void ema_rank_kernel(EmaArgs a) {
       const float v = lam * ema[i] + oml * (m * inv_hq);
       ema[i] = v;
       amax = fmaxf(amax, v);
+      const int p = pos[i];
+      pmin = min(pmin, p);
+      pmax = max(pmax, p);
     }
   }
   if (threadIdx.x == 0) {
     float m = 0.f;
     for (int j = 0; j < H; ++j) m += mass[(size_t)j * cap + n];
     ema[n] = oml * (m * inv_hq);
-    pend[0] = n > 0 ? pos[0] : 0;
-    pend[1] = n > 0 ? pos[n - 1] : 0;
-    pos[n] = a.t;
   }
   amax = wave_max(amax);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
-  __syncthreads();
+  for (int o = 32; o > 0; o >>= 1) {
+    pmin = min(pmin, __shfl_xor(pmin, o, 64));
+    pmax = max(pmax, __shfl_xor(pmax, o, 64));
+  }
+  if ((threadIdx.x & 63) == 0) {
+    red[threadIdx.x >> 6] = amax;
+    redp[0][threadIdx.x >> 6] = pmin;
+    redp[1][threadIdx.x >> 6] = pmax;
+  }
+  __syncthreads();  // also orders every read of pos[] before the write of pos[n]
+  if (threadIdx.x == 0) pos[n] = a.t;
   amax = red[0];
+  int p0 = redp[0][0], p1 = redp[1][0];
 #pragma unroll
-  for (int q = 1; q < kThreads / 64; ++q) amax = fmaxf(amax, red[q]);
+  for (int q = 1; q < kThreads / 64; ++q) {
+    amax = fmaxf(amax, red[q]);
+    p0 = min(p0, redp[0][q]);
+    p1 = max(p1, redp[1][q]);
+  }
   if (n == 0) return;
 
-  const int p0 = pend[0];
-  const int p1 = pend[1];
   const float inv_a = amax > 0.f ? 1.f / amax : 0.f;
   const float inv_r = p1 > p0 ? 1.f / (float)(p1 - p0) : 0.f;
   const float alpha = a.alpha;

@@ -68,7 +68,7 @@ class DeviceCache:
         return m[..., L.META_N], m[..., L.META_N8]
 
     def snapshot(self, l, b):
-        """Host copy of one (layer, sequence) in logical order (oldest first)."""
+        """Host copy of one (layer, sequence) in logical order (INT8 part first)."""
         m = self.meta[l, b].cpu().numpy()
         n, n8, b8, b16 = int(m[L.META_N]), int(m[L.META_N8]), int(m[L.META_BASE8]), int(m[L.META_BASE16])
         f = n - n8

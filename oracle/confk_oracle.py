@@ -117,7 +117,9 @@ def budget(c, tau, n_high, n_low):
 
 @dataclass
 class SeqCache:
-    """Retained tokens of one (layer, sequence), ordered by ascending position.
+    """Retained tokens of one (layer, sequence), in slot order: the INT8
+    entries first, then the FP16 ones in ascending position (the INT8 part is
+    in ascending position too unless compact(..., fill=True) reordered it).
 
     Each token is either FP16 (k16/v16 hold its values) or INT8 (k8/v8 hold
     its codes, dequantised with the per-(kv-head, channel) scales ks/vs).
@@ -272,9 +274,30 @@ def select_keep(s, pos, N, P, block=0):
     return keep
 
 
-def compact(cache, keep):
-    """Survivors packed densely in ascending position order (stable)."""
-    idx = np.flatnonzero(keep)
+def compact(cache, keep, fill=False):
+    """Survivors packed densely; the INT8 entries stay ahead of the FP16 ones.
+
+    The pages ask for a contiguous layout without indirection tables and fix
+    no order inside it. fill=False keeps slot order (stable). fill=True
+    (reading R24, token eviction): in the INT8 part, the survivors that lie at
+    or beyond its new end m take the holes below m, the j-th such survivor
+    (in slot order) the j-th hole; every other survivor keeps its slot. The
+    FP16 part is always stable, so it stays in position order.
+    """
+    keep = np.asarray(keep, bool)
+    n8 = int(cache.is8.sum())
+    assert cache.is8[:n8].all() and not cache.is8[n8:].any(), "INT8 entries first"
+    if fill:
+        k8 = keep[:n8]
+        m = int(k8.sum())
+        order8 = np.arange(m)
+        holes = np.flatnonzero(~k8[:m])
+        tails = m + np.flatnonzero(k8[m:])
+        assert len(holes) == len(tails)
+        order8[holes] = tails
+        idx = np.concatenate([order8, n8 + np.flatnonzero(keep[n8:])]).astype(np.int64)
+    else:
+        idx = np.flatnonzero(keep)
     c = cache.copy()
     for name in ("pos", "is8", "k16", "v16", "k8", "v8", "ema"):
         setattr(c, name, getattr(cache, name)[idx].copy())
@@ -417,7 +440,7 @@ def step_one(cache, q, k_new, v_new, t, pol, N, score_given=None):
     kp = select_keep(s_sel, cache.pos, N, pol.protect, getattr(pol, "block", 0))
     c1 = cache.copy()
     c1.ema = a
-    c1 = compact(c1, kp)
+    c1 = compact(c1, kp, fill=getattr(pol, "block", 0) == 0)
     c1 = append(c1, k_new, v_new, t, a_new)
     c1 = quantize_window(c1, t, pol.window)
     return dict(o=o, mass=m, ema=a, a_new=a_new, score=s, keep=kp, cache=c1)

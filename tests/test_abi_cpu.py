@@ -133,6 +133,7 @@ def test_compact_quantize_ema_validation(lib):
     assert cp(c, _pol(window=64), stride=5) == M.ERR_INVALID_ARG
     assert cp(c, _pol(window=80)) == M.ERR_BUDGET              # FP16 ring too small
     assert cp(c, _pol(lam=1.5)) == M.ERR_INVALID_ARG
+    assert cp(c, _pol(protect=20, window=16, n_high=24)) == M.ERR_BUDGET  # P > W, token eviction
     assert cp(c, _pol(block=8)) == M.ERR_INVALID_ARG          # blocks below 16 tokens
     assert cp(c, _pol(block=-16)) == M.ERR_INVALID_ARG
     big = _fake_cache(cap=16 * 513, cap16=65)                 # 513 blocks of 16

@@ -341,8 +341,8 @@ def test_parity_many_heads_multi_round_moves():
 @pytest.mark.parametrize("d", [64, 128])
 def test_many_movers_in_both_rings(d):
     """Crafted uniform scores scatter the evictions over the whole cache, so
-    one step moves several hundred INT8 rows and about a hundred FP16 rows
-    per ring: several move rounds and source-window reloads in each ring."""
+    the first step fills about 250 INT8 holes (several passes of the fill
+    loop) and packs about a hundred FP16 rows per ring (several rounds)."""
     import mixed_precision_attention_amd as M
     hq, hkv = (4, 4) if d == 64 else (10, 2)
     cfg = _cfg(f"many_movers_d{d}", 1, 2, hq, hkv, d, 500, 1200, 600, 900, 16, 200)
@@ -354,7 +354,8 @@ def test_many_movers_in_both_rings(d):
         run.step(i, scores=s)
         if i == 0:
             meta = run.eng.cache.meta.cpu().numpy()
-            assert meta[..., M.META_MOVED].max() > 256 and meta[..., M.META_MOVED16].max() > 64
+            moved8, moved16 = meta[..., M.META_MOVED].max(), meta[..., M.META_MOVED16].max()
+            assert moved8 > 200 and moved16 > 64, (moved8, moved16)
 
 
 def test_overlapped_step_matches_serial():

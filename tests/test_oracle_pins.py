@@ -445,6 +445,54 @@ def test_compact_and_append_preserve_rows():
     assert c3.pos[-1] == 99 and c3.ema[-1] == 0.125 and not c3.is8[-1]
 
 
+def _int8_cache(n8, n16, rng):
+    k = rng.standard_normal((n8 + n16, 2, 4)); v = rng.standard_normal((n8 + n16, 2, 4))
+    c = _cache_from_fp16(k, v)
+    c.is8 = np.arange(n8 + n16) < n8
+    c.ema = rng.random(n8 + n16)
+    return c
+
+
+def test_compact_fill_hand_worked():
+    # INT8 part of 8 entries keeps [0, 2, 3, 5, 6]: new INT8 length 5, holes
+    # below it at slots 1 and 4, surviving tail entries 5 and 6 -> 5 fills
+    # slot 1 and 6 fills slot 4; the FP16 part (slots 8-10) stays in order.
+    c = _int8_cache(8, 3, np.random.default_rng(12))
+    keep = np.array([1, 0, 1, 1, 0, 1, 1, 0, 1, 0, 1], bool)
+    c2 = O.compact(c, keep, fill=True)
+    assert c2.pos.tolist() == [c.pos[i] for i in (0, 5, 2, 3, 6, 8, 10)]
+    assert np.array_equal(c2.is8, [1, 1, 1, 1, 1, 0, 0])
+    assert np.array_equal(O.compact(c, keep).pos, c.pos[np.flatnonzero(keep)])  # stable form
+
+
+def test_compact_fill_invariants():
+    rng = np.random.default_rng(13)
+    for _ in range(300):
+        n8, n16 = int(rng.integers(0, 40)), int(rng.integers(1, 12))
+        c = _int8_cache(n8, n16, rng)
+        keep = rng.random(n8 + n16) < rng.random()
+        f, st = O.compact(c, keep, fill=True), O.compact(c, keep)
+        m = int(keep[:n8].sum())
+        # same survivors with the same rows, INT8 first, FP16 part identical
+        assert sorted(f.pos.tolist()) == sorted(st.pos.tolist())
+        assert np.array_equal(f.is8, st.is8) and np.array_equal(f.pos[m:], st.pos[m:])
+        for name in ("k16", "v16", "k8", "v8", "ema"):
+            got = dict(zip(f.pos.tolist(), getattr(f, name)))
+            want = dict(zip(c.pos.tolist(), getattr(c, name)))
+            assert all(np.array_equal(got[p], want[p]) for p in got)
+        # INT8 survivors below the new end keep their slot; the others move,
+        # fewer than the evicted INT8 entries, and in slot order
+        stay = [i for i in range(m) if keep[i]]
+        assert all(f.pos[i] == c.pos[i] for i in stay)
+        moved = [i for i in range(m) if not keep[i]]
+        src = [int(np.flatnonzero(c.pos == f.pos[i])[0]) for i in moved]
+        assert src == sorted(src) and all(s_ >= m for s_ in src)
+        assert len(moved) <= n8 - m
+        # evictions only at the INT8 tail move nothing
+        tail_only = keep.copy(); tail_only[:n8] = np.arange(n8) < m
+        assert np.array_equal(O.compact(c, tail_only, fill=True).pos, O.compact(c, tail_only).pos)
+
+
 # --------------------------------------------------------------- quantisation
 
 def test_quantize_round_trip_bound_and_absmax():
@@ -505,6 +553,7 @@ def test_end_to_end_invariants():
     kp, vp = synth.prefill_kv(cfg, seed=0)
     caches = [[O.prefill(kp[l, b], vp[l, b], pol.window) for b in range(cfg.batch)] for l in range(cfg.layers)]
     lengths = []
+    reordered = False
     for i in range(cfg.steps):
         t = cfg.prefill + i
         logits = synth.logits_for_step(cfg, 0, i)
@@ -518,10 +567,14 @@ def test_end_to_end_invariants():
                 if c0.n > N:
                     assert c1.n == N + 1
                     assert (~out.keep[l][b]).sum() == c0.n - N
-                assert c1.pos[-1] == t and (np.diff(c1.pos) > 0).all()
+                # new token last, positions unique, the FP16 part in ascending order
+                n8 = int(c1.is8.sum())
+                assert c1.pos[-1] == t and len(set(c1.pos.tolist())) == c1.n
+                assert c1.is8[:n8].all() and (np.diff(c1.pos[n8:]) > 0).all()
+                reordered |= bool((np.diff(c1.pos[:n8]) < 0).any())
                 assert (c1.is8 == (c1.pos <= t - pol.window)).all()      # FP16 = window positions
                 # protected newest P of the pre-step cache survive
-                assert set(c0.pos[-pol.protect:].tolist()) <= set(c1.pos.tolist())
+                assert set(np.sort(c0.pos)[-pol.protect:].tolist()) <= set(c1.pos.tolist())
                 assert ((c1.ema >= 0) & (c1.ema <= 1)).all()
                 assert abs(out.mass[l][b].sum() - 1) < 1e-12
         lengths.append(out.caches[0][0].n)
@@ -529,6 +582,7 @@ def test_end_to_end_invariants():
     # sawtooth: the cache both shrinks (confident steps) and regrows
     d = np.diff(lengths)
     assert (d < 0).any() and (d > 0).any()
+    assert reordered  # the INT8 hole filling took place
 
 
 def test_ema_of_retained_token_follows_closed_recurrence():
