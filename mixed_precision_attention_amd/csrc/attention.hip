@@ -35,9 +35,9 @@
 // row (their scores are masked), so loads carry no branches.
 //
 // Mass: the log2-domain scores are kept in LDS (or, in a separate kernel
-// instance, partly in a global spill area for// caches too long for the LDS budget); once the waves' running maxima and
-// normalisers are merged, each key's mass sum_h 2^(s_h - M_h) / L_h is
-// formed exactly.
+// instance, partly in a global spill area for caches too long for the LDS
+// budget); once the waves' running maxima and normalisers are merged, each
+// key's mass sum_h 2^(s_h - M_h) / L_h is formed exactly.
 #include "confk_internal.h"
 
 namespace confk {
@@ -582,17 +582,19 @@ void attn_decode_kernel(AttnArgs a) {
       const int i0 = r8 ? 4 * gi : n8 + 4 * (gi - q8);
       const int lim = r8 ? n8 : nk;
       const float u = usc[r8 ? 0 : 1];
-      float4_t sv[16];
-#pragma unroll
-      for (int hh = 0; hh < 16; ++hh)
-        if (hh < g) sv[hh] = *reinterpret_cast<const float4_t*>(sc + (size_t)hh * n_lds + slot);
       float4_t sum = {0.f, 0.f, 0.f, 0.f};
+      for (int h0 = 0; h0 < g; h0 += 4) {  // four heads' scores fetched before their exponentials
+        float4_t sv[4];
 #pragma unroll
-      for (int hh = 0; hh < 16; ++hh) {
-        if (hh < g) {
-          const float m = Mh[hh], il = iL[hh];
+        for (int j = 0; j < 4; ++j)
+          if (h0 + j < g) sv[j] = *reinterpret_cast<const float4_t*>(sc + (size_t)(h0 + j) * n_lds + slot);
 #pragma unroll
-          for (int v = 0; v < 4; ++v) sum[v] += __builtin_amdgcn_exp2f(fmaf(sv[hh][v], u, -m)) * il;
+        for (int j = 0; j < 4; ++j) {
+          if (h0 + j < g) {
+            const float m = Mh[h0 + j], il = iL[h0 + j];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) sum[v] += __builtin_amdgcn_exp2f(fmaf(sv[j][v], u, -m)) * il;
+          }
         }
       }
 #pragma unroll
