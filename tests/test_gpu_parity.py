@@ -256,6 +256,75 @@ def test_block_eviction_with_tied_block_maxima():
         run.step(i, scores=s.astype(np.float32))
 
 
+@pytest.mark.parametrize("prefill", [4095, 4096])
+def test_parity_register_and_long_plan_boundary(prefill):
+    """Capacity 4096 (the last one whose plan keeps keys in registers) and
+    4097 (the first on the long-cache path)."""
+    cfg = _cfg(f"cap_edge_{prefill}", 1, 2, 5, 1, 128, 600, prefill, 400, 800, 16, 64)
+    assert cfg.cap == prefill + 1
+    print(f"[parity] plan path edge cap={cfg.cap}", flush=True)
+    run = Run(cfg, seed=21)
+    events = sum(run.step(i) for i in range(4))
+    assert events > 0
+
+
+def test_parity_protect_equals_window():
+    """P = W, the largest protected window token eviction accepts."""
+    cfg = _cfg("p_eq_w", 2, 2, 10, 2, 128, 500, 300, 64, 120, 32, 32)
+    print("[parity] protect == window", flush=True)
+    run = Run(cfg, seed=22)
+    events = sum(run.step(i) for i in range(30))
+    assert events > 0
+
+
+def test_parity_block_eviction_d64():
+    cfg = _block_cfg(_cfg("blk64", 2, 2, 4, 4, 64, 700, 400, 96, 200, 16, 48), 16)
+    print("[parity] block eviction d64", flush=True)
+    run = Run(cfg, seed=23)
+    events = sum(run.step(i) for i in range(30))
+    assert events > 2
+
+
+def test_no_free_slot_sets_status_and_leaves_the_sequence_alone():
+    """A (layer, sequence) whose metadata leaves no slot for the new token
+    (forced from the host: n = cap) is flagged with CONFK_STATUS_CAPACITY by
+    every call and left as it is; the other sequences step normally."""
+    import mixed_precision_attention_amd as M
+    dev = _dev()
+    cfg = TINY["g5_d128"]
+    kp, vp = synth.prefill_kv(cfg, 5)
+    eng = M.DecodeEngine(cfg, dev)
+    eng.prefill(_t(kp, dev), _t(vp, dev))
+    twin = M.DecodeEngine(cfg, dev)
+    twin.prefill(_t(kp, dev), _t(vp, dev))
+    for i in range(3):
+        logits, q, kn, vn, t = _inputs(cfg, 5, i)
+        for e in (eng, twin):
+            e.step(_t(logits, dev), _t(q, dev), _t(kn, dev), _t(vn, dev), t)
+    torch.cuda.synchronize()
+    bad = eng.cache.meta[1, 0].clone()
+    bad[M.META_N], bad[M.META_N8] = cfg.cap, 0
+    eng.cache.meta[1, 0] = bad
+    print("[capacity] forced n = cap on (1, 0)", flush=True)
+    logits, q, kn, vn, t = _inputs(cfg, 5, 3)
+    for e in (eng, twin):
+        e.step(_t(logits, dev), _t(q, dev), _t(kn, dev), _t(vn, dev), t)
+    torch.cuda.synchronize()
+    assert int(eng.cache.status.cpu()[0]) & M.STATUS_CAPACITY
+    assert int(twin.cache.status.cpu()[0]) == 0
+    after = eng.cache.meta[1, 0].cpu().numpy()
+    for w in (M.META_N, M.META_N8, M.META_BASE8, M.META_BASE16):
+        assert after[w] == bad.cpu().numpy()[w]
+    # every other (layer, sequence) matches the twin that never saw the fault
+    for l in range(cfg.layers):
+        for b in range(cfg.batch):
+            if (l, b) != (1, 0):
+                assert torch.equal(eng.cache.meta[l, b], twin.cache.meta[l, b])
+                assert torch.equal(eng.cache.pos[l, b], twin.cache.pos[l, b])
+                assert torch.equal(eng.cache.k8[l, b], twin.cache.k8[l, b])
+                assert torch.equal(eng.cache.k16[l, b], twin.cache.k16[l, b])
+
+
 def test_confidence_closed_forms_and_flags():
     import mixed_precision_attention_amd as M
     dev = _dev()
