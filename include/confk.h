@@ -240,6 +240,22 @@ int confk_compact(const confk_cache* cache, int32_t layer0, int32_t nlayers, con
                   size_t ws_bytes, void* stream);
 
 /*
+ * confk_ema_compact -- confk_ema_rank followed by confk_compact in one launch
+ * (one workgroup per (layer, sequence) updates the EMA, forms the rank scores
+ * and evicts / compacts / appends, without a second pass over the metadata).
+ * Same arguments, results and errors as the two calls in sequence (the score
+ * buffer receives the rank scores), bit for bit; the split calls stay for
+ * callers that inspect or replace the scores in between.
+ *   mass   as for confk_ema_rank; t >= 0 the new token's position
+ *   score  fp32 [nlayers][B][cap], written
+ *   other arguments as for confk_compact
+ */
+int confk_ema_compact(const confk_cache* cache, int32_t layer0, int32_t nlayers, const float* mass,
+                      const confk_policy* pol, int32_t t, float* score, const int32_t* budget,
+                      int32_t budget_layer_stride, const uint16_t* k_new, const uint16_t* v_new,
+                      int32_t* evicted_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * confk_quantize -- FP16 -> INT8 storage per (head, channel).
  * Summary "Methodik" (gemischte Praezisionsspeicherung: newest W tokens FP16,
  * older retained tokens INT8 per head and channel); review Algorithm 1

@@ -152,10 +152,12 @@ int confk_ema_rank(const confk_cache* cache, int32_t layer0, int32_t nlayers, co
   return launch_status(launch_ema_rank(a, (hipStream_t)stream));
 }
 
-int confk_compact(const confk_cache* cache, int32_t layer0, int32_t nlayers, const int32_t* budget,
-                  int32_t budget_layer_stride, const float* score, const confk_policy* pol,
-                  const uint16_t* k_new, const uint16_t* v_new, int32_t* evicted_out, void* ws,
-                  size_t ws_bytes, void* stream) {
+namespace {
+// Validation and argument set-up shared by the split and the fused entry.
+int compact_args(const confk_cache* cache, int32_t layer0, int32_t nlayers, const int32_t* budget,
+                 int32_t budget_layer_stride, const float* score, const confk_policy* pol,
+                 const uint16_t* k_new, const uint16_t* v_new, int32_t* evicted_out, void* ws,
+                 size_t ws_bytes, confk::CompactArgs& a) {
   if (!cache_ok(cache) || !layers_ok(cache, layer0, nlayers)) return CONFK_ERR_INVALID_ARG;
   if (!budget || !score || !k_new || !v_new || !policy_ok(pol)) return CONFK_ERR_INVALID_ARG;
   if (budget_layer_stride != 0 && budget_layer_stride != cache->batch) return CONFK_ERR_INVALID_ARG;
@@ -169,7 +171,7 @@ int confk_compact(const confk_cache* cache, int32_t layer0, int32_t nlayers, con
   if (pol->block > 0 && cache->d != 64 && cache->d != 128) return CONFK_ERR_UNSUPPORTED;
   const size_t need = compact_ws_bytes(nlayers, cache->batch, cache->cap);
   if (!ws || ws_bytes < need) return CONFK_ERR_WORKSPACE;
-  CompactArgs a{};
+  a = CompactArgs{};
   a.plan = (int32_t*)ws;
   a.stage = (int32_t*)((char*)ws + compact_plan_bytes(nlayers, cache->batch, cache->cap));
   a.c = view_of(cache);
@@ -183,6 +185,36 @@ int confk_compact(const confk_cache* cache, int32_t layer0, int32_t nlayers, con
   a.k_new = k_new;
   a.v_new = v_new;
   a.evicted_out = evicted_out;
+  return CONFK_OK;
+}
+}  // namespace
+
+int confk_compact(const confk_cache* cache, int32_t layer0, int32_t nlayers, const int32_t* budget,
+                  int32_t budget_layer_stride, const float* score, const confk_policy* pol,
+                  const uint16_t* k_new, const uint16_t* v_new, int32_t* evicted_out, void* ws,
+                  size_t ws_bytes, void* stream) {
+  CompactArgs a;
+  const int e = compact_args(cache, layer0, nlayers, budget, budget_layer_stride, score, pol, k_new, v_new,
+                             evicted_out, ws, ws_bytes, a);
+  if (e != CONFK_OK) return e;
+  return launch_status(launch_compact(a, (hipStream_t)stream));
+}
+
+int confk_ema_compact(const confk_cache* cache, int32_t layer0, int32_t nlayers, const float* mass,
+                      const confk_policy* pol, int32_t t, float* score, const int32_t* budget,
+                      int32_t budget_layer_stride, const uint16_t* k_new, const uint16_t* v_new,
+                      int32_t* evicted_out, void* ws, size_t ws_bytes, void* stream) {
+  if (!mass || t < 0) return CONFK_ERR_INVALID_ARG;
+  CompactArgs a;
+  const int e = compact_args(cache, layer0, nlayers, budget, budget_layer_stride, score, pol, k_new, v_new,
+                             evicted_out, ws, ws_bytes, a);
+  if (e != CONFK_OK) return e;
+  a.fuse = 1;
+  a.t = t;
+  a.lambda = pol->lambda;
+  a.alpha = pol->alpha;
+  a.mass = mass;
+  a.score_out = score;
   return launch_status(launch_compact(a, (hipStream_t)stream));
 }
 

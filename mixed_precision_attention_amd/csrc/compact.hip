@@ -102,6 +102,8 @@ __device__ __forceinline__ int wave_prefix16(int x, int& total) {
 
 struct Shared {
   uint32_t hist[kBuckets];
+  float rmax[kWaves];  // fused EMA: per-wave max EMA and position range
+  int rpmin[kWaves], rpmax[kWaves];
   int wsum[3][kWaves];  // per-wave keeps, e8, e16
   int wfill[2][kWaves];  // per-wave INT8 holes and tails
   int wfirst[2][kWaves], wlast[2][kWaves];
@@ -118,6 +120,16 @@ constexpr int kFillMax = kRegKeys * kThreads / 2;
 struct FillShared {
   float e[kFillMax];
   int32_t p[kFillMax], i[kFillMax], h[kFillMax];
+};
+// The fused EMA phase hands its results (EMA, position per logical index)
+// from lane-strided to run-contiguous ownership through the same LDS, before
+// the fill lists are written.
+union RegShared {
+  FillShared fill;
+  struct {
+    float e[kRegKeys * kThreads];
+    int32_t p[kRegKeys * kThreads];
+  } x;
 };
 
 // Workspace words per (layer, sequence) for long caches: staged metadata of
@@ -191,7 +203,9 @@ __device__ uint32_t radix_select(int& kk, int cnt, Part part, Val val, Shared& s
   return prefix;
 }
 
-template <bool REG, bool BLOCK>
+// FUSE: the EMA update and rank scores of ema_rank_kernel run first, in this
+// kernel, with the same arithmetic and summation order (bit-identical).
+template <bool REG, bool BLOCK, bool FUSE>
 __global__ __launch_bounds__(kThreads) void compact_plan_kernel(CompactArgs a) {
   const CacheView& c = a.c;
   const int lb = blockIdx.x;
@@ -213,7 +227,7 @@ __global__ __launch_bounds__(kThreads) void compact_plan_kernel(CompactArgs a) {
   int32_t* pos = c.pos + (size_t)lbc * cap;
   const float* score = a.score + (size_t)lb * cap;
   __shared__ Shared sh;
-  __shared__ std::conditional_t<REG && !BLOCK, FillShared, char> fsh;
+  __shared__ std::conditional_t<REG && (!BLOCK || FUSE), RegShared, char> rsh;
   // the new token's K and V rows into the FP16 rings at `slot`
   auto append_rows = [&](int slot) {
     const int H = c.hkv, d = c.d, p16 = d >> 3, rp16 = 2 * H * p16;
@@ -253,7 +267,141 @@ __global__ __launch_bounds__(kThreads) void compact_plan_kernel(CompactArgs a) {
     k = kb * B;
   }
 
+  const int chunk = (nn + kThreads - 1) / kThreads;
+  const int lo = min(nn, (int)threadIdx.x * chunk);
+  const int cnt = min(nn, lo + chunk) - lo;
+  // this thread's run: score keys, EMA and positions (read before any write)
+  uint32_t kreg[REG ? kRegKeys : 1];
+  float ereg[REG ? kRegKeys : 1];
+  int preg[REG ? kRegKeys : 1];
+  int bk[REG ? kRegKeys : 1];
+  float sreg[REG && FUSE ? kRegKeys : 1];
+
+  // ------------------------------------------------- 0. EMA + rank (fused)
+  if constexpr (FUSE) {
+    const int H = c.hkv;
+    const float* mass = a.mass + (size_t)lb * H * cap;
+    const float inv_hq = 1.f / (float)c.hq, lam = a.lambda, oml = 1.f - lam;
+    float amax = 0.f;
+    int pmin = INT32_MAX, pmax = INT32_MIN;
+    // a_i = lam a_i + (1 - lam) Abar_i for cached tokens, (1 - lam) Abar_n for
+    // the new one (zero prior); kv heads summed in order. Lane-strided
+    // ownership (index threadIdx.x + r * kThreads) keeps the loads coalesced.
+    if constexpr (REG) {
+      float ms[kRegKeys], av[kRegKeys];
+      int pv[kRegKeys];
+#pragma unroll
+      for (int r = 0; r < kRegKeys; ++r) {
+        const int i = threadIdx.x + r * kThreads;
+        ms[r] = 0.f;
+        av[r] = i < n ? ema[i] : 0.f;
+        pv[r] = i < n ? pos[i] : a.t;
+      }
+      for (int j0 = 0; j0 < H; j0 += 8) {
+        float t8[8][kRegKeys];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+#pragma unroll
+          for (int r = 0; r < kRegKeys; ++r) {
+            const int i = threadIdx.x + r * kThreads;
+            t8[q][r] = (j0 + q < H && i < nn) ? mass[(size_t)(j0 + q) * cap + i] : 0.f;
+          }
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+#pragma unroll
+          for (int r = 0; r < kRegKeys; ++r)
+            if (j0 + q < H) ms[r] += t8[q][r];
+      }
+#pragma unroll
+      for (int r = 0; r < kRegKeys; ++r) {
+        const int i = threadIdx.x + r * kThreads;
+        if (i < n) {
+          av[r] = fmaf(lam, av[r], oml * (ms[r] * inv_hq));
+          amax = fmaxf(amax, av[r]);
+          pmin = min(pmin, pv[r]);
+          pmax = max(pmax, pv[r]);
+        } else {
+          av[r] = oml * (ms[r] * inv_hq);
+        }
+        if (i < nn) {
+          rsh.x.e[i] = av[r];
+          rsh.x.p[i] = pv[r];
+        }
+      }
+    } else {
+      for (int i = threadIdx.x; i < nn; i += kThreads) {
+        float m = 0.f;
+        for (int j = 0; j < H; ++j) m += mass[(size_t)j * cap + i];
+        if (i < n) {
+          const float v = fmaf(lam, ema[i], oml * (m * inv_hq));
+          ema[i] = v;
+          amax = fmaxf(amax, v);
+          const int p = pos[i];
+          pmin = min(pmin, p);
+          pmax = max(pmax, p);
+        } else {
+          ema[n] = oml * (m * inv_hq);
+          pos[n] = a.t;
+        }
+      }
+    }
+    amax = wave_max(amax);
+    for (int o = 32; o > 0; o >>= 1) {
+      pmin = min(pmin, __shfl_xor(pmin, o, 64));
+      pmax = max(pmax, __shfl_xor(pmax, o, 64));
+    }
+    if (lane == 0) {
+      sh.rmax[w] = amax;
+      sh.rpmin[w] = pmin;
+      sh.rpmax[w] = pmax;
+    }
+    __syncthreads();  // the exchange, and the long-cache form's EMA writes, are visible
+    amax = sh.rmax[0];
+    int p0 = sh.rpmin[0], p1 = sh.rpmax[0];
+#pragma unroll
+    for (int q = 1; q < kWaves; ++q) {
+      amax = fmaxf(amax, sh.rmax[q]);
+      p0 = min(p0, sh.rpmin[q]);
+      p1 = max(p1, sh.rpmax[q]);
+    }
+    const float inv_a = amax > 0.f ? 1.f / amax : 0.f;
+    const float inv_r = p1 > p0 ? 1.f / (float)(p1 - p0) : 0.f;
+    const float alpha = a.alpha;
+    float* score_w = a.score_out + (size_t)lb * cap;  // this (layer, sequence)'s scores
+    if constexpr (REG) {
+#pragma unroll
+      for (int r = 0; r < kRegKeys; ++r) {  // this thread's run, from the exchange
+        const int i = lo + r;
+        ereg[r] = r < cnt ? rsh.x.e[i] : 0.f;
+        preg[r] = r < cnt ? rsh.x.p[i] : 0;
+        sreg[r] = 0.f;
+        if (r < cnt && i < n) {
+          const float rh = p1 > p0 ? (float)(preg[r] - p0) * inv_r : 1.f;
+          sreg[r] = fmaf(alpha, ereg[r] * inv_a, (1.f - alpha) * rh);
+          score_w[i] = sreg[r];
+        }
+      }
+    } else {
+      for (int r = 0; r < cnt; ++r) {
+        const int i = lo + r;
+        if (i < n) {
+          const float rh = p1 > p0 ? (float)(pos[i] - p0) * inv_r : 1.f;
+          score_w[i] = fmaf(alpha, ema[i] * inv_a, (1.f - alpha) * rh);
+        }
+      }
+      __syncthreads();  // scores are read back from memory below
+    }
+  }
+
   if (k == 0) {  // nothing leaves: the new token (metadata slot n) is appended
+    if constexpr (FUSE && REG) {  // every entry stays: its updated EMA in place
+#pragma unroll
+      for (int r = 0; r < kRegKeys; ++r)
+        if (r < cnt) {
+          ema[lo + r] = ereg[r];
+          if (lo + r == n) pos[n] = a.t;
+        }
+    }
     int slot = base16 + f;
     slot = slot >= c.cap16 ? slot - c.cap16 : slot;
     if constexpr (!BLOCK) append_rows(slot);
@@ -271,25 +419,19 @@ __global__ __launch_bounds__(kThreads) void compact_plan_kernel(CompactArgs a) {
     return;
   }
 
-  const int chunk = (nn + kThreads - 1) / kThreads;
-  const int lo = min(nn, (int)threadIdx.x * chunk);
-  const int cnt = min(nn, lo + chunk) - lo;
-  // this thread's run: score keys, EMA and positions (read before any write)
-  uint32_t kreg[REG ? kRegKeys : 1];
-  float ereg[REG ? kRegKeys : 1];
-  int preg[REG ? kRegKeys : 1];
-  int bk[REG ? kRegKeys : 1];
   if constexpr (REG) {
 #pragma unroll
     for (int j = 0; j < kRegKeys; ++j) {
       const int i = lo + j;
       const bool in = j < cnt;
       const bool cand = in && i < ncand;
-      const float s = cand ? score[i] : 0.f;
+      const float s = cand ? (FUSE ? sreg[j] : score[i]) : 0.f;
       kreg[j] = cand ? ord_bits(s) : 0xFFFFFFFFu;
       bk[j] = cand ? bucket_of(s) : kBuckets;
-      ereg[j] = in ? ema[i] : 0.f;
-      preg[j] = in ? pos[i] : 0;
+      if constexpr (!FUSE) {
+        ereg[j] = in ? ema[i] : 0.f;
+        preg[j] = in ? pos[i] : 0;
+      }
     }
   }
   auto key_at = [&](int j) -> uint32_t {
@@ -654,10 +796,10 @@ __global__ __launch_bounds__(kThreads) void compact_plan_kernel(CompactArgs a) {
     float* tse;
     int32_t *tsp, *tsi, *hd;
     if constexpr (REG) {
-      tse = fsh.e;
-      tsp = fsh.p;
-      tsi = fsh.i;
-      hd = fsh.h;
+      tse = rsh.fill.e;
+      tsp = rsh.fill.p;
+      tsi = rsh.fill.i;
+      hd = rsh.fill.h;
     } else {
       tse = reinterpret_cast<float*>(st + 3 * cap);
       tsp = st + 3 * cap + half;
@@ -681,7 +823,9 @@ __global__ __launch_bounds__(kThreads) void compact_plan_kernel(CompactArgs a) {
           if (!((evm >> j) & 1u)) {
             if (i >= n8) {
               emit16(i, jn, ereg[j], preg[j]);
-            } else if (i >= m8) {
+            } else if (i < m8) {
+              if constexpr (FUSE) ema[i] = ereg[j];  // stays in its slot
+            } else {
               tse[t] = ereg[j];
               tsp[t] = preg[j];
               tsi[t] = i;
@@ -939,20 +1083,21 @@ size_t compact_plan_bytes(int nlayers, int batch, int cap) {
   return (size_t)nlayers * batch * (kHdr + 2 * (size_t)cap) * 4;
 }
 
-hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
+template <bool FUSE>
+hipError_t launch_compact_t(const CompactArgs& a, hipStream_t s) {
   const int blocks = a.nl * a.c.B;
   const bool reg = a.c.cap <= kRegKeys * kThreads;
   if (a.block == 0) {  // token eviction: one kernel plans, fills, packs and appends
     if (reg)
-      hipLaunchKernelGGL((compact_plan_kernel<true, false>), dim3(blocks), dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((compact_plan_kernel<true, false, FUSE>), dim3(blocks), dim3(kThreads), 0, s, a);
     else
-      hipLaunchKernelGGL((compact_plan_kernel<false, false>), dim3(blocks), dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((compact_plan_kernel<false, false, FUSE>), dim3(blocks), dim3(kThreads), 0, s, a);
     return hipGetLastError();
   }
   if (reg)
-    hipLaunchKernelGGL((compact_plan_kernel<true, true>), dim3(blocks), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((compact_plan_kernel<true, true, FUSE>), dim3(blocks), dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((compact_plan_kernel<false, true>), dim3(blocks), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((compact_plan_kernel<false, true, FUSE>), dim3(blocks), dim3(kThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 mgrid(blocks, a.c.hkv), mblock(128);
@@ -962,6 +1107,10 @@ hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(compact_move_kernel<64>, mgrid, mblock, 0, s, a);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
+  return a.fuse ? launch_compact_t<true>(a, s) : launch_compact_t<false>(a, s);
 }
 
 }  // namespace confk

@@ -84,6 +84,12 @@ struct CompactArgs {
   const uint16_t* k_new;
   const uint16_t* v_new;
   int32_t* evicted_out;
+  // fused form (EMA + rank in the same kernel): mass in, scores out to
+  // score_out (the buffer `score` also points at)
+  int32_t fuse, t;
+  float lambda, alpha;
+  const float* mass;
+  float* score_out;
 };
 
 struct QuantArgs {

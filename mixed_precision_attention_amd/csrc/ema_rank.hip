@@ -85,7 +85,7 @@ __global__ __launch_bounds__(kThreads) void ema_rank_kernel(EmaArgs a) {
     for (int r = 0; r < kPer; ++r) {
       const int i = threadIdx.x + r * kThreads;
       if (i < n) {
-        av[r] = lam * av[r] + oml * (ms[r] * inv_hq);
+        av[r] = fmaf(lam, av[r], oml * (ms[r] * inv_hq));
         ema[i] = av[r];
         amax = fmaxf(amax, av[r]);
         pmin = min(pmin, pv[r]);
@@ -96,7 +96,7 @@ __global__ __launch_bounds__(kThreads) void ema_rank_kernel(EmaArgs a) {
     for (int i = threadIdx.x; i < n; i += kThreads) {
       float m = 0.f;
       for (int j = 0; j < H; ++j) m += mass[(size_t)j * cap + i];
-      const float v = lam * ema[i] + oml * (m * inv_hq);
+      const float v = fmaf(lam, ema[i], oml * (m * inv_hq));
       ema[i] = v;
       amax = fmaxf(amax, v);
       const int p = pos[i];
@@ -140,13 +140,13 @@ __global__ __launch_bounds__(kThreads) void ema_rank_kernel(EmaArgs a) {
       const int i = threadIdx.x + r * kThreads;
       if (i < n) {
         const float rh = p1 > p0 ? (float)(pv[r] - p0) * inv_r : 1.f;
-        score[i] = alpha * (av[r] * inv_a) + (1.f - alpha) * rh;
+        score[i] = fmaf(alpha, av[r] * inv_a, (1.f - alpha) * rh);
       }
     }
   } else {
     for (int i = threadIdx.x; i < n; i += kThreads) {
       const float rh = p1 > p0 ? (float)(pos[i] - p0) * inv_r : 1.f;
-      score[i] = alpha * (ema[i] * inv_a) + (1.f - alpha) * rh;
+      score[i] = fmaf(alpha, ema[i] * inv_a, (1.f - alpha) * rh);
     }
   }
 }

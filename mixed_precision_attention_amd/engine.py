@@ -122,6 +122,17 @@ def compact(cache, budget, budget_stride, score, pol, k_new, v_new, ws, evicted=
         _p(k_new), _p(v_new), _p(evicted), _p(ws), ws.numel() * ws.element_size(), _stream()))
 
 
+def ema_compact(cache, mass, pol, t, score, budget, budget_stride, k_new, v_new, ws, evicted=None,
+                layer0=0, nlayers=None):
+    """confk_ema_compact: ema_rank and compact in one launch."""
+    lib = L.load()
+    nl = cache.layers - layer0 if nlayers is None else nlayers
+    L.check("confk_ema_compact", lib.confk_ema_compact(
+        cache.ref(), layer0, nl, _p(mass), ctypes.byref(pol), int(t), _p(score), _p(budget),
+        int(budget_stride), _p(k_new), _p(v_new), _p(evicted), _p(ws), ws.numel() * ws.element_size(),
+        _stream()))
+
+
 def quantize(cache, pol, t, mode=L.QUANT_STEP, k_src=None, v_src=None, n_src=0, layer0=0,
              nlayers=None):
     lib = L.load()
@@ -202,6 +213,12 @@ class DecodeEngine:
         compact(self.cache, self.budget, self.budget_stride, self.score, self.pol, k_new, v_new,
                 self.compact_ws, self.evicted)
 
+    def step_ema_compact(self, t, k_new, v_new):
+        """EMA, rank scores and compaction in one launch (same state as
+        step_ema_rank followed by step_compact)."""
+        ema_compact(self.cache, self.mass, self.pol, t, self.score, self.budget, self.budget_stride,
+                    k_new, v_new, self.compact_ws, self.evicted)
+
     def step_quantize(self, t):
         quantize(self.cache, self.pol, t)
 
@@ -221,8 +238,7 @@ class DecodeEngine:
                 self.step_confidence(logits)
             self.conf_done.record(self.side)
         self.step_attention(q, k_new, v_new)
-        self.step_ema_rank(t)
         if self.side is not None:
             torch.cuda.current_stream().wait_event(self.conf_done)
-        self.step_compact(k_new, v_new)
+        self.step_ema_compact(t, k_new, v_new)
         self.step_quantize(t)

@@ -139,6 +139,14 @@ def test_compact_quantize_ema_validation(lib):
     big = _fake_cache(cap=16 * 513, cap16=65)                 # 513 blocks of 16
     wbig = lib.confk_workspace_size(M._lib.WS_COMPACT, ctypes.byref(big), 2, 0, 0)
     assert cp(big, _pol(block=16), n=wbig) == M.ERR_UNSUPPORTED
+    # the fused EMA + compaction call validates like the two calls it replaces
+    ec = lambda cc, p, mass=FAKE, t=5, ws=FAKE, n=wsb: lib.confk_ema_compact(  # noqa: E731
+        ctypes.byref(cc), 0, 2, mass, ctypes.byref(p), t, FAKE, FAKE, 0, FAKE, FAKE, None, ws, n, None)
+    assert ec(c, _pol(), mass=None) == M.ERR_INVALID_ARG
+    assert ec(c, _pol(), t=-1) == M.ERR_INVALID_ARG
+    assert ec(c, _pol(), ws=None) == M.ERR_WORKSPACE
+    assert ec(c, _pol(protect=30)) == M.ERR_BUDGET
+    assert ec(c, _pol(lam=1.5)) == M.ERR_INVALID_ARG
     q = lambda mode, n_src=10, k=FAKE: lib.confk_quantize(  # noqa: E731
         ctypes.byref(c), 0, 2, 0, ctypes.byref(pol), mode, k, FAKE, n_src, None)
     assert q(7) == M.ERR_INVALID_ARG

@@ -428,8 +428,10 @@ def test_many_movers_in_both_rings(d):
 
 
 def test_overlapped_step_matches_serial():
-    """DecodeEngine.step (confidence on a second stream) leaves exactly the
-    state of the five calls issued one after another on one stream."""
+    """DecodeEngine.step (confidence on a second stream, EMA and compaction in
+    one fused call) leaves exactly the state of the five calls issued one
+    after another on one stream. EMA and position slots past the new length
+    (evicted tokens) are not part of the state: the fused call leaves them."""
     import mixed_precision_attention_amd as M
     dev = _dev()
     cfg = TINY["g5_d128"]
@@ -449,8 +451,15 @@ def test_overlapped_step_matches_serial():
         e.step_quantize(t)
     torch.cuda.synchronize()
     a, b = engs
-    for name in ("meta", "k8", "v8", "k16", "v16", "kscale", "vscale", "ema", "pos", "status"):
+    for name in ("meta", "k8", "v8", "k16", "v16", "kscale", "vscale", "status"):
         assert torch.equal(getattr(a.cache, name), getattr(b.cache, name)), name
+    nlen = a.cache.meta[..., M.META_N].cpu().numpy()
+    for l in range(cfg.layers):
+        for bb in range(cfg.batch):
+            n = int(nlen[l, bb])
+            for name in ("ema", "pos"):
+                x, y = getattr(a.cache, name)[l, bb, :n], getattr(b.cache, name)[l, bb, :n]
+                assert torch.equal(x, y), (name, l, bb)
     for name in ("c", "budget", "out", "mass", "score"):
         assert torch.equal(getattr(a, name), getattr(b, name)), name
 
