@@ -31,6 +31,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kPerThread = 16;
 constexpr int kChunk = kThreads * kPerThread;
+constexpr int kLanePer = kChunk / 64;  // elements per lane in the sampling scan
 constexpr float kLog2e = 1.4426950408889634f;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -263,17 +264,30 @@ __global__ __launch_bounds__(64) void conf_final_kernel(ConfArgs a) {
       // rounding left the target at the total: the last chunk's last element
       const bool past_end = cstar < 0;
       if (past_end) cstar = a.nchunks - 1;
-      // inside chunk cstar: lane L sums elements [start + L*per, +per) in order
+      // inside chunk cstar: lane L owns elements [start + L*kLanePer, +kLanePer)
+      // in index order; their weights are read once and kept in registers
+      static_assert(kChunk == 64 * kLanePer, "one chunk is 64 lanes' runs");
       const float* row = a.logits + (int64_t)b * a.ld;
       const int start = cstar * a.chunk;
       const int end = min(a.vocab, start + a.chunk);
-      const int per = (a.chunk + 63) / 64;
-      const int lo = start + lane * per, hi = min(end, lo + per);
-      float wsum = 0.f;
-      for (int i = lo; i < hi; ++i) {
-        const float v = row[i];
-        if (v > -INFINITY) wsum += exp_neg((v - r.M) * inv_t);
+      const int lo = start + lane * kLanePer, hi = min(end, lo + kLanePer);
+      float wt[kLanePer];
+#pragma unroll
+      for (int k = 0; k < kLanePer / 4; ++k) {
+        const int i = lo + 4 * k;
+        f32x4 v;
+        if (a.vec4 && i + 3 < hi) {
+          v = *reinterpret_cast<const f32x4*>(row + i);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = i + e < hi ? row[i + e] : -INFINITY;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) wt[4 * k + e] = v[e] > -INFINITY ? exp_neg((v[e] - r.M) * inv_t) : 0.f;
       }
+      float wsum = 0.f;
+#pragma unroll
+      for (int j = 0; j < kLanePer; ++j) wsum += wt[j];
       float incl = wsum;
       for (int o = 1; o < 64; o <<= 1) {
         const float yv = __shfl_up(incl, o, 64);
@@ -285,13 +299,14 @@ __global__ __launch_bounds__(64) void conf_final_kernel(ConfArgs a) {
       float acc = __shfl(incl - wsum, src, 64);
       if (lane == src) {
         tok = hi - 1;  // rounding: the lane's last element
-        for (int i = lo; i < hi; ++i) {
-          const float v = row[i];
-          if (v > -INFINITY) {
-            acc += exp_neg((v - r.M) * inv_t);
+        bool found = false;
+#pragma unroll
+        for (int j = 0; j < kLanePer; ++j) {
+          if (!found && lo + j < hi && wt[j] > 0.f) {
+            acc += wt[j];
             if (acc > t2) {
-              tok = i;
-              break;
+              tok = lo + j;
+              found = true;
             }
           }
         }
