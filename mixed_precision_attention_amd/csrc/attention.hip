@@ -93,13 +93,32 @@ __device__ __forceinline__ uint32_t half_pair_rows(uint32_t row0w, uint32_t row1
 __device__ __forceinline__ half8_t as_half8(u32x4 v) { return __builtin_bit_cast(half8_t, v); }
 __device__ __forceinline__ half4_t as_half4(u32x2 v) { return __builtin_bit_cast(half4_t, v); }
 
-// V rows are read once per step, each load instruction covering whole 128-byte
-// lines: non-temporal (streaming) loads, measured 3% faster for the kernel.
-// K loads stay cached: in the matrix-core operand layout one instruction reads
-// half of each of 16 rows and the next one the other half, which then hits.
-// Streaming the mass stores, or the K loads, was measured slower.
+// INT8 K and all V rows are read with non-temporal (streaming) loads, each
+// instruction covering whole 128-byte lines (INT8 K rows through lane pairs,
+// see unpair); the INT8 K change took the kernel from 241 to 233 us on the
+// Qwen-32B-shape batch-8 cache. FP16 K rows stay on plain loads (one
+// instruction reads half a line of each of 16 rows, the next the other half,
+// which then hits): paired
+// streaming loads there were measured 2-3% slower, also with a 1 GiB read
+// between launches. Streaming the mass stores was measured slower.
 template <typename T>
 __device__ __forceinline__ T stream_load(const T* p) { return __builtin_nontemporal_load(p); }
+
+// Paired K-row loads: the lanes of key rows r and r ^ 8 (r of the 16 rows of
+// the operand layout) read the two 64-byte halves of one 128-byte row in one
+// instruction, a = the rows r & 7, b = the rows (r & 7) + 8. Afterwards lane r < 8 holds its own first
+// half (a) and row r + 8's first half (b), lane r >= 8 row r - 8's second half
+// (a) and its own second half (b). One row rotation by 8 lanes swaps the
+// foreign halves, leaving each lane its row's first and second half.
+__device__ __forceinline__ void unpair(const u32x4& a, const u32x4& b, bool lo, u32x4& first,
+                                       u32x4& second) {
+  const u32x4 x = lo ? b : a;
+  u32x4 y;
+#pragma unroll
+  for (int z = 0; z < 4; ++z) y[z] = (uint32_t)__builtin_amdgcn_mov_dpp((int)x[z], 0x128, 0xF, 0xF, false);
+  first = lo ? a : y;
+  second = lo ? y : b;
+}
 
 template <int D>
 struct Tile {
@@ -216,7 +235,7 @@ __device__ __forceinline__ half4_t softmax_tile(float4_t s, float unscale, SoftS
 // Raw registers of one 16-key INT8 tile of this lane.
 template <int D>
 struct Raw8 {
-  u32x4 k[Tile<D>::KU];            // K row r16: 16 bytes per 64-byte half
+  u32x4 k[Tile<D>::KU];            // K rows: 16 bytes per 64-byte half (lane pairs when KU = 2)
   uint32_t v[4][Tile<D>::CB / 4];  // V rows 4kg+j: D/16 bytes at channel (D/16)*r16
 };
 
@@ -323,10 +342,9 @@ void attn_decode_kernel(AttnArgs a) {
   };
 
   // ------------------------------------------------------------ tile loads
-  // INT8 rows: running ring slots of this lane's K row and first V row in
-  // the next tile this wave loads (tiles w, w+kWaves, ... in order). Loads
-  // past the region repeat the wave's last tile (cache hits), so the
-  // pipelined loops below need no conditional loads. 32-bit byte offsets
+  // INT8 rows: running ring slots of this lane's first K row and first V
+  // row in the next tile this wave loads (tiles w, w+kWaves, ... in order;
+  // the slot stops advancing at the wave's last tile). 32-bit byte offsets
   // from the uniform ring base.
   const int last8 = max(nt8 - 1, 0);
   const uint32_t cap = (uint32_t)c.cap;
@@ -336,12 +354,21 @@ void attn_decode_kernel(AttnArgs a) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) vinc[j] = (uint32_t)j % cap;
   int tnext = min(w, last8);  // tile of the next load (uniform)
-  uint32_t sk = (uint32_t)((base8 + 16 * tnext + r16) % c.cap);
+  // 128-byte INT8 K rows are read in lane pairs (see unpair): each
+  // instruction covers whole rows.
+  constexpr bool kpair = KU == 2;
+  const int krow0 = kpair ? (r16 & 7) : r16;
+  const uint32_t kcol = 16 * kg + (kpair ? 64 * (r16 >> 3) : 0);
+  const uint32_t kinc8 = 8u % cap;
+  uint32_t sk = (uint32_t)((base8 + 16 * tnext + krow0) % c.cap);
   uint32_t sv = (uint32_t)((base8 + 16 * tnext + 4 * kg) % c.cap);
   auto load8 = [&](Raw8<D>& r) {
-    const uint32_t ko = sk * D + 16 * kg;
-#pragma unroll
-    for (int uu = 0; uu < KU; ++uu) r.k[uu] = *reinterpret_cast<const u32x4*>(k8 + ko + 64 * uu);
+    if constexpr (kpair) {
+      r.k[0] = stream_load(reinterpret_cast<const u32x4*>(k8 + sk * D + kcol));
+      r.k[1] = stream_load(reinterpret_cast<const u32x4*>(k8 + wrap(sk + kinc8) * D + kcol));
+    } else {  // 64-byte rows: one instruction covers 16 consecutive rows
+      r.k[0] = stream_load(reinterpret_cast<const u32x4*>(k8 + sk * D + kcol));
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t vo = wrap(sv + vinc[j]) * D + (D / 16) * r16;
@@ -432,9 +459,16 @@ void attn_decode_kernel(AttnArgs a) {
     auto tile8 = [&](const Raw8<D>& r, int t) {
       const int i0 = t * 16;
       float4_t s = {0.f, 0.f, 0.f, 0.f};
+      u32x4 kk[KU];
+      if constexpr (kpair) {
+        unpair(r.k[0], r.k[1], r16 < 8, kk[0], kk[1]);
+      } else {
+#pragma unroll
+        for (int uu = 0; uu < KU; ++uu) kk[uu] = r.k[uu];
+      }
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        const u32x4 xw = r.k[kc >> 1] ^ 0x80808080u;
+        const u32x4 xw = kk[kc >> 1] ^ 0x80808080u;
         const int o = 2 * (kc & 1);
         u32x4 hv;
         hv[0] = codes_to_h2(xw[o], kSelLo);
