@@ -56,6 +56,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU time budget of the oracle baseline sample (0 disables it)")
+    ap.add_argument("--read-ceiling-mib", type=int, default=2048,
+                    help="buffer size of the streaming-read ceiling measurement (0 disables it)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the run, one plain device copy of this size (counter scaling)")
     return ap.parse_args()
@@ -105,6 +107,33 @@ def cpu_baseline(cfg, kp, vp, logits0, q0, kn0, vn0, budget_s):
             break
     per_step = t_conf + t_pairs / done * cfg.layers * cfg.batch
     return dict(per_step_s=per_step, pairs=done, threads=threads)
+
+
+def read_ceiling(dev, mib=2048, reps=10):
+    """Streaming-read ceiling: GB/s of the library's read probe (the attention
+    kernel's 16-byte streaming loads, whole lines per instruction) over a
+    seeded random buffer, untimed warm-up then `reps` launches between two
+    events. Outside the timed step loop."""
+    import torch
+    from mixed_precision_attention_amd import engine as E
+    nbytes = mib << 20
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    buf = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device=dev, generator=gen)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        E.read_probe(buf, sink)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
+    a.record(stream)
+    for _ in range(reps):
+        E.read_probe(buf, sink)
+    b.record(stream)
+    torch.cuda.synchronize()
+    gbs = nbytes / (a.elapsed_time(b) / reps * 1e-3) / 1e9
+    del buf
+    return {"value": round(gbs, 1), "unit": "GB/s", "bytes": nbytes, "kernel": "read_probe_kernel",
+            "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 def main():
@@ -229,6 +258,8 @@ def main():
                      "kept_layers_per_depth": kept.sum(axis=0).tolist(), "layers": cfg.layers,
                      "all_kept": bool(kept.all())}
 
+    ceiling = read_ceiling(dev, args.read_ceiling_mib) if args.read_ceiling_mib else None
+
     if args.calib_copy_mib:
         n = args.calib_copy_mib << 20
         src = torch.ones(n, dtype=torch.uint8, device=dev)
@@ -289,6 +320,9 @@ def main():
             "bytes_per_launch": int(attn_bytes),
         },
     }
+    if ceiling is not None:
+        out["read_ceiling"] = ceiling
+        out["roofline"]["frac_of_read_ceiling"] = round(achieved / ceiling["value"], 4)
     if retention is not None:
         out["retention"] = retention
     if args.cpu_seconds > 0:

@@ -1,0 +1,55 @@
+// Streaming-read probe: reads a buffer once with the load form the attention
+// kernel streams its K/V tiles with (16-byte non-temporal loads, whole lines
+// per instruction), so a timed launch gives the read rate HBM sustains for
+// that form on this part. A measurement aid beside the decode step, not a
+// step of it. The words read are folded into one XOR so that the loads stay
+// live and the result can be checked exactly.
+#include "confk_internal.h"
+
+namespace confk {
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;  // independent 16-byte loads in flight per thread
+
+// Block b of the buffer is kProbeBlock contiguous bytes; workgroup g reads
+// blocks g, g + grid, g + 2 grid, ...
+__global__ __launch_bounds__(kThreads) void read_probe_kernel(const u32x4* p, uint64_t nblocks,
+                                                              uint32_t* sink) {
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (uint64_t blk = blockIdx.x; blk < nblocks; blk += gridDim.x) {
+    const u32x4* q = p + blk * (kThreads * kUnroll) + threadIdx.x;
+    u32x4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) v[u] = __builtin_nontemporal_load(q + u * kThreads);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) acc ^= v[u];
+  }
+  uint32_t x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x ^= (uint32_t)__shfl_xor((int)x, off, 64);
+  __shared__ uint32_t red[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t t = 0;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) t ^= red[w];
+    atomicXor(sink, t);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_read_probe(const void* buf, uint64_t bytes, uint32_t* sink, hipStream_t s) {
+  const uint64_t nblocks = bytes / kProbeBlock;
+  // 8 four-wave workgroups per compute unit fill every wave slot
+  const unsigned grid = (unsigned)(nblocks < 2048 ? nblocks : 2048);
+  read_probe_kernel<<<grid, kThreads, 0, s>>>(reinterpret_cast<const u32x4*>(buf), nblocks, sink);
+  return hipGetLastError();
+}
+
+}  // namespace confk

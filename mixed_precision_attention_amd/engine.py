@@ -142,6 +142,14 @@ def quantize(cache, pol, t, mode=L.QUANT_STEP, k_src=None, v_src=None, n_src=0, 
         int(n_src), _stream()))
 
 
+def read_probe(buf, sink):
+    """One streaming read of the device buffer `buf` (a measurement aid);
+    `sink` (device uint32 [1]) is XOR-ed with the XOR of its 32-bit words."""
+    lib = L.load()
+    L.check("confk_read_probe", lib.confk_read_probe(
+        _p(buf), buf.numel() * buf.element_size(), _p(sink), _stream()))
+
+
 def workspace_bytes(which, cache=None, nlayers=0, batch=0, vocab=0):
     lib = L.load()
     ref = cache.ref() if cache is not None else None
