@@ -58,6 +58,9 @@ def parse():
                     help="CPU time budget of the oracle baseline sample (0 disables it)")
     ap.add_argument("--read-ceiling-mib", type=int, default=2048,
                     help="buffer size of the streaming-read ceiling measurement (0 disables it)")
+    ap.add_argument("--cpu-full", action="store_true",
+                    help="time the oracle over every step of the run instead of a first-step sample "
+                         "(small configs)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the run, one plain device copy of this size (counter scaling)")
     return ap.parse_args()
@@ -107,6 +110,29 @@ def cpu_baseline(cfg, kp, vp, logits0, q0, kn0, vn0, budget_s):
             break
     per_step = t_conf + t_pairs / done * cfg.layers * cfg.batch
     return dict(per_step_s=per_step, pairs=done, threads=threads)
+
+
+def cpu_full(cfg, kp, vp, inputs):
+    """Oracle (fp64 numpy) over every step of the run from the prefill, on the
+    same inputs (for the small configs, where it finishes in seconds). Host
+    copies of the inputs are made before the clock starts."""
+    import numpy as np
+    from oracle import confk_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    pol = cfg.policy
+    host = [(lg.cpu().numpy(), q.cpu().numpy(), kn.cpu().numpy(), vn.cpu().numpy(), t)
+            for lg, q, kn, vn, t in inputs]
+    lb = (np.asarray(cfg.layer_n_low), np.asarray(cfg.layer_n_high)) if cfg.layer_n_low else None
+    caches = [[O.prefill(kp[l, b].cpu().numpy(), vp[l, b].cpu().numpy(), pol.window) if cfg.prefill
+               else O.empty_cache(cfg.hkv, cfg.d) for b in range(cfg.batch)] for l in range(cfg.layers)]
+    t0 = time.perf_counter()
+    for lg, q, kn, vn, t in host:
+        caches = O.step(caches, lg, q, kn, vn, t, pol, layer_budgets=lb).caches
+    return dict(seconds=time.perf_counter() - t0, threads=threads)
 
 
 def read_ceiling(dev, mib=2048, reps=10):
@@ -316,7 +342,8 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": counted_traffic(cfg.name),
-            "kernel": "attn_decode_kernel<128, false, false>" if full else "attn_decode_kernel<128, false, true>",
+            "kernel": (f"attn_decode_kernel<{cfg.d}, {'true' if eng.attn_ws is not None and not full else 'false'}, "
+                       f"{'false' if full else 'true'}>"),
             "bytes_per_launch": int(attn_bytes),
         },
     }
@@ -325,7 +352,17 @@ def main():
         out["roofline"]["frac_of_read_ceiling"] = round(achieved / ceiling["value"], 4)
     if retention is not None:
         out["retention"] = retention
-    if args.cpu_seconds > 0:
+    if args.cpu_full:
+        cf = cpu_full(cfg, kp, vp, inputs)
+        out["cpu_baseline"] = {
+            "value": round(sum(p["total"] for p in per_step) / cf["seconds"] / 1e9, 4),
+            "unit": "GB/s",
+            "cores": cf["threads"],
+            "kind": "oracle",
+            "sample": f"all {len(inputs)} steps of the run from the prefill, every (layer, sequence)",
+            "steps_per_s": round(len(inputs) / cf["seconds"], 3),
+        }
+    elif args.cpu_seconds > 0:
         lg0, q0, kn0, vn0, _ = inputs[0]
         cb = cpu_baseline(cfg, kp, vp, lg0.cpu().numpy(), q0.cpu().numpy(), kn0.cpu().numpy(),
                           vn0.cpu().numpy(), args.cpu_seconds)
