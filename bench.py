@@ -183,7 +183,7 @@ def main():
     K, Wm = args.steps, args.warmup
     S = K + Wm
 
-    eng = M.DecodeEngine(cfg, dev)
+    eng = M.DecodeEngine(cfg, dev, overlap=True)  # confidence on a second stream, beside attention
     kp, vp = synth.gen.prefill_kv_device(cfg, args.seed, dev)
     inputs = []
     for s in range(S):

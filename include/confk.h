@@ -291,12 +291,12 @@ size_t confk_workspace_size(int32_t which, const confk_cache* cache, int32_t nla
  * the streaming-read rate HBM sustains for that load form (the ceiling the
  * attention kernel is compared with, beside the 8 TB/s peak).
  *   buf    device, 16-byte aligned, read only
- *   bytes  a positive multiple of 16384
+ *   bytes  a positive multiple of 65536
  *   sink   device uint32 [1]: XOR-ed (atomically) with the XOR of every
  *          little-endian 32-bit word of the buffer; a zeroed sink ends up
  *          holding that checksum
  * Errors: CONFK_ERR_INVALID_ARG for a null pointer, a misaligned buffer or a
- * size that is not a positive multiple of 16384.
+ * size that is not a positive multiple of 65536.
  */
 int confk_read_probe(const void* buf, uint64_t bytes, uint32_t* sink, void* stream);
 

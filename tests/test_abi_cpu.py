@@ -167,10 +167,10 @@ def test_binding_raises_on_error_code():
 
 def test_read_probe_validation(lib):
     addr = FAKE.value
-    r = lambda buf=addr, nbytes=16384, sink=FAKE: lib.confk_read_probe(  # noqa: E731
+    r = lambda buf=addr, nbytes=65536, sink=FAKE: lib.confk_read_probe(  # noqa: E731
         ctypes.c_void_p(buf), nbytes, sink, None)
     assert r(buf=None) == M.ERR_INVALID_ARG
     assert r(nbytes=0) == M.ERR_INVALID_ARG
-    assert r(nbytes=16384 + 4096) == M.ERR_INVALID_ARG   # not a whole number of blocks
+    assert r(nbytes=65536 + 16384) == M.ERR_INVALID_ARG  # not a whole number of blocks
     assert r(buf=addr + 4) == M.ERR_INVALID_ARG          # not 16-byte aligned
     assert r(sink=None) == M.ERR_INVALID_ARG

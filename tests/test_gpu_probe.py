@@ -8,7 +8,7 @@ import torch
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("nbytes", [16384 * 3, 64 << 20])
+@pytest.mark.parametrize("nbytes", [65536 * 3, 64 << 20])
 def test_read_probe_checksum(nbytes):
     assert torch.cuda.is_available(), "GPU tests need a GPU"
     from mixed_precision_attention_amd import engine as E
