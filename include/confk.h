@@ -248,12 +248,18 @@ int confk_compact(const confk_cache* cache, int32_t layer0, int32_t nlayers, con
  * callers that inspect or replace the scores in between.
  *   mass   as for confk_ema_rank; t >= 0 the new token's position
  *   score  fp32 [nlayers][B][cap], written
+ *   flags  0, or CONFK_FUSE_QUANTIZE: then confk_quantize's window step
+ *          (CONFK_QUANT_STEP, same t and layers) follows the append, bit for
+ *          bit as the separate call would do it: in the same kernel under
+ *          token eviction, as one more launch under block eviction (whose
+ *          rows move in a second kernel). Other bits: CONFK_ERR_INVALID_ARG.
  *   other arguments as for confk_compact
  */
+#define CONFK_FUSE_QUANTIZE 1
 int confk_ema_compact(const confk_cache* cache, int32_t layer0, int32_t nlayers, const float* mass,
                       const confk_policy* pol, int32_t t, float* score, const int32_t* budget,
                       int32_t budget_layer_stride, const uint16_t* k_new, const uint16_t* v_new,
-                      int32_t* evicted_out, void* ws, size_t ws_bytes, void* stream);
+                      int32_t* evicted_out, int32_t flags, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * confk_quantize -- FP16 -> INT8 storage per (head, channel).

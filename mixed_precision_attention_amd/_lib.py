@@ -27,6 +27,7 @@ META_WORDS = 16
 
 QUANT_STEP = 0
 QUANT_PREFILL = 1
+FUSE_QUANTIZE = 1
 WS_CONFIDENCE = 0
 WS_ATTENTION = 1
 WS_COMPACT = 2
@@ -89,8 +90,8 @@ def load():
     lib.confk_quantize.argtypes = [P(Cache), c_int32, c_int32, c_int32, P(Policy), c_int32,
                                    c_void_p, c_void_p, c_int32, c_void_p]
     lib.confk_ema_compact.argtypes = [P(Cache), c_int32, c_int32, c_void_p, P(Policy), c_int32, c_void_p,
-                                      c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
-                                      c_void_p]
+                                      c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_int32, c_void_p,
+                                      c_size_t, c_void_p]
     lib.confk_read_probe.argtypes = [c_void_p, ctypes.c_uint64, c_void_p, c_void_p]
     lib.confk_workspace_size.argtypes = [c_int32, P(Cache), c_int32, c_int32, c_int32]
     lib.confk_workspace_size.restype = c_size_t

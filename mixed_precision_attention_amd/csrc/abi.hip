@@ -203,8 +203,8 @@ int confk_compact(const confk_cache* cache, int32_t layer0, int32_t nlayers, con
 int confk_ema_compact(const confk_cache* cache, int32_t layer0, int32_t nlayers, const float* mass,
                       const confk_policy* pol, int32_t t, float* score, const int32_t* budget,
                       int32_t budget_layer_stride, const uint16_t* k_new, const uint16_t* v_new,
-                      int32_t* evicted_out, void* ws, size_t ws_bytes, void* stream) {
-  if (!mass || t < 0) return CONFK_ERR_INVALID_ARG;
+                      int32_t* evicted_out, int32_t flags, void* ws, size_t ws_bytes, void* stream) {
+  if (!mass || t < 0 || (flags & ~CONFK_FUSE_QUANTIZE) != 0) return CONFK_ERR_INVALID_ARG;
   CompactArgs a;
   const int e = compact_args(cache, layer0, nlayers, budget, budget_layer_stride, score, pol, k_new, v_new,
                              evicted_out, ws, ws_bytes, a);
@@ -215,6 +215,8 @@ int confk_ema_compact(const confk_cache* cache, int32_t layer0, int32_t nlayers,
   a.alpha = pol->alpha;
   a.mass = mass;
   a.score_out = score;
+  a.quantize = (flags & CONFK_FUSE_QUANTIZE) ? 1 : 0;
+  a.window = pol->window;
   return launch_status(launch_compact(a, (hipStream_t)stream));
 }
 

@@ -37,7 +37,7 @@
 // is written to the FP16 ring.
 #include <type_traits>
 
-#include "confk_internal.h"
+#include "quantize_seq.h"
 
 namespace confk {
 
@@ -242,6 +242,17 @@ __global__ __launch_bounds__(kThreads) void compact_plan_kernel(CompactArgs a) {
     }
   };
 
+  // Fused form with the window step: once the cache holds the step's
+  // survivors and the new token, the FP16 tokens at positions <= t - W move
+  // to INT8 in this workgroup, as the quantisation kernel would do next.
+  auto quantize_tail = [&](int n_after, int n8_after, int base16_after) {
+    if (!a.quantize) return;  // uniform (a kernel argument)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // the rows, positions and metadata written above are visible
+    quantize_window<kThreads>(c, lbc, a.t, a.window, n_after, n8_after, base8, base16_after,
+                              meta[CONFK_META_CALIB]);
+  };
+
   const int nn = n + 1;  // tokens incl. the new one
   const int f = n - n8;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -416,6 +427,7 @@ __global__ __launch_bounds__(kThreads) void compact_plan_kernel(CompactArgs a) {
       meta[CONFK_META_MOVED16] = 0;
       if (a.evicted_out) a.evicted_out[lb] = 0;
     }
+    if constexpr (FUSE && !BLOCK) quantize_tail(nn, n8, base16);
     return;
   }
 
@@ -958,6 +970,7 @@ __global__ __launch_bounds__(kThreads) void compact_plan_kernel(CompactArgs a) {
       meta[CONFK_META_MOVED16] = mv16;
       if (a.evicted_out) a.evicted_out[lb] = k;
     }
+    if constexpr (FUSE) quantize_tail(nkeep, m8, b16);
   }
 }
 
@@ -1106,7 +1119,16 @@ hipError_t launch_compact_t(const CompactArgs& a, hipStream_t s) {
   } else {
     hipLaunchKernelGGL(compact_move_kernel<64>, mgrid, mblock, 0, s, a);
   }
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (e != hipSuccess || !a.quantize) return e;
+  // block eviction moves its rows in the move kernel: the window step follows it
+  QuantArgs q{};
+  q.c = a.c;
+  q.layer0 = a.layer0;
+  q.nl = a.nl;
+  q.t = a.t;
+  q.window = a.window;
+  return launch_quantize_step(q, s);
 }
 
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {

@@ -90,6 +90,8 @@ struct CompactArgs {
   float lambda, alpha;
   const float* mass;
   float* score_out;
+  // fused form with the window step (token eviction: in the same kernel)
+  int32_t quantize, window;
 };
 
 struct QuantArgs {

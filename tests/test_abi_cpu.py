@@ -140,9 +140,12 @@ def test_compact_quantize_ema_validation(lib):
     wbig = lib.confk_workspace_size(M._lib.WS_COMPACT, ctypes.byref(big), 2, 0, 0)
     assert cp(big, _pol(block=16), n=wbig) == M.ERR_UNSUPPORTED
     # the fused EMA + compaction call validates like the two calls it replaces
-    ec = lambda cc, p, mass=FAKE, t=5, ws=FAKE, n=wsb: lib.confk_ema_compact(  # noqa: E731
-        ctypes.byref(cc), 0, 2, mass, ctypes.byref(p), t, FAKE, FAKE, 0, FAKE, FAKE, None, ws, n, None)
+    ec = lambda cc, p, mass=FAKE, t=5, ws=FAKE, n=wsb, flags=0: lib.confk_ema_compact(  # noqa: E731
+        ctypes.byref(cc), 0, 2, mass, ctypes.byref(p), t, FAKE, FAKE, 0, FAKE, FAKE, None, flags, ws, n, None)
     assert ec(c, _pol(), mass=None) == M.ERR_INVALID_ARG
+    assert ec(c, _pol(), flags=2) == M.ERR_INVALID_ARG      # unknown flag bit
+    assert ec(c, _pol(), flags=-1) == M.ERR_INVALID_ARG
+    assert ec(c, _pol(), flags=M._lib.FUSE_QUANTIZE, ws=None) == M.ERR_WORKSPACE
     assert ec(c, _pol(), t=-1) == M.ERR_INVALID_ARG
     assert ec(c, _pol(), ws=None) == M.ERR_WORKSPACE
     assert ec(c, _pol(protect=30)) == M.ERR_BUDGET

@@ -427,19 +427,38 @@ def test_many_movers_in_both_rings(d):
             assert moved8 > 200 and moved16 > 64, (moved8, moved16)
 
 
-def test_overlapped_step_matches_serial():
-    """DecodeEngine.step (confidence on a second stream, EMA and compaction in
-    one fused call) leaves exactly the state of the five calls issued one
-    after another on one stream. EMA and position slots past the new length
-    (evicted tokens) are not part of the state: the fused call leaves them."""
+FUSED_CASES = {
+    "g5_d128": lambda: TINY["g5_d128"],
+    # empty start: the window step calibrates the scales inside the fused kernel
+    "g3_d64_empty": lambda: TINY["g3_d64_empty"],
+    # block eviction: the window step is a third launch after the move kernel
+    "g5_d128_block16": lambda: _block_cfg(TINY["g5_d128"], 16),
+    # more than 4096 slots: the long-cache plan form
+    "long_cache": lambda: _cfg("long_cache", 1, 2, 4, 2, 64, 300, 4200, 1500, 3000, 16, 64),
+}
+
+
+@pytest.mark.parametrize("case", list(FUSED_CASES))
+def test_overlapped_step_matches_serial(case):
+    """DecodeEngine.step (confidence on a second stream, EMA, compaction and
+    the window step in one fused call) leaves exactly the state of the five
+    calls issued one after another on one stream. EMA and position slots past
+    the new length (evicted tokens) are not part of the state: the fused call
+    leaves them."""
     import mixed_precision_attention_amd as M
     dev = _dev()
-    cfg = TINY["g5_d128"]
-    kp, vp = synth.prefill_kv(cfg, 3)
+    cfg = FUSED_CASES[case]()
     engs = [M.DecodeEngine(cfg, dev, overlap=True), M.DecodeEngine(cfg, dev, overlap=False)]
-    for e in engs:
-        e.prefill(_t(kp, dev), _t(vp, dev))
-    for i in range(20):
+    if cfg.prefill:
+        kp, vp = synth.prefill_kv(cfg, 3)
+        for e in engs:
+            e.prefill(_t(kp, dev), _t(vp, dev))
+    else:
+        for e in engs:
+            e.prefill(None, None)
+    steps = 20 if cfg.prefill else cfg.policy.window + 24  # past the first calibration
+    quantised = 0
+    for i in range(steps):
         logits, q, kn, vn, t = _inputs(cfg, 3, i)
         lg, qd, kd, vd = _t(logits, dev), _t(q, dev), _t(kn, dev), _t(vn, dev)
         engs[0].step(lg, qd, kd, vd, t)
@@ -448,8 +467,11 @@ def test_overlapped_step_matches_serial():
         e.step_attention(qd, kd, vd)
         e.step_ema_rank(t)
         e.step_compact(kd, vd)
+        n8 = e.cache.meta[..., M.META_N8].clone()
         e.step_quantize(t)
+        quantised += int((e.cache.meta[..., M.META_N8] > n8).sum())
     torch.cuda.synchronize()
+    assert quantised > 0  # the window step moved tokens
     a, b = engs
     for name in ("meta", "k8", "v8", "k16", "v16", "kscale", "vscale", "status"):
         assert torch.equal(getattr(a.cache, name), getattr(b.cache, name)), name
