@@ -591,7 +591,7 @@ void attn_decode_kernel(AttnArgs a) {
     wl[w][r16] = lt;
   }
   __syncthreads();
-  if (threadIdx.x < g) {
+  if ((int)threadIdx.x < g) {
     const int hh = threadIdx.x;
     float M = -INFINITY;
     for (int q = 0; q < kWaves; ++q) M = fmaxf(M, wm[q][hh]);
