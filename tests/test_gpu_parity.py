@@ -170,6 +170,32 @@ def test_parity_tiny(name):
     assert run.band <= 1
 
 
+def test_parity_gpt2_layer_workload():
+    """The GPT-2 single-layer workload as configured (a 1024-token cache, the
+    newest 64 FP16, 64 decode steps), free-running against the oracle."""
+    cfg = synth.get_config("gpt2_layer")
+    print(f"[parity] gpt2_layer steps={cfg.steps}", flush=True)
+    run = Run(cfg, seed=0)
+    events = sum(run.step(i) for i in range(cfg.steps))
+    assert events > 0
+    assert run.band <= 1
+
+
+def test_parity_gpt2_stack_from_empty():
+    """The GPT-2 stack workload (12 layers from an empty cache, four sink
+    keys): past the first calibration at step W and through repeated
+    evictions, on three sampled layers."""
+    cfg = synth.get_config("gpt2_stack")
+    steps = 600
+    print(f"[parity] gpt2_stack steps={steps}", flush=True)
+    run = Run(cfg, seed=0, pairs=[(0, 0), (5, 0), (11, 0)])
+    events = sum(run.step(i) for i in range(steps))
+    n, n8 = run.eng.cache.lengths()
+    assert events > 0
+    assert (n8 > 0).all()  # the INT8 region was calibrated and populated
+    assert run.band <= 2
+
+
 def test_parity_pyramid_budgets():
     lo = (60, 52, 44)
     hi = tuple(x // 2 for x in lo)
