@@ -205,8 +205,11 @@ __device__ uint32_t radix_select(int& kk, int cnt, Part part, Val val, Shared& s
 
 // FUSE: the EMA update and rank scores of ema_rank_kernel run first, in this
 // kernel, with the same arithmetic and summation order (bit-identical).
+// REG: the form for a cache of at most kRegKeys * kThreads tokens with the
+// new one (keys and fill lists in registers and LDS); the long form stages
+// through the workspace.
 template <bool REG, bool BLOCK, bool FUSE>
-__global__ __launch_bounds__(kThreads) void compact_plan_kernel(CompactArgs a) {
+__device__ __forceinline__ void plan_body(const CompactArgs& a) {
   const CacheView& c = a.c;
   const int lb = blockIdx.x;
   const int l = lb / c.B;
@@ -974,6 +977,24 @@ __global__ __launch_bounds__(kThreads) void compact_plan_kernel(CompactArgs a) {
   }
 }
 
+// One workgroup per (layer, sequence). SHORTCAP: the capacity itself fits the
+// register form. Otherwise each workgroup takes the register form when its
+// own cache (with the new token) fits and the long form when it does not, so
+// a long-capacity cache pays for the long form only while it is long.
+template <bool SHORTCAP, bool BLOCK, bool FUSE>
+__global__ __launch_bounds__(kThreads) void compact_plan_kernel(CompactArgs a) {
+  if constexpr (SHORTCAP) {
+    plan_body<true, BLOCK, FUSE>(a);
+  } else {
+    const int lb = blockIdx.x, l = lb / a.c.B, b = lb - l * a.c.B;
+    const int n = a.c.meta[((a.layer0 + l) * a.c.B + b) * CONFK_META_WORDS + CONFK_META_N];
+    if (n + 1 <= kRegKeys * kThreads)  // uniform; a corrupt length is flagged by either form
+      plan_body<true, BLOCK, FUSE>(a);
+    else
+      plan_body<false, BLOCK, FUSE>(a);
+  }
+}
+
 template <int D, int LGP, int NW, int NR>
 __device__ __forceinline__ void ring_rounds(unsigned char* ring, int C, int movers, int left, int e, int jlo,
                                             int base, const int32_t* src, int* sv, bool have) {
@@ -1099,7 +1120,7 @@ size_t compact_plan_bytes(int nlayers, int batch, int cap) {
 template <bool FUSE>
 hipError_t launch_compact_t(const CompactArgs& a, hipStream_t s) {
   const int blocks = a.nl * a.c.B;
-  const bool reg = a.c.cap <= kRegKeys * kThreads;
+  const bool reg = a.c.cap <= kRegKeys * kThreads;  // every cache fits the register form
   if (a.block == 0) {  // token eviction: one kernel plans, fills, packs and appends
     if (reg)
       hipLaunchKernelGGL((compact_plan_kernel<true, false, FUSE>), dim3(blocks), dim3(kThreads), 0, s, a);
