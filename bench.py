@@ -50,7 +50,8 @@ def counted_traffic(workload):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: the workload's generated tokens minus the warmup)")
     ap.add_argument("--warmup", type=int, default=48)
     ap.add_argument("--config", default="qwen32b")
     ap.add_argument("--seed", type=int, default=0)
@@ -180,7 +181,8 @@ def main():
     dev = torch.device("cuda:0")
     cfg = synth.get_config(args.config)
     pol = cfg.policy
-    K, Wm = args.steps, args.warmup
+    Wm = args.warmup
+    K = args.steps if args.steps is not None else max(1, cfg.steps - Wm)
     S = K + Wm
 
     eng = M.DecodeEngine(cfg, dev, overlap=True)  # confidence on a second stream, beside attention
