@@ -97,8 +97,9 @@ def cpu_baseline(cfg, kp, vp, logits0, q0, kn0, vn0, budget_s):
     t0 = time.perf_counter()
     cs = [O.confidence(logits0[b])[0] for b in range(cfg.batch)]
     t_conf = time.perf_counter() - t0
-    rng = np.random.default_rng(0)
-    pairs = [(int(l), int(b)) for l, b in zip(rng.integers(0, cfg.layers, 64), rng.integers(0, cfg.batch, 64))]
+    # (layer, sequence) pairs in a seeded order, as many as the budget allows
+    order = np.random.default_rng(0).permutation(cfg.layers * cfg.batch)
+    pairs = [(int(i) // cfg.batch, int(i) % cfg.batch) for i in order]
     done, t_pairs = 0, 0.0
     for (l, b) in pairs:
         c = O.prefill(kp[l, b].cpu().numpy(), vp[l, b].cpu().numpy(), pol.window)
@@ -374,9 +375,12 @@ def main():
             "unit": "GB/s",
             "cores": cb["threads"],
             "kind": "oracle",
-            "sample": f"first decode step after the prefill: confidence of all {cfg.batch} rows plus "
-                      f"{cb['pairs']} of {cfg.layers * cfg.batch} (layer, sequence) pairs, "
-                      f"extrapolated to the whole step",
+            "sample": (f"the whole first decode step after the prefill: confidence of all {cfg.batch} rows "
+                       f"and all {cb['pairs']} (layer, sequence) pairs"
+                       if cb["pairs"] == cfg.layers * cfg.batch else
+                       f"first decode step after the prefill: confidence of all {cfg.batch} rows plus "
+                       f"{cb['pairs']} of {cfg.layers * cfg.batch} (layer, sequence) pairs, "
+                       f"extrapolated to the whole step"),
             "steps_per_s": round(1.0 / cb["per_step_s"], 5),
         }
     print(json.dumps(out), flush=True)
