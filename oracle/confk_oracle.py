@@ -30,7 +30,7 @@ Where the pages are silent the oracle takes one reading; every reading is
 named in a comment as "Reading:" and listed with the design notes.
 
 Precision: everything is fp64 except the INT8 quantiser, whose scale and
-quotient are IEEE fp32 by definition of the stored format (reading Q1).
+quotient are IEEE fp32 by definition of the stored format (reading R16).
 """
 from dataclasses import dataclass, field
 import math
@@ -204,7 +204,7 @@ def attention(q, cache, k_new, v_new):
 
 def ema_update(ema, mass, lam):
     """a_i <- lam*a_i + (1-lam)*Abar_i for the cached tokens; the new token
-    starts from a zero prior under the same rule (reading E1).
+    starts from a zero prior under the same rule (reading R8).
     Returns (a' [n], a_new)."""
     ema = np.asarray(ema, np.float64)
     n = ema.shape[0]
@@ -326,7 +326,7 @@ def append(cache, k_new, v_new, t, a_new):
 def absmax_scale(x):
     """Per-(kv-head, channel) symmetric scale of rows x [m, Hkv, d].
 
-    Reading Q1: scale = fp32(absmax) / 127 with the IEEE fp32 quotient.
+    Reading R16: scale = fp32(absmax) / 127 with the IEEE fp32 quotient.
     """
     amax = np.abs(np.asarray(x, np.float32)).max(axis=0)
     return (amax.astype(np.float32) / np.float32(127.0)).astype(np.float32)
@@ -349,7 +349,7 @@ def quantize_rows(x, scale):
 
 
 def calibrate(cache):
-    """Reading Q2: scales are set once per (layer, sequence, K|V, kv-head,
+    """Reading R17: scales are set once per (layer, sequence, K|V, kv-head,
     channel) when the INT8 region is first populated, over every token then
     in the cache (all FP16 at that moment), and frozen afterwards."""
     c = cache.copy()
@@ -363,7 +363,7 @@ def calibrate(cache):
 def quantize_window(cache, t, W):
     """Move retained FP16 tokens that left the FP16 window to INT8.
 
-    Reading Q3: after step t the FP16 window is positions t-W+1 .. t, so
+    Reading R15: after step t the FP16 window is positions t-W+1 .. t, so
     every FP16 token with pos <= t - W is quantised (at most one per step in
     steady state, exactly once per token).
     """
@@ -388,7 +388,7 @@ def quantize_window(cache, t, W):
 def prefill(k, v, W):
     """Cache after a prefill of L0 tokens: positions 0..L0-1, EMA 0, scales
     calibrated over all L0 tokens when any token is older than the window,
-    INT8 for pos <= L0-1-W and FP16 for the newest W (reading Q2, Q3).
+    INT8 for pos <= L0-1-W and FP16 for the newest W (readings R17, R15).
 
     k, v: [Hkv, L0, d] fp16 for one (layer, sequence).
     """
@@ -428,7 +428,7 @@ def step_one(cache, q, k_new, v_new, t, pol, N, score_given=None):
 
     Returns dict(o, mass, ema, a_new, score, keep, cache) where ema is the
     updated EMA of the cached tokens and cache the state after the step.
-    Order (reading S1): attention over C plus the new token; EMA update;
+    Order (reading R18): attention over C plus the new token; EMA update;
     rank; evict and compact; append the new token; quantise tokens that left
     the FP16 window. score_given replaces the computed scores in the
     selection (lock-step comparison on identical inputs).
