@@ -123,14 +123,14 @@ def compact(cache, budget, budget_stride, score, pol, k_new, v_new, ws, evicted=
 
 
 def ema_compact(cache, mass, pol, t, score, budget, budget_stride, k_new, v_new, ws, evicted=None,
-                layer0=0, nlayers=None, quantize=False):
+                layer0=0, nlayers=None, fuse_quantize=False):
     """confk_ema_compact: ema_rank and compact in one launch (and, with
-    quantize, the window step of quantize after the append)."""
+    fuse_quantize, the window step of quantize after the append)."""
     lib = L.load()
     nl = cache.layers - layer0 if nlayers is None else nlayers
     L.check("confk_ema_compact", lib.confk_ema_compact(
         cache.ref(), layer0, nl, _p(mass), ctypes.byref(pol), int(t), _p(score), _p(budget),
-        int(budget_stride), _p(k_new), _p(v_new), _p(evicted), L.FUSE_QUANTIZE if quantize else 0, _p(ws),
+        int(budget_stride), _p(k_new), _p(v_new), _p(evicted), L.FUSE_QUANTIZE if fuse_quantize else 0, _p(ws),
         ws.numel() * ws.element_size(), _stream()))
 
 
@@ -222,12 +222,12 @@ class DecodeEngine:
         compact(self.cache, self.budget, self.budget_stride, self.score, self.pol, k_new, v_new,
                 self.compact_ws, self.evicted)
 
-    def step_ema_compact(self, t, k_new, v_new, quantize=False):
+    def step_ema_compact(self, t, k_new, v_new, fuse_quantize=False):
         """EMA, rank scores and compaction in one launch (same state as
-        step_ema_rank followed by step_compact; with quantize, also as
+        step_ema_rank followed by step_compact; with fuse_quantize, also as
         step_quantize after them)."""
         ema_compact(self.cache, self.mass, self.pol, t, self.score, self.budget, self.budget_stride,
-                    k_new, v_new, self.compact_ws, self.evicted, quantize=quantize)
+                    k_new, v_new, self.compact_ws, self.evicted, fuse_quantize=fuse_quantize)
 
     def step_quantize(self, t):
         quantize(self.cache, self.pol, t)
@@ -250,4 +250,4 @@ class DecodeEngine:
         self.step_attention(q, k_new, v_new)
         if self.side is not None:
             torch.cuda.current_stream().wait_event(self.conf_done)
-        self.step_ema_compact(t, k_new, v_new, quantize=True)
+        self.step_ema_compact(t, k_new, v_new, fuse_quantize=True)
