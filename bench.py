@@ -323,7 +323,8 @@ def main():
                         f"batch {cfg.batch}, {cfg.prefill}-token prefill, V={cfg.vocab}, "
                         f"N_high/N_low={pol.n_high}/{pol.n_low}, P={pol.protect}, W={pol.window}, "
                         f"alpha={pol.alpha}" + (", full FP16 cache (comparison run)" if full else "")
-                        + (f", block eviction B={pol.block}" if pol.block else ""),
+                        + (f", block eviction B={pol.block}" if pol.block else "")
+                        + (", stable survivor order" if getattr(pol, "order", 0) and not pol.block else ""),
             "layers": cfg.layers, "batch": cfg.batch, "hq": cfg.hq, "hkv": cfg.hkv, "d": cfg.d,
             "prefill": cfg.prefill, "vocab": cfg.vocab, "parallelism": "single GPU",
         },

@@ -91,10 +91,20 @@ extern "C" {
  * grouped into blocks of B from the oldest (a trailing partial block is kept),
  * a block ranks by the largest score of its tokens, and the ceil((n-N)/B)
  * lowest-ranked blocks leave (the older block first among equals).
+ * order: the order of the survivors inside the compacted cache under token
+ * eviction (the pages ask for a dense layout without indirection tables and
+ * fix no order). CONFK_ORDER_FILL (0): the surviving INT8 tokens at or beyond
+ * the new INT8 length fill the INT8 holes below it, in slot order (the
+ * fewest row moves, one kernel; needs protect <= window). CONFK_ORDER_STABLE
+ * (1): both parts keep position order (a stable gather, packed toward
+ * whichever end of each ring moves fewer rows; a second kernel moves the
+ * rows). Block eviction always packs stably and ignores this field.
  */
+#define CONFK_ORDER_FILL 0
+#define CONFK_ORDER_STABLE 1
 typedef struct confk_policy {
   float tau, alpha, lambda, w_h, w_m, w_p;
-  int32_t n_high, n_low, protect, window, block;
+  int32_t n_high, n_low, protect, window, block, order;
 } confk_policy;
 
 /*
@@ -215,10 +225,11 @@ int confk_ema_rank(const confk_cache* cache, int32_t layer0, int32_t nlayers, co
  * newest `protect` tokens are evicted and the survivors are packed densely;
  * the new token (slot n metadata from confk_ema_rank, K/V from k_new/v_new)
  * is appended as FP16. The FP16 part keeps position order, packed toward
- * whichever end moves fewer rows. The INT8 part: with token eviction, the
- * surviving INT8 tokens at or beyond its new length fill the holes below it,
- * in slot order (the fewest moves; the INT8 part is then no longer in
- * position order); with block eviction it is packed like the FP16 part.
+ * whichever end moves fewer rows. The INT8 part: with token eviction and
+ * pol->order = CONFK_ORDER_FILL, the surviving INT8 tokens at or beyond its
+ * new length fill the holes below it, in slot order (the fewest moves; the
+ * INT8 part is then no longer in position order); with CONFK_ORDER_STABLE or
+ * block eviction it is packed like the FP16 part.
  *   budget       int32, entry for (l, b) at budget[l * budget_layer_stride + b]
  *                (stride 0: one budget per sequence; stride B: per layer)
  *   score        fp32 [nlayers][B][cap] from confk_ema_rank
@@ -231,7 +242,7 @@ int confk_ema_rank(const confk_cache* cache, int32_t layer0, int32_t nlayers, co
  * Sets CONFK_STATUS_CAPACITY (and skips the append) if a sequence has no
  * free slot. Errors: INVALID_ARG, BUDGET (protect > n_low or > n_high,
  * capacity below n_low + 2, FP16 ring below window + 1, protect > window
- * with token eviction), UNSUPPORTED (more than 512 blocks per sequence;
+ * with token eviction in the fill order), UNSUPPORTED (more than 512 blocks per sequence;
  * block eviction with d other than 64 or 128), WORKSPACE.
  */
 int confk_compact(const confk_cache* cache, int32_t layer0, int32_t nlayers, const int32_t* budget,

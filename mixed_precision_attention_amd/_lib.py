@@ -28,6 +28,8 @@ META_WORDS = 16
 QUANT_STEP = 0
 QUANT_PREFILL = 1
 FUSE_QUANTIZE = 1
+ORDER_FILL = 0
+ORDER_STABLE = 1
 WS_CONFIDENCE = 0
 WS_ATTENTION = 1
 WS_COMPACT = 2
@@ -44,7 +46,7 @@ class Policy(ctypes.Structure):
         ("tau", c_float), ("alpha", c_float), ("lambda_", c_float),
         ("w_h", c_float), ("w_m", c_float), ("w_p", c_float),
         ("n_high", c_int32), ("n_low", c_int32), ("protect", c_int32), ("window", c_int32),
-        ("block", c_int32),
+        ("block", c_int32), ("order", c_int32),
     ]
 
 

@@ -27,6 +27,7 @@ bool policy_ok(const confk_policy* p) {
   if (p->n_high < 1 || p->n_low < 1 || p->protect < 0 || p->window < 1) return false;
   if (!(p->lambda >= 0.f && p->lambda <= 1.f) || !(p->alpha >= 0.f && p->alpha <= 1.f)) return false;
   if (p->block != 0 && p->block < 16) return false;
+  if (p->order != CONFK_ORDER_FILL && p->order != CONFK_ORDER_STABLE) return false;
   return true;
 }
 
@@ -166,7 +167,7 @@ int compact_args(const confk_cache* cache, int32_t layer0, int32_t nlayers, cons
   if (pol->n_low + 1 > cache->cap - 1 || pol->n_high + 1 > cache->cap - 1) return CONFK_ERR_BUDGET;
   if (pol->window + 1 > cache->cap16) return CONFK_ERR_BUDGET;
   // token eviction reorders the INT8 part: the newest P tokens must be FP16
-  if (pol->block == 0 && pol->protect > pol->window) return CONFK_ERR_BUDGET;
+  if (pol->block == 0 && pol->order == CONFK_ORDER_FILL && pol->protect > pol->window) return CONFK_ERR_BUDGET;
   if (pol->block > 0 && cache->cap / pol->block > kMaxEvictBlocks) return CONFK_ERR_UNSUPPORTED;
   if (pol->block > 0 && cache->d != 64 && cache->d != 128) return CONFK_ERR_UNSUPPORTED;
   const size_t need = compact_ws_bytes(nlayers, cache->batch, cache->cap);
@@ -180,6 +181,7 @@ int compact_args(const confk_cache* cache, int32_t layer0, int32_t nlayers, cons
   a.budget_stride = budget_layer_stride;
   a.protect = pol->protect;
   a.block = pol->block;
+  a.stable = pol->block == 0 && pol->order == CONFK_ORDER_STABLE;
   a.budget = budget;
   a.score = score;
   a.k_new = k_new;

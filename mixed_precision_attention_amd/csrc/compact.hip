@@ -46,6 +46,9 @@ namespace {
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 constexpr int kRegKeys = 8;    // indices per thread held in registers
+// plan kernel modes: token eviction with INT8 hole filling, token eviction
+// with stable packing, block eviction (stable packing)
+constexpr int kFill = 0, kStable = 1, kBlock = 2;
 constexpr int kBuckets = 1024;
 constexpr int kRankMax = 64;   // boundary-bucket keys ranked by one wave
 constexpr int kHdr = 16;       // plan header words per (layer, sequence)
@@ -208,8 +211,13 @@ __device__ uint32_t radix_select(int& kk, int cnt, Part part, Val val, Shared& s
 // REG: the form for a cache of at most kRegKeys * kThreads tokens with the
 // new one (keys and fill lists in registers and LDS); the long form stages
 // through the workspace.
-template <bool REG, bool BLOCK, bool FUSE>
+template <bool REG, int MODE, bool FUSE>
 __device__ __forceinline__ void plan_body(const CompactArgs& a) {
+  // MODE: kFill (token eviction, INT8 holes filled from the INT8 tail, one
+  // kernel), kStable (token eviction, stable packing by the move kernel) or
+  // kBlock (block eviction, stable packing by the move kernel)
+  constexpr bool BLOCK = MODE == kBlock;   // block selection
+  constexpr bool MOVEK = MODE != kFill;    // stable packing, rows moved by the move kernel
   const CacheView& c = a.c;
   const int lb = blockIdx.x;
   const int l = lb / c.B;
@@ -230,7 +238,7 @@ __device__ __forceinline__ void plan_body(const CompactArgs& a) {
   int32_t* pos = c.pos + (size_t)lbc * cap;
   const float* score = a.score + (size_t)lb * cap;
   __shared__ Shared sh;
-  __shared__ std::conditional_t<REG && (!BLOCK || FUSE), RegShared, char> rsh;
+  __shared__ std::conditional_t<REG && (!MOVEK || FUSE), RegShared, char> rsh;
   // the new token's K and V rows into the FP16 rings at `slot`
   auto append_rows = [&](int slot) {
     const int H = c.hkv, d = c.d, p16 = d >> 3, rp16 = 2 * H * p16;
@@ -418,9 +426,9 @@ __device__ __forceinline__ void plan_body(const CompactArgs& a) {
     }
     int slot = base16 + f;
     slot = slot >= c.cap16 ? slot - c.cap16 : slot;
-    if constexpr (!BLOCK) append_rows(slot);
+    if constexpr (!MOVEK) append_rows(slot);
     if (threadIdx.x == 0) {
-      if constexpr (BLOCK) {
+      if constexpr (MOVEK) {
         hdr[H_MOV8] = hdr[H_MOV16] = 0;
         hdr[H_APPEND] = slot;
       }
@@ -430,7 +438,7 @@ __device__ __forceinline__ void plan_body(const CompactArgs& a) {
       meta[CONFK_META_MOVED16] = 0;
       if (a.evicted_out) a.evicted_out[lb] = 0;
     }
-    if constexpr (FUSE && !BLOCK) quantize_tail(nn, n8, base16);
+    if constexpr (FUSE && !MOVEK) quantize_tail(nn, n8, base16);
     return;
   }
 
@@ -672,8 +680,9 @@ __device__ __forceinline__ void plan_body(const CompactArgs& a) {
   plan_region(r16);
   const int js16 = n8 - r8.e;  // new logical index of the first FP16 survivor
 
-  if constexpr (BLOCK) {
-    // ------------------------ block eviction: stable packing, moves planned
+  if constexpr (MOVEK) {
+    // ------------- block eviction or stable token order: stable packing,
+    // moves planned
 
     // ------------------------------------- 3. metadata and 4. move plan
     // plan entries are stored in move order: ascending new index when packing
@@ -981,17 +990,17 @@ __device__ __forceinline__ void plan_body(const CompactArgs& a) {
 // register form. Otherwise each workgroup takes the register form when its
 // own cache (with the new token) fits and the long form when it does not, so
 // a long-capacity cache pays for the long form only while it is long.
-template <bool SHORTCAP, bool BLOCK, bool FUSE>
+template <bool SHORTCAP, int MODE, bool FUSE>
 __global__ __launch_bounds__(kThreads) void compact_plan_kernel(CompactArgs a) {
   if constexpr (SHORTCAP) {
-    plan_body<true, BLOCK, FUSE>(a);
+    plan_body<true, MODE, FUSE>(a);
   } else {
     const int lb = blockIdx.x, l = lb / a.c.B, b = lb - l * a.c.B;
     const int n = a.c.meta[((a.layer0 + l) * a.c.B + b) * CONFK_META_WORDS + CONFK_META_N];
     if (n + 1 <= kRegKeys * kThreads)  // uniform; a corrupt length is flagged by either form
-      plan_body<true, BLOCK, FUSE>(a);
+      plan_body<true, MODE, FUSE>(a);
     else
-      plan_body<false, BLOCK, FUSE>(a);
+      plan_body<false, MODE, FUSE>(a);
   }
 }
 
@@ -1117,24 +1126,23 @@ size_t compact_plan_bytes(int nlayers, int batch, int cap) {
   return (size_t)nlayers * batch * (kHdr + 2 * (size_t)cap) * 4;
 }
 
+template <int MODE, bool FUSE>
+hipError_t launch_plan(const CompactArgs& a, hipStream_t s) {
+  const int blocks = a.nl * a.c.B;
+  if (a.c.cap <= kRegKeys * kThreads)  // every cache fits the register form
+    hipLaunchKernelGGL((compact_plan_kernel<true, MODE, FUSE>), dim3(blocks), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((compact_plan_kernel<false, MODE, FUSE>), dim3(blocks), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
 template <bool FUSE>
 hipError_t launch_compact_t(const CompactArgs& a, hipStream_t s) {
-  const int blocks = a.nl * a.c.B;
-  const bool reg = a.c.cap <= kRegKeys * kThreads;  // every cache fits the register form
-  if (a.block == 0) {  // token eviction: one kernel plans, fills, packs and appends
-    if (reg)
-      hipLaunchKernelGGL((compact_plan_kernel<true, false, FUSE>), dim3(blocks), dim3(kThreads), 0, s, a);
-    else
-      hipLaunchKernelGGL((compact_plan_kernel<false, false, FUSE>), dim3(blocks), dim3(kThreads), 0, s, a);
-    return hipGetLastError();
-  }
-  if (reg)
-    hipLaunchKernelGGL((compact_plan_kernel<true, true, FUSE>), dim3(blocks), dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((compact_plan_kernel<false, true, FUSE>), dim3(blocks), dim3(kThreads), 0, s, a);
-  hipError_t e = hipGetLastError();
+  if (a.block == 0 && !a.stable)  // token eviction: one kernel plans, fills, packs and appends
+    return launch_plan<kFill, FUSE>(a, s);
+  hipError_t e = a.block ? launch_plan<kBlock, FUSE>(a, s) : launch_plan<kStable, FUSE>(a, s);
   if (e != hipSuccess) return e;
-  const dim3 mgrid(blocks, a.c.hkv), mblock(128);
+  const dim3 mgrid(a.nl * a.c.B, a.c.hkv), mblock(128);
   if (a.c.d == 128) {
     hipLaunchKernelGGL(compact_move_kernel<128>, mgrid, mblock, 0, s, a);
   } else {
@@ -1142,7 +1150,7 @@ hipError_t launch_compact_t(const CompactArgs& a, hipStream_t s) {
   }
   e = hipGetLastError();
   if (e != hipSuccess || !a.quantize) return e;
-  // block eviction moves its rows in the move kernel: the window step follows it
+  // the move kernel moves the rows here: the window step follows it
   QuantArgs q{};
   q.c = a.c;
   q.layer0 = a.layer0;

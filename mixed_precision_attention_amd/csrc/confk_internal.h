@@ -77,6 +77,7 @@ struct CompactArgs {
   CacheView c;
   int32_t layer0, nl, budget_stride, protect;
   int32_t block;  // 0: token eviction; B: whole blocks of B tokens
+  int32_t stable; // token eviction with stable packing (the move kernel moves the rows)
   int32_t* plan;   // workspace: per-(layer, sequence) move plans
   int32_t* stage;  // workspace: metadata staging (caches above 4096 tokens)
   const int32_t* budget;

@@ -25,10 +25,10 @@ def _stream():
 
 def make_policy(p) -> L.Policy:
     """C policy struct from any object with tau, alpha, lam, w_h, w_m, w_p,
-    n_high, n_low, protect, window and (optionally) block attributes."""
+    n_high, n_low, protect, window and (optionally) block and order attributes."""
     return L.Policy(float(p.tau), float(p.alpha), float(p.lam), float(p.w_h), float(p.w_m),
                     float(p.w_p), int(p.n_high), int(p.n_low), int(p.protect), int(p.window),
-                    int(getattr(p, "block", 0)))
+                    int(getattr(p, "block", 0)), int(getattr(p, "order", 0)))
 
 
 class DeviceCache:

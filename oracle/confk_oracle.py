@@ -440,7 +440,10 @@ def step_one(cache, q, k_new, v_new, t, pol, N, score_given=None):
     kp = select_keep(s_sel, cache.pos, N, pol.protect, getattr(pol, "block", 0))
     c1 = cache.copy()
     c1.ema = a
-    c1 = compact(c1, kp, fill=getattr(pol, "block", 0) == 0)
+    # reading R24: token eviction fills INT8 holes from the INT8 tail unless
+    # the stable order (1) is asked for; block eviction packs stably
+    fill = getattr(pol, "block", 0) == 0 and getattr(pol, "order", 0) == 0
+    c1 = compact(c1, kp, fill=fill)
     c1 = append(c1, k_new, v_new, t, a_new)
     c1 = quantize_window(c1, t, pol.window)
     return dict(o=o, mass=m, ema=a, a_new=a_new, score=s, keep=kp, cache=c1)

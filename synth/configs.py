@@ -22,6 +22,7 @@ class Policy:
     protect: int = 32
     window: int = 64
     block: int = 0     # 0: token eviction; B: whole blocks of B tokens
+    order: int = 0     # token eviction: 0 fills INT8 holes from the tail, 1 keeps position order
 
 
 @dataclass(frozen=True)
@@ -123,6 +124,12 @@ CONFIGS = {
         name="qwen32b_block128", layers=64, batch=8, hq=40, hkv=8, d=128, vocab=152064,
         prefill=2048, steps=4096,
         policy=Policy(n_high=1024, n_low=2048, protect=64, window=256, block=128)),
+    # The Qwen-32B workload with the stable survivor order (both parts kept in
+    # position order, rows moved by a second kernel), same budgets
+    "qwen32b_stable": Config(
+        name="qwen32b_stable", layers=64, batch=8, hq=40, hkv=8, d=128, vocab=152064,
+        prefill=2048, steps=4096,
+        policy=Policy(n_high=1024, n_low=2048, protect=64, window=256, order=1)),
     # Long-context pyramid with one planted key per sequence at depths
     # 10/30/50/70/90 % of the prefill (five sequences, one per depth)
     "qwen32b_niah": Config(

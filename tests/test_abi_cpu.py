@@ -43,8 +43,9 @@ def test_struct_layout_matches_header():
     # 7 int32 dims, 4 bytes padding, 10 pointers
     assert ctypes.sizeof(_lib.Cache) == 7 * 4 + 4 + 10 * 8
     assert _lib.Cache.k8.offset == 32
-    assert ctypes.sizeof(_lib.Policy) == 11 * 4
+    assert ctypes.sizeof(_lib.Policy) == 12 * 4
     assert _lib.Policy.block.offset == 40
+    assert _lib.Policy.order.offset == 44
 
 
 def _fake_cache(**kw):
@@ -57,10 +58,10 @@ def _fake_cache(**kw):
 
 def _pol(**kw):
     p = dict(tau=0.7, alpha=0.65, lam=0.9, w_h=0.4, w_m=0.3, w_p=0.3, n_high=24, n_low=48,
-             protect=8, window=64, block=0)
+             protect=8, window=64, block=0, order=0)
     p.update(kw)
     return _lib.Policy(p["tau"], p["alpha"], p["lam"], p["w_h"], p["w_m"], p["w_p"], p["n_high"],
-                       p["n_low"], p["protect"], p["window"], p["block"])
+                       p["n_low"], p["protect"], p["window"], p["block"], p["order"])
 
 
 FAKE = ctypes.c_void_p(0x1000)
@@ -134,6 +135,8 @@ def test_compact_quantize_ema_validation(lib):
     assert cp(c, _pol(window=80)) == M.ERR_BUDGET              # FP16 ring too small
     assert cp(c, _pol(lam=1.5)) == M.ERR_INVALID_ARG
     assert cp(c, _pol(protect=20, window=16, n_high=24)) == M.ERR_BUDGET  # P > W, token eviction
+    assert cp(c, _pol(order=2)) == M.ERR_INVALID_ARG          # unknown survivor order
+    assert cp(c, _pol(order=-1)) == M.ERR_INVALID_ARG
     assert cp(c, _pol(block=8)) == M.ERR_INVALID_ARG          # blocks below 16 tokens
     assert cp(c, _pol(block=-16)) == M.ERR_INVALID_ARG
     big = _fake_cache(cap=16 * 513, cap16=65)                 # 513 blocks of 16

@@ -243,6 +243,37 @@ def test_selection_with_tied_scores():
         run.step(i, scores=s)
 
 
+def _stable_cfg(cfg, **pol):
+    from dataclasses import replace
+    return cfg.with_(name=f"{cfg.name}_stable", policy=replace(cfg.policy, order=1, **pol))
+
+
+@pytest.mark.parametrize("case", ["regs", "long", "protect_above_window"])
+def test_parity_token_eviction_stable_order(case):
+    """Token eviction with the stable survivor order (pol.order = 1): both
+    parts keep position order and the move kernel moves the rows; every cache
+    byte against the oracle's stable compaction. The stable order also takes
+    a protected window larger than the FP16 window."""
+    if case == "regs":
+        cfg = _stable_cfg(TINY["g5_d128"])
+        steps = 24
+    elif case == "long":
+        cfg = _stable_cfg(_cfg("st_long", 1, 2, 5, 1, 128, 900, 5000, 600, 1200, 16, 64))
+        assert cfg.cap > 4096
+        steps = 8
+    else:
+        cfg = _stable_cfg(_cfg("st_pw", 2, 2, 4, 2, 64, 500, 200, 60, 120, 24, 16))
+        steps = 40
+    print(f"[parity] stable order {case} cap={cfg.cap}", flush=True)
+    run = Run(cfg, seed=17)
+    events = sum(run.step(i) for i in range(steps))
+    assert events > 0
+    assert run.band <= 1
+    for (l, b) in run.pairs:  # both parts in position order
+        p = run.eng.cache.snapshot(l, b)["pos"]
+        assert (np.diff(p) > 0).all(), (l, b)
+
+
 def _block_cfg(cfg, block):
     from dataclasses import replace
     return cfg.with_(name=f"{cfg.name}_block{block}", policy=replace(cfg.policy, block=block))
@@ -459,6 +490,8 @@ FUSED_CASES = {
     "g3_d64_empty": lambda: TINY["g3_d64_empty"],
     # block eviction: the window step is a third launch after the move kernel
     "g5_d128_block16": lambda: _block_cfg(TINY["g5_d128"], 16),
+    # token eviction in the stable order: plan, move kernel, window step
+    "g5_d128_stable": lambda: _stable_cfg(TINY["g5_d128"]),
     # more than 4096 slots: the long-cache plan form
     "long_cache": lambda: _cfg("long_cache", 1, 2, 4, 2, 64, 300, 4200, 1500, 3000, 16, 64),
 }
