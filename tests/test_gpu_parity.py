@@ -497,6 +497,63 @@ FUSED_CASES = {
 }
 
 
+def _assert_same_state(a, b):
+    """Two engines hold the same cache and step outputs, bit for bit. EMA and
+    position slots past the new length (evicted tokens) are not part of the
+    state: the fused call leaves them."""
+    import mixed_precision_attention_amd as M
+    for name in ("meta", "k8", "v8", "k16", "v16", "kscale", "vscale", "status"):
+        assert torch.equal(getattr(a.cache, name), getattr(b.cache, name)), name
+    nlen = a.cache.meta[..., M.META_N].cpu().numpy()
+    for l in range(nlen.shape[0]):
+        for bb in range(nlen.shape[1]):
+            n = int(nlen[l, bb])
+            for name in ("ema", "pos"):
+                x, y = getattr(a.cache, name)[l, bb, :n], getattr(b.cache, name)[l, bb, :n]
+                assert torch.equal(x, y), (name, l, bb)
+    for name in ("c", "budget", "out", "mass", "score"):
+        assert torch.equal(getattr(a, name), getattr(b, name)), name
+
+
+def _split_step(e, lg, q, kn, vn, t):
+    """The five calls in sequence; returns how many sequences the window step
+    moved a token for."""
+    import mixed_precision_attention_amd as M
+    e.step_confidence(lg)
+    e.step_attention(q, kn, vn)
+    e.step_ema_rank(t)
+    e.step_compact(kn, vn)
+    n8 = e.cache.meta[..., M.META_N8].clone()
+    e.step_quantize(t)
+    return int((e.cache.meta[..., M.META_N8] > n8).sum())
+
+
+def test_qwen32b_full_launch_fused_matches_split():
+    """The step as bench.py times it (confidence on a second stream, EMA +
+    compaction + window step fused) against the five calls issued one after
+    another, bit for bit, at the full 64-layer, batch-8 size (the split calls
+    themselves are checked against the oracle at this size above)."""
+    import mixed_precision_attention_amd as M
+    dev = _dev()
+    cfg = synth.get_config("qwen32b")
+    print(f"[parity] qwen32b full fused vs split cap={cfg.cap}", flush=True)
+    engs = [M.DecodeEngine(cfg, dev, overlap=True), M.DecodeEngine(cfg, dev, overlap=False)]
+    kp, vp = synth.gen.prefill_kv_device(cfg, 2, dev)
+    for e in engs:
+        e.prefill(kp, vp)
+    del kp, vp
+    quantised = 0
+    for i in range(8):
+        lg = synth.gen.logits_device(cfg, 2, i, dev)
+        q, kn, vn = synth.gen.decode_inputs_device(cfg, 2, i, dev)
+        t = cfg.prefill + i
+        engs[0].step(lg, q, kn, vn, t)
+        quantised += _split_step(engs[1], lg, q, kn, vn, t)
+    torch.cuda.synchronize()
+    assert quantised > 0
+    _assert_same_state(*engs)
+
+
 @pytest.mark.parametrize("case", list(FUSED_CASES))
 def test_overlapped_step_matches_serial(case):
     """DecodeEngine.step (confidence on a second stream, EMA, compaction and
@@ -521,28 +578,10 @@ def test_overlapped_step_matches_serial(case):
         logits, q, kn, vn, t = _inputs(cfg, 3, i)
         lg, qd, kd, vd = _t(logits, dev), _t(q, dev), _t(kn, dev), _t(vn, dev)
         engs[0].step(lg, qd, kd, vd, t)
-        e = engs[1]
-        e.step_confidence(lg)
-        e.step_attention(qd, kd, vd)
-        e.step_ema_rank(t)
-        e.step_compact(kd, vd)
-        n8 = e.cache.meta[..., M.META_N8].clone()
-        e.step_quantize(t)
-        quantised += int((e.cache.meta[..., M.META_N8] > n8).sum())
+        quantised += _split_step(engs[1], lg, qd, kd, vd, t)
     torch.cuda.synchronize()
     assert quantised > 0  # the window step moved tokens
-    a, b = engs
-    for name in ("meta", "k8", "v8", "k16", "v16", "kscale", "vscale", "status"):
-        assert torch.equal(getattr(a.cache, name), getattr(b.cache, name)), name
-    nlen = a.cache.meta[..., M.META_N].cpu().numpy()
-    for l in range(cfg.layers):
-        for bb in range(cfg.batch):
-            n = int(nlen[l, bb])
-            for name in ("ema", "pos"):
-                x, y = getattr(a.cache, name)[l, bb, :n], getattr(b.cache, name)[l, bb, :n]
-                assert torch.equal(x, y), (name, l, bb)
-    for name in ("c", "budget", "out", "mass", "score"):
-        assert torch.equal(getattr(a, name), getattr(b, name)), name
+    _assert_same_state(*engs)
 
 
 def test_attention_without_mass_gives_the_same_output():
