@@ -547,9 +547,14 @@ def _small_cfg():
                         prefill=40, steps=60, policy=pol)
 
 
-def test_end_to_end_invariants():
+@pytest.mark.parametrize("order", [0, 1])
+def test_end_to_end_invariants(order):
+    """Over a free run: lengths, counts, protection, the FP16 window, EMA range
+    and mass; the fill order (0) reorders the INT8 part at some step, the
+    stable order (1) keeps every position ascending (reading R24)."""
+    from dataclasses import replace
     cfg = _small_cfg()
-    pol = cfg.policy
+    pol = replace(cfg.policy, order=order)
     kp, vp = synth.prefill_kv(cfg, seed=0)
     caches = [[O.prefill(kp[l, b], vp[l, b], pol.window) for b in range(cfg.batch)] for l in range(cfg.layers)]
     lengths = []
@@ -572,6 +577,8 @@ def test_end_to_end_invariants():
                 assert c1.pos[-1] == t and len(set(c1.pos.tolist())) == c1.n
                 assert c1.is8[:n8].all() and (np.diff(c1.pos[n8:]) > 0).all()
                 reordered |= bool((np.diff(c1.pos[:n8]) < 0).any())
+                if order == 1:
+                    assert (np.diff(c1.pos) > 0).all()
                 assert (c1.is8 == (c1.pos <= t - pol.window)).all()      # FP16 = window positions
                 # protected newest P of the pre-step cache survive
                 assert set(np.sort(c0.pos)[-pol.protect:].tolist()) <= set(c1.pos.tolist())
@@ -582,7 +589,7 @@ def test_end_to_end_invariants():
     # sawtooth: the cache both shrinks (confident steps) and regrows
     d = np.diff(lengths)
     assert (d < 0).any() and (d > 0).any()
-    assert reordered  # the INT8 hole filling took place
+    assert reordered == (order == 0)  # the INT8 hole filling took place (fill order only)
 
 
 def test_ema_of_retained_token_follows_closed_recurrence():
