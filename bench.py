@@ -186,7 +186,10 @@ def main():
     K = args.steps if args.steps is not None else max(1, cfg.steps - Wm)
     S = K + Wm
 
-    eng = M.DecodeEngine(cfg, dev, overlap=True)  # confidence on a second stream, beside attention
+    # one stream, in a model's order of dependence (the engine can also run the
+    # confidence beside the attention on a second stream, which a model whose
+    # logits come out of the same step's forward pass could not)
+    eng = M.DecodeEngine(cfg, dev)
     kp, vp = synth.gen.prefill_kv_device(cfg, args.seed, dev)
     inputs = []
     for s in range(S):

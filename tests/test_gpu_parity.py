@@ -529,15 +529,16 @@ def _split_step(e, lg, q, kn, vn, t):
 
 
 def test_qwen32b_full_launch_fused_matches_split():
-    """The step as bench.py times it (confidence on a second stream, EMA +
-    compaction + window step fused) against the five calls issued one after
-    another, bit for bit, at the full 64-layer, batch-8 size (the split calls
-    themselves are checked against the oracle at this size above)."""
+    """DecodeEngine.step (EMA + compaction + window step fused; on one stream
+    as bench.py times it, and with the confidence on a second stream) against
+    the five calls issued one after another, bit for bit, at the full
+    64-layer, batch-8 size (the split calls themselves are checked against
+    the oracle at this size above)."""
     import mixed_precision_attention_amd as M
     dev = _dev()
     cfg = synth.get_config("qwen32b")
     print(f"[parity] qwen32b full fused vs split cap={cfg.cap}", flush=True)
-    engs = [M.DecodeEngine(cfg, dev, overlap=True), M.DecodeEngine(cfg, dev, overlap=False)]
+    engs = [M.DecodeEngine(cfg, dev), M.DecodeEngine(cfg, dev, overlap=True), M.DecodeEngine(cfg, dev)]
     kp, vp = synth.gen.prefill_kv_device(cfg, 2, dev)
     for e in engs:
         e.prefill(kp, vp)
@@ -548,10 +549,12 @@ def test_qwen32b_full_launch_fused_matches_split():
         q, kn, vn = synth.gen.decode_inputs_device(cfg, 2, i, dev)
         t = cfg.prefill + i
         engs[0].step(lg, q, kn, vn, t)
-        quantised += _split_step(engs[1], lg, q, kn, vn, t)
+        engs[1].step(lg, q, kn, vn, t)
+        quantised += _split_step(engs[2], lg, q, kn, vn, t)
     torch.cuda.synchronize()
     assert quantised > 0
-    _assert_same_state(*engs)
+    _assert_same_state(engs[0], engs[2])
+    _assert_same_state(engs[1], engs[2])
 
 
 @pytest.mark.parametrize("case", list(FUSED_CASES))
