@@ -50,3 +50,16 @@ def test_step_bytes_full_cache_run_counts_kv_and_q_only():
     assert got["attn"] == 2 * 64 * 4 * 11 + 4 * 4 * 64
     assert got["meta"] == 0 and got["conf"] == 0 and got["quant"] == 0
     assert got["total"] == got["attn"] + 8 * 2 * 64
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """This build runs on one GPU: bench.py --gpus 2 exits with a message
+    that says so, before touching a device."""
+    import json
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0
+    msg = json.loads(r.stdout.strip().splitlines()[-1])
+    assert "one GPU" in msg["error"] and msg["n_gpus"] == 2
