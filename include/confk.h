@@ -18,6 +18,9 @@
  *   confk_ema_rank     mass -> EMA update, new-token metadata, rank scores
  *   confk_compact      scores, budget -> evict, compact, append new token
  *   confk_quantize     FP16 token that left the window -> INT8   (step 10)
+ * confk_ema_compact runs confk_ema_rank and confk_compact (and, with
+ * CONFK_FUSE_QUANTIZE, confk_quantize's window step) as one launch with the
+ * same results; confk_read_probe is a measurement aid beside the step.
  *
  * Conventions for every entry point:
  *  - Pointers named in a confk_cache and every tensor argument are DEVICE
@@ -320,7 +323,8 @@ int confk_read_probe(const void* buf, uint64_t bytes, uint32_t* sink, void* stre
 /* Static text for an error code. */
 const char* confk_strerror(int code);
 
-/* ABI version (major * 100 + minor). */
+/* ABI version (major * 100 + minor). 101: confk_policy.order and the flags
+ * argument of confk_ema_compact. */
 int confk_version(void);
 
 #ifdef __cplusplus
