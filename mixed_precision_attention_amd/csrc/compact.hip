@@ -22,15 +22,18 @@
 //  2. Ballot bit-plane scans give each survivor its new logical index and
 //     each region (INT8 ring, FP16 ring) its eviction count and first / last
 //     hole.
-//  3. Token eviction does everything in this kernel: the surviving INT8
-//     tokens at or beyond the new INT8 length fill the holes below it (slot
-//     order; sources and destinations are disjoint, so the rows move in one
-//     pass), the FP16 part is packed toward the end that moves fewer rows
-//     (keep the base and shift the survivors after the first hole down, or
-//     advance the base and shift the survivors before the last hole up), and
-//     the new token's rows are appended. EMA / position metadata are
-//     rewritten in place after a barrier that follows every read.
-//  4. Block eviction packs both regions that way and leaves the moves to:
+//  3. Token eviction in the fill order (kFill) does everything in this
+//     kernel: the surviving INT8 tokens at or beyond the new INT8 length fill
+//     the holes below it (slot order; sources and destinations are disjoint,
+//     so the rows move in one pass), the FP16 part is packed toward the end
+//     that moves fewer rows (keep the base and shift the survivors after the
+//     first hole down, or advance the base and shift the survivors before the
+//     last hole up), and the new token's rows are appended. EMA / position
+//     metadata are rewritten in place after a barrier that follows every
+//     read. The fused form (FUSE) starts with the EMA update and rank scores
+//     and may end with the window step of the quantisation.
+//  4. Token eviction in the stable order (kStable) and block eviction
+//     (kBlock) pack both regions that way and leave the moves to:
 // Move kernel (one wave per (layer, sequence, kv head, K|V) ring): the
 // planned rows move in rounds (read all rows of a round, wait, write them) in
 // an order that never overwrites an unread source; then the new token's row
