@@ -31,10 +31,6 @@ __device__ __forceinline__ int8_t quant_code(float x, float s, int& sat) {
   return (int8_t)r;
 }
 
-typedef uint32_t qu32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t qu32x2 __attribute__((ext_vector_type(2)));
-typedef float qf32x4 __attribute__((ext_vector_type(4)));
-
 // Codes of 8 consecutive channels (fp16 bits in h) under 8 scales.
 __device__ __forceinline__ qu32x2 quant8(qu32x4 h, const float* s, int& sat) {
   qu32x2 out = {0u, 0u};
