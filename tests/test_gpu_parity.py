@@ -444,11 +444,13 @@ def test_qwen32b_shape_two_layers():
         run.step(i)
 
 
-def test_qwen32b_full_launch_sampled():
-    """All 64 layers x batch 8 in the benchmark's launch configuration;
-    three (layer, sequence) pairs checked against the oracle."""
-    cfg = synth.get_config("qwen32b")
-    print(f"[parity] qwen32b full cap={cfg.cap}", flush=True)
+@pytest.mark.parametrize("name", ["qwen32b", "qwen32b_stable", "qwen32b_block128"])
+def test_qwen32b_full_launch_sampled(name):
+    """All 64 layers x batch 8 in the benchmark's launch configuration (token
+    eviction with either survivor order, and 128-token block eviction); three
+    (layer, sequence) pairs checked against the oracle."""
+    cfg = synth.get_config(name)
+    print(f"[parity] {name} full cap={cfg.cap} block={cfg.policy.block} order={cfg.policy.order}", flush=True)
     run = Run(cfg, seed=2, pairs=[(0, 0), (31, 4), (63, 7)], device_prefill=True)
     for i in range(2):
         run.step(i)
