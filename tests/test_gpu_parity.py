@@ -444,14 +444,17 @@ def test_qwen32b_shape_two_layers():
         run.step(i)
 
 
-@pytest.mark.parametrize("name", ["qwen32b", "qwen32b_stable", "qwen32b_block128"])
+@pytest.mark.parametrize("name", ["qwen32b", "qwen32b_stable", "qwen32b_block128", "qwen32b_pyramid"])
 def test_qwen32b_full_launch_sampled(name):
-    """All 64 layers x batch 8 in the benchmark's launch configuration (token
-    eviction with either survivor order, and 128-token block eviction); three
-    (layer, sequence) pairs checked against the oracle."""
+    """All 64 layers in the benchmark's launch configuration (batch 8: token
+    eviction with either survivor order, and 128-token block eviction; the
+    long-context pyramid at batch 1 after a 32768-token prefill, whose first
+    step evicts down to the per-layer budgets); three (layer, sequence) pairs
+    checked against the oracle."""
     cfg = synth.get_config(name)
+    B = cfg.batch
     print(f"[parity] {name} full cap={cfg.cap} block={cfg.policy.block} order={cfg.policy.order}", flush=True)
-    run = Run(cfg, seed=2, pairs=[(0, 0), (31, 4), (63, 7)], device_prefill=True)
+    run = Run(cfg, seed=2, pairs=[(0, 0), (31, min(4, B - 1)), (63, B - 1)], device_prefill=True)
     for i in range(2):
         run.step(i)
 
