@@ -444,17 +444,20 @@ def test_qwen32b_shape_two_layers():
         run.step(i)
 
 
-@pytest.mark.parametrize("name", ["qwen32b", "qwen32b_stable", "qwen32b_block128", "qwen32b_pyramid"])
-def test_qwen32b_full_launch_sampled(name):
-    """All 64 layers in the benchmark's launch configuration (batch 8: token
-    eviction with either survivor order, and 128-token block eviction; the
-    long-context pyramid at batch 1 after a 32768-token prefill, whose first
-    step evicts down to the per-layer budgets); three (layer, sequence) pairs
-    checked against the oracle."""
+@pytest.mark.parametrize("name", ["qwen32b", "qwen32b_stable", "qwen32b_block128", "qwen32b_pyramid",
+                                  "qwen32b_sw512", "qwen14b"])
+def test_full_launch_sampled(name):
+    """Every layer of a benchmarked workload in the benchmark's launch
+    configuration: the Qwen-32B shape at batch 8 (token eviction with either
+    survivor order, 128-token block eviction, the recency-only sliding
+    window of 512), the long-context pyramid at batch 1 after a 32768-token
+    prefill (the first step evicts down to the per-layer budgets), and the
+    Qwen-14B shape after an 8192-token prefill (scores spill past shared
+    memory); three (layer, sequence) pairs checked against the oracle."""
     cfg = synth.get_config(name)
-    B = cfg.batch
+    L, B = cfg.layers, cfg.batch
     print(f"[parity] {name} full cap={cfg.cap} block={cfg.policy.block} order={cfg.policy.order}", flush=True)
-    run = Run(cfg, seed=2, pairs=[(0, 0), (31, min(4, B - 1)), (63, B - 1)], device_prefill=True)
+    run = Run(cfg, seed=2, pairs=[(0, 0), (L // 2, min(4, B - 1)), (L - 1, B - 1)], device_prefill=True)
     for i in range(2):
         run.step(i)
 
