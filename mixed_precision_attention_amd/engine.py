@@ -235,8 +235,12 @@ class DecodeEngine:
     def step(self, logits, q, k_new, v_new, t):
         if self.cfg.mode == "full_kv":
             # comparison run: attention output only, then the append (the
-            # budget covers every token, so nothing is evicted or quantised)
+            # budget covers every token, so nothing is evicted or quantised).
+            # The rank call runs on the mass buffer, which stays all zero in
+            # this mode, because it writes the new token's position and EMA
+            # slot that the append stores.
             attn_decode(self.cache, q, k_new, v_new, self.out, None, None)
+            self.step_ema_rank(t)
             self.step_compact(k_new, v_new)
             return
         if self.side is None:

@@ -462,6 +462,39 @@ def test_full_launch_sampled(name):
         run.step(i)
 
 
+def test_full_kv_comparison_run_sampled():
+    """The full FP16 comparison run at its size (64 layers x batch 8, a
+    2048-token prefill, window and budget 4094): attention without the
+    per-key mass over an all-FP16 cache, then the append; nothing is evicted
+    or quantised. Three (layer, sequence) pairs checked against the oracle;
+    the EMA decays under an all-zero mass in this run and is not compared."""
+    import mixed_precision_attention_amd as M
+    dev = _dev()
+    cfg = synth.get_config("qwen32b_fullkv")
+    L, B = cfg.layers, cfg.batch
+    print(f"[parity] qwen32b_fullkv full cap={cfg.cap}", flush=True)
+    eng = M.DecodeEngine(cfg, dev)
+    kp, vp = synth.gen.prefill_kv_device(cfg, 4, dev)
+    eng.prefill(kp, vp)
+    pairs = [(0, 0), (L // 2, 4), (L - 1, B - 1)]
+    orc = {(l, b): O.prefill(kp[l, b].cpu().numpy(), vp[l, b].cpu().numpy(), cfg.policy.window)
+           for (l, b) in pairs}
+    del kp, vp
+    for i in range(2):
+        logits, q, kn, vn, t = _inputs(cfg, 4, i)
+        eng.step(_t(logits, dev), _t(q, dev), _t(kn, dev), _t(vn, dev), t)
+        torch.cuda.synchronize()
+        assert int(eng.cache.status.cpu()[0]) == 0, "device status set"
+        out = eng.out.float().cpu().numpy()
+        for (l, b) in pairs:
+            w = f"step {i} l={l} b={b}"
+            o, _ = O.attention(q[l, b], orc[(l, b)], kn[l, b], vn[l, b])
+            assert rel_maxabs(out[l, b], o) <= OTOL, f"{w}: attention output"
+            orc[(l, b)] = O.append(orc[(l, b)], kn[l, b], vn[l, b], t, 0.0)
+            assert not orc[(l, b)].is8.any()
+            assert_state_equal(eng.cache.snapshot(l, b), orc[(l, b)], ema_tol=np.inf, what=w)
+
+
 def test_parity_many_heads_multi_round_moves():
     """16 kv heads of d128 and a large first eviction: the compaction moves
     take several rounds of the single-kernel path."""
