@@ -95,16 +95,18 @@ extern "C" {
  * a block ranks by the largest score of its tokens, and the ceil((n-N)/B)
  * lowest-ranked blocks leave (the older block first among equals).
  * order: the order of the survivors inside the compacted cache under token
- * eviction (the pages ask for a dense layout without indirection tables and
- * fix no order). CONFK_ORDER_FILL (0): the surviving INT8 tokens at or beyond
- * the new INT8 length fill the INT8 holes below it, in slot order (the
- * fewest row moves, one kernel; needs protect <= window). CONFK_ORDER_STABLE
- * (1): both parts keep position order (a stable gather, packed toward
- * whichever end of each ring moves fewer rows; a second kernel moves the
- * rows). Block eviction always packs stably and ignores this field.
+ * eviction. CONFK_ORDER_STABLE (0, the default): the survivors keep position
+ * order in both parts, a stable gather (the review's Algorithm 1 compacts the
+ * survivors in place; the summary's "Implementierung" asks for a dense
+ * layout without indirection tables), each ring packed toward whichever end
+ * moves fewer rows. CONFK_ORDER_FILL (1), an option: the surviving INT8
+ * tokens at or beyond the new INT8 length fill the INT8 holes below it, in
+ * slot order (fewer row moves; the INT8 part then leaves position order;
+ * needs protect <= window). Block eviction always packs stably and ignores
+ * this field.
  */
-#define CONFK_ORDER_FILL 0
-#define CONFK_ORDER_STABLE 1
+#define CONFK_ORDER_STABLE 0
+#define CONFK_ORDER_FILL 1
 typedef struct confk_policy {
   float tau, alpha, lambda, w_h, w_m, w_p;
   int32_t n_high, n_low, protect, window, block, order;
@@ -208,8 +210,11 @@ int confk_attn_decode(const confk_cache* cache, int32_t layer0, int32_t nlayers,
  * Review "前置知识" (EMA: a_i <- lambda a_i + (1-lambda) Abar_i) and "核心方法"
  * (s_i = alpha a^_i + (1-alpha) r^_i). Abar_i = sum_j mass[j][i] / hq.
  * For cached tokens i < n: ema[i] is updated in place, then
- * score[i] = alpha * ema[i] / max(ema) + (1 - alpha) * (pos[i]-pos[0]) /
- * (pos[n-1]-pos[0]) (first term 0 when max(ema) = 0, second 1 when n = 1).
+ * score[i] = alpha * ema[i] / max(ema) + (1 - alpha) * (pos[i] - pmin) /
+ * (pmax - pmin), with pmin and pmax the smallest and largest position among
+ * the n cached tokens (first term 0 when max(ema) = 0, second 1 when
+ * pmax = pmin, e.g. n = 1). The positions are reduced, not read at the ends,
+ * because the hole-filling order leaves the INT8 part out of position order.
  * The new token's metadata is written to slot n: ema[n] = (1-lambda) Abar_n,
  * pos[n] = t.
  *   mass   fp32 [nlayers][B][hkv][cap] from confk_attn_decode
@@ -227,12 +232,11 @@ int confk_ema_rank(const confk_cache* cache, int32_t layer0, int32_t nlayers, co
  * k = n - N tokens with the smallest (score, position) among all but the
  * newest `protect` tokens are evicted and the survivors are packed densely;
  * the new token (slot n metadata from confk_ema_rank, K/V from k_new/v_new)
- * is appended as FP16. The FP16 part keeps position order, packed toward
- * whichever end moves fewer rows. The INT8 part: with token eviction and
- * pol->order = CONFK_ORDER_FILL, the surviving INT8 tokens at or beyond its
- * new length fill the holes below it, in slot order (the fewest moves; the
- * INT8 part is then no longer in position order); with CONFK_ORDER_STABLE or
- * block eviction it is packed like the FP16 part.
+ * is appended as FP16. Each part (INT8, FP16) keeps position order, packed
+ * toward whichever end of its ring moves fewer rows, except that with token
+ * eviction and pol->order = CONFK_ORDER_FILL the surviving INT8 tokens at or
+ * beyond the INT8 part's new length fill the holes below it, in slot order
+ * (the INT8 part is then no longer in position order).
  *   budget       int32, entry for (l, b) at budget[l * budget_layer_stride + b]
  *                (stride 0: one budget per sequence; stride B: per layer)
  *   score        fp32 [nlayers][B][cap] from confk_ema_rank
@@ -246,7 +250,7 @@ int confk_ema_rank(const confk_cache* cache, int32_t layer0, int32_t nlayers, co
  * free slot. Errors: INVALID_ARG, BUDGET (protect > n_low or > n_high,
  * capacity below n_low + 2, FP16 ring below window + 1, protect > window
  * with token eviction in the fill order), UNSUPPORTED (more than 512 blocks per sequence;
- * block eviction with d other than 64 or 128), WORKSPACE.
+ * d above 512 with stable packing, i.e. the stable order or block eviction), WORKSPACE.
  */
 int confk_compact(const confk_cache* cache, int32_t layer0, int32_t nlayers, const int32_t* budget,
                   int32_t budget_layer_stride, const float* score, const confk_policy* pol,
@@ -324,7 +328,8 @@ int confk_read_probe(const void* buf, uint64_t bytes, uint32_t* sink, void* stre
 const char* confk_strerror(int code);
 
 /* ABI version (major * 100 + minor). 101: confk_policy.order and the flags
- * argument of confk_ema_compact. */
+ * argument of confk_ema_compact. 102: the stable survivor order is order 0
+ * (the default) and the hole-filling order is 1. */
 int confk_version(void);
 
 #ifdef __cplusplus

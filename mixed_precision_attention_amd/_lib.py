@@ -28,8 +28,8 @@ META_WORDS = 16
 QUANT_STEP = 0
 QUANT_PREFILL = 1
 FUSE_QUANTIZE = 1
-ORDER_FILL = 0
-ORDER_STABLE = 1
+ORDER_STABLE = 0
+ORDER_FILL = 1
 WS_CONFIDENCE = 0
 WS_ATTENTION = 1
 WS_COMPACT = 2

@@ -37,7 +37,7 @@ int launch_status(hipError_t e) { return e == hipSuccess ? CONFK_OK : CONFK_ERR_
 
 extern "C" {
 
-int confk_version(void) { return 101; }
+int confk_version(void) { return 102; }
 
 const char* confk_strerror(int code) {
   switch (code) {
@@ -169,11 +169,14 @@ int compact_args(const confk_cache* cache, int32_t layer0, int32_t nlayers, cons
   // token eviction reorders the INT8 part: the newest P tokens must be FP16
   if (pol->block == 0 && pol->order == CONFK_ORDER_FILL && pol->protect > pol->window) return CONFK_ERR_BUDGET;
   if (pol->block > 0 && cache->cap / pol->block > kMaxEvictBlocks) return CONFK_ERR_UNSUPPORTED;
-  if (pol->block > 0 && cache->d != 64 && cache->d != 128) return CONFK_ERR_UNSUPPORTED;
+  // stable packing moves rows in a kernel that holds a head's scales on chip
+  const bool packs = pol->block > 0 || pol->order == CONFK_ORDER_STABLE;
+  if (packs && (cache->d > kMaxMoveHeadDim || nlayers * cache->batch > kMaxMovePairs)) return CONFK_ERR_UNSUPPORTED;
   const size_t need = compact_ws_bytes(nlayers, cache->batch, cache->cap);
   if (!ws || ws_bytes < need) return CONFK_ERR_WORKSPACE;
   a = CompactArgs{};
   a.plan = (int32_t*)ws;
+  a.jobs = (int32_t*)((char*)ws + compact_jobs_offset(nlayers, cache->batch, cache->cap));
   a.stage = (int32_t*)((char*)ws + compact_plan_bytes(nlayers, cache->batch, cache->cap));
   a.c = view_of(cache);
   a.layer0 = layer0;

@@ -56,21 +56,25 @@ constexpr int kBuckets = 1024;
 constexpr int kRankMax = 64;   // boundary-bucket keys ranked by one wave
 constexpr int kHdr = 16;       // plan header words per (layer, sequence)
 static_assert(2 * kMaxEvictBlocks <= kBuckets, "block keys and flags share the histogram");
-// 16-byte pieces per lane per move round (d = 128; d = 64 takes 4 fewer) and
-// the move kernel's waves per SIMD: compile-time tuning knobs
-#ifndef CONFK_MOVE_PIECES
-#define CONFK_MOVE_PIECES 16
+// 16-byte pieces per thread per round of the move kernel (half K, half V):
+// 192 INT8 or 96 FP16 rows of a head per round at d = 128
+#ifndef CONFK_MOVE_ROUND
+#define CONFK_MOVE_ROUND 12
 #endif
-#ifndef CONFK_MOVE_OCCUPANCY
-#define CONFK_MOVE_OCCUPANCY 4
-#endif
-constexpr int kMovePieces = CONFK_MOVE_PIECES;
+constexpr int kMoveRound = CONFK_MOVE_ROUND;
+constexpr int kMaxHeadDim = kMaxMoveHeadDim;  // move kernel's window step (scales in shared memory)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// plan header words
+// plan header words (the move kernel's instructions for one (layer, sequence)):
+// per region movers, packing side, evictions, first moved new index; the old
+// ring bases; the new token's FP16 slot (-1: nothing left to do); the window
+// step's token count and whether it calibrates; the new ring bases and INT8
+// length after the packing
 enum { H_MOV8 = 0, H_LEFT8, H_E8, H_JLO8, H_MOV16, H_LEFT16, H_E16, H_JLO16, H_BASE8, H_BASE16,
-       H_APPEND };
+       H_APPEND, H_Q, H_CAL, H_B8N, H_B16N, H_M8 };
+constexpr int kMoveThreads = 256;  // move kernel workgroup: one (layer, sequence, kv head) item at a time
+constexpr int kMoveGrid = 1024;    // move kernel workgroups at most (4 per compute unit)
 
 // Order-preserving uint32 image of an fp32 score; NaN sorts above +inf
 // (0xFFFFFFFF stays free as the "not a candidate" key).
@@ -106,11 +110,19 @@ __device__ __forceinline__ int wave_prefix16(int x, int& total) {
   return pre;
 }
 
+// A pointer every lane holds the same value of, in scalar registers.
+__device__ __forceinline__ unsigned char* uniform_ptr(const void* p) {
+  const uint64_t rp = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)rp);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(rp >> 32));
+  return (unsigned char*)(((uint64_t)hi << 32) | lo);
+}
+
 struct Shared {
   uint32_t hist[kBuckets];
   float rmax[kWaves];  // fused EMA: per-wave max EMA and position range
   int rpmin[kWaves], rpmax[kWaves];
-  int wsum[3][kWaves];  // per-wave keeps, e8, e16
+  int wsum[4][kWaves];  // per-wave keeps, e8, e16, window-step tokens
   int wfill[2][kWaves];  // per-wave INT8 holes and tails
   int wfirst[2][kWaves], wlast[2][kWaves];
   uint64_t rank_keys[kRankMax];
@@ -216,11 +228,13 @@ __device__ uint32_t radix_select(int& kk, int cnt, Part part, Val val, Shared& s
 // through the workspace.
 template <bool REG, int MODE, bool FUSE>
 __device__ __forceinline__ void plan_body(const CompactArgs& a) {
-  // MODE: kFill (token eviction, INT8 holes filled from the INT8 tail, one
-  // kernel), kStable (token eviction, stable packing by the move kernel) or
-  // kBlock (block eviction, stable packing by the move kernel)
+  // MODE: kStable (token eviction, both regions packed stably), kBlock (block
+  // eviction, packed stably) or kFill (token eviction, INT8 holes filled from
+  // the INT8 tail). Stable packing leaves its row moves (and then the append
+  // and the window step) to the move kernel; the fill order moves its few
+  // rows here.
   constexpr bool BLOCK = MODE == kBlock;   // block selection
-  constexpr bool MOVEK = MODE != kFill;    // stable packing, rows moved by the move kernel
+  constexpr bool MOVEK = MODE != kFill;    // rows moved by the move kernel
   const CacheView& c = a.c;
   const int lb = blockIdx.x;
   const int l = lb / c.B;
@@ -259,11 +273,11 @@ __device__ __forceinline__ void plan_body(const CompactArgs& a) {
   // Fused form with the window step: once the cache holds the step's
   // survivors and the new token, the FP16 tokens at positions <= t - W move
   // to INT8 in this workgroup, as the quantisation kernel would do next.
-  auto quantize_tail = [&](int n_after, int n8_after, int base16_after) {
+  auto quantize_tail = [&](int n_after, int n8_after, int base8_after, int base16_after) {
     if (!a.quantize) return;  // uniform (a kernel argument)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // the rows, positions and metadata written above are visible
-    quantize_window<kThreads>(c, lbc, a.t, a.window, n_after, n8_after, base8, base16_after,
+    quantize_window<kThreads>(c, lbc, a.t, a.window, n_after, n8_after, base8_after, base16_after,
                               meta[CONFK_META_CALIB]);
   };
 
@@ -278,6 +292,7 @@ __device__ __forceinline__ void plan_body(const CompactArgs& a) {
       meta[CONFK_META_MOVED16] = 0;
       hdr[H_MOV8] = hdr[H_MOV16] = 0;
       hdr[H_APPEND] = -1;
+      if constexpr (MOVEK) a.jobs[lb] = 0;
       if (a.evicted_out) a.evicted_out[lb] = 0;
     }
     return;
@@ -429,19 +444,16 @@ __device__ __forceinline__ void plan_body(const CompactArgs& a) {
     }
     int slot = base16 + f;
     slot = slot >= c.cap16 ? slot - c.cap16 : slot;
-    if constexpr (!MOVEK) append_rows(slot);
+    append_rows(slot);
     if (threadIdx.x == 0) {
-      if constexpr (MOVEK) {
-        hdr[H_MOV8] = hdr[H_MOV16] = 0;
-        hdr[H_APPEND] = slot;
-      }
+      if constexpr (MOVEK) a.jobs[lb] = 0;  // the move kernel has nothing to do here
       meta[CONFK_META_N] = nn;
       meta[CONFK_META_EVICTED] = 0;
       meta[CONFK_META_MOVED] = 0;
       meta[CONFK_META_MOVED16] = 0;
       if (a.evicted_out) a.evicted_out[lb] = 0;
     }
-    if constexpr (FUSE && !MOVEK) quantize_tail(nn, n8, base16);
+    if constexpr (FUSE) quantize_tail(nn, n8, base8, base16);
     return;
   }
 
@@ -603,6 +615,11 @@ __device__ __forceinline__ void plan_body(const CompactArgs& a) {
   };
   uint32_t evm = 0;  // bit j: index lo + j leaves (register path)
   int keeps = 0, e8 = 0, e16 = 0;
+  // fused window step after stable packing: the FP16 survivors that leave the
+  // window (position at most t - window; the oldest ones, as the FP16 part is
+  // in position order)
+  const bool qcount = MOVEK && FUSE && a.quantize;
+  int q16 = 0;
   int f8 = INT32_MAX, l8 = -1, f16 = INT32_MAX, l16 = -1;
   auto tally = [&](int j) {
     const int i = lo + j;
@@ -619,6 +636,7 @@ __device__ __forceinline__ void plan_body(const CompactArgs& a) {
       }
     } else {
       ++keeps;
+      if (qcount && i >= n8 && i < n && (int)pos_at(j) <= a.t - a.window) ++q16;
     }
   };
   if constexpr (REG) {
@@ -656,22 +674,25 @@ __device__ __forceinline__ void plan_body(const CompactArgs& a) {
   const int wf16 = h16 ? __shfl(f16, __ffsll((unsigned long long)h16) - 1, 64) : INT32_MAX;
   const int wl16 = h16 ? __shfl(l16, 63 - __clzll((long long)h16), 64) : -1;
   __syncthreads();  // the select's shared values other than bsel are no longer read
+  const int tq = qcount ? wave_sum_i(q16) : 0;
   if (lane == 0) {
     sh.wsum[0][w] = tk;
     sh.wsum[1][w] = t8;
     sh.wsum[2][w] = t16;
+    sh.wsum[3][w] = tq;
     sh.wfirst[0][w] = wf8;
     sh.wlast[0][w] = wl8;
     sh.wfirst[1][w] = wf16;
     sh.wlast[1][w] = wl16;
   }
   __syncthreads();
-  int keep_base = pre_keep, nkeep = 0;
+  int keep_base = pre_keep, nkeep = 0, nq = 0;
   Region r8{0, n8, 0, INT32_MAX, -1, 1, 0, 0}, r16{n8, f, 0, INT32_MAX, -1, 1, 0, 0};
 #pragma unroll
   for (int q = 0; q < kWaves; ++q) {
     keep_base += q < w ? sh.wsum[0][q] : 0;
     nkeep += sh.wsum[0][q];
+    nq += sh.wsum[3][q];
     r8.e += sh.wsum[1][q];
     r16.e += sh.wsum[2][q];
     r8.first_ev = min(r8.first_ev, sh.wfirst[0][q]);
@@ -683,13 +704,14 @@ __device__ __forceinline__ void plan_body(const CompactArgs& a) {
   plan_region(r16);
   const int js16 = n8 - r8.e;  // new logical index of the first FP16 survivor
 
-  if constexpr (MOVEK) {
-    // ------------- block eviction or stable token order: stable packing,
-    // moves planned
+  if constexpr (MODE != kFill) {
+    // ------------- stable packing of both regions (token eviction in the
+    // stable order, or block eviction)
 
-    // ------------------------------------- 3. metadata and 4. move plan
-    // plan entries are stored in move order: ascending new index when packing
-    // toward the base, descending otherwise
+    // ------------------------------------- 3. metadata and 4. move lists
+    // List entries (the mover's region-local old index) are stored in move
+    // order: ascending new index when packing toward the base, descending
+    // otherwise.
     auto emit = [&](int i, int jn, float ev_, int pv_) {
       ema[jn] = ev_;
       pos[jn] = pv_;
@@ -707,39 +729,61 @@ __device__ __forceinline__ void plan_body(const CompactArgs& a) {
       for (int j = 0; j < kRegKeys; ++j)
         if (j < cnt && !((evm >> j) & 1u)) emit(lo + j, jn++, ereg[j], preg[j]);
     } else {
-      // long caches: survivors' metadata goes through a staging area; every
-      // read of a run precedes the barrier, every in-place write follows it
-      float* se = reinterpret_cast<float*>(a.stage + (size_t)lb * stage_words(cap));
-      int32_t* sp = a.stage + (size_t)lb * stage_words(cap) + cap;
+      // long caches: each survivor's metadata and old index go through a
+      // staging area, so that the in-place writes after the barrier need no
+      // second look at the (by then rewritten) positions
+      int32_t* st = a.stage + (size_t)lb * stage_words(cap);
+      float* se = reinterpret_cast<float*>(st);
+      int32_t* sp = st + cap;
+      int32_t* si = st + 2 * cap;
       int jn = keep_base;
       for (int j = 0; j < cnt; ++j) {
         if (!leaves(j)) {
           se[jn] = ema[lo + j];
           sp[jn] = pos[lo + j];
+          si[jn] = lo + j;
           ++jn;
         }
       }
       __syncthreads();
-      jn = keep_base;
-      for (int j = 0; j < cnt; ++j) {
-        if (!leaves(j)) {
-          emit(lo + j, jn, se[jn], sp[jn]);
-          ++jn;
-        }
-      }
+      for (jn = keep_base; jn < keep_base + keeps; ++jn) emit(si[jn], jn, se[jn], sp[jn]);
     }
-
-    // ------------------------------------------------------------ header
-    if (threadIdx.x == 0) {
-      int b8 = base8, b16 = base16;
-      if (!r8.left) {
-        b8 += r8.e;
-        if (b8 >= cap) b8 -= cap;
+    int b8 = base8, b16 = base16;  // ring bases after the packing
+    if (!r8.left) {
+      b8 += r8.e;
+      if (b8 >= cap) b8 -= cap;
+    }
+    if (!r16.left) {
+      b16 += r16.e;
+      if (b16 >= c.cap16) b16 -= c.cap16;
+    }
+    int slot = b16 + (f - r16.e);  // the new token's FP16 slot
+    slot = slot >= c.cap16 ? slot - c.cap16 : slot;
+    const int m8 = n8 - r8.e;
+    if (r8.movers + r16.movers == 0) {  // uniform
+      // nothing moves (the evicted tokens sat at the packing ends): append
+      // and window step here, the move kernel skips this (layer, sequence).
+      // The append slot is no FP16 source when no FP16 row moves.
+      append_rows(slot);
+      if (threadIdx.x == 0) {
+        a.jobs[lb] = 0;
+        meta[CONFK_META_N] = nkeep;
+        meta[CONFK_META_N8] = m8;
+        meta[CONFK_META_BASE8] = b8;
+        meta[CONFK_META_BASE16] = b16;
+        meta[CONFK_META_EVICTED] = k;
+        meta[CONFK_META_MOVED] = 0;
+        meta[CONFK_META_MOVED16] = 0;
+        if (a.evicted_out) a.evicted_out[lb] = k;
       }
-      if (!r16.left) {
-        b16 += r16.e;
-        if (b16 >= c.cap16) b16 -= c.cap16;
-      }
+      if constexpr (FUSE) quantize_tail(nkeep, m8, b8, b16);
+    } else if (threadIdx.x == 0) {
+      // the move kernel moves the rows, appends the new token and (fused
+      // form) moves the nq oldest FP16 survivors to INT8; the header below
+      // is the state after all of that
+      const int calib = meta[CONFK_META_CALIB];
+      int b16q = b16 + nq;
+      b16q = b16q >= c.cap16 ? b16q - c.cap16 : b16q;
       hdr[H_MOV8] = r8.movers;
       hdr[H_LEFT8] = r8.left;
       hdr[H_E8] = r8.e;
@@ -750,12 +794,18 @@ __device__ __forceinline__ void plan_body(const CompactArgs& a) {
       hdr[H_JLO16] = r16.jlo;
       hdr[H_BASE8] = base8;
       hdr[H_BASE16] = base16;
-      const int slot = b16 + (f - r16.e);
-      hdr[H_APPEND] = slot >= c.cap16 ? slot - c.cap16 : slot;
+      hdr[H_APPEND] = slot;
+      hdr[H_Q] = nq;
+      hdr[H_CAL] = nq > 0 && !calib;
+      hdr[H_B8N] = b8;
+      hdr[H_B16N] = b16;
+      hdr[H_M8] = m8;
+      a.jobs[lb] = 1;
       meta[CONFK_META_N] = nkeep;
-      meta[CONFK_META_N8] = n8 - r8.e;
+      meta[CONFK_META_N8] = m8 + nq;
       meta[CONFK_META_BASE8] = b8;
-      meta[CONFK_META_BASE16] = b16;
+      meta[CONFK_META_BASE16] = b16q;
+      meta[CONFK_META_CALIB] = calib | (nq > 0);
       meta[CONFK_META_EVICTED] = k;
       meta[CONFK_META_MOVED] = r8.movers;
       meta[CONFK_META_MOVED16] = r16.movers;
@@ -985,7 +1035,7 @@ __device__ __forceinline__ void plan_body(const CompactArgs& a) {
       meta[CONFK_META_MOVED16] = mv16;
       if (a.evicted_out) a.evicted_out[lb] = k;
     }
-    if constexpr (FUSE) quantize_tail(nkeep, m8, b16);
+    if constexpr (FUSE) quantize_tail(nkeep, m8, base8, b16);
   }
 }
 
@@ -1007,126 +1057,279 @@ __global__ __launch_bounds__(kThreads) void compact_plan_kernel(CompactArgs a) {
   }
 }
 
-template <int D, int LGP, int NW, int NR>
-__device__ __forceinline__ void ring_rounds(unsigned char* ring, int C, int movers, int left, int e, int jlo,
-                                            int base, const int32_t* src, int* sv, bool have) {
-  constexpr int ROWS = (NR * 64) >> LGP;  // rows per round
-  constexpr int ROWB = 16 << LGP;         // bytes per row
-  static_assert(ROWS <= 64 * NW, "a round's movers must fit one source window");
-  const int lane = threadIdx.x & 63;
-  int win = have ? 0 : -64 * NW;  // first mover of the source window held in sv (64 * NW movers)
-  for (int m0 = 0; m0 < movers; m0 += ROWS) {
-    if (m0 + ROWS > win + 64 * NW) {  // the round leaves the window: reload it from m0 (uniform)
-      win = m0;
+// Move kernel: one workgroup of kMoveThreads per (layer, sequence, kv head).
+// The planned rows of that head's four rings (K and V, INT8 and FP16) move in
+// rounds, then the new token's K and V rows of the head are appended, then
+// (fused form) the head's rows of the tokens that left the FP16 window are
+// quantised. A (layer, sequence) whose plan needs no move (header slot -1) is
+// finished by the plan kernel. Rounds follow plan order: round r+1 reads only
+// slots beyond round r's destinations in the packing direction, and within a
+// round every source is read before any destination is written. Thread t
+// copies piece column t % P (P 16-byte pieces per row) of movers t / P,
+// t / P + mpp, ... (mpp = kMoveThreads / P movers per pass), the K piece and
+// the V piece at the same ring offset. Loads and stores are unconditional: a
+// piece past the last mover takes the last mover's piece and writes it again
+// (same bytes, same place), since branches around each piece would make every
+// memory operation wait for all earlier ones; a thread past the last whole
+// mover of a pass (P not dividing the workgroup) repeats the round's first.
+__device__ __forceinline__ void move_rounds(unsigned char* kb, unsigned char* vb, uint32_t rowb, int C, int P,
+                                            int mv, int left, int e, int jlo, int base, const int32_t* lst) {
+  typedef __attribute__((address_space(1))) u32x4 gvec;
+  constexpr int HALF = kMoveRound / 2;
+  gvec* kg = (gvec*)kb;
+  gvec* vg = (gvec*)vb;
+  const int mpp = kMoveThreads / P;
+  const int mq = threadIdx.x / P, pc = threadIdx.x - mq * P;
+  const bool act = mq < mpp;  // threads past the last whole mover of a pass repeat the round's first
+  for (int m0 = 0; m0 < mv; m0 += HALF * mpp) {
+    u32x4 v[2 * HALF];
+    uint32_t dof[HALF];
 #pragma unroll
-      for (int q = 0; q < NW; ++q) sv[q] = win + lane + 64 * q < movers ? src[win + lane + 64 * q] : 0;
-    }
-    u32x4 bk[NR];
-#pragma unroll
-    for (int q = 0; q < NR; ++q) {
-      const int u = lane + 64 * q;
-      const int r = m0 + (u >> LGP);  // mover of this piece
-      int sel = sv[0];
-#pragma unroll
-      for (int z = 1; z < NW; ++z) sel = ((r - win) >> 6) == z ? sv[z] : sel;  // uniform for a given q
-      const int sidx = __shfl(sel, (r - win) & 63, 64);
-      if (r < movers) {
-        int ss = base + sidx;
-        ss = ss >= C ? ss - C : ss;
-        bk[q] = *reinterpret_cast<const u32x4*>(ring + (uint32_t)ss * ROWB + (u & ((1 << LGP) - 1)) * 16);
-      }
+    for (int u = 0; u < HALF; ++u) {
+      const int r = act ? min(m0 + mq + u * mpp, mv - 1) : m0;
+      int ss = base + lst[r];
+      ss = ss >= C ? ss - C : ss;
+      const uint32_t off = ((uint32_t)ss * rowb + (uint32_t)pc * 16u) >> 4;
+      v[u] = kg[off];
+      v[HALF + u] = vg[off];
+      const int j = jlo + (left ? r : mv - 1 - r);
+      int ds = base + (left ? j : j + e);
+      ds = ds >= C ? ds - C : ds;
+      dof[u] = ((uint32_t)ds * rowb + (uint32_t)pc * 16u) >> 4;
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // every source of the round has been read
 #pragma unroll
-    for (int q = 0; q < NR; ++q) {
-      const int u = lane + 64 * q;
-      const int r = m0 + (u >> LGP);
-      if (r < movers) {
-        const int j = jlo + (left ? r : movers - 1 - r);
-        int ds = base + (left ? j : j + e);
-        ds = ds >= C ? ds - C : ds;
-        *reinterpret_cast<u32x4*>(ring + (uint32_t)ds * ROWB + (u & ((1 << LGP) - 1)) * 16) = bk[q];
-      }
+    for (int u = 0; u < HALF; ++u) {
+      kg[dof[u]] = v[u];
+      vg[dof[u]] = v[HALF + u];
     }
   }
 }
 
-__device__ __forceinline__ unsigned char* uniform_ptr(const void* p) {
-  const uint64_t rp = (uint64_t)p;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)rp);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(rp >> 32));
-  return (unsigned char*)(((uint64_t)hi << 32) | lo);
-}
-
-// One workgroup of two waves per (layer, sequence, kv head): wave 0 moves the
-// K rings, wave 1 the V rings (planned INT8 moves, then FP16 moves, then the
-// append of the new token's row). Round trip 1 reads the plan header, the
-// first 256 INT8 movers' source indices (speculatively) and the new row;
-// round trip 2 reads the first round's rows (128 INT8 / 64 FP16 rows at
-// d = 128), which are then written; longer plans take more rounds. A wave
-// orders its own loads before its stores with a counter wait, so no barrier
-// is needed. Rounds follow plan order: round r+1 reads only slots beyond
-// round r's destinations in the packing direction.
-template <int D>
-__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(CONFK_MOVE_OCCUPANCY)))
-void compact_move_kernel(CompactArgs a) {
+// One (layer, sequence, kv head) item of the move kernel.
+template <bool WINDOW>
+__device__ __forceinline__ void move_item(const CompactArgs& a, const int lb, const int hh) {
   typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
-  constexpr int L8 = D == 128 ? 3 : 2, L16 = L8 + 1;  // log2 of 16-byte pieces per row
-  constexpr int P16 = D / 8;
-  constexpr int NR = D == 128 ? kMovePieces : kMovePieces - 4;  // pieces per lane per round
+  typedef __attribute__((address_space(1))) u32x4 gvec;
+  constexpr int HALF = kMoveRound / 2;
   const CacheView& c = a.c;
-  const int lane = threadIdx.x & 63;
-  const int kv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // 0: K, 1: V
-  const int lb = blockIdx.x;
-  const int hh = blockIdx.y;
   const int l = lb / c.B;
   const int b = lb - l * c.B;
   const int lbc = (a.layer0 + l) * c.B + b;
-  const int H = c.hkv;
-  const int cap = c.cap, cap16 = c.cap16;
+  const int H = c.hkv, d = c.d, cap = c.cap, cap16 = c.cap16;
   const int32_t* hdr = a.plan + (size_t)lb * (kHdr + 2 * (size_t)cap);
   const int32_t* src8 = hdr + kHdr;
   const int32_t* src16 = src8 + cap;
   const size_t hrow = (size_t)lbc * H + hh;
+  const int P8 = d >> 4, p16 = d >> 3, g8 = d >> 3;
+  const int mpp = kMoveThreads / P8;
+  const int mq = threadIdx.x / P8, pc = threadIdx.x - mq * P8;
 
-  // round trip 1
+  // ---- round trip 1: everything whose address is known at launch: the
+  // header, this thread's list entries of the first INT8 round and the first
+  // mover's (speculatively, as the mover count is still unknown), the new
+  // row, and the scales the window step needs
   const i32x4 hA = reinterpret_cast<const i32x4*>(hdr)[0];  // MOV8, LEFT8, E8, JLO8
   const i32x4 hB = reinterpret_cast<const i32x4*>(hdr)[1];  // MOV16, LEFT16, E16, JLO16
-  const i32x4 hC = reinterpret_cast<const i32x4*>(hdr)[2];  // BASE8, BASE16, APPEND
-  // source windows (64 * NW movers) cover at least one round; the INT8 one
-  // is read speculatively with the header and covers 256 movers or more
-  constexpr int NW8 = ((NR * 64 >> L8) + 63) / 64 > 4 ? ((NR * 64 >> L8) + 63) / 64 : 4;
-  constexpr int NW16 = ((NR * 64 >> L16) + 63) / 64;
-  int sv8[NW8], sv16[NW16] = {};
+  const i32x4 hC = reinterpret_cast<const i32x4*>(hdr)[2];  // BASE8, BASE16, APPEND, Q
+  const i32x4 hD = reinterpret_cast<const i32x4*>(hdr)[3];  // CAL, B8N, B16N, M8
+  int lsp[HALF];
 #pragma unroll
-  for (int q = 0; q < NW8; ++q) sv8[q] = lane + 64 * q < cap ? src8[lane + 64 * q] : 0;
-  u32x4 nrow = {0u, 0u, 0u, 0u};
-  if (lane < P16) nrow = *reinterpret_cast<const u32x4*>((kv ? a.v_new : a.k_new) + ((size_t)lb * H + hh) * D + lane * 8);
+  for (int u = 0; u < HALF; ++u) lsp[u] = src8[min(mq + u * mpp, cap - 1)];
+  const int l0 = src8[0];
+  const bool nrow_lane = (int)threadIdx.x < 2 * p16;
+  const int nkind = (int)threadIdx.x >= p16, npc = threadIdx.x - nkind * p16;
+  u32x4 nv = {0u, 0u, 0u, 0u};
+  if (nrow_lane) nv = *reinterpret_cast<const u32x4*>((nkind ? a.v_new : a.k_new) + ((size_t)lb * H + hh) * d + npc * 8);
+  const bool q_lane = WINDOW && (int)threadIdx.x < 2 * g8;
+  const int qkind = (int)threadIdx.x >= g8, qch = 8 * (threadIdx.x - qkind * g8);
+  qf32x4 qs0 = {0.f, 0.f, 0.f, 0.f}, qs1 = qs0;
+  if (q_lane) {
+    const float* sp = (qkind ? c.vs : c.ks) + hrow * d + qch;
+    qs0 = *reinterpret_cast<const qf32x4*>(sp);
+    qs1 = *reinterpret_cast<const qf32x4*>(sp + 4);
+  }
+  asm volatile("" ::: "memory");  // the loads above are issued before the exit test
+
   const int append = hC[2];
-  if (append < 0) return;  // the plan flagged a capacity error
+  unsigned char* k8r = uniform_ptr(c.k8 + hrow * cap * d);
+  unsigned char* v8r = uniform_ptr(c.v8 + hrow * cap * d);
+  unsigned char* k16r = uniform_ptr(c.k16 + hrow * cap16 * d);
+  unsigned char* v16r = uniform_ptr(c.v16 + hrow * cap16 * d);
+  const int mv8 = hA[0], mv16 = hB[0], nq = WINDOW ? hC[3] : 0;
+  const int cal = hD[0], b8n = hD[1], b16n = hD[2], m8 = hD[3];
+  int* satp = c.meta + lbc * CONFK_META_WORDS + CONFK_META_SAT;
 
-  ring_rounds<D, L8, NW8, NR>(uniform_ptr((kv ? c.v8 : c.k8) + hrow * cap * D), cap, hA[0], hA[1], hA[2], hA[3],
-                            hC[0], src8, sv8, true);
-  unsigned char* r16 = uniform_ptr((kv ? c.v16 : c.k16) + hrow * cap16 * D);
-  ring_rounds<D, L16, NW16, NR>(r16, cap16, hB[0], hB[1], hB[2], hB[3], hC[1], src16, sv16, false);
+  if (mv8 <= HALF * mpp && mv16 == 0 && nq <= 1 && !(nq && cal)) {  // uniform
+    // ---- the common case: one INT8 round, no FP16 row moves, at most one
+    // token leaves the window and the scales exist. Round trip 2 reads the
+    // movers' rows and the leaving token's FP16 row (no FP16 row moves, so
+    // it is in place) and writes the appended row (its slot is no source).
+    gvec* kg = (gvec*)k8r;
+    gvec* vg = (gvec*)v8r;
+    const int left = hA[1], e = hA[2], jlo = hA[3], base = hC[0];
+    u32x4 v[2 * HALF];
+    uint32_t dof[HALF];
+    if (mv8 > 0) {
+#pragma unroll
+      for (int u = 0; u < HALF; ++u) {
+        const int rr = mq + u * mpp;
+        const bool in = rr < mv8;  // beyond the movers: repeat the first mover's piece
+        const int r = in ? rr : 0;
+        int ss = base + (in ? lsp[u] : l0);
+        ss = ss >= cap ? ss - cap : ss;
+        const uint32_t off = ((uint32_t)ss * (uint32_t)d + (uint32_t)pc * 16u) >> 4;
+        v[u] = kg[off];
+        v[HALF + u] = vg[off];
+        const int j = jlo + (left ? r : mv8 - 1 - r);
+        int ds = base + (left ? j : j + e);
+        ds = ds >= cap ? ds - cap : ds;
+        dof[u] = ((uint32_t)ds * (uint32_t)d + (uint32_t)pc * 16u) >> 4;
+      }
+    }
+    if (nrow_lane) *reinterpret_cast<u32x4*>((nkind ? v16r : k16r) + (size_t)append * 2 * d + npc * 16) = nv;
+    qu32x4 qh = {0u, 0u, 0u, 0u};
+    if (nq && q_lane) qh = *reinterpret_cast<const qu32x4*>((qkind ? v16r : k16r) + ((size_t)b16n * d + qch) * 2);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // every INT8 source has been read
+    if (mv8 > 0) {
+#pragma unroll
+      for (int u = 0; u < HALF; ++u) {
+        kg[dof[u]] = v[u];
+        vg[dof[u]] = v[HALF + u];
+      }
+    }
+    if (nq && q_lane) {
+      int ds = b8n + m8;
+      ds = ds >= cap ? ds - cap : ds;
+      float s8[8];
+#pragma unroll
+      for (int z = 0; z < 4; ++z) {
+        s8[z] = qs0[z];
+        s8[4 + z] = qs1[z];
+      }
+      int sat = 0;
+      *reinterpret_cast<qu32x2*>((qkind ? v8r : k8r) + (size_t)ds * d + qch) = quant8(qh, s8, sat);
+      if (sat) atomicAdd(satp, sat);
+    }
+    return;
+  }
 
-  // append: every FP16 source has been read (the waits above), and the slot
-  // is not a destination
-  if (lane < P16) *reinterpret_cast<u32x4*>(r16 + (uint32_t)append * (2 * D) + lane * 16) = nrow;
+  // ---- the general form: rounds over the lists, then the append, then the
+  // window step
+  move_rounds(k8r, v8r, (uint32_t)d, cap, P8, mv8, hA[1], hA[2], hA[3], hC[0], src8);
+  move_rounds(k16r, v16r, (uint32_t)(2 * d), cap16, p16, mv16, hB[1], hB[2], hB[3], hC[1], src16);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();  // every FP16 source has been read before the append slot is written
+  if (nrow_lane) *reinterpret_cast<u32x4*>((nkind ? v16r : k16r) + (size_t)append * 2 * d + npc * 16) = nv;
+  if constexpr (WINDOW) {
+    if (nq == 0) return;  // uniform
+    // the window step of this head: the nq oldest FP16 survivors become INT8
+    // (scales over every FP16 token of the head first, if the sequence has
+    // none yet), as quantize_window does for all heads
+    int fa = append - b16n;
+    fa = (fa < 0 ? fa + cap16 : fa) + 1;  // FP16 tokens after the append
+    __shared__ float sc[2 * kMaxHeadDim];
+    __shared__ int red[kMoveThreads / 64];
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // moved and appended rows are written
+    for (int e = threadIdx.x; e < 2 * d; e += kMoveThreads) {
+      const int kind = e >= d, ch = e - kind * d;
+      float* sp = (kind ? c.vs : c.ks) + hrow * d + ch;
+      if (cal) {
+        const uint16_t* ring = reinterpret_cast<const uint16_t*>(kind ? v16r : k16r);
+        float amax = 0.f;
+        for (int j = 0; j < fa; ++j) {
+          int slot = b16n + j;
+          if (slot >= cap16) slot -= cap16;
+          amax = fmaxf(amax, fabsf(half_bits_to_float(ring[(size_t)slot * d + ch])));
+        }
+        const float sv = __fdiv_rn(amax, 127.f);
+        *sp = sv;
+        sc[e] = sv;
+      } else {
+        sc[e] = *sp;
+      }
+    }
+    __syncthreads();  // scales in shared memory
+    int sat = 0;
+    for (int i = 0; i < nq; ++i) {
+      int ss = b16n + i;
+      ss = ss >= cap16 ? ss - cap16 : ss;
+      int ds = b8n + m8 + i;
+      ds = ds >= cap ? ds - cap : ds;
+      for (int g = threadIdx.x; g < 2 * g8; g += kMoveThreads) {
+        const int kind = g >= g8, ch = 8 * (g - kind * g8);
+        const qu32x4 h = *reinterpret_cast<const qu32x4*>((kind ? v16r : k16r) + ((size_t)ss * d + ch) * 2);
+        *reinterpret_cast<qu32x2*>((kind ? v8r : k8r) + (size_t)ds * d + ch) = quant8(h, sc + kind * d + ch, sat);
+      }
+    }
+    sat = wave_sum_i(sat);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = sat;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int tot = 0;
+      for (int q = 0; q < kMoveThreads / 64; ++q) tot += red[q];
+      if (tot) atomicAdd(satp, tot);
+    }
+  }
+}
+
+// The move kernel: a grid of at most kMoveGrid workgroups. Each reads the job
+// flags the plan kernel left (one per (layer, sequence): 1 when rows move),
+// lists the flagged pairs in shared memory with wave ballots, and walks the
+// items (flagged pair, kv head) from its own index in steps of the grid, so
+// that the work, not the cache shape, sets how many workgroups run.
+template <bool WINDOW>
+__global__ __launch_bounds__(kMoveThreads) void compact_move_kernel(CompactArgs a) {
+  extern __shared__ int jobl[];  // [nl * B]: the flagged (layer, sequence) pairs
+  __shared__ int wtot[kMoveThreads / 64];
+  const int npair = a.nl * a.c.B, H = a.c.hkv;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int njobs = 0;
+  for (int p0 = 0; p0 < npair; p0 += kMoveThreads) {
+    const int p = p0 + (int)threadIdx.x;
+    const bool f = p < npair && a.jobs[p] != 0;
+    const uint64_t m = __ballot(f);
+    const int pre = __popcll(m & lanemask_lt());
+    if (lane == 0) wtot[w] = __popcll(m);
+    __syncthreads();
+    int base = njobs, tot = 0;
+#pragma unroll
+    for (int q = 0; q < kMoveThreads / 64; ++q) {
+      base += q < w ? wtot[q] : 0;
+      tot += wtot[q];
+    }
+    if (f) jobl[base + pre] = p;
+    njobs += tot;
+    __syncthreads();  // wtot is rewritten by the next chunk; jobl is complete after the last
+  }
+  for (int it = blockIdx.x; it < njobs * H; it += gridDim.x) {
+    const int j = it / H;
+    move_item<WINDOW>(a, jobl[j], it - j * H);
+    __syncthreads();  // shared memory of the window step is reused by the next item
+  }
 }
 
 }  // namespace
 
-size_t compact_ws_bytes(int nlayers, int batch, int cap) {
-  // plan: header + two source lists per (layer, sequence); staging of the
-  // long-cache path: EMA and positions per (layer, sequence)
-  const size_t plan = (size_t)nlayers * batch * (kHdr + 2 * (size_t)cap) * 4;
-  const size_t stage = cap > kRegKeys * kThreads ? (size_t)nlayers * batch * stage_words(cap) * 4 : 0;
-  return plan + stage;
+size_t compact_jobs_offset(int nlayers, int batch, int cap) {
+  return (size_t)nlayers * batch * (kHdr + 2 * (size_t)cap) * 4;
 }
 
 size_t compact_plan_bytes(int nlayers, int batch, int cap) {
-  return (size_t)nlayers * batch * (kHdr + 2 * (size_t)cap) * 4;
+  // plan: header + two source lists per (layer, sequence), then one job flag
+  // per (layer, sequence), padded to 256 bytes
+  const size_t jobs = ((size_t)nlayers * batch * 4 + 255) / 256 * 256;
+  return compact_jobs_offset(nlayers, batch, cap) + jobs;
+}
+
+size_t compact_ws_bytes(int nlayers, int batch, int cap) {
+  // plan and job flags; staging of the long-cache path: EMA, positions and
+  // old indices per (layer, sequence)
+  const size_t stage = cap > kRegKeys * kThreads ? (size_t)nlayers * batch * stage_words(cap) * 4 : 0;
+  return compact_plan_bytes(nlayers, batch, cap) + stage;
 }
 
 template <int MODE, bool FUSE>
@@ -1141,26 +1344,22 @@ hipError_t launch_plan(const CompactArgs& a, hipStream_t s) {
 
 template <bool FUSE>
 hipError_t launch_compact_t(const CompactArgs& a, hipStream_t s) {
-  if (a.block == 0 && !a.stable)  // token eviction: one kernel plans, fills, packs and appends
-    return launch_plan<kFill, FUSE>(a, s);
+  // token eviction in the fill order: one kernel selects, fills, packs,
+  // moves and appends
+  if (a.block == 0 && !a.stable) return launch_plan<kFill, FUSE>(a, s);
+  // stable packing (token eviction in the stable order, block eviction): the
+  // plan kernel selects and plans, and finishes the (layer, sequence) pairs
+  // with nothing to move; the move kernel does the rest, spread over kv heads
   hipError_t e = a.block ? launch_plan<kBlock, FUSE>(a, s) : launch_plan<kStable, FUSE>(a, s);
   if (e != hipSuccess) return e;
-  const dim3 mgrid(a.nl * a.c.B, a.c.hkv), mblock(128);
-  if (a.c.d == 128) {
-    hipLaunchKernelGGL(compact_move_kernel<128>, mgrid, mblock, 0, s, a);
-  } else {
-    hipLaunchKernelGGL(compact_move_kernel<64>, mgrid, mblock, 0, s, a);
-  }
-  e = hipGetLastError();
-  if (e != hipSuccess || !a.quantize) return e;
-  // the move kernel moves the rows here: the window step follows it
-  QuantArgs q{};
-  q.c = a.c;
-  q.layer0 = a.layer0;
-  q.nl = a.nl;
-  q.t = a.t;
-  q.window = a.window;
-  return launch_quantize_step(q, s);
+  const int npair = a.nl * a.c.B;
+  const dim3 mgrid(min(npair * a.c.hkv, kMoveGrid)), mblock(kMoveThreads);
+  const size_t lds = (size_t)npair * sizeof(int);
+  if (FUSE && a.quantize)
+    hipLaunchKernelGGL(compact_move_kernel<true>, mgrid, mblock, lds, s, a);
+  else
+    hipLaunchKernelGGL(compact_move_kernel<false>, mgrid, mblock, lds, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {

@@ -72,6 +72,8 @@ struct EmaArgs {
 };
 
 constexpr int kMaxEvictBlocks = 512;  // blocks per sequence in block eviction
+constexpr int kMaxMoveHeadDim = 512;  // head dimension limit of stable packing (move kernel)
+constexpr int kMaxMovePairs = 16384;  // (layer, sequence) pairs per stable-packing call (move kernel)
 
 struct CompactArgs {
   CacheView c;
@@ -79,6 +81,7 @@ struct CompactArgs {
   int32_t block;  // 0: token eviction; B: whole blocks of B tokens
   int32_t stable; // token eviction with stable packing (the move kernel moves the rows)
   int32_t* plan;   // workspace: per-(layer, sequence) move plans
+  int32_t* jobs;   // workspace: per (layer, sequence), 1 if the move kernel has work there
   int32_t* stage;  // workspace: metadata staging (caches above 4096 tokens)
   const int32_t* budget;
   const float* score;
@@ -114,6 +117,7 @@ hipError_t launch_ema_rank(const EmaArgs& a, hipStream_t s);
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
 size_t compact_ws_bytes(int nlayers, int batch, int cap);
 size_t compact_plan_bytes(int nlayers, int batch, int cap);
+size_t compact_jobs_offset(int nlayers, int batch, int cap);
 hipError_t launch_quantize_step(const QuantArgs& a, hipStream_t s);
 hipError_t launch_prefill(const QuantArgs& a, hipStream_t s);
 

@@ -277,9 +277,11 @@ def select_keep(s, pos, N, P, block=0):
 def compact(cache, keep, fill=False):
     """Survivors packed densely; the INT8 entries stay ahead of the FP16 ones.
 
-    The pages ask for a contiguous layout without indirection tables and fix
-    no order inside it. fill=False keeps slot order (stable). fill=True
-    (reading R24, token eviction): in the INT8 part, the survivors that lie at
+    The pages ask for a contiguous layout without indirection tables; the
+    default, fill=False, is the stable gather: survivors keep slot order, so
+    a cache in position order stays in position order. fill=True (reading
+    R24, the hole-filling option of token eviction): in the INT8 part, the
+    survivors that lie at
     or beyond its new end m take the holes below m, the j-th such survivor
     (in slot order) the j-th hole; every other survivor keeps its slot. The
     FP16 part is always stable, so it stays in position order.
@@ -440,9 +442,11 @@ def step_one(cache, q, k_new, v_new, t, pol, N, score_given=None):
     kp = select_keep(s_sel, cache.pos, N, pol.protect, getattr(pol, "block", 0))
     c1 = cache.copy()
     c1.ema = a
-    # reading R24: token eviction fills INT8 holes from the INT8 tail unless
-    # the stable order (1) is asked for; block eviction packs stably
-    fill = getattr(pol, "block", 0) == 0 and getattr(pol, "order", 0) == 0
+    # Survivors keep position order (the review's Algorithm 1 compacts the
+    # survivors of C_l; the summary's "Implementierung" asks for a dense layout
+    # without indirection tables). Reading R24: order 1 is the hole-filling
+    # option of token eviction; block eviction always packs stably.
+    fill = getattr(pol, "block", 0) == 0 and getattr(pol, "order", 0) == 1
     c1 = compact(c1, kp, fill=fill)
     c1 = append(c1, k_new, v_new, t, a_new)
     c1 = quantize_window(c1, t, pol.window)

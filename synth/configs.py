@@ -22,7 +22,7 @@ class Policy:
     protect: int = 32
     window: int = 64
     block: int = 0     # 0: token eviction; B: whole blocks of B tokens
-    order: int = 0     # token eviction: 0 fills INT8 holes from the tail, 1 keeps position order
+    order: int = 0     # token eviction: 0 keeps position order (stable gather), 1 fills INT8 holes from the tail
 
 
 @dataclass(frozen=True)
@@ -124,10 +124,10 @@ CONFIGS = {
         name="qwen32b_block128", layers=64, batch=8, hq=40, hkv=8, d=128, vocab=152064,
         prefill=2048, steps=4096,
         policy=Policy(n_high=1024, n_low=2048, protect=64, window=256, block=128)),
-    # The Qwen-32B workload with the stable survivor order (both parts kept in
-    # position order, rows moved by a second kernel), same budgets
-    "qwen32b_stable": Config(
-        name="qwen32b_stable", layers=64, batch=8, hq=40, hkv=8, d=128, vocab=152064,
+    # The Qwen-32B workload with the hole-filling survivor order (the INT8
+    # holes below the new INT8 length take the INT8 tail), same budgets
+    "qwen32b_fill": Config(
+        name="qwen32b_fill", layers=64, batch=8, hq=40, hkv=8, d=128, vocab=152064,
         prefill=2048, steps=4096,
         policy=Policy(n_high=1024, n_low=2048, protect=64, window=256, order=1)),
     # Long-context pyramid with one planted key per sequence at depths

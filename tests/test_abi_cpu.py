@@ -34,7 +34,7 @@ def test_header_declares_the_five_calls():
 def test_library_exports_every_declared_symbol(lib):
     for n in declared():
         assert hasattr(lib, n), n
-    assert lib.confk_version() == 101
+    assert lib.confk_version() == 102
     assert lib.confk_strerror(-1) == b"invalid argument"
     assert lib.confk_strerror(12345) == b"unknown error"
 
@@ -124,7 +124,7 @@ def test_compact_quantize_ema_validation(lib):
     c = _fake_cache(cap=100, cap16=65)
     pol = _pol()
     wsb = lib.confk_workspace_size(M._lib.WS_COMPACT, ctypes.byref(c), 2, 0, 0)
-    assert wsb == 2 * 3 * (16 + 2 * 100) * 4
+    assert wsb == 2 * 3 * (16 + 2 * 100) * 4 + 256  # plans, then one job flag per (layer, sequence) padded to 256 B
     cp = lambda cc, p, stride=0, ws=FAKE, n=wsb: lib.confk_compact(  # noqa: E731
         ctypes.byref(cc), 0, 2, FAKE, stride, FAKE, ctypes.byref(p), FAKE, FAKE, None, ws, n, None)
     assert cp(c, _pol(), ws=None) == M.ERR_WORKSPACE
@@ -134,7 +134,7 @@ def test_compact_quantize_ema_validation(lib):
     assert cp(c, _pol(window=64), stride=5) == M.ERR_INVALID_ARG
     assert cp(c, _pol(window=80)) == M.ERR_BUDGET              # FP16 ring too small
     assert cp(c, _pol(lam=1.5)) == M.ERR_INVALID_ARG
-    assert cp(c, _pol(protect=20, window=16, n_high=24)) == M.ERR_BUDGET  # P > W, token eviction
+    assert cp(c, _pol(protect=20, window=16, n_high=24, order=1)) == M.ERR_BUDGET  # P > W, fill order
     assert cp(c, _pol(order=2)) == M.ERR_INVALID_ARG          # unknown survivor order
     assert cp(c, _pol(order=-1)) == M.ERR_INVALID_ARG
     assert cp(c, _pol(block=8)) == M.ERR_INVALID_ARG          # blocks below 16 tokens

@@ -232,10 +232,20 @@ def test_parity_plan_and_move_kernels_path():
     assert events > 0
 
 
-def test_selection_with_tied_scores():
-    """Crafted scores with heavy ties (same array on both sides)."""
-    cfg = TINY["g5_d128"]
-    print("[parity] tied scores", flush=True)
+@pytest.mark.parametrize("case", ["regs", "long", "long_block"])
+def test_selection_with_tied_scores(case):
+    """Crafted scores with heavy ties (same array on both sides), so that the
+    k-th key falls inside a large group of equal scores and the position
+    tie-break decides. The long cases (capacity above 4096: the plan rewrites
+    the metadata in place after staging it) put the tie boundary below the
+    kept count, where the rewritten slots are destinations of survivors."""
+    if case == "regs":
+        cfg = TINY["g5_d128"]
+    elif case == "long":
+        cfg = _cfg("tie_long", 1, 2, 5, 1, 128, 900, 5000, 600, 1200, 16, 64)
+    else:
+        cfg = _block_cfg(_cfg("tie_long", 1, 2, 5, 1, 128, 900, 5000, 600, 1200, 16, 64), 32)
+    print(f"[parity] tied scores {case}", flush=True)
     run = Run(cfg, seed=4)
     rng = np.random.default_rng(9)
     for i in range(8):
@@ -243,35 +253,54 @@ def test_selection_with_tied_scores():
         run.step(i, scores=s)
 
 
-def _stable_cfg(cfg, **pol):
+def _fill_cfg(cfg, **pol):
     from dataclasses import replace
-    return cfg.with_(name=f"{cfg.name}_stable", policy=replace(cfg.policy, order=1, **pol))
+    return cfg.with_(name=f"{cfg.name}_fill", policy=replace(cfg.policy, order=1, **pol))
 
 
-@pytest.mark.parametrize("case", ["regs", "long", "protect_above_window"])
-def test_parity_token_eviction_stable_order(case):
-    """Token eviction with the stable survivor order (pol.order = 1): both
-    parts keep position order and the move kernel moves the rows; every cache
-    byte against the oracle's stable compaction. The stable order also takes
-    a protected window larger than the FP16 window."""
+@pytest.mark.parametrize("case", ["regs", "long"])
+def test_parity_token_eviction_fill_order(case):
+    """Token eviction with the hole-filling option (pol.order = 1): the INT8
+    holes below the new INT8 length take the INT8 tail in slot order; every
+    cache byte against the oracle's fill compaction."""
     if case == "regs":
-        cfg = _stable_cfg(TINY["g5_d128"])
+        cfg = _fill_cfg(TINY["g5_d128"])
         steps = 24
-    elif case == "long":
-        cfg = _stable_cfg(_cfg("st_long", 1, 2, 5, 1, 128, 900, 5000, 600, 1200, 16, 64))
+    else:
+        cfg = _fill_cfg(_cfg("fl_long", 1, 2, 5, 1, 128, 900, 5000, 600, 1200, 16, 64))
         assert cfg.cap > 4096
         steps = 8
-    else:
-        cfg = _stable_cfg(_cfg("st_pw", 2, 2, 4, 2, 64, 500, 200, 60, 120, 24, 16))
-        steps = 40
-    print(f"[parity] stable order {case} cap={cfg.cap}", flush=True)
+    print(f"[parity] fill order {case} cap={cfg.cap}", flush=True)
     run = Run(cfg, seed=17)
     events = sum(run.step(i) for i in range(steps))
     assert events > 0
     assert run.band <= 1
-    for (l, b) in run.pairs:  # both parts in position order
-        p = run.eng.cache.snapshot(l, b)["pos"]
-        assert (np.diff(p) > 0).all(), (l, b)
+
+
+@pytest.mark.parametrize("case", ["long", "protect_above_window"])
+def test_parity_stable_order_positions_ascending(case):
+    """The default, stable survivor order: both parts keep position order
+    after every step (checked on every (layer, sequence), beside the
+    byte-for-byte comparison with the oracle); also with a protected window
+    larger than the FP16 window, which only this order accepts, and on a
+    cache above 4096 slots (long-form plan, lists in the workspace)."""
+    if case == "long":
+        cfg = _cfg("st_long", 1, 2, 5, 1, 128, 900, 5000, 600, 1200, 16, 64)
+        assert cfg.cap > 4096
+        steps = 8
+    else:
+        cfg = _cfg("st_pw", 2, 2, 4, 2, 64, 500, 200, 60, 120, 24, 16)
+        steps = 40
+    print(f"[parity] stable order {case} cap={cfg.cap}", flush=True)
+    run = Run(cfg, seed=17)
+    events = 0
+    for i in range(steps):
+        events += run.step(i)
+        for (l, b) in run.pairs:
+            p = run.eng.cache.snapshot(l, b)["pos"]
+            assert (np.diff(p) > 0).all(), (i, l, b)
+    assert events > 0
+    assert run.band <= 1
 
 
 def _block_cfg(cfg, block):
@@ -444,7 +473,7 @@ def test_qwen32b_shape_two_layers():
         run.step(i)
 
 
-@pytest.mark.parametrize("name", ["qwen32b", "qwen32b_stable", "qwen32b_block128", "qwen32b_pyramid",
+@pytest.mark.parametrize("name", ["qwen32b", "qwen32b_fill", "qwen32b_block128", "qwen32b_pyramid",
                                   "qwen32b_sw512", "qwen14b"])
 def test_full_launch_sampled(name):
     """Every layer of a benchmarked workload in the benchmark's launch
@@ -526,13 +555,14 @@ def test_many_movers_in_both_rings(d):
 
 
 FUSED_CASES = {
+    # the default, stable order: select, pack, move, append and window step in one kernel
     "g5_d128": lambda: TINY["g5_d128"],
     # empty start: the window step calibrates the scales inside the fused kernel
     "g3_d64_empty": lambda: TINY["g3_d64_empty"],
     # block eviction: the window step is a third launch after the move kernel
     "g5_d128_block16": lambda: _block_cfg(TINY["g5_d128"], 16),
-    # token eviction in the stable order: plan, move kernel, window step
-    "g5_d128_stable": lambda: _stable_cfg(TINY["g5_d128"]),
+    # token eviction in the hole-filling order (one kernel too)
+    "g5_d128_fill": lambda: _fill_cfg(TINY["g5_d128"]),
     # more than 4096 slots: the long-cache plan form
     "long_cache": lambda: _cfg("long_cache", 1, 2, 4, 2, 64, 300, 4200, 1500, 3000, 16, 64),
 }

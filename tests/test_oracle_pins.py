@@ -550,8 +550,10 @@ def _small_cfg():
 @pytest.mark.parametrize("order", [0, 1])
 def test_end_to_end_invariants(order):
     """Over a free run: lengths, counts, protection, the FP16 window, EMA range
-    and mass; the fill order (0) reorders the INT8 part at some step, the
-    stable order (1) keeps every position ascending (reading R24)."""
+    and mass. The default, stable order (0) keeps every position ascending
+    after every step, the new token last (the compacted survivors in their
+    original order); the hole-filling option (1, reading R24) reorders the
+    INT8 part at some step."""
     from dataclasses import replace
     cfg = _small_cfg()
     pol = replace(cfg.policy, order=order)
@@ -577,7 +579,7 @@ def test_end_to_end_invariants(order):
                 assert c1.pos[-1] == t and len(set(c1.pos.tolist())) == c1.n
                 assert c1.is8[:n8].all() and (np.diff(c1.pos[n8:]) > 0).all()
                 reordered |= bool((np.diff(c1.pos[:n8]) < 0).any())
-                if order == 1:
+                if order == 0:
                     assert (np.diff(c1.pos) > 0).all()
                 assert (c1.is8 == (c1.pos <= t - pol.window)).all()      # FP16 = window positions
                 # protected newest P of the pre-step cache survive
@@ -589,7 +591,7 @@ def test_end_to_end_invariants(order):
     # sawtooth: the cache both shrinks (confident steps) and regrows
     d = np.diff(lengths)
     assert (d < 0).any() and (d > 0).any()
-    assert reordered == (order == 0)  # the INT8 hole filling took place (fill order only)
+    assert reordered == (order == 1)  # the INT8 hole filling took place (fill order only)
 
 
 def test_ema_of_retained_token_follows_closed_recurrence():
