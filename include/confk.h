@@ -280,6 +280,30 @@ int confk_ema_compact(const confk_cache* cache, int32_t layer0, int32_t nlayers,
                       int32_t* evicted_out, int32_t flags, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * confk_ema_compact_static -- confk_ema_compact for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same call, results and errors, with
+ * the compaction scratch in a static device array of the library instead of
+ * a caller workspace. Nothing is allocated and no allocating routine is
+ * called (the array's address is looked up once per device, on the first
+ * call with that device current).
+ *   Limit: confk_workspace_size(CONFK_WS_COMPACT, cache, nlayers, ...) must
+ *   not exceed CONFK_STATIC_SCRATCH_BYTES (64 MiB; e.g. 64 layers x 8
+ *   sequences at 2050 slots need 8.4 MB); larger calls return
+ *   CONFK_ERR_WORKSPACE and enqueue nothing.
+ *   Each GPU holds one array for the life of the process, shared by every
+ *   call on that GPU: calls that overlap on one GPU (other streams, other
+ *   threads) race and must be serialised by the caller.
+ * Other errors: as confk_ema_compact; CONFK_ERR_LAUNCH if the device or the
+ * array's address cannot be obtained.
+ */
+#define CONFK_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+int confk_ema_compact_static(const confk_cache* cache, int32_t layer0, int32_t nlayers,
+                             const float* mass, const confk_policy* pol, int32_t t, float* score,
+                             const int32_t* budget, int32_t budget_layer_stride, const uint16_t* k_new,
+                             const uint16_t* v_new, int32_t* evicted_out, int32_t flags, void* stream);
+
+/*
  * confk_quantize -- FP16 -> INT8 storage per (head, channel).
  * Summary "Methodik" (gemischte Praezisionsspeicherung: newest W tokens FP16,
  * older retained tokens INT8 per head and channel); review Algorithm 1
@@ -329,7 +353,7 @@ const char* confk_strerror(int code);
 
 /* ABI version (major * 100 + minor). 101: confk_policy.order and the flags
  * argument of confk_ema_compact. 102: the stable survivor order is order 0
- * (the default) and the hole-filling order is 1. */
+ * (the default) and the hole-filling order is 1. 103: confk_ema_compact_static. */
 int confk_version(void);
 
 #ifdef __cplusplus

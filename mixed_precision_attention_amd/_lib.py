@@ -28,6 +28,7 @@ META_WORDS = 16
 QUANT_STEP = 0
 QUANT_PREFILL = 1
 FUSE_QUANTIZE = 1
+STATIC_SCRATCH_BYTES = 64 << 20
 ORDER_STABLE = 0
 ORDER_FILL = 1
 WS_CONFIDENCE = 0
@@ -37,7 +38,7 @@ WS_COMPACT = 2
 EXPORTS = [
     "confk_confidence", "confk_attn_decode", "confk_ema_rank", "confk_compact",
     "confk_quantize", "confk_workspace_size", "confk_strerror", "confk_version", "confk_ema_compact",
-    "confk_read_probe",
+    "confk_read_probe", "confk_ema_compact_static",
 ]
 
 
@@ -94,6 +95,9 @@ def load():
     lib.confk_ema_compact.argtypes = [P(Cache), c_int32, c_int32, c_void_p, P(Policy), c_int32, c_void_p,
                                       c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_int32, c_void_p,
                                       c_size_t, c_void_p]
+    lib.confk_ema_compact_static.argtypes = [P(Cache), c_int32, c_int32, c_void_p, P(Policy), c_int32,
+                                             c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
+                                             c_int32, c_void_p]
     lib.confk_read_probe.argtypes = [c_void_p, ctypes.c_uint64, c_void_p, c_void_p]
     lib.confk_workspace_size.argtypes = [c_int32, P(Cache), c_int32, c_int32, c_int32]
     lib.confk_workspace_size.restype = c_size_t
@@ -101,7 +105,7 @@ def load():
     lib.confk_strerror.restype = ctypes.c_char_p
     lib.confk_version.restype = ctypes.c_int
     for name in ("confk_confidence", "confk_attn_decode", "confk_ema_rank", "confk_compact", "confk_ema_compact",
-                 "confk_quantize", "confk_read_probe"):
+                 "confk_ema_compact_static", "confk_quantize", "confk_read_probe"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib

@@ -14,7 +14,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libconfk.so")
 
 SOURCES = ["abi.hip", "confidence.hip", "attention.hip", "ema_rank.hip", "compact.hip", "quantize.hip",
-           "probe.hip"]
+           "probe.hip", "noalloc.hip"]
 
 # Packed fp32 VALU instructions are disabled: the compiler still vectorises
 # fp16 work, and every fp32 op is a plain VOP.

@@ -37,7 +37,7 @@ int launch_status(hipError_t e) { return e == hipSuccess ? CONFK_OK : CONFK_ERR_
 
 extern "C" {
 
-int confk_version(void) { return 102; }
+int confk_version(void) { return 103; }
 
 const char* confk_strerror(int code) {
   switch (code) {

@@ -134,6 +134,18 @@ def ema_compact(cache, mass, pol, t, score, budget, budget_stride, k_new, v_new,
         ws.numel() * ws.element_size(), _stream()))
 
 
+def ema_compact_static(cache, mass, pol, t, score, budget, budget_stride, k_new, v_new, evicted=None,
+                       layer0=0, nlayers=None, fuse_quantize=False):
+    """confk_ema_compact_static: ema_compact with the library's static
+    scratch instead of a workspace (for callers that cannot allocate)."""
+    lib = L.load()
+    nl = cache.layers - layer0 if nlayers is None else nlayers
+    L.check("confk_ema_compact_static", lib.confk_ema_compact_static(
+        cache.ref(), layer0, nl, _p(mass), ctypes.byref(pol), int(t), _p(score), _p(budget),
+        int(budget_stride), _p(k_new), _p(v_new), _p(evicted), L.FUSE_QUANTIZE if fuse_quantize else 0,
+        _stream()))
+
+
 def quantize(cache, pol, t, mode=L.QUANT_STEP, k_src=None, v_src=None, n_src=0, layer0=0,
              nlayers=None):
     lib = L.load()
