@@ -526,6 +526,51 @@ def test_quantize_saturation_counted():
     assert list(codes[0, 0]) == [127, -50] and sat == 1
 
 
+def _empty_start_steps(rows_k, rows_v, W):
+    """Runs the oracle from an empty cache over len(rows_k) steps (one kv head,
+    no eviction), appending the given K/V rows; returns the caches after each step."""
+    from types import SimpleNamespace
+    pol = SimpleNamespace(lam=0.9, alpha=0.65, protect=0, window=W, block=0, order=0)
+    d = len(rows_k[0])
+    c = O.empty_cache(1, d)
+    out = []
+    q = np.ones((1, d))
+    for t, (k, v) in enumerate(zip(rows_k, rows_v)):
+        r = O.step_one(c, q, np.asarray([k], np.float16), np.asarray([v], np.float16), t, pol, N=100)
+        c = r["cache"]
+        out.append(c)
+    return out
+
+
+def test_first_calibration_from_an_empty_cache_hand_worked():
+    """Readings R17 + R18 from an empty cache with W = 2: the first token
+    leaves the FP16 window at step t = 2, after the append, so the scales are
+    set over the three tokens then cached (positions 0, 1, 2): the exiting
+    token, the middle one and the token just appended. Hand-worked rows put
+    each channel's absolute maximum on a different token, so leaving out the
+    appended token (channel 2) or the exiting one (channel 0 of K, channel 1
+    of V) changes a scale and the codes."""
+    K = [[3.0, -1.0, 0.5], [1.0, -5.0, 2.0], [-0.25, 4.0, -7.0]]
+    V = [[0.5, 6.0, -2.0], [-4.0, 1.0, 1.0], [1.0, -0.5, 2.5]]
+    c0, c1, c2 = _empty_start_steps(K, V, W=2)
+    # steps 0 and 1: nothing has left the window, no scales yet
+    for c in (c0, c1):
+        assert not c.calibrated and not c.is8.any()
+    # step 2: scales = fp32(absmax over positions 0, 1, 2) / 127, per channel
+    f = np.float32
+    want_ks = np.array([[f(3) / f(127), f(5) / f(127), f(7) / f(127)]], np.float32)
+    want_vs = np.array([[f(4) / f(127), f(6) / f(127), f(2.5) / f(127)]], np.float32)
+    assert c2.calibrated
+    assert np.array_equal(c2.ks.view(np.uint32), want_ks.view(np.uint32))
+    assert np.array_equal(c2.vs.view(np.uint32), want_vs.view(np.uint32))
+    # token 0 (and only it) is INT8 now: K 3/(3/127) = 127, -1/(5/127) = -25.4,
+    # 0.5/(7/127) = 9.07; V 0.5/(4/127) = 15.9, 6/(6/127) = 127, -2/(2.5/127) = -101.6
+    assert c2.pos.tolist() == [0, 1, 2] and c2.is8.tolist() == [True, False, False]
+    assert c2.k8[0, 0].tolist() == [127, -25, 9]
+    assert c2.v8[0, 0].tolist() == [16, 127, -102]
+    assert c2.saturated == 0
+
+
 def test_prefill_layout():
     rng = np.random.default_rng(12)
     H, L0, d, W = 2, 40, 8, 16
