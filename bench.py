@@ -270,6 +270,8 @@ def main():
         a1.record(stream)
         if not full:
             eng.step_ema_rank(t)
+        else:  # the comparison run's step: the new token's metadata slot only
+            M.engine.ema_rank(eng.cache, None, eng.pol, t, eng.score)
         c0.record(stream)
         eng.step_compact(kn, vn)
         c1.record(stream)

@@ -217,7 +217,11 @@ int confk_attn_decode(const confk_cache* cache, int32_t layer0, int32_t nlayers,
  * because the hole-filling order leaves the INT8 part out of position order.
  * The new token's metadata is written to slot n: ema[n] = (1-lambda) Abar_n,
  * pos[n] = t.
- *   mass   fp32 [nlayers][B][hkv][cap] from confk_attn_decode
+ *   mass   fp32 [nlayers][B][hkv][cap] from confk_attn_decode, or NULL for a
+ *          step without attention mass (a run that never evicts, e.g. the
+ *          full-cache comparison): then only slot n is written (ema[n] = 0,
+ *          pos[n] = t) and the cached tokens' EMA and the scores are left as
+ *          they are
  *   score  fp32 [nlayers][B][cap]
  * Errors: INVALID_ARG.
  */

@@ -140,7 +140,7 @@ int confk_attn_decode(const confk_cache* cache, int32_t layer0, int32_t nlayers,
 int confk_ema_rank(const confk_cache* cache, int32_t layer0, int32_t nlayers, const float* mass,
                    const confk_policy* pol, int32_t t, float* score, void* stream) {
   if (!cache_ok(cache) || !layers_ok(cache, layer0, nlayers)) return CONFK_ERR_INVALID_ARG;
-  if (!mass || !score || !policy_ok(pol) || t < 0) return CONFK_ERR_INVALID_ARG;
+  if (!score || !policy_ok(pol) || t < 0) return CONFK_ERR_INVALID_ARG;
   EmaArgs a{};
   a.c = view_of(cache);
   a.layer0 = layer0;

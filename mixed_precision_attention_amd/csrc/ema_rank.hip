@@ -32,7 +32,7 @@ __global__ __launch_bounds__(kThreads) void ema_rank_kernel(EmaArgs a) {
   const int n = meta[CONFK_META_N];
   float* ema = c.ema + (size_t)lbc * cap;
   int32_t* pos = c.pos + (size_t)lbc * cap;
-  const float* mass = a.mass + (size_t)lb * c.hkv * cap;
+  const float* mass = a.mass ? a.mass + (size_t)lb * c.hkv * cap : nullptr;
   float* score = a.score + (size_t)lb * cap;
   const float inv_hq = 1.f / (float)c.hq;
   const float lam = a.lambda;
@@ -42,6 +42,13 @@ __global__ __launch_bounds__(kThreads) void ema_rank_kernel(EmaArgs a) {
   if (!meta_ok(n, meta[CONFK_META_N8], meta[CONFK_META_BASE8], meta[CONFK_META_BASE16], cap,
                c.cap16)) {  // no slot for the new token: flag, leave the state alone
     if (threadIdx.x == 0) atomicOr(c.status, (uint32_t)CONFK_STATUS_CAPACITY);
+    return;
+  }
+  if (a.mass == nullptr) {  // no attention mass this step: only the new token's slot
+    if (threadIdx.x == 0) {
+      ema[n] = 0.f;
+      pos[n] = a.t;
+    }
     return;
   }
   __shared__ float red[kThreads / 64];

@@ -248,11 +248,10 @@ class DecodeEngine:
         if self.cfg.mode == "full_kv":
             # comparison run: attention output only, then the append (the
             # budget covers every token, so nothing is evicted or quantised).
-            # The rank call runs on the mass buffer, which stays all zero in
-            # this mode, because it writes the new token's position and EMA
-            # slot that the append stores.
+            # With no attention mass the rank call writes only the new
+            # token's metadata slot (position t), which the append stores.
             attn_decode(self.cache, q, k_new, v_new, self.out, None, None)
-            self.step_ema_rank(t)
+            ema_rank(self.cache, None, self.pol, t, self.score)
             self.step_compact(k_new, v_new)
             return
         if self.side is None:

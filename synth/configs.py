@@ -107,12 +107,13 @@ CONFIGS = {
         name="qwen32b", layers=64, batch=8, hq=40, hkv=8, d=128, vocab=152064,
         prefill=2048, steps=4096,
         policy=Policy(n_high=1024, n_low=2048, protect=64, window=256)),
-    # Comparison runs on the Qwen-32B shape: every token kept in FP16 (the
-    # window covers the whole run, the budget is never exceeded) ...
+    # Comparison runs on the Qwen-32B shape: every token kept in FP16 over the
+    # workload's 4096 generated tokens (window and budget cover the 6144
+    # tokens of prefill + generation, so nothing is evicted or quantised) ...
     "qwen32b_fullkv": Config(
         name="qwen32b_fullkv", layers=64, batch=8, hq=40, hkv=8, d=128, vocab=152064,
-        prefill=2048, steps=2048,
-        policy=Policy(n_high=4094, n_low=4094, protect=64, window=4094), mode="full_kv"),
+        prefill=2048, steps=4096,
+        policy=Policy(n_high=6144, n_low=6144, protect=64, window=6144), mode="full_kv"),
     # ... and a sliding window of the newest 512 tokens (recency-only rank)
     "qwen32b_sw512": Config(
         name="qwen32b_sw512", layers=64, batch=8, hq=40, hkv=8, d=128, vocab=152064,

@@ -161,8 +161,8 @@ def test_compact_quantize_ema_validation(lib):
     assert q(M.QUANT_PREFILL, n_src=-1) == M.ERR_INVALID_ARG
     assert lib.confk_ema_rank(ctypes.byref(c), 0, 2, FAKE, ctypes.byref(pol), -1, FAKE, None) \
         == M.ERR_INVALID_ARG
-    assert lib.confk_ema_rank(ctypes.byref(c), 0, 2, None, ctypes.byref(pol), 3, FAKE, None) \
-        == M.ERR_INVALID_ARG
+    assert lib.confk_ema_rank(ctypes.byref(c), 0, 2, FAKE, ctypes.byref(pol), 3, None, None) \
+        == M.ERR_INVALID_ARG  # no score buffer (a NULL mass is allowed: a step without mass)
 
 
 def test_binding_raises_on_error_code():

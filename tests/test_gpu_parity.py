@@ -182,18 +182,23 @@ def test_parity_gpt2_layer_workload():
 
 
 def test_parity_gpt2_stack_from_empty():
-    """The GPT-2 stack workload (12 layers from an empty cache, four sink
-    keys): past the first calibration at step W and through repeated
-    evictions, on three sampled layers."""
+    """The GPT-2 stack workload as configured: 12 layers from an empty cache
+    with four sink keys, all 2048 generated steps, every layer compared with
+    the oracle after every step (past the first calibration at step W and
+    through repeated evictions at both budgets)."""
     cfg = synth.get_config("gpt2_stack")
-    steps = 600
-    print(f"[parity] gpt2_stack steps={steps}", flush=True)
-    run = Run(cfg, seed=0, pairs=[(0, 0), (5, 0), (11, 0)])
-    events = sum(run.step(i) for i in range(steps))
+    steps = cfg.steps
+    print(f"[parity] gpt2_stack steps={steps} layers={cfg.layers}", flush=True)
+    run = Run(cfg, seed=0)
+    events = 0
+    for i in range(steps):
+        events += run.step(i)
+        if i % 256 == 255:
+            print(f"[parity] gpt2_stack step {i + 1}: {events} eviction events", flush=True)
     n, n8 = run.eng.cache.lengths()
     assert events > 0
     assert (n8 > 0).all()  # the INT8 region was calibrated and populated
-    assert run.band <= 2
+    assert run.band <= 4
 
 
 def test_parity_pyramid_budgets():
@@ -493,10 +498,12 @@ def test_full_launch_sampled(name):
 
 def test_full_kv_comparison_run_sampled():
     """The full FP16 comparison run at its size (64 layers x batch 8, a
-    2048-token prefill, window and budget 4094): attention without the
-    per-key mass over an all-FP16 cache, then the append; nothing is evicted
-    or quantised. Three (layer, sequence) pairs checked against the oracle;
-    the EMA decays under an all-zero mass in this run and is not compared."""
+    2048-token prefill, window and budget 6144 for its 4096 generated
+    tokens): attention without the per-key mass over an all-FP16 cache, the
+    rank call without mass (the new token's metadata slot only), then the
+    append; nothing is evicted or quantised. Three (layer, sequence) pairs
+    checked against the oracle, every cache byte, positions and the EMA (zero
+    throughout: no mass is accumulated in this run)."""
     import mixed_precision_attention_amd as M
     dev = _dev()
     cfg = synth.get_config("qwen32b_fullkv")
@@ -521,7 +528,7 @@ def test_full_kv_comparison_run_sampled():
             assert rel_maxabs(out[l, b], o) <= OTOL, f"{w}: attention output"
             orc[(l, b)] = O.append(orc[(l, b)], kn[l, b], vn[l, b], t, 0.0)
             assert not orc[(l, b)].is8.any()
-            assert_state_equal(eng.cache.snapshot(l, b), orc[(l, b)], ema_tol=np.inf, what=w)
+            assert_state_equal(eng.cache.snapshot(l, b), orc[(l, b)], what=w)
 
 
 def test_parity_many_heads_multi_round_moves():
