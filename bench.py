@@ -351,6 +351,11 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": counted_traffic(cfg.name),
+            "traffic_source": ("counted HBM bytes per launch (FETCH_SIZE x 2 + WRITE_SIZE) from the committed "
+                               "counter summary profiles/attn_decode_qwen32b_b8_traffic.md, taken on this "
+                               "attention source and workload, not in this run"
+                               if counted_traffic(cfg.name) is not None else
+                               "none: no counter summary matches this attention source and workload"),
             "kernel": (f"attn_decode_kernel<{cfg.d}, {'true' if eng.attn_ws is not None and not full else 'false'}, "
                        f"{'false' if full else 'true'}>"),
             "bytes_per_launch": int(attn_bytes),
@@ -367,6 +372,8 @@ def main():
             "value": round(sum(p["total"] for p in per_step) / cf["seconds"] / 1e9, 4),
             "unit": "GB/s",
             "cores": cf["threads"],
+            "host_cpus": os.cpu_count(),
+            "blas_threads": cf["threads"],
             "kind": "oracle",
             "sample": f"all {len(inputs)} steps of the run from the prefill, every (layer, sequence)",
             "steps_per_s": round(len(inputs) / cf["seconds"], 3),
@@ -380,6 +387,8 @@ def main():
             "value": round(step0 / cb["per_step_s"] / 1e9, 4),
             "unit": "GB/s",
             "cores": cb["threads"],
+            "host_cpus": os.cpu_count(),
+            "blas_threads": cb["threads"],
             "kind": "oracle",
             "sample": (f"the whole first decode step after the prefill: confidence of all {cfg.batch} rows "
                        f"and all {cb['pairs']} (layer, sequence) pairs"

@@ -139,6 +139,17 @@ CONFIGS = {
         policy=Policy(n_high=_PYR_HI[0], n_low=_PYR_LO[0], protect=64, window=256),
         layer_n_low=_PYR_LO, layer_n_high=_PYR_HI,
         plant_depths=(0.1, 0.3, 0.5, 0.7, 0.9), plant_beta=2.0 * 128 ** 0.5, plant_gamma=4.0),
+    # The same with a weak needle (a stand-in for the over-confident
+    # rare-entity lookups the pages name as a failure mode): the planted key
+    # has the norm of the other keys (beta = sqrt(d)) and the queries lean
+    # only gamma = 1 toward it, so its score is N(1, 1) against N(0, 1) for
+    # the others; retention can and does fail, most at the oldest depths
+    "qwen32b_niah_weak": Config(
+        name="qwen32b_niah_weak", layers=64, batch=5, hq=40, hkv=8, d=128, vocab=152064,
+        prefill=32768, steps=512,
+        policy=Policy(n_high=_PYR_HI[0], n_low=_PYR_LO[0], protect=64, window=256),
+        layer_n_low=_PYR_LO, layer_n_high=_PYR_HI,
+        plant_depths=(0.1, 0.3, 0.5, 0.7, 0.9), plant_beta=128 ** 0.5, plant_gamma=1.0),
     # Long-context pyramid (CONF-KV-L), Qwen-32B layer shape, batch 1
     "qwen32b_pyramid": Config(
         name="qwen32b_pyramid", layers=64, batch=1, hq=40, hkv=8, d=128, vocab=152064,
