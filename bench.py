@@ -47,6 +47,16 @@ def counted_traffic(workload):
     return int(rec["traffic_bytes_per_launch"])
 
 
+def attn_kernel_name(cfg, eng, full):
+    """Instance of the attention kernel the timed launches ran: spill store
+    (a workspace was needed), per-key mass (not in the full-cache run), and
+    the two-kv-heads-per-workgroup mass sum (fewer mass rows than kv heads)."""
+    spill = eng.attn_ws is not None and not full
+    acc = not full and bool((eng.cache.mass_rows() < cfg.hkv).any())
+    b = lambda x: "true" if x else "false"  # noqa: E731
+    return f"attn_decode_kernel<{cfg.d}, {b(spill)}, {b(not full)}, {b(acc)}>"
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -356,8 +366,7 @@ def main():
                                "attention source and workload, not in this run"
                                if counted_traffic(cfg.name) is not None else
                                "none: no counter summary matches this attention source and workload"),
-            "kernel": (f"attn_decode_kernel<{cfg.d}, {'true' if eng.attn_ws is not None and not full else 'false'}, "
-                       f"{'false' if full else 'true'}>"),
+            "kernel": attn_kernel_name(cfg, eng, full),
             "bytes_per_launch": int(attn_bytes),
         },
     }

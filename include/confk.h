@@ -69,6 +69,8 @@ extern "C" {
 #define CONFK_META_EVICTED 6 /* tokens evicted by the last confk_compact        */
 #define CONFK_META_MOVED 7   /* INT8 tokens moved by the last confk_compact     */
 #define CONFK_META_MOVED16 8 /* FP16 tokens moved by the last confk_compact     */
+#define CONFK_META_MASSROWS 9 /* mass rows written by the last confk_attn_decode
+                                 (0, as in a fresh cache, reads as hkv)          */
 #define CONFK_META_WORDS 16
 
 /* ---- confk_quantize modes ---------------------------------------------- */
@@ -190,10 +192,21 @@ int confk_confidence(const float* logits, int64_t ld, int32_t batch, int32_t voc
  *   q             fp16 [nlayers][B][hq][d]
  *   k_new, v_new  fp16 [nlayers][B][hkv][d]
  *   out           fp16 [nlayers][B][hq][d]
- *   mass          fp32 [nlayers][B][hkv][cap]: mass[..][j][i] = sum over the
- *                 query heads of kv head j of P_h,i, for i = 0..n (the
- *                 per-key mean over all query heads is sum_j / hq); or NULL
- *                 when the caller needs only the output (no workspace then)
+ *   mass          fp32 [nlayers][B][hkv][cap], rows of partial sums: the
+ *                 first R rows of a (layer, sequence), R = its meta word
+ *                 CONFK_META_MASSROWS (1 <= R <= hkv, written by this call),
+ *                 hold sums over disjoint runs of its kv heads of P_h,i
+ *                 summed over each kv head's query heads, i = 0..n, so that
+ *                 sum over rows r < R of mass[..][r][i] = sum over all query
+ *                 heads of P_h,i (the per-key mean is that sum / hq). Rows
+ *                 r >= R are left as they were. R = hkv (row j = kv head j)
+ *                 unless the launch's units (layer, sequence, kv head) fill
+ *                 at least two rounds of the GPU's resident workgroups; then
+ *                 each workgroup runs two consecutive units (kv heads
+ *                 fastest) and writes one row per (layer, sequence) of the
+ *                 two, so R = hkv / 2 for an even hkv. NULL
+ *                 when the caller needs only the output (no workspace then;
+ *                 the meta word is not touched)
  *   ws            >= confk_workspace_size(CONFK_WS_ATTENTION, ...) bytes
  *                 (score spill for caches too long for on-chip memory)
  * Layers layer0 .. layer0+nlayers-1 of the cache are processed; tensor
@@ -208,7 +221,9 @@ int confk_attn_decode(const confk_cache* cache, int32_t layer0, int32_t nlayers,
 /*
  * confk_ema_rank -- EMA update of the attention mass and rank scores.
  * Review "前置知识" (EMA: a_i <- lambda a_i + (1-lambda) Abar_i) and "核心方法"
- * (s_i = alpha a^_i + (1-alpha) r^_i). Abar_i = sum_j mass[j][i] / hq.
+ * (s_i = alpha a^_i + (1-alpha) r^_i). Abar_i = sum_{r<R} mass[r][i] / hq,
+ * R the (layer, sequence)'s CONFK_META_MASSROWS word (0 reads as hkv; a
+ * value above hkv is taken as hkv), rows summed in order.
  * For cached tokens i < n: ema[i] is updated in place, then
  * score[i] = alpha * ema[i] / max(ema) + (1 - alpha) * (pos[i] - pmin) /
  * (pmax - pmin), with pmin and pmax the smallest and largest position among
@@ -217,7 +232,8 @@ int confk_attn_decode(const confk_cache* cache, int32_t layer0, int32_t nlayers,
  * because the hole-filling order leaves the INT8 part out of position order.
  * The new token's metadata is written to slot n: ema[n] = (1-lambda) Abar_n,
  * pos[n] = t.
- *   mass   fp32 [nlayers][B][hkv][cap] from confk_attn_decode, or NULL for a
+ *   mass   fp32 [nlayers][B][hkv][cap] as confk_attn_decode writes it
+ *          (any per-kv-head mass with CONFK_META_MASSROWS = 0), or NULL for a
  *          step without attention mass (a run that never evicts, e.g. the
  *          full-cache comparison): then only slot n is written (ema[n] = 0,
  *          pos[n] = t) and the cached tokens' EMA and the scores are left as
@@ -357,7 +373,8 @@ const char* confk_strerror(int code);
 
 /* ABI version (major * 100 + minor). 101: confk_policy.order and the flags
  * argument of confk_ema_compact. 102: the stable survivor order is order 0
- * (the default) and the hole-filling order is 1. 103: confk_ema_compact_static. */
+ * (the default) and the hole-filling order is 1. 103: confk_ema_compact_static.
+ * 104: mass rows are partial sums over runs of kv heads (CONFK_META_MASSROWS). */
 int confk_version(void);
 
 #ifdef __cplusplus

@@ -9,7 +9,7 @@ from ._lib import (  # noqa: F401
     OK, ERR_INVALID_ARG, ERR_BUDGET, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_LAUNCH,
     STATUS_NONFINITE_LOGITS, STATUS_CAPACITY, QUANT_STEP, QUANT_PREFILL,
     META_N, META_N8, META_BASE8, META_BASE16, META_CALIB, META_SAT, META_EVICTED,
-    META_MOVED, META_MOVED16, META_WORDS,
+    META_MOVED, META_MOVED16, META_MASSROWS, META_WORDS,
 )
 from .engine import (  # noqa: F401
     make_policy, DeviceCache, DecodeEngine, confidence, attn_decode, ema_rank, compact, quantize,

@@ -22,7 +22,7 @@ STATUS_NONFINITE_LOGITS = 1
 STATUS_CAPACITY = 2
 
 (META_N, META_N8, META_BASE8, META_BASE16, META_CALIB, META_SAT, META_EVICTED, META_MOVED,
- META_MOVED16) = range(9)
+ META_MOVED16, META_MASSROWS) = range(10)
 META_WORDS = 16
 
 QUANT_STEP = 0

@@ -37,7 +37,7 @@ int launch_status(hipError_t e) { return e == hipSuccess ? CONFK_OK : CONFK_ERR_
 
 extern "C" {
 
-int confk_version(void) { return 103; }
+int confk_version(void) { return 104; }
 
 const char* confk_strerror(int code) {
   switch (code) {
@@ -101,6 +101,7 @@ int confk_confidence(const float* logits, int64_t ld, int32_t batch, int32_t voc
   a.layer_n_high = layer_n_high;
   a.layer_n_low = layer_n_low;
   a.partial = (float*)ws;
+  a.vecrec = ((uintptr_t)ws & 31) == 0;
   a.c_out = c_out;
   a.budget_out = budget_out;
   a.token_out = token_out;

@@ -38,6 +38,8 @@
 // instance, partly in a global spill area for caches too long for the LDS
 // budget); once the waves' running maxima and normalisers are merged, each
 // key's mass sum_h 2^(s_h - M_h) / L_h is formed exactly.
+#include <mutex>
+
 #include "confk_internal.h"
 
 namespace confk {
@@ -262,30 +264,80 @@ __host__ __device__ __forceinline__ int score_area_floats(int d, int g, int n_ld
   return sc > red ? sc : red;
 }
 
+// Units (layer, sequence, kv head) per workgroup with the LDS mass sum.
+// Two kv heads per workgroup halve the mass rows written; more would leave
+// a long last round of dispatch (e.g. 4 per workgroup: 4096 units of the
+// 64-layer, batch-8 shape become 1024 workgroups, 1.33 rounds of 768).
+constexpr int kAccUnits = 2;
+
+// Workgroup that runs unit x when U units are split into G contiguous
+// ranges, range w = [floor(w U / G), floor((w + 1) U / G)).
+__device__ __forceinline__ int unit_owner(uint32_t x, uint32_t U, uint32_t G) {
+  return (int)(((x + 1) * G - 1) / U);
+}
+
 // SPILL: scores past the LDS budget go to global memory. Kept out of the
 // common instance because global stores in the tile loop make the load
 // counter unusable for partial waits (stores complete out of order).
 // MASS = false: no per-key mass (no score store; for callers that only need
 // the attention output, e.g. a full-cache baseline).
-template <int D, bool SPILL, bool MASS>
+// ACC: workgroup w of G runs the contiguous unit range [w U / G, (w+1) U / G)
+// (kv heads fastest, at most kAccUnits units) and sums the mass of the
+// consecutive kv heads of one (layer, sequence) in LDS, so it writes one
+// partial mass row per (layer, sequence) it touches instead of one per kv
+// head. Row r of a (layer, sequence) is the r-th workgroup that covers it;
+// the row count goes to its metadata.
+template <int D, bool SPILL, bool MASS, bool ACC>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(CONFK_ATTN_OCCUPANCY)))
 void attn_decode_kernel(AttnArgs a) {
   constexpr int KC = Tile<D>::KC;
   constexpr int CB = Tile<D>::CB;
   constexpr int KU = Tile<D>::KU;
+  static_assert(!ACC || (MASS && !SPILL), "mass rows are summed in LDS only with the LDS score store");
   extern __shared__ float lds[];
 
   const CacheView& c = a.c;
-  const int u = blockIdx.x;
   const int H = c.hkv;
-  const int h = u % H;
-  const int lb = u / H;  // local (layer, sequence)
-  const int l = lb / c.B;
-  const int b = lb - l * c.B;
-  const int lbc = (a.layer0 + l) * c.B + b;
   const int g = a.g;
+  const uint32_t U = (uint32_t)a.nl * c.B * H;  // units of this launch (U * G < 2^32)
+  const uint32_t G = ACC ? gridDim.x : U;
+  const int wg = blockIdx.x;
+  const int u_begin = ACC ? (int)((uint32_t)wg * U / G) : wg;
+  const int u_end = ACC ? (int)((uint32_t)(wg + 1) * U / G) : wg + 1;
+  // (layer, sequence, kv head) of the current unit, advanced without
+  // divisions; a (layer, sequence) that starts inside this range has its
+  // first unit here, so this workgroup writes its row 0
+  int h = u_begin % H;
+  int lb = u_begin / H;  // local (layer, sequence)
+  int b = lb % c.B;
+  int l = lb / c.B;
+  const int lb_first = lb;
+  const int mrow_first = ACC ? wg - unit_owner((uint32_t)(lb * H), U, G) : h;
 
-  const int32_t* meta = c.meta + lbc * CONFK_META_WORDS;
+  // the work of one unit; ACC runs it for each unit of the range in turn
+  auto unit_body = [&](int u) __attribute__((always_inline)) {
+  if (u != u_begin) {
+    if (++h == H) {
+      h = 0;
+      ++lb;
+      if (++b == c.B) {
+        b = 0;
+        ++l;
+      }
+    }
+  }
+  // the thread index, opaque per unit: values derived from it are formed
+  // again in each unit instead of being held in registers across units
+  int tid = threadIdx.x;
+  if constexpr (ACC) asm volatile("" : "+v"(tid));
+  const int lbc = (a.layer0 + l) * c.B + b;
+  // mass row of this unit; its (layer, sequence)'s first workgroup writes
+  // the row count
+  const int mrow = !ACC ? h : (lb == lb_first ? mrow_first : 0);
+  const bool acc_first = !ACC || h == 0 || u == u_begin;    // first of this row's heads
+  const bool acc_last = !ACC || h == H - 1 || u == u_end - 1;  // last: write the row
+
+  int32_t* meta = c.meta + lbc * CONFK_META_WORDS;
   const int n = meta[CONFK_META_N];
   const int n8 = meta[CONFK_META_N8];
   const int base8 = meta[CONFK_META_BASE8];
@@ -293,9 +345,11 @@ void attn_decode_kernel(AttnArgs a) {
   const int f = n - n8;
   const int nk = n + 1;
   if (!meta_ok(n, n8, base8, base16, c.cap, c.cap16)) {  // uniform per workgroup
-    if (threadIdx.x == 0) atomicOr(c.status, (uint32_t)CONFK_STATUS_CAPACITY);
+    if (tid == 0) atomicOr(c.status, (uint32_t)CONFK_STATUS_CAPACITY);
     return;
   }
+  if (MASS && h == 0 && tid == 0)
+    meta[CONFK_META_MASSROWS] = ACC ? unit_owner((uint32_t)(lb * H + H - 1), U, G) - wg + 1 : H;
   const int nt8 = (n8 + 15) >> 4;
   const int nt16 = (f + 1 + 15) >> 4;
   const int p16 = nt8 * 16;  // first score slot of the FP16 region
@@ -310,8 +364,8 @@ void attn_decode_kernel(AttnArgs a) {
   const uint16_t* vn = a.v_new + ((size_t)lb * H + h) * D;
   float* spill = SPILL ? a.spill + (size_t)u * g * a.spill_stride : nullptr;
 
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index (uniform)
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
   const int r16 = lane & 15;
   const int kg = lane >> 4;
   const bool head_ok = r16 < g;
@@ -321,6 +375,7 @@ void attn_decode_kernel(AttnArgs a) {
   uint16_t* q_lds = reinterpret_cast<uint16_t*>(lds + score_area_floats(D, g, n_lds));  // [g][D]
   float* ks_lds = reinterpret_cast<float*>(q_lds + g * D);                               // [D]
   float* vs_lds = ks_lds + D;                                                            // [D]
+  float* acc_lds = vs_lds + D;  // [cap] mass of this row's earlier kv heads (ACC)
   const uint16_t* qrow = q_lds + (size_t)(head_ok ? r16 : 0) * D;
 
   float4_t acc[CB];
@@ -424,7 +479,7 @@ void attn_decode_kernel(AttnArgs a) {
   u32x4 piece[2];
 #pragma unroll
   for (int z = 0; z < 2; ++z) {  // unconditional loads (spare threads re-read piece 0)
-    const int e = threadIdx.x + z * kThreads;
+    const int e = tid + z * kThreads;
     const u32x4* src = e < qp             ? qsrc4 + e
                        : e < qp + D / 4   ? ks4 + (e - qp)
                        : e < npieces      ? vs4 + (e - qp - D / 4)
@@ -437,12 +492,12 @@ void attn_decode_kernel(AttnArgs a) {
   // tile, and the loads inside a loop body are unconditional, so the load
   // counter allows partial waits there.
   const int m8 = (nt8 - w + kWaves - 1) / kWaves;
-  Raw8<D> ra8, rb8, rc8;
+  Raw8<D> ra8{}, rb8{}, rc8{};  // defined on every path (the unit loop carries no undefined values)
   if (m8 >= 1) load8(ra8);
   if (m8 >= 2) load8(rb8);
 #pragma unroll
   for (int z = 0; z < 2; ++z) {
-    const int e = threadIdx.x + z * kThreads;
+    const int e = tid + z * kThreads;
     if (e < qp) {
       reinterpret_cast<u32x4*>(q_lds)[e] = piece[z];
     } else if (e < npieces) {
@@ -524,7 +579,7 @@ void attn_decode_kernel(AttnArgs a) {
 
   // ------------------------------------------------------ FP16 region + new
   const bool has16 = nt16 > w;
-  Raw16<D> ra, rb;
+  Raw16<D> ra{}, rb{};
   if (has16) load16(ra, w);
   if (has8) {
     // V scales of the INT8 part: channel of acc[cb][v] is CB*(4kg+v)+cb
@@ -591,8 +646,8 @@ void attn_decode_kernel(AttnArgs a) {
     wl[w][r16] = lt;
   }
   __syncthreads();
-  if ((int)threadIdx.x < g) {
-    const int hh = threadIdx.x;
+  if ((int)tid < g) {
+    const int hh = tid;
     float M = -INFINITY;
     for (int q = 0; q < kWaves; ++q) M = fmaxf(M, wm[q][hh]);
     float L = 0.f;
@@ -603,14 +658,15 @@ void attn_decode_kernel(AttnArgs a) {
   }
   __syncthreads();
 
-  // per-key mass (summed over this kv head's query heads)
-  float* mout = a.mass + ((size_t)lb * H + h) * c.cap;
+  // per-key mass (summed over this kv head's query heads, and with ACC
+  // over this row's earlier kv heads)
+  float* mout = a.mass + ((size_t)lb * H + mrow) * c.cap;
   if constexpr (MASS && !SPILL) {
     // groups of 4 slots (both regions start 16-aligned; slots past a region
     // hold masked scores and are not written out); all heads' scores of a
     // group are fetched before the exponentials
     const int q8 = (n8 + 3) >> 2, q16 = (f + 1 + 3) >> 2;
-    for (int gi = threadIdx.x; gi < q8 + q16; gi += kThreads) {
+    for (int gi = tid; gi < q8 + q16; gi += kThreads) {
       const bool r8 = gi < q8;
       const int slot = r8 ? 4 * gi : p16 + 4 * (gi - q8);
       const int i0 = r8 ? 4 * gi : n8 + 4 * (gi - q8);
@@ -632,11 +688,19 @@ void attn_decode_kernel(AttnArgs a) {
         }
       }
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
-        if (i0 + v < lim) mout[i0 + v] = sum[v];
+      for (int v = 0; v < 4; ++v) {
+        if (i0 + v < lim) {
+          float m = sum[v];
+          if constexpr (ACC) {  // each thread owns the same keys in every unit of a row
+            if (!acc_first) m += acc_lds[i0 + v];
+            if (!acc_last) acc_lds[i0 + v] = m;
+          }
+          if (acc_last) mout[i0 + v] = m;
+        }
+      }
     }
   } else if constexpr (MASS) {
-    for (int i = threadIdx.x; i < nk; i += kThreads) {
+    for (int i = tid; i < nk; i += kThreads) {
       const int p = i < n8 ? i : p16 + (i - n8);
       const float u = i < n8 ? usc[0] : usc[1];
       float sum = 0.f;
@@ -667,13 +731,24 @@ void attn_decode_kernel(AttnArgs a) {
   }
   __syncthreads();
   uint16_t* ob = a.out + qoff;
-  for (int idx = threadIdx.x; idx < g * D; idx += kThreads) {
+  for (int idx = tid; idx < g * D; idx += kThreads) {
     const int hh = idx / D, ch = idx - hh * D;
     const int off = hh * RR + (ch / (D / 4)) * RB + ch % (D / 4);
     float o = 0.f;
 #pragma unroll
     for (int q = 0; q < kWaves; ++q) o += red[(size_t)q * g * RR + off];
     ob[idx] = float_to_half_bits(o);
+  }
+  if constexpr (ACC) __syncthreads();  // the next unit reuses the LDS
+  };
+  if constexpr (ACC) {
+    // written out once per unit rather than as a loop: a loop keeps values
+    // live across its back edge and spills registers in the tile loops
+#pragma unroll
+    for (int k = 0; k < kAccUnits; ++k)
+      if (u_begin + k < u_end) unit_body(u_begin + k);
+  } else {
+    unit_body(u_begin);
   }
 }
 
@@ -704,19 +779,76 @@ int attention_plan_n_lds(int d, int g, int cap, int* spill_stride) {
   return fit;
 }
 
-hipError_t launch_attention(const AttnArgs& a, int lds_bytes, hipStream_t s) {
-  const int units = a.nl * a.c.B * a.c.hkv;
-  const dim3 grid(units), block(kThreads);
-  if (a.c.d == 128) {
-    if (!a.mass) hipLaunchKernelGGL((attn_decode_kernel<128, false, false>), grid, block, lds_bytes, s, a);
-    else if (a.spill) hipLaunchKernelGGL((attn_decode_kernel<128, true, true>), grid, block, lds_bytes, s, a);
-    else hipLaunchKernelGGL((attn_decode_kernel<128, false, true>), grid, block, lds_bytes, s, a);
+namespace {
+
+// Compute units of the current device, read once per device.
+int device_cus() {
+  static std::mutex mu;
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if (dev < 64 && cus[dev]) return cus[dev];
+  int v = 0;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) v = 0;
+  if (dev < 64) cus[dev] = v;
+  return v;
+}
+
+// Resident workgroups per compute unit of a kernel at a dynamic LDS size,
+// remembered per (kernel, size).
+int resident_per_cu(const void* fn, int lds_bytes) {
+  struct Entry {
+    const void* fn;
+    int lds, dev, occ;
+  };
+  static std::mutex mu;
+  static Entry seen[32];
+  static int nseen = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  for (int i = 0; i < nseen; ++i)
+    if (seen[i].fn == fn && seen[i].lds == lds_bytes && seen[i].dev == dev) return seen[i].occ;
+  int occ = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, kThreads, (size_t)lds_bytes) != hipSuccess) occ = 0;
+  seen[nseen % 32] = Entry{fn, lds_bytes, dev, occ};
+  ++nseen;
+  return occ;
+}
+
+template <int D>
+hipError_t launch_d(const AttnArgs& a, int lds_bytes, hipStream_t s) {
+  const int64_t units = (int64_t)a.nl * a.c.B * a.c.hkv;
+  const dim3 block(kThreads);
+  if (!a.mass) {
+    hipLaunchKernelGGL((attn_decode_kernel<D, false, false, false>), dim3(units), block, lds_bytes, s, a);
+  } else if (a.spill) {
+    hipLaunchKernelGGL((attn_decode_kernel<D, true, true, false>), dim3(units), block, lds_bytes, s, a);
   } else {
-    if (!a.mass) hipLaunchKernelGGL((attn_decode_kernel<64, false, false>), grid, block, lds_bytes, s, a);
-    else if (a.spill) hipLaunchKernelGGL((attn_decode_kernel<64, true, true>), grid, block, lds_bytes, s, a);
-    else hipLaunchKernelGGL((attn_decode_kernel<64, false, true>), grid, block, lds_bytes, s, a);
+    // At least two rounds of resident workgroups: kAccUnits kv heads per
+    // workgroup with the mass summed in LDS, if the accumulator costs no
+    // residency (the launch keeps at least one round).
+    const int acc_bytes = lds_bytes + 4 * ((a.c.cap + 3) / 4 * 4);
+    const void* plain = reinterpret_cast<const void*>(&attn_decode_kernel<D, false, true, false>);
+    const void* acc = reinterpret_cast<const void*>(&attn_decode_kernel<D, false, true, true>);
+    const int occ_acc = resident_per_cu(acc, acc_bytes);
+    const int64_t slots = (int64_t)occ_acc * device_cus();
+    const int64_t groups = (units + kAccUnits - 1) / kAccUnits;
+    if (occ_acc > 0 && slots > 0 && groups >= slots && units * (groups + 1) < ((int64_t)1 << 32) &&
+        occ_acc >= resident_per_cu(plain, lds_bytes)) {
+      hipLaunchKernelGGL((attn_decode_kernel<D, false, true, true>), dim3(groups), block, acc_bytes, s, a);
+    } else {
+      hipLaunchKernelGGL((attn_decode_kernel<D, false, true, false>), dim3(units), block, lds_bytes, s, a);
+    }
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attention(const AttnArgs& a, int lds_bytes, hipStream_t s) {
+  return a.c.d == 128 ? launch_d<128>(a, lds_bytes, s) : launch_d<64>(a, lds_bytes, s);
 }
 
 }  // namespace confk

@@ -319,13 +319,13 @@ __device__ __forceinline__ void plan_body(const CompactArgs& a) {
 
   // ------------------------------------------------- 0. EMA + rank (fused)
   if constexpr (FUSE) {
-    const int H = c.hkv;
-    const float* mass = a.mass + (size_t)lb * H * cap;
+    const int H = mass_rows(meta, c.hkv);  // rows of partial mass sums
+    const float* mass = a.mass + (size_t)lb * c.hkv * cap;
     const float inv_hq = 1.f / (float)c.hq, lam = a.lambda, oml = 1.f - lam;
     float amax = 0.f;
     int pmin = INT32_MAX, pmax = INT32_MIN;
     // a_i = lam a_i + (1 - lam) Abar_i for cached tokens, (1 - lam) Abar_n for
-    // the new one (zero prior); kv heads summed in order. Lane-strided
+    // the new one (zero prior); mass rows summed in order. Lane-strided
     // ownership (index threadIdx.x + r * kThreads) keeps the loads coalesced.
     if constexpr (REG) {
       float ms[kRegKeys], av[kRegKeys];

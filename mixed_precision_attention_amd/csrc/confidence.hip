@@ -184,14 +184,18 @@ __global__ __launch_bounds__(kThreads) void conf_partial_kernel(ConfArgs a) {
     RowState r = red[0];
     for (int i = 1; i < kThreads / 64; ++i) r = merge<CH>(r, red[i], inv_t);
     float* p = a.partial + ((int64_t)b * a.nchunks + chunk) * kRec;
-    p[0] = r.M;
-    p[1] = r.S;
-    p[2] = r.T;
-    p[3] = r.t1;
-    p[4] = r.t2;
-    p[5] = __builtin_bit_cast(float, r.flag);
-    p[6] = r.ST;
-    p[7] = __builtin_bit_cast(float, r.i1);
+    const f32x4 lo = {r.M, r.S, r.T, r.t1};
+    const f32x4 hi = {r.t2, __builtin_bit_cast(float, r.flag), r.ST, __builtin_bit_cast(float, r.i1)};
+    if (a.vecrec) {
+      reinterpret_cast<f32x4*>(p)[0] = lo;
+      reinterpret_cast<f32x4*>(p)[1] = hi;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        p[e] = lo[e];
+        p[4 + e] = hi[e];
+      }
+    }
   }
 }
 
@@ -204,15 +208,29 @@ __global__ __launch_bounds__(64) void conf_final_kernel(ConfArgs a) {
   const float* p = a.partial + (int64_t)b * a.nchunks * kRec;
   const float inv_t = a.inv_temp;
   auto load = [&](int i) {
+    f32x4 lo, hi;
+    if (a.vecrec) {
+      lo = reinterpret_cast<const f32x4*>(p + kRec * i)[0];
+      hi = reinterpret_cast<const f32x4*>(p + kRec * i)[1];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        lo[e] = p[kRec * i + e];
+        hi[e] = p[kRec * i + 4 + e];
+      }
+    }
     RowState q;
-    q.M = p[kRec * i + 0];
-    q.S = p[kRec * i + 1];
-    q.T = p[kRec * i + 2];
-    q.t1 = p[kRec * i + 3];
-    q.t2 = p[kRec * i + 4];
-    q.flag = __builtin_bit_cast(uint32_t, p[kRec * i + 5]);
-    q.ST = p[kRec * i + 6];
-    q.i1 = __builtin_bit_cast(int32_t, p[kRec * i + 7]);
+    q.M = lo[0];
+    q.S = lo[1];
+    q.T = lo[2];
+    q.t1 = lo[3];
+    q.t2 = hi[0];
+    // vector elements are copied to scalars before the bit casts (a bit cast
+    // of the element expression itself reads element 0)
+    const float flag_bits = hi[1], i1_bits = hi[3];
+    q.flag = __builtin_bit_cast(uint32_t, flag_bits);
+    q.ST = hi[2];
+    q.i1 = __builtin_bit_cast(int32_t, i1_bits);
     return q;
   };
   RowState r;
@@ -316,11 +334,12 @@ __global__ __launch_bounds__(64) void conf_final_kernel(ConfArgs a) {
     if (lane == 0) a.token_out[b] = tok;
   }
 
-  if (lane != 0) return;
+  // every lane holds the merged state: each computes c, lane l writes the
+  // budgets of layers l, l + 64, ... (per-layer budgets in parallel)
   float c;
   if (bad) {
     c = __builtin_nanf("");
-    if (a.status) atomicOr(a.status, (uint32_t)CONFK_STATUS_NONFINITE_LOGITS);
+    if (lane == 0 && a.status) atomicOr(a.status, (uint32_t)CONFK_STATUS_NONFINITE_LOGITS);
   } else {
     const float H = logf(r.S) - r.T / r.S;
     const float Hn = H / logf((float)a.vocab);
@@ -329,9 +348,9 @@ __global__ __launch_bounds__(64) void conf_final_kernel(ConfArgs a) {
     const float p1 = 1.f / r.S;
     c = a.w_h * (1.f - Hn) + a.w_m * sig + a.w_p * p1;
   }
-  a.c_out[b] = c;
+  if (lane == 0) a.c_out[b] = c;
   const bool tight = c >= a.tau;  // false for NaN
-  for (int l = 0; l < a.nbl; ++l) {
+  for (int l = lane; l < a.nbl; l += 64) {
     const int nh = a.layer_n_high ? a.layer_n_high[l] : a.n_high;
     const int nlo = a.layer_n_low ? a.layer_n_low[l] : a.n_low;
     a.budget_out[(int64_t)l * a.batch + b] = tight ? nh : nlo;

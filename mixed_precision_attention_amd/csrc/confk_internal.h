@@ -37,6 +37,7 @@ struct ConfArgs {
   int64_t ld;
   int32_t batch, vocab, chunk, nchunks, nbl;
   int32_t vec4;  // rows are 16-byte aligned: vector loads
+  int32_t vecrec;  // partial records are 32-byte aligned: vector loads/stores
   float tau, w_h, w_m, w_p;
   int32_t n_high, n_low;
   const int32_t* layer_n_high;
@@ -143,6 +144,13 @@ __device__ __forceinline__ int wave_sum_i(int x) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
   return x;
+}
+
+// Mass rows of a (layer, sequence): its CONFK_META_MASSROWS word, where 0
+// (a fresh cache) or a value outside 1..hkv reads as hkv (one row per kv head).
+__device__ __forceinline__ int mass_rows(const int32_t* meta, int hkv) {
+  const int r = meta[CONFK_META_MASSROWS];
+  return (r >= 1 && r <= hkv) ? r : hkv;
 }
 
 // A (layer, sequence) header the kernels can act on: room for the new token

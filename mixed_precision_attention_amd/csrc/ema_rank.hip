@@ -37,7 +37,7 @@ __global__ __launch_bounds__(kThreads) void ema_rank_kernel(EmaArgs a) {
   const float inv_hq = 1.f / (float)c.hq;
   const float lam = a.lambda;
   const float oml = 1.f - lam;
-  const int H = c.hkv;
+  const int H = mass_rows(meta, c.hkv);  // rows of partial mass sums
 
   if (!meta_ok(n, meta[CONFK_META_N8], meta[CONFK_META_BASE8], meta[CONFK_META_BASE16], cap,
                c.cap16)) {  // no slot for the new token: flag, leave the state alone
@@ -72,7 +72,7 @@ __global__ __launch_bounds__(kThreads) void ema_rank_kernel(EmaArgs a) {
         pv[r] = pos[i];
       }
     }
-    // eight kv heads' partial masses per round trip, summed in head order
+    // eight partial mass rows per round trip, summed in row order
     for (int j0 = 0; j0 < H; j0 += 8) {
       float t8[8][kPer];
 #pragma unroll

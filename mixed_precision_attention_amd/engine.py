@@ -67,6 +67,12 @@ class DeviceCache:
         m = self.meta.cpu().numpy()
         return m[..., L.META_N], m[..., L.META_N8]
 
+    def mass_rows(self):
+        """Rows of partial mass sums of each (layer, sequence) from the last
+        attention call (the meta word; 0 in a fresh cache reads as hkv)."""
+        r = self.meta[..., L.META_MASSROWS].cpu().numpy()
+        return np.where((r >= 1) & (r <= self.hkv), r, self.hkv)
+
     def snapshot(self, l, b):
         """Host copy of one (layer, sequence) in logical order (INT8 part first)."""
         m = self.meta[l, b].cpu().numpy()

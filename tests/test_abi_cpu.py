@@ -34,7 +34,7 @@ def test_header_declares_the_five_calls():
 def test_library_exports_every_declared_symbol(lib):
     for n in declared():
         assert hasattr(lib, n), n
-    assert lib.confk_version() == 103
+    assert lib.confk_version() == 104
     assert lib.confk_strerror(-1) == b"invalid argument"
     assert lib.confk_strerror(12345) == b"unknown error"
 

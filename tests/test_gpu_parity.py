@@ -109,6 +109,7 @@ class Run:
         eng.step_attention(qd, kd, vd)
         out = eng.out.float().cpu().numpy()
         mass = eng.mass.cpu().numpy()
+        rows = eng.cache.mass_rows()
         eng.step_ema_rank(t)
         ema = eng.cache.ema.cpu().numpy()
         if scores is not None:
@@ -138,7 +139,7 @@ class Run:
             sg = None if scores is None else scores[l, b, :n]
             r = O.step_one(pre, q[l, b], kn[l, b], vn[l, b], t, pol, N, score_given=sg)
             assert rel_maxabs(out[l, b], r["o"]) <= OTOL, f"{w}: attention output"
-            m = mass[l, b, :, : n + 1].sum(0) / cfg.hq
+            m = mass[l, b, : rows[l, b], : n + 1].sum(0) / cfg.hq
             assert np.abs(m - r["mass"]).max() <= ATOL, f"{w}: mass"
             assert np.abs(ema[l, b, :n] - r["ema"]).max(initial=0) <= ATOL, f"{w}: EMA"
             assert abs(ema[l, b, n] - r["a_new"]) <= ATOL, f"{w}: new-token EMA"
@@ -690,6 +691,47 @@ def test_attention_without_mass_gives_the_same_output():
         eng.step_ema_rank(t)
         eng.step_compact(kd, vd)
         eng.step_quantize(t)
+
+
+def test_two_kv_heads_per_workgroup_mass_rows():
+    """At the Qwen-32B shape and batch 8 the launch's 4096 units fill more
+    than two rounds of resident workgroups, so attention runs two kv heads
+    per workgroup and writes hkv / 2 summed mass rows per (layer, sequence)
+    (recorded in the metadata); a launch over one layer (64 units) writes one
+    row per kv head. Each summed row equals the sum of its two per-head rows
+    to fp32 rounding, and the output is the same."""
+    import mixed_precision_attention_amd as M
+    dev = _dev()
+    cfg = synth.get_config("qwen32b")
+    H = cfg.hkv
+    eng = M.DecodeEngine(cfg, dev)
+    kp, vp = synth.gen.prefill_kv_device(cfg, 5, dev)
+    eng.prefill(kp, vp)
+    del kp, vp
+    for s in range(3):  # mixed lengths: the first steps evict to either budget
+        lg = synth.gen.logits_device(cfg, 5, s, dev)
+        q, kn, vn = synth.gen.decode_inputs_device(cfg, 5, s, dev)
+        eng.step(lg, q, kn, vn, cfg.prefill + s)
+    q, kn, vn = synth.gen.decode_inputs_device(cfg, 5, 3, dev)
+    M.engine.attn_decode(eng.cache, q, kn, vn, eng.out, eng.mass, eng.attn_ws)
+    torch.cuda.synchronize()
+    assert (eng.cache.mass_rows() == H // 2).all()
+    out_all, mass_all = eng.out.clone(), eng.mass.clone()
+    n = eng.cache.lengths()[0]
+    for l in (0, 37, cfg.layers - 1):
+        M.engine.attn_decode(eng.cache, q[l:], kn[l:], vn[l:], eng.out[l:], eng.mass[l:], eng.attn_ws,
+                             layer0=l, nlayers=1)
+        torch.cuda.synchronize()
+        assert (eng.cache.mass_rows()[l] == H).all()
+        for b in range(cfg.batch):
+            k = int(n[l, b]) + 1
+            per_head = eng.mass[l, b, :, :k].double().cpu().numpy()
+            summed = mass_all[l, b, : H // 2, :k].double().cpu().numpy()
+            want = per_head[0::2] + per_head[1::2]
+            assert np.abs(summed - want).max() <= 1e-6 * max(1.0, np.abs(want).max()), f"l={l} b={b}: mass rows"
+            got = out_all[l, b].float().cpu().numpy()
+            ref = eng.out[l, b].float().cpu().numpy()
+            assert rel_maxabs(got, ref) <= OTOL / 2, f"l={l} b={b}: output"
 
 
 def test_long_context_pyramid_retains_planted_keys():
