@@ -32,12 +32,15 @@
 //     metadata are rewritten in place after a barrier that follows every
 //     read. The fused form (FUSE) starts with the EMA update and rank scores
 //     and may end with the window step of the quantisation.
-//  4. Token eviction in the stable order (kStable) and block eviction
-//     (kBlock) pack both regions that way and leave the moves to:
-// Move kernel (one wave per (layer, sequence, kv head, K|V) ring): the
-// planned rows move in rounds (read all rows of a round, wait, write them) in
-// an order that never overwrites an unread source; then the new token's row
-// is written to the FP16 ring.
+//  4. Token eviction in the stable order (kStable, the default) and block
+//     eviction (kBlock) pack both regions that way. A (layer, sequence)
+//     with nothing to move is finished here (append, window step); the
+//     others are flagged for:
+// Move kernel (a fixed grid over the flagged (layer, sequence, kv head)
+// items): the planned rows of a head's rings move in rounds (read all rows
+// of a round, wait, write them) in an order that never overwrites an unread
+// source; then the new token's rows are written to the FP16 rings, and in
+// the fused form the head's window step follows.
 #include <type_traits>
 
 #include "quantize_seq.h"
