@@ -20,7 +20,8 @@
  *   confk_quantize     FP16 token that left the window -> INT8   (step 10)
  * confk_ema_compact runs confk_ema_rank and confk_compact (and, with
  * CONFK_FUSE_QUANTIZE, confk_quantize's window step) as one launch with the
- * same results; confk_read_probe is a measurement aid beside the step.
+ * same results. The streaming-read probe that measurements compare the
+ * attention kernel with is a separate library (confk_probe.h).
  *
  * Conventions for every entry point:
  *  - Pointers named in a confk_cache and every tensor argument are DEVICE
@@ -350,23 +351,6 @@ int confk_quantize(const confk_cache* cache, int32_t layer0, int32_t nlayers, in
  * none is needed. */
 size_t confk_workspace_size(int32_t which, const confk_cache* cache, int32_t nlayers,
                             int32_t batch, int32_t vocab);
-
-/*
- * confk_read_probe -- a measurement aid beside the five calls, not a step of
- * the method: reads `bytes` of device memory at `buf` once, with the 16-byte
- * non-temporal loads (whole 128-byte lines per instruction) that
- * confk_attn_decode streams its cache with, so that a timed launch measures
- * the streaming-read rate HBM sustains for that load form (the ceiling the
- * attention kernel is compared with, beside the 8 TB/s peak).
- *   buf    device, 16-byte aligned, read only
- *   bytes  a positive multiple of 65536
- *   sink   device uint32 [1]: XOR-ed (atomically) with the XOR of every
- *          little-endian 32-bit word of the buffer; a zeroed sink ends up
- *          holding that checksum
- * Errors: CONFK_ERR_INVALID_ARG for a null pointer, a misaligned buffer or a
- * size that is not a positive multiple of 65536.
- */
-int confk_read_probe(const void* buf, uint64_t bytes, uint32_t* sink, void* stream);
 
 /* Static text for an error code. */
 const char* confk_strerror(int code);

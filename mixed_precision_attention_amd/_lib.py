@@ -4,6 +4,7 @@ import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libconfk.so")
+PROBE_LIB_PATH = os.path.join(_HERE, "libconfk_probe.so")
 
 c_int32 = ctypes.c_int32
 c_float = ctypes.c_float
@@ -38,8 +39,9 @@ WS_COMPACT = 2
 EXPORTS = [
     "confk_confidence", "confk_attn_decode", "confk_ema_rank", "confk_compact",
     "confk_quantize", "confk_workspace_size", "confk_strerror", "confk_version", "confk_ema_compact",
-    "confk_read_probe", "confk_ema_compact_static",
+    "confk_ema_compact_static",
 ]
+PROBE_EXPORTS = ["confk_read_probe"]
 
 
 class Policy(ctypes.Structure):
@@ -98,16 +100,33 @@ def load():
     lib.confk_ema_compact_static.argtypes = [P(Cache), c_int32, c_int32, c_void_p, P(Policy), c_int32,
                                              c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
                                              c_int32, c_void_p]
-    lib.confk_read_probe.argtypes = [c_void_p, ctypes.c_uint64, c_void_p, c_void_p]
     lib.confk_workspace_size.argtypes = [c_int32, P(Cache), c_int32, c_int32, c_int32]
     lib.confk_workspace_size.restype = c_size_t
     lib.confk_strerror.argtypes = [ctypes.c_int]
     lib.confk_strerror.restype = ctypes.c_char_p
     lib.confk_version.restype = ctypes.c_int
     for name in ("confk_confidence", "confk_attn_decode", "confk_ema_rank", "confk_compact", "confk_ema_compact",
-                 "confk_ema_compact_static", "confk_quantize", "confk_read_probe"):
+                 "confk_ema_compact_static", "confk_quantize"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
+    return lib
+
+
+_probe = None
+
+
+def load_probe():
+    """Loads libconfk_probe.so (the streaming-read probe); raises if missing."""
+    global _probe
+    if _probe is not None:
+        return _probe
+    if not os.path.exists(PROBE_LIB_PATH):
+        raise RuntimeError(
+            f"{PROBE_LIB_PATH} is missing: build it with `python -m mixed_precision_attention_amd.build`")
+    lib = ctypes.CDLL(PROBE_LIB_PATH)
+    lib.confk_read_probe.argtypes = [c_void_p, ctypes.c_uint64, c_void_p, c_void_p]
+    lib.confk_read_probe.restype = ctypes.c_int
+    _probe = lib
     return lib
 
 

@@ -1,4 +1,5 @@
-"""Builds libconfk.so (HIP, gfx950) in-tree with hipcc.
+"""Builds libconfk.so (the decode step) and libconfk_probe.so (the
+streaming-read probe, a measurement aid) for gfx950, in-tree, with hipcc.
 
 Usage: python -m mixed_precision_attention_amd.build
 """
@@ -12,9 +13,11 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libconfk.so")
+PROBE_LIB = os.path.join(HERE, "libconfk_probe.so")
 
 SOURCES = ["abi.hip", "confidence.hip", "attention.hip", "ema_rank.hip", "compact.hip", "quantize.hip",
-           "probe.hip", "noalloc.hip"]
+           "noalloc.hip"]
+PROBE_SOURCES = ["probe.hip"]
 
 # Packed fp32 VALU instructions are disabled: the compiler still vectorises
 # fp16 work, and every fp32 op is a plain VOP.
@@ -32,9 +35,9 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
+def _link(sources, out, verbose):
+    srcs = [os.path.join(CSRC, x) for x in sources]
+    tmp = out + ".tmp"
     cmd = [hipcc(), *FLAGS, "-I", INCLUDE, "-I", CSRC, *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -42,7 +45,12 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError(f"hipcc failed ({r.returncode})")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    _link(SOURCES, LIB, verbose)
+    _link(PROBE_SOURCES, PROBE_LIB, verbose)
     return LIB
 
 

@@ -253,10 +253,4 @@ int confk_quantize(const confk_cache* cache, int32_t layer0, int32_t nlayers, in
   return CONFK_ERR_INVALID_ARG;
 }
 
-int confk_read_probe(const void* buf, uint64_t bytes, uint32_t* sink, void* stream) {
-  if (!buf || !sink || bytes == 0 || bytes % kProbeBlock != 0) return CONFK_ERR_INVALID_ARG;
-  if (reinterpret_cast<uintptr_t>(buf) % 16 != 0) return CONFK_ERR_INVALID_ARG;
-  return launch_status(launch_read_probe(buf, bytes, sink, (hipStream_t)stream));
-}
-
 }  // extern "C"

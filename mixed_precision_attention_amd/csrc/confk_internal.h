@@ -122,10 +122,6 @@ size_t compact_jobs_offset(int nlayers, int batch, int cap);
 hipError_t launch_quantize_step(const QuantArgs& a, hipStream_t s);
 hipError_t launch_prefill(const QuantArgs& a, hipStream_t s);
 
-// Streaming-read probe (a measurement aid): bytes is a positive multiple of
-// kProbeBlock, buf 16-byte aligned.
-constexpr uint64_t kProbeBlock = 65536;
-hipError_t launch_read_probe(const void* buf, uint64_t bytes, uint32_t* sink, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Small device helpers.

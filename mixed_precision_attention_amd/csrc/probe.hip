@@ -11,7 +11,9 @@
 // bytes in flight read slower (6.3 TB/s at eight workgroups per unit, 5.4
 // with 16384 one-load workgroups), and contiguous per-workgroup runs read
 // as fast as interleaved blocks.
-#include "confk_internal.h"
+#include <hip/hip_runtime.h>
+
+#include "confk_probe.h"
 
 namespace confk {
 
@@ -26,6 +28,7 @@ constexpr int kGrid = 512;   // two four-wave workgroups per compute unit
 // Block b of the buffer is kBlock contiguous bytes (one load per thread and
 // unrolled step); workgroup g reads blocks g, g + grid, g + 2 grid, ...
 constexpr uint64_t kBlock = (uint64_t)kThreads * kUnroll * 16;
+constexpr uint64_t kProbeBlock = 65536;  // the size granule of the entry point
 static_assert(kProbeBlock % kBlock == 0, "the size granule must be whole blocks");
 __global__ __launch_bounds__(kThreads) void read_probe_kernel(const u32x4* p, uint64_t nblocks,
                                                               uint32_t* sink) {
@@ -54,11 +57,15 @@ __global__ __launch_bounds__(kThreads) void read_probe_kernel(const u32x4* p, ui
 
 }  // namespace
 
-hipError_t launch_read_probe(const void* buf, uint64_t bytes, uint32_t* sink, hipStream_t s) {
+}  // namespace confk
+
+extern "C" int confk_read_probe(const void* buf, uint64_t bytes, uint32_t* sink, void* stream) {
+  using namespace confk;
+  if (!buf || !sink || bytes == 0 || bytes % kProbeBlock != 0) return CONFK_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(buf) % 16 != 0) return CONFK_ERR_INVALID_ARG;
   const uint64_t nblocks = bytes / kBlock;
   const unsigned grid = (unsigned)(nblocks < kGrid ? nblocks : kGrid);
-  read_probe_kernel<<<grid, kThreads, 0, s>>>(reinterpret_cast<const u32x4*>(buf), nblocks, sink);
-  return hipGetLastError();
+  read_probe_kernel<<<grid, kThreads, 0, (hipStream_t)stream>>>(reinterpret_cast<const u32x4*>(buf), nblocks,
+                                                                 sink);
+  return hipGetLastError() == hipSuccess ? CONFK_OK : CONFK_ERR_LAUNCH;
 }
-
-}  // namespace confk

@@ -162,9 +162,10 @@ def quantize(cache, pol, t, mode=L.QUANT_STEP, k_src=None, v_src=None, n_src=0, 
 
 
 def read_probe(buf, sink):
-    """One streaming read of the device buffer `buf` (a measurement aid);
-    `sink` (device uint32 [1]) is XOR-ed with the XOR of its 32-bit words."""
-    lib = L.load()
+    """One streaming read of the device buffer `buf` (a measurement aid, in
+    libconfk_probe.so); `sink` (device uint32 [1]) is XOR-ed with the XOR of
+    its 32-bit words."""
+    lib = L.load_probe()
     L.check("confk_read_probe", lib.confk_read_probe(
         _p(buf), buf.numel() * buf.element_size(), _p(sink), _stream()))
 

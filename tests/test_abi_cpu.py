@@ -11,10 +11,11 @@ from mixed_precision_attention_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "confk.h")
+PROBE_HEADER = os.path.join(ROOT, "include", "confk_probe.h")
 
 
-def declared():
-    text = open(HEADER).read()
+def declared(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(confk_[a-z_]+)\s*\(", text)))
 
@@ -29,6 +30,23 @@ def test_header_declares_the_five_calls():
     for n in ("confk_confidence", "confk_attn_decode", "confk_ema_rank", "confk_compact", "confk_quantize"):
         assert n in names
     assert set(names) == set(_lib.EXPORTS)
+
+
+def test_every_header_is_covered():
+    headers = sorted(f for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h"))
+    assert headers == ["confk.h", "confk_probe.h"]
+    assert declared(PROBE_HEADER) == sorted(_lib.PROBE_EXPORTS)
+    assert not set(declared()) & set(declared(PROBE_HEADER))
+
+
+def test_probe_library_exports_its_symbol():
+    probe = _lib.load_probe()
+    for n in declared(PROBE_HEADER):
+        assert hasattr(probe, n), n
+
+
+def test_product_library_does_not_export_the_probe(lib):
+    assert not hasattr(lib, "confk_read_probe")
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -171,9 +189,10 @@ def test_binding_raises_on_error_code():
     assert e.value.code == M.ERR_BUDGET
 
 
-def test_read_probe_validation(lib):
+def test_read_probe_validation():
+    probe = _lib.load_probe()
     addr = FAKE.value
-    r = lambda buf=addr, nbytes=65536, sink=FAKE: lib.confk_read_probe(  # noqa: E731
+    r = lambda buf=addr, nbytes=65536, sink=FAKE: probe.confk_read_probe(  # noqa: E731
         ctypes.c_void_p(buf), nbytes, sink, None)
     assert r(buf=None) == M.ERR_INVALID_ARG
     assert r(nbytes=0) == M.ERR_INVALID_ARG
