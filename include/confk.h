@@ -20,7 +20,8 @@
  *   confk_quantize     FP16 token that left the window -> INT8   (step 10)
  * confk_ema_compact runs confk_ema_rank and confk_compact (and, with
  * CONFK_FUSE_QUANTIZE, confk_quantize's window step) as one launch with the
- * same results. The streaming-read probe that measurements compare the
+ * same results; confk_confidence_attn_decode runs confk_confidence and
+ * confk_attn_decode in two launches instead of three. The streaming-read probe that measurements compare the
  * attention kernel with is a separate library (confk_probe.h).
  *
  * Conventions for every entry point:
@@ -220,6 +221,31 @@ int confk_attn_decode(const confk_cache* cache, int32_t layer0, int32_t nlayers,
                       uint16_t* out, float* mass, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * confk_confidence_attn_decode -- confk_confidence followed by
+ * confk_attn_decode on the same stream, with the same results bit for bit,
+ * in two launches instead of three: the confidence pass over the logits,
+ * then the attention launch, whose first workgroups merge the per-chunk
+ * confidence states, take the next token (greedy or none) and write c and
+ * the budgets while the others run attention. Summary "Methodik"
+ * (Konfidenzschaetzung, Implementierung); review Algorithm 1 steps 1-4.
+ * Arguments: those of confk_confidence (conf_ws as its ws), then those of
+ * confk_attn_decode (attn_ws as its ws); each set is validated as there,
+ * and an error enqueues nothing. With temperature sampling (token_out and
+ * temperature > 0) the confidence call's own final kernel runs instead (its
+ * draw holds a chunk of weights in registers), so the call is three launches.
+ * Errors: those of the two calls.
+ */
+int confk_confidence_attn_decode(const float* logits, int64_t ld, int32_t batch, int32_t vocab,
+                                 const confk_policy* pol, const int32_t* layer_n_high,
+                                 const int32_t* layer_n_low, int32_t nbl, float* c_out,
+                                 int32_t* budget_out, uint32_t* status, const float* uniform,
+                                 float temperature, int32_t* token_out, void* conf_ws,
+                                 size_t conf_ws_bytes, const confk_cache* cache, int32_t layer0,
+                                 int32_t nlayers, const uint16_t* q, const uint16_t* k_new,
+                                 const uint16_t* v_new, uint16_t* out, float* mass, void* attn_ws,
+                                 size_t attn_ws_bytes, void* stream);
+
+/*
  * confk_ema_rank -- EMA update of the attention mass and rank scores.
  * Review "前置知识" (EMA: a_i <- lambda a_i + (1-lambda) Abar_i) and "核心方法"
  * (s_i = alpha a^_i + (1-alpha) r^_i). Abar_i = sum_{r<R} mass[r][i] / hq,
@@ -358,7 +384,8 @@ const char* confk_strerror(int code);
 /* ABI version (major * 100 + minor). 101: confk_policy.order and the flags
  * argument of confk_ema_compact. 102: the stable survivor order is order 0
  * (the default) and the hole-filling order is 1. 103: confk_ema_compact_static.
- * 104: mass rows are partial sums over runs of kv heads (CONFK_META_MASSROWS). */
+ * 104: mass rows are partial sums over runs of kv heads (CONFK_META_MASSROWS).
+ * 105: confk_confidence_attn_decode. */
 int confk_version(void);
 
 #ifdef __cplusplus

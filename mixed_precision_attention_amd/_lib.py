@@ -39,7 +39,7 @@ WS_COMPACT = 2
 EXPORTS = [
     "confk_confidence", "confk_attn_decode", "confk_ema_rank", "confk_compact",
     "confk_quantize", "confk_workspace_size", "confk_strerror", "confk_version", "confk_ema_compact",
-    "confk_ema_compact_static",
+    "confk_ema_compact_static", "confk_confidence_attn_decode",
 ]
 PROBE_EXPORTS = ["confk_read_probe"]
 
@@ -87,6 +87,11 @@ def load():
                                      c_float, c_void_p, c_void_p, c_size_t, c_void_p]
     lib.confk_attn_decode.argtypes = [P(Cache), c_int32, c_int32, c_void_p, c_void_p, c_void_p,
                                       c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.confk_confidence_attn_decode.argtypes = [
+        c_void_p, c_int64, c_int32, c_int32, P(Policy), c_void_p, c_void_p, c_int32, c_void_p, c_void_p,
+        c_void_p, c_void_p, c_float, c_void_p, c_void_p, c_size_t,
+        P(Cache), c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+        c_void_p]
     lib.confk_ema_rank.argtypes = [P(Cache), c_int32, c_int32, c_void_p, P(Policy), c_int32,
                                    c_void_p, c_void_p]
     lib.confk_compact.argtypes = [P(Cache), c_int32, c_int32, c_void_p, c_int32, c_void_p,
@@ -106,7 +111,7 @@ def load():
     lib.confk_strerror.restype = ctypes.c_char_p
     lib.confk_version.restype = ctypes.c_int
     for name in ("confk_confidence", "confk_attn_decode", "confk_ema_rank", "confk_compact", "confk_ema_compact",
-                 "confk_ema_compact_static", "confk_quantize"):
+                 "confk_ema_compact_static", "confk_quantize", "confk_confidence_attn_decode"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib

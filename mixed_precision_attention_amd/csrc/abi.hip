@@ -37,7 +37,7 @@ int launch_status(hipError_t e) { return e == hipSuccess ? CONFK_OK : CONFK_ERR_
 
 extern "C" {
 
-int confk_version(void) { return 104; }
+int confk_version(void) { return 105; }
 
 const char* confk_strerror(int code) {
   switch (code) {
@@ -71,11 +71,13 @@ size_t confk_workspace_size(int32_t which, const confk_cache* cache, int32_t nla
   return 0;
 }
 
-int confk_confidence(const float* logits, int64_t ld, int32_t batch, int32_t vocab,
-                     const confk_policy* pol, const int32_t* layer_n_high,
-                     const int32_t* layer_n_low, int32_t nbl, float* c_out, int32_t* budget_out,
-                     uint32_t* status, const float* uniform, float temperature, int32_t* token_out,
-                     void* ws, size_t ws_bytes, void* stream) {
+namespace {
+// Validation and argument set-up of the confidence call (shared by the fused
+// confidence + attention call).
+int conf_args(const float* logits, int64_t ld, int32_t batch, int32_t vocab, const confk_policy* pol,
+              const int32_t* layer_n_high, const int32_t* layer_n_low, int32_t nbl, float* c_out,
+              int32_t* budget_out, uint32_t* status, const float* uniform, float temperature,
+              int32_t* token_out, void* ws, size_t ws_bytes, ConfArgs* out) {
   if (!logits || !c_out || !budget_out || !pol) return CONFK_ERR_INVALID_ARG;
   if (!(temperature >= 0.f) || temperature == INFINITY) return CONFK_ERR_INVALID_ARG;
   if (token_out && temperature > 0.f && !uniform) return CONFK_ERR_INVALID_ARG;
@@ -108,12 +110,15 @@ int confk_confidence(const float* logits, int64_t ld, int32_t batch, int32_t voc
   a.uniform = uniform;
   a.inv_temp = (token_out && temperature > 0.f) ? 1.f / temperature : 0.f;
   a.status = status;
-  return launch_status(launch_confidence(a, (hipStream_t)stream));
+  *out = a;
+  return CONFK_OK;
 }
 
-int confk_attn_decode(const confk_cache* cache, int32_t layer0, int32_t nlayers, const uint16_t* q,
-                      const uint16_t* k_new, const uint16_t* v_new, uint16_t* out, float* mass,
-                      void* ws, size_t ws_bytes, void* stream) {
+// Validation and argument set-up of the attention call; *lds_bytes is the
+// launch's shared memory for the default plan.
+int attn_args(const confk_cache* cache, int32_t layer0, int32_t nlayers, const uint16_t* q,
+              const uint16_t* k_new, const uint16_t* v_new, uint16_t* out, float* mass, void* ws,
+              size_t ws_bytes, AttnArgs* res, int* lds_bytes) {
   if (!cache_ok(cache) || !layers_ok(cache, layer0, nlayers)) return CONFK_ERR_INVALID_ARG;
   if (!q || !k_new || !v_new || !out) return CONFK_ERR_INVALID_ARG;
   const int g = cache->hq / cache->hkv;
@@ -135,7 +140,60 @@ int confk_attn_decode(const confk_cache* cache, int32_t layer0, int32_t nlayers,
   a.out = out;
   a.mass = mass;
   a.spill = need ? (float*)ws : nullptr;
-  return launch_status(launch_attention(a, attention_lds_bytes(cache->d, g, n_lds), (hipStream_t)stream));
+  *res = a;
+  *lds_bytes = attention_lds_bytes(cache->d, g, n_lds);
+  return CONFK_OK;
+}
+}  // namespace
+
+int confk_confidence(const float* logits, int64_t ld, int32_t batch, int32_t vocab,
+                     const confk_policy* pol, const int32_t* layer_n_high,
+                     const int32_t* layer_n_low, int32_t nbl, float* c_out, int32_t* budget_out,
+                     uint32_t* status, const float* uniform, float temperature, int32_t* token_out,
+                     void* ws, size_t ws_bytes, void* stream) {
+  ConfArgs a;
+  const int rc = conf_args(logits, ld, batch, vocab, pol, layer_n_high, layer_n_low, nbl, c_out, budget_out,
+                           status, uniform, temperature, token_out, ws, ws_bytes, &a);
+  if (rc != CONFK_OK) return rc;
+  return launch_status(launch_confidence(a, (hipStream_t)stream));
+}
+
+int confk_attn_decode(const confk_cache* cache, int32_t layer0, int32_t nlayers, const uint16_t* q,
+                      const uint16_t* k_new, const uint16_t* v_new, uint16_t* out, float* mass,
+                      void* ws, size_t ws_bytes, void* stream) {
+  AttnArgs a;
+  int lds = 0;
+  const int rc = attn_args(cache, layer0, nlayers, q, k_new, v_new, out, mass, ws, ws_bytes, &a, &lds);
+  if (rc != CONFK_OK) return rc;
+  return launch_status(launch_attention(a, lds, (hipStream_t)stream));
+}
+
+int confk_confidence_attn_decode(const float* logits, int64_t ld, int32_t batch, int32_t vocab,
+                                 const confk_policy* pol, const int32_t* layer_n_high,
+                                 const int32_t* layer_n_low, int32_t nbl, float* c_out,
+                                 int32_t* budget_out, uint32_t* status, const float* uniform,
+                                 float temperature, int32_t* token_out, void* conf_ws,
+                                 size_t conf_ws_bytes, const confk_cache* cache, int32_t layer0,
+                                 int32_t nlayers, const uint16_t* q, const uint16_t* k_new,
+                                 const uint16_t* v_new, uint16_t* out, float* mass, void* attn_ws,
+                                 size_t attn_ws_bytes, void* stream) {
+  ConfArgs ca;
+  int rc = conf_args(logits, ld, batch, vocab, pol, layer_n_high, layer_n_low, nbl, c_out, budget_out, status,
+                     uniform, temperature, token_out, conf_ws, conf_ws_bytes, &ca);
+  if (rc != CONFK_OK) return rc;
+  AttnArgs a;
+  int lds = 0;
+  rc = attn_args(cache, layer0, nlayers, q, k_new, v_new, out, mass, attn_ws, attn_ws_bytes, &a, &lds);
+  if (rc != CONFK_OK) return rc;
+  if (token_out && temperature > 0.f) {  // sampling: the confidence call's own two kernels
+    const hipError_t e = launch_confidence(ca, (hipStream_t)stream);
+    if (e != hipSuccess) return launch_status(e);
+    return launch_status(launch_attention(a, lds, (hipStream_t)stream));
+  }
+  const hipError_t e = launch_confidence_partial(ca, (hipStream_t)stream);
+  if (e != hipSuccess) return launch_status(e);
+  a.conf = ca;  // with the chunking the partial pass used
+  return launch_status(launch_attention(a, lds, (hipStream_t)stream));
 }
 
 int confk_ema_rank(const confk_cache* cache, int32_t layer0, int32_t nlayers, const float* mass,

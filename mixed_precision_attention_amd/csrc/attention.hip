@@ -40,6 +40,7 @@
 // key's mass sum_h 2^(s_h - M_h) / L_h is formed exactly.
 #include <mutex>
 
+#include "confidence_merge.h"
 #include "confk_internal.h"
 
 namespace confk {
@@ -296,12 +297,27 @@ void attn_decode_kernel(AttnArgs a) {
   static_assert(!ACC || (MASS && !SPILL), "mass rows are summed in LDS only with the LDS score store");
   extern __shared__ float lds[];
 
+  // Fused confidence call: the launch's first conf_groups workgroups merge
+  // the confidence rows (one wave per row, the confidence call's final
+  // step) while the others run the units.
+  if (a.conf_groups > 0 && (int)blockIdx.x < a.conf_groups) {  // uniform per workgroup
+    const int row = (int)blockIdx.x * kWaves + (int)(threadIdx.x >> 6);
+    if (row < a.conf.batch) {  // uniform per wave
+      const int lane = threadIdx.x & 63;
+      // (a pass with temperature sampling keeps its own final kernel: the
+      // draw holds a chunk of weights in registers)
+      if (a.conf.choice == confm::kGreedy) confm::conf_final_row<confm::kGreedy>(a.conf, row, lane);
+      else confm::conf_final_row<confm::kNoChoice>(a.conf, row, lane);
+    }
+    return;
+  }
+
   const CacheView& c = a.c;
   const int H = c.hkv;
   const int g = a.g;
   const uint32_t U = (uint32_t)a.nl * c.B * H;  // units of this launch (U * G < 2^32)
-  const uint32_t G = ACC ? gridDim.x : U;
-  const int wg = blockIdx.x;
+  const uint32_t G = ACC ? gridDim.x - a.conf_groups : U;
+  const int wg = blockIdx.x - a.conf_groups;
   const int u_begin = ACC ? (int)((uint32_t)wg * U / G) : wg;
   const int u_end = ACC ? (int)((uint32_t)(wg + 1) * U / G) : wg + 1;
   // (layer, sequence, kv head) of the current unit, advanced without
@@ -820,11 +836,12 @@ int resident_per_cu(const void* fn, int lds_bytes) {
 template <int D>
 hipError_t launch_d(const AttnArgs& a, int lds_bytes, hipStream_t s) {
   const int64_t units = (int64_t)a.nl * a.c.B * a.c.hkv;
+  const int64_t cg = a.conf_groups;  // leading workgroups of the fused confidence merge
   const dim3 block(kThreads);
   if (!a.mass) {
-    hipLaunchKernelGGL((attn_decode_kernel<D, false, false, false>), dim3(units), block, lds_bytes, s, a);
+    hipLaunchKernelGGL((attn_decode_kernel<D, false, false, false>), dim3(units + cg), block, lds_bytes, s, a);
   } else if (a.spill) {
-    hipLaunchKernelGGL((attn_decode_kernel<D, true, true, false>), dim3(units), block, lds_bytes, s, a);
+    hipLaunchKernelGGL((attn_decode_kernel<D, true, true, false>), dim3(units + cg), block, lds_bytes, s, a);
   } else {
     // At least two rounds of resident workgroups: kAccUnits kv heads per
     // workgroup with the mass summed in LDS, if the accumulator costs no
@@ -837,9 +854,9 @@ hipError_t launch_d(const AttnArgs& a, int lds_bytes, hipStream_t s) {
     const int64_t groups = (units + kAccUnits - 1) / kAccUnits;
     if (occ_acc > 0 && slots > 0 && groups >= slots && units * (groups + 1) < ((int64_t)1 << 32) &&
         occ_acc >= resident_per_cu(plain, lds_bytes)) {
-      hipLaunchKernelGGL((attn_decode_kernel<D, false, true, true>), dim3(groups), block, acc_bytes, s, a);
+      hipLaunchKernelGGL((attn_decode_kernel<D, false, true, true>), dim3(groups + cg), block, acc_bytes, s, a);
     } else {
-      hipLaunchKernelGGL((attn_decode_kernel<D, false, true, false>), dim3(units), block, lds_bytes, s, a);
+      hipLaunchKernelGGL((attn_decode_kernel<D, false, true, false>), dim3(units + cg), block, lds_bytes, s, a);
     }
   }
   return hipGetLastError();
@@ -847,7 +864,9 @@ hipError_t launch_d(const AttnArgs& a, int lds_bytes, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_attention(const AttnArgs& a, int lds_bytes, hipStream_t s) {
+hipError_t launch_attention(const AttnArgs& in, int lds_bytes, hipStream_t s) {
+  AttnArgs a = in;
+  a.conf_groups = a.conf.c_out ? (a.conf.batch + kWaves - 1) / kWaves : 0;
   return a.c.d == 128 ? launch_d<128>(a, lds_bytes, s) : launch_d<64>(a, lds_bytes, s);
 }
 

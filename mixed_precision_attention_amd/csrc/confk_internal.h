@@ -49,6 +49,7 @@ struct ConfArgs {
   const float* uniform;  // [batch] in [0, 1): temperature sampling
   float inv_temp;        // 1 / temperature, 0 for greedy or no choice
   int32_t* token_out;    // [batch] or null
+  int32_t choice;        // next-token choice of the pass (set by the launch)
 };
 
 struct AttnArgs {
@@ -62,6 +63,10 @@ struct AttnArgs {
   uint16_t* out;
   float* mass;
   float* spill;  // [nl*B*hkv][g][spill_stride] or null
+  // fused confidence call: the launch's first conf_groups workgroups merge the
+  // confidence rows of `conf` (one wave per row) before the units start
+  ConfArgs conf;
+  int32_t conf_groups;
 };
 
 struct EmaArgs {
@@ -112,6 +117,8 @@ struct QuantArgs {
 hipError_t launch_confidence(const ConfArgs& a, hipStream_t s);
 size_t confidence_ws_bytes(int32_t batch, int32_t vocab);
 hipError_t launch_attention(const AttnArgs& a, int lds_bytes, hipStream_t s);
+// The confidence pass without the final merge (sets chunking and choice in a).
+hipError_t launch_confidence_partial(ConfArgs& a, hipStream_t s);
 int attention_lds_bytes(int d, int g, int n_lds);
 int attention_plan_n_lds(int d, int g, int cap, int* spill_stride);
 hipError_t launch_ema_rank(const EmaArgs& a, hipStream_t s);

@@ -103,6 +103,23 @@ def confidence(logits, pol, c_out, budget_out, status, ws, layer_n_high=None, la
         _stream()))
 
 
+def confidence_attn_decode(logits, pol, c_out, budget_out, status, conf_ws, cache, q, k_new, v_new, out,
+                           mass, attn_ws, layer_n_high=None, layer_n_low=None, token_out=None,
+                           temperature=0.0, uniform=None, layer0=0, nlayers=None):
+    """confk_confidence_attn_decode: confidence then attention in two launches
+    (the confidence merge runs in the attention launch), same results."""
+    lib = L.load()
+    nbl = 1 if layer_n_high is None else int(layer_n_high.numel())
+    nl = cache.layers - layer0 if nlayers is None else nlayers
+    awsb = 0 if attn_ws is None else attn_ws.numel() * attn_ws.element_size()
+    L.check("confk_confidence_attn_decode", lib.confk_confidence_attn_decode(
+        _p(logits), logits.stride(0), logits.shape[0], logits.shape[1], ctypes.byref(pol),
+        _p(layer_n_high), _p(layer_n_low), nbl, _p(c_out), _p(budget_out), _p(status),
+        _p(uniform), float(temperature), _p(token_out), _p(conf_ws), conf_ws.numel() * conf_ws.element_size(),
+        cache.ref(), layer0, nl, _p(q), _p(k_new), _p(v_new), _p(out), _p(mass), _p(attn_ws), awsb,
+        _stream()))
+
+
 def attn_decode(cache, q, k_new, v_new, out, mass, ws, layer0=0, nlayers=None):
     lib = L.load()
     nl = cache.layers - layer0 if nlayers is None else nlayers
@@ -234,6 +251,15 @@ class DecodeEngine:
     def step_attention(self, q, k_new, v_new):
         attn_decode(self.cache, q, k_new, v_new, self.out, self.mass, self.attn_ws)
 
+    def step_confidence_attention(self, logits, q, k_new, v_new, temperature=None, uniform=None):
+        """step_confidence then step_attention as one call (two launches: the
+        confidence merge runs inside the attention launch), same results."""
+        confidence_attn_decode(logits, self.pol, self.c, self.budget, self.cache.status, self.conf_ws,
+                               self.cache, q, k_new, v_new, self.out, self.mass, self.attn_ws,
+                               self.layer_n_high, self.layer_n_low,
+                               token_out=None if temperature is None else self.token,
+                               temperature=0.0 if temperature is None else temperature, uniform=uniform)
+
     def step_ema_rank(self, t):
         ema_rank(self.cache, self.mass, self.pol, t, self.score)
 
@@ -262,14 +288,13 @@ class DecodeEngine:
             self.step_compact(k_new, v_new)
             return
         if self.side is None:
-            self.step_confidence(logits)
+            self.step_confidence_attention(logits, q, k_new, v_new)
         else:
             main = torch.cuda.current_stream()
             self.side.wait_stream(main)  # the logits, and the previous step's use of the budget
             with torch.cuda.stream(self.side):
                 self.step_confidence(logits)
             self.conf_done.record(self.side)
-        self.step_attention(q, k_new, v_new)
-        if self.side is not None:
+            self.step_attention(q, k_new, v_new)
             torch.cuda.current_stream().wait_event(self.conf_done)
         self.step_ema_compact(t, k_new, v_new, fuse_quantize=True)

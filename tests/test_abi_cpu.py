@@ -52,7 +52,7 @@ def test_product_library_does_not_export_the_probe(lib):
 def test_library_exports_every_declared_symbol(lib):
     for n in declared():
         assert hasattr(lib, n), n
-    assert lib.confk_version() == 104
+    assert lib.confk_version() == 105
     assert lib.confk_strerror(-1) == b"invalid argument"
     assert lib.confk_strerror(12345) == b"unknown error"
 
@@ -125,6 +125,27 @@ def test_attention_validation(lib):
     assert r(bad) == M.ERR_INVALID_ARG
     assert lib.confk_attn_decode(ctypes.byref(c), 0, 2, None, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) \
         == M.ERR_INVALID_ARG
+
+
+def test_fused_confidence_attention_validation(lib):
+    """Each argument set of confk_confidence_attn_decode is validated as in
+    its own call, before anything is launched."""
+    pol = _pol()
+    c = _fake_cache()
+
+    def call(logits=FAKE, vocab=10, conf_ws=FAKE, conf_wsb=1 << 20, cache=c, nl=2, q=FAKE, temperature=0.0,
+             token=None, uniform=None):
+        return lib.confk_confidence_attn_decode(
+            logits, 10, 3, vocab, ctypes.byref(pol), None, None, 1, FAKE, FAKE, None, uniform, temperature,
+            token, conf_ws, conf_wsb, ctypes.byref(cache), 0, nl, q, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert call(logits=None) == M.ERR_INVALID_ARG
+    assert call(vocab=1) == M.ERR_INVALID_ARG
+    assert call(conf_ws=None) == M.ERR_WORKSPACE
+    assert call(conf_wsb=4) == M.ERR_WORKSPACE
+    assert call(temperature=0.8, token=FAKE) == M.ERR_INVALID_ARG   # sampling needs uniforms
+    assert call(q=None) == M.ERR_INVALID_ARG
+    assert call(nl=3) == M.ERR_INVALID_ARG
+    assert call(cache=_fake_cache(d=96)) == M.ERR_UNSUPPORTED
 
 
 def test_attention_workspace_needed_only_for_long_caches(lib):

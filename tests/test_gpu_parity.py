@@ -608,8 +608,9 @@ def _split_step(e, lg, q, kn, vn, t):
 
 
 def test_qwen32b_full_launch_fused_matches_split():
-    """DecodeEngine.step (EMA + compaction + window step fused; on one stream
-    as bench.py times it, and with the confidence on a second stream) against
+    """DecodeEngine.step (the confidence merge inside the attention launch and
+    EMA + compaction + window step fused, on one stream as bench.py times it;
+    and with the confidence on a second stream) against
     the five calls issued one after another, bit for bit, at the full
     64-layer, batch-8 size (the split calls themselves are checked against
     the oracle at this size above)."""
@@ -732,6 +733,38 @@ def test_two_kv_heads_per_workgroup_mass_rows():
             got = out_all[l, b].float().cpu().numpy()
             ref = eng.out[l, b].float().cpu().numpy()
             assert rel_maxabs(got, ref) <= OTOL / 2, f"l={l} b={b}: output"
+
+
+@pytest.mark.parametrize("choice", ["none", "greedy", "sample"])
+def test_fused_confidence_attention_matches_split(choice):
+    """confk_confidence_attn_decode (the confidence merge inside the attention
+    launch; with sampling the confidence call's own final kernel) against
+    confk_confidence then confk_attn_decode, bit for bit: c, budgets, the
+    next token, the output and the mass, at the Qwen-32B shape with two
+    layers and at a small shape with a ragged vocabulary."""
+    import mixed_precision_attention_amd as M
+    dev = _dev()
+    for cfg in (synth.get_config("qwen32b").with_(layers=2), TINY["g5_d128"]):
+        engs = [M.DecodeEngine(cfg, dev), M.DecodeEngine(cfg, dev)]
+        kp, vp = synth.prefill_kv(cfg, 6)
+        for e in engs:
+            e.prefill(_t(kp, dev), _t(vp, dev))
+        for i in range(3):
+            logits, q, kn, vn, t = _inputs(cfg, 6, i)
+            lg, qd, kd, vd = _t(logits, dev), _t(q, dev), _t(kn, dev), _t(vn, dev)
+            temp = None if choice == "none" else (0.0 if choice == "greedy" else 0.8)
+            u = torch.rand(cfg.batch, generator=torch.Generator().manual_seed(i)).to(dev)
+            engs[0].step_confidence(lg, temperature=temp, uniform=u)
+            engs[0].step_attention(qd, kd, vd)
+            engs[1].step_confidence_attention(lg, qd, kd, vd, temperature=temp, uniform=u)
+            torch.cuda.synchronize()
+            for name in ("c", "budget", "out", "mass"):
+                assert torch.equal(getattr(engs[0], name), getattr(engs[1], name)), (cfg.name, i, name)
+            if temp is not None:
+                assert torch.equal(engs[0].token, engs[1].token), (cfg.name, i, "token")
+            assert torch.equal(engs[0].cache.meta, engs[1].cache.meta)
+            for e in engs:
+                e.step_ema_compact(t, kd, vd, fuse_quantize=True)
 
 
 def test_long_context_pyramid_retains_planted_keys():
