@@ -21,7 +21,8 @@
  * confk_ema_compact runs confk_ema_rank and confk_compact (and, with
  * CONFK_FUSE_QUANTIZE, confk_quantize's window step) as one launch with the
  * same results; confk_confidence_attn_decode runs confk_confidence and
- * confk_attn_decode in two launches instead of three. The streaming-read probe that measurements compare the
+ * confk_attn_decode in two launches instead of three, and confk_decode_step
+ * runs the whole step (all five) in three. The streaming-read probe that measurements compare the
  * attention kernel with is a separate library (confk_probe.h).
  *
  * Conventions for every entry point:
@@ -351,6 +352,32 @@ int confk_ema_compact_static(const confk_cache* cache, int32_t layer0, int32_t n
                              const uint16_t* v_new, int32_t* evicted_out, int32_t flags, void* stream);
 
 /*
+ * confk_decode_step -- one whole decode step in three launches:
+ * confk_confidence, confk_attn_decode and confk_ema_compact on the same
+ * stream, with the same results bit for bit. The confidence pass over the
+ * logits runs as the last workgroups of the attention launch (they fill the
+ * slots its last round of dispatch leaves idle); each workgroup of the
+ * compaction's plan kernel merges its sequence's confidence states, takes
+ * its budget from them and, for the call's first layer, writes c, the token
+ * and the budgets. Review Algorithm 1 (the whole step); summary "Methodik".
+ * Arguments are those of the three calls: batch is cache->batch, the status
+ * word is cache->status, the budget rows are budget_out (nbl = 1: shared,
+ * nbl = nlayers: one row per layer of the call), q/k_new/v_new are shared
+ * by attention and the append, flags as for confk_ema_compact. conf_ws,
+ * attn_ws and compact_ws are the three calls' workspaces. With temperature
+ * sampling the confidence call's own two kernels run first (four launches).
+ * Errors: those of the three calls; INVALID_ARG also for a NULL mass or nbl
+ * other than 1 or nlayers.
+ */
+int confk_decode_step(const float* logits, int64_t ld, int32_t vocab, const confk_policy* pol,
+                      const int32_t* layer_n_high, const int32_t* layer_n_low, int32_t nbl, float* c_out,
+                      int32_t* budget_out, const float* uniform, float temperature, int32_t* token_out,
+                      const confk_cache* cache, int32_t layer0, int32_t nlayers, int32_t t, const uint16_t* q,
+                      const uint16_t* k_new, const uint16_t* v_new, uint16_t* out, float* mass, float* score,
+                      int32_t* evicted_out, int32_t flags, void* conf_ws, size_t conf_ws_bytes, void* attn_ws,
+                      size_t attn_ws_bytes, void* compact_ws, size_t compact_ws_bytes, void* stream);
+
+/*
  * confk_quantize -- FP16 -> INT8 storage per (head, channel).
  * Summary "Methodik" (gemischte Praezisionsspeicherung: newest W tokens FP16,
  * older retained tokens INT8 per head and channel); review Algorithm 1
@@ -385,7 +412,7 @@ const char* confk_strerror(int code);
  * argument of confk_ema_compact. 102: the stable survivor order is order 0
  * (the default) and the hole-filling order is 1. 103: confk_ema_compact_static.
  * 104: mass rows are partial sums over runs of kv heads (CONFK_META_MASSROWS).
- * 105: confk_confidence_attn_decode. */
+ * 105: confk_confidence_attn_decode. 106: confk_decode_step. */
 int confk_version(void);
 
 #ifdef __cplusplus

@@ -12,6 +12,6 @@ from ._lib import (  # noqa: F401
     META_MOVED, META_MOVED16, META_MASSROWS, META_WORDS,
 )
 from .engine import (  # noqa: F401
-    make_policy, DeviceCache, DecodeEngine, confidence, attn_decode, confidence_attn_decode, ema_rank, compact,
-    quantize,
+    make_policy, DeviceCache, DecodeEngine, confidence, attn_decode, confidence_attn_decode, decode_step, ema_rank,
+    compact, quantize,
 )

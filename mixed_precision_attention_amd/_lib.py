@@ -39,7 +39,7 @@ WS_COMPACT = 2
 EXPORTS = [
     "confk_confidence", "confk_attn_decode", "confk_ema_rank", "confk_compact",
     "confk_quantize", "confk_workspace_size", "confk_strerror", "confk_version", "confk_ema_compact",
-    "confk_ema_compact_static", "confk_confidence_attn_decode",
+    "confk_ema_compact_static", "confk_confidence_attn_decode", "confk_decode_step",
 ]
 PROBE_EXPORTS = ["confk_read_probe"]
 
@@ -105,13 +105,19 @@ def load():
     lib.confk_ema_compact_static.argtypes = [P(Cache), c_int32, c_int32, c_void_p, P(Policy), c_int32,
                                              c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
                                              c_int32, c_void_p]
+    lib.confk_decode_step.argtypes = [
+        c_void_p, c_int64, c_int32, P(Policy), c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
+        c_float, c_void_p, P(Cache), c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+        c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_size_t, c_void_p, c_size_t, c_void_p, c_size_t,
+        c_void_p]
     lib.confk_workspace_size.argtypes = [c_int32, P(Cache), c_int32, c_int32, c_int32]
     lib.confk_workspace_size.restype = c_size_t
     lib.confk_strerror.argtypes = [ctypes.c_int]
     lib.confk_strerror.restype = ctypes.c_char_p
     lib.confk_version.restype = ctypes.c_int
     for name in ("confk_confidence", "confk_attn_decode", "confk_ema_rank", "confk_compact", "confk_ema_compact",
-                 "confk_ema_compact_static", "confk_quantize", "confk_confidence_attn_decode"):
+                 "confk_ema_compact_static", "confk_quantize", "confk_confidence_attn_decode",
+                 "confk_decode_step"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib

@@ -37,7 +37,7 @@ int launch_status(hipError_t e) { return e == hipSuccess ? CONFK_OK : CONFK_ERR_
 
 extern "C" {
 
-int confk_version(void) { return 105; }
+int confk_version(void) { return 106; }
 
 const char* confk_strerror(int code) {
   switch (code) {
@@ -193,6 +193,7 @@ int confk_confidence_attn_decode(const float* logits, int64_t ld, int32_t batch,
   const hipError_t e = launch_confidence_partial(ca, (hipStream_t)stream);
   if (e != hipSuccess) return launch_status(e);
   a.conf = ca;  // with the chunking the partial pass used
+  a.conf_mode = kConfMerge;
   return launch_status(launch_attention(a, lds, (hipStream_t)stream));
 }
 
@@ -282,6 +283,53 @@ int confk_ema_compact(const confk_cache* cache, int32_t layer0, int32_t nlayers,
   a.quantize = (flags & CONFK_FUSE_QUANTIZE) ? 1 : 0;
   a.window = pol->window;
   return launch_status(launch_compact(a, (hipStream_t)stream));
+}
+
+int confk_decode_step(const float* logits, int64_t ld, int32_t vocab, const confk_policy* pol,
+                      const int32_t* layer_n_high, const int32_t* layer_n_low, int32_t nbl, float* c_out,
+                      int32_t* budget_out, const float* uniform, float temperature, int32_t* token_out,
+                      const confk_cache* cache, int32_t layer0, int32_t nlayers, int32_t t, const uint16_t* q,
+                      const uint16_t* k_new, const uint16_t* v_new, uint16_t* out, float* mass, float* score,
+                      int32_t* evicted_out, int32_t flags, void* conf_ws, size_t conf_ws_bytes, void* attn_ws,
+                      size_t attn_ws_bytes, void* compact_ws, size_t compact_ws_bytes, void* stream) {
+  if (!cache_ok(cache)) return CONFK_ERR_INVALID_ARG;
+  if (!mass || t < 0 || (flags & ~CONFK_FUSE_QUANTIZE) != 0) return CONFK_ERR_INVALID_ARG;
+  if (nbl != 1 && nbl != nlayers) return CONFK_ERR_INVALID_ARG;
+  ConfArgs ca;
+  int rc = conf_args(logits, ld, cache->batch, vocab, pol, layer_n_high, layer_n_low, nbl, c_out, budget_out,
+                     cache->status, uniform, temperature, token_out, conf_ws, conf_ws_bytes, &ca);
+  if (rc != CONFK_OK) return rc;
+  AttnArgs aa;
+  int lds = 0;
+  rc = attn_args(cache, layer0, nlayers, q, k_new, v_new, out, mass, attn_ws, attn_ws_bytes, &aa, &lds);
+  if (rc != CONFK_OK) return rc;
+  CompactArgs cp;
+  rc = compact_args(cache, layer0, nlayers, budget_out, nbl > 1 ? cache->batch : 0, score, pol, k_new, v_new,
+                    evicted_out, compact_ws, compact_ws_bytes, cp);
+  if (rc != CONFK_OK) return rc;
+  cp.fuse = 1;
+  cp.t = t;
+  cp.lambda = pol->lambda;
+  cp.alpha = pol->alpha;
+  cp.mass = mass;
+  cp.score_out = score;
+  cp.quantize = (flags & CONFK_FUSE_QUANTIZE) ? 1 : 0;
+  cp.window = pol->window;
+  const hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (token_out && temperature > 0.f) {  // sampling: the confidence call's own two kernels first
+    e = launch_confidence(ca, s);
+    if (e == hipSuccess) e = launch_attention(aa, lds, s);
+  } else {
+    confidence_prepare(ca);
+    aa.conf = ca;
+    aa.conf_mode = kConfPass;  // the pass in the attention launch
+    e = launch_attention(aa, lds, s);
+    cp.conf = ca;
+    cp.conf_merge = 1;  // the merge and the budgets in the plan kernel
+  }
+  if (e != hipSuccess) return launch_status(e);
+  return launch_status(launch_compact(cp, s));
 }
 
 int confk_quantize(const confk_cache* cache, int32_t layer0, int32_t nlayers, int32_t t,

@@ -40,7 +40,7 @@
 // key's mass sum_h 2^(s_h - M_h) / L_h is formed exactly.
 #include <mutex>
 
-#include "confidence_merge.h"
+#include "confidence_dev.h"
 #include "confk_internal.h"
 
 namespace confk {
@@ -311,12 +311,23 @@ void attn_decode_kernel(AttnArgs a) {
     }
     return;
   }
+  // Whole-step call: the launch's last conf_tail workgroups run the
+  // confidence pass, one chunk of one row each; dispatched last, they fill
+  // the slots the units' last round leaves idle.
+  if (a.conf_tail > 0 && (int)blockIdx.x >= (int)gridDim.x - a.conf_tail) {  // uniform per workgroup
+    const int p = (int)blockIdx.x - ((int)gridDim.x - a.conf_tail);
+    const int row = p / a.conf.nchunks, chunk = p - row * a.conf.nchunks;
+    static_assert(kThreads == confm::kConfThreads, "a pass workgroup is an attention workgroup");
+    if (a.conf.choice == confm::kGreedy) confm::conf_partial_block<confm::kGreedy>(a.conf, chunk, row, threadIdx.x);
+    else confm::conf_partial_block<confm::kNoChoice>(a.conf, chunk, row, threadIdx.x);
+    return;
+  }
 
   const CacheView& c = a.c;
   const int H = c.hkv;
   const int g = a.g;
   const uint32_t U = (uint32_t)a.nl * c.B * H;  // units of this launch (U * G < 2^32)
-  const uint32_t G = ACC ? gridDim.x - a.conf_groups : U;
+  const uint32_t G = ACC ? gridDim.x - a.conf_groups - a.conf_tail : U;
   const int wg = blockIdx.x - a.conf_groups;
   const int u_begin = ACC ? (int)((uint32_t)wg * U / G) : wg;
   const int u_end = ACC ? (int)((uint32_t)(wg + 1) * U / G) : wg + 1;
@@ -836,7 +847,7 @@ int resident_per_cu(const void* fn, int lds_bytes) {
 template <int D>
 hipError_t launch_d(const AttnArgs& a, int lds_bytes, hipStream_t s) {
   const int64_t units = (int64_t)a.nl * a.c.B * a.c.hkv;
-  const int64_t cg = a.conf_groups;  // leading workgroups of the fused confidence merge
+  const int64_t cg = a.conf_groups + a.conf_tail;  // workgroups of the fused confidence work
   const dim3 block(kThreads);
   if (!a.mass) {
     hipLaunchKernelGGL((attn_decode_kernel<D, false, false, false>), dim3(units + cg), block, lds_bytes, s, a);
@@ -866,7 +877,10 @@ hipError_t launch_d(const AttnArgs& a, int lds_bytes, hipStream_t s) {
 
 hipError_t launch_attention(const AttnArgs& in, int lds_bytes, hipStream_t s) {
   AttnArgs a = in;
-  a.conf_groups = a.conf.c_out ? (a.conf.batch + kWaves - 1) / kWaves : 0;
+  // the fused confidence work: the merge in leading workgroups (the pass ran
+  // before), or the pass in trailing ones (the merge runs after)
+  a.conf_groups = a.conf_mode == kConfMerge ? (a.conf.batch + kWaves - 1) / kWaves : 0;
+  a.conf_tail = a.conf_mode == kConfPass ? a.conf.nchunks * a.conf.batch : 0;
   return a.c.d == 128 ? launch_d<128>(a, lds_bytes, s) : launch_d<64>(a, lds_bytes, s);
 }
 

@@ -43,6 +43,7 @@
 // the fused form the head's window step follows.
 #include <type_traits>
 
+#include "confidence_dev.h"
 #include "quantize_seq.h"
 
 namespace confk {
@@ -253,7 +254,30 @@ __device__ __forceinline__ void plan_body(const CompactArgs& a) {
   const int base8 = meta[CONFK_META_BASE8];
   const int base16 = meta[CONFK_META_BASE16];
   const int P = a.protect;
-  const int N = max(a.budget[l * a.budget_stride + b], P);
+  int N;
+  if (a.conf_merge) {  // uniform (a kernel argument): the budget from this sequence's confidence
+    __shared__ float conf_c;
+    const int brow = a.conf.nbl > 1 ? l : 0;  // budget row of this layer
+    if (threadIdx.x < 64) {
+      int tok;
+      const float cc = a.conf.choice == confm::kGreedy
+                           ? confm::conf_row_c<confm::kGreedy>(a.conf, b, threadIdx.x, tok)
+                           : confm::conf_row_c<confm::kNoChoice>(a.conf, b, threadIdx.x, tok);
+      if (threadIdx.x == 0) {
+        conf_c = cc;
+        if (l == 0) {  // the call's first layer writes the sequence's outputs
+          a.conf.c_out[b] = cc;
+          if (a.conf.choice == confm::kGreedy) a.conf.token_out[b] = tok;
+          if (cc != cc && a.conf.status) atomicOr(a.conf.status, (uint32_t)CONFK_STATUS_NONFINITE_LOGITS);
+        }
+        if (brow == l) a.conf.budget_out[(int64_t)brow * a.conf.batch + b] = confm::conf_budget(a.conf, brow, cc);
+      }
+    }
+    __syncthreads();
+    N = max(confm::conf_budget(a.conf, brow, conf_c), P);
+  } else {
+    N = max(a.budget[l * a.budget_stride + b], P);
+  }
   float* ema = c.ema + (size_t)lbc * cap;
   int32_t* pos = c.pos + (size_t)lbc * cap;
   const float* score = a.score + (size_t)lb * cap;

@@ -24,7 +24,7 @@
 // needs.
 #include "confk_internal.h"
 
-#include "confidence_merge.h"
+#include "confidence_dev.h"
 
 namespace confk {
 
@@ -32,105 +32,10 @@ using namespace confm;
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kPerThread = 16;
-static_assert(kThreads * kPerThread == kChunk, "one workgroup reduces one chunk");
 
 template <int CH>
-__global__ __launch_bounds__(kThreads) void conf_partial_kernel(ConfArgs a) {
-  const int b = blockIdx.y;
-  const int chunk = blockIdx.x;
-  const float* row = a.logits + (int64_t)b * a.ld;
-  const int start = chunk * a.chunk;
-  const int end = min(a.vocab, start + a.chunk);
-
-  float x[kPerThread];
-  if (a.vec4) {
-    // 16-byte loads: thread t reads groups t, t+256, ... of 4 logits
-#pragma unroll
-    for (int k = 0; k < kPerThread / 4; ++k) {
-      const int i = start + 4 * (threadIdx.x + k * kThreads);
-      if (i + 3 < end) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(row + i);
-        x[4 * k] = v[0];
-        x[4 * k + 1] = v[1];
-        x[4 * k + 2] = v[2];
-        x[4 * k + 3] = v[3];
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[4 * k + e] = (i + e < end) ? row[i + e] : -INFINITY;
-      }
-    }
-  } else {
-#pragma unroll
-    for (int k = 0; k < kPerThread; ++k) {
-      const int i = start + threadIdx.x + k * kThreads;
-      x[k] = (i < end) ? row[i] : -INFINITY;
-    }
-  }
-  // logical index of x[k], ascending in k
-  auto idx = [&](int k) {
-    return a.vec4 ? start + 4 * (threadIdx.x + (k >> 2) * kThreads) + (k & 3) : start + threadIdx.x + k * kThreads;
-  };
-  const float inv_t = a.inv_temp;
-  RowState s;
-  s.M = -INFINITY;
-  s.t1 = -INFINITY;
-  s.t2 = -INFINITY;
-  s.flag = 0;
-  s.i1 = INT32_MAX;
-#pragma unroll
-  for (int k = 0; k < kPerThread; ++k) {
-    const float v = x[k];
-    if (v != v || v == INFINITY) {
-      s.flag = 1;
-    } else {
-      s.M = fmaxf(s.M, v);
-      if constexpr (CH == kGreedy)
-        if (v > s.t1) s.i1 = idx(k);  // strict: the first of equal maxima stays
-      top2_insert(s.t1, s.t2, v);
-    }
-  }
-  s.S = 0.f;
-  s.T = 0.f;
-  s.ST = 0.f;
-  if (s.M > -INFINITY) {
-#pragma unroll
-    for (int k = 0; k < kPerThread; ++k) {
-      const float v = x[k];
-      if (v > -INFINITY && v < INFINITY) {  // finite (NaN fails both)
-        const float d = v - s.M;
-        const float e = exp_neg(d);
-        s.S += e;
-        s.T += d * e;
-        if constexpr (CH == kSample) s.ST += exp_neg(d * inv_t);
-      }
-    }
-  }
-  // wave reduction
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) s = merge<CH>(s, shfl_state<CH>(s, o), inv_t);
-  __shared__ RowState red[kThreads / 64];
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) red[w] = s;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    RowState r = red[0];
-    for (int i = 1; i < kThreads / 64; ++i) r = merge<CH>(r, red[i], inv_t);
-    float* p = a.partial + ((int64_t)b * a.nchunks + chunk) * kRec;
-    const f32x4 lo = {r.M, r.S, r.T, r.t1};
-    const f32x4 hi = {r.t2, __builtin_bit_cast(float, r.flag), r.ST, __builtin_bit_cast(float, r.i1)};
-    if (a.vecrec) {
-      reinterpret_cast<f32x4*>(p)[0] = lo;
-      reinterpret_cast<f32x4*>(p)[1] = hi;
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        p[e] = lo[e];
-        p[4 + e] = hi[e];
-      }
-    }
-  }
+__global__ __launch_bounds__(kConfThreads) void conf_partial_kernel(ConfArgs a) {
+  conf_partial_block<CH>(a, blockIdx.x, blockIdx.y, threadIdx.x);
 }
 
 template <int CH>
@@ -149,14 +54,18 @@ namespace {
 int choice_of(const ConfArgs& a) { return !a.token_out ? kNoChoice : (a.inv_temp > 0.f ? kSample : kGreedy); }
 }  // namespace
 
-hipError_t launch_confidence_partial(ConfArgs& a, hipStream_t s) {
+void confidence_prepare(ConfArgs& a) {
   a.chunk = kChunk;
   a.nchunks = (a.vocab + kChunk - 1) / kChunk;
   a.choice = choice_of(a);
+}
+
+hipError_t launch_confidence_partial(ConfArgs& a, hipStream_t s) {
+  confidence_prepare(a);
   const dim3 grid(a.nchunks, a.batch);
-  if (a.choice == kNoChoice) hipLaunchKernelGGL(conf_partial_kernel<kNoChoice>, grid, dim3(kThreads), 0, s, a);
-  else if (a.choice == kSample) hipLaunchKernelGGL(conf_partial_kernel<kSample>, grid, dim3(kThreads), 0, s, a);
-  else hipLaunchKernelGGL(conf_partial_kernel<kGreedy>, grid, dim3(kThreads), 0, s, a);
+  if (a.choice == kNoChoice) hipLaunchKernelGGL(conf_partial_kernel<kNoChoice>, grid, dim3(kConfThreads), 0, s, a);
+  else if (a.choice == kSample) hipLaunchKernelGGL(conf_partial_kernel<kSample>, grid, dim3(kConfThreads), 0, s, a);
+  else hipLaunchKernelGGL(conf_partial_kernel<kGreedy>, grid, dim3(kConfThreads), 0, s, a);
   return hipGetLastError();
 }
 

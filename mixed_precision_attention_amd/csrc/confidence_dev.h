@@ -1,14 +1,18 @@
-// Merge of the per-chunk confidence states and the budget gate, one wave
-// per row. CONF-KV summary, "Methodik: CONF-KV" (Konfidenzschaetzung,
-// adaptive Budgetauswahl) and the review's "核心方法": from the merged row
-// state (M, S = sum e^(z-M), T = sum (z-M) e^(z-M), top1 >= top2) the
-// confidence is c = w_H (1 - H/ln V) + w_m sigmoid(top1 - top2) + w_p / S with
+// Device code of the confidence pass, shared by the confidence call's
+// kernels and by the fused calls that run it inside other launches.
+// CONF-KV summary, "Methodik: CONF-KV" (Konfidenzschaetzung, adaptive
+// Budgetauswahl) and the review's "核心方法": from the merged row state
+// (M, S = sum e^(z-M), T = sum (z-M) e^(z-M), top1 >= top2) the confidence is
+// c = w_H (1 - H/ln V) + w_m sigmoid(top1 - top2) + w_p / S with
 // H = ln S - T/S, and the budget is N_high when c >= tau, else N_low. The
 // review's Algorithm 1, step 13: the next token (greedy, or by inversion of
 // the tempered softmax with the caller's uniform number).
 //
-// Shared by the confidence call's final kernel and the fused confidence +
-// attention call, which runs it in workgroups of the attention launch.
+//  conf_partial_block: one 256-thread workgroup reduces one 4096-logit chunk
+//    of a row to a state record;
+//  conf_row_c: one wave merges a row's records in a fixed order (every lane
+//    ends with the same state), takes the next token and returns c;
+//  conf_final_row: conf_row_c plus the outputs (c, token, status, budgets).
 #pragma once
 
 #include "confk_internal.h"
@@ -16,7 +20,9 @@
 namespace confk {
 namespace confm {
 
-constexpr int kChunk = 4096;           // logits per partial state (one workgroup of the pass)
+constexpr int kConfThreads = 256;       // workgroup of the pass
+constexpr int kConfPerThread = 16;      // logits per thread
+constexpr int kChunk = kConfThreads * kConfPerThread;  // logits per partial state
 constexpr int kLanePer = kChunk / 64;  // elements per lane in the sampling scan
 constexpr float kLog2e = 1.4426950408889634f;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -88,11 +94,109 @@ __device__ __forceinline__ RowState shfl_state(const RowState& s, int o) {
   return r;
 }
 
+// One 256-thread workgroup (tid = its thread index) reduces chunk `chunk`
+// of row b to a state record in a.partial.
+template <int CH>
+__device__ __forceinline__ void conf_partial_block(const ConfArgs& a, const int chunk, const int b, const int tid) {
+  const float* row = a.logits + (int64_t)b * a.ld;
+  const int start = chunk * a.chunk;
+  const int end = min(a.vocab, start + a.chunk);
+
+  float x[kConfPerThread];
+  if (a.vec4) {
+    // 16-byte loads: thread t reads groups t, t+256, ... of 4 logits
+#pragma unroll
+    for (int k = 0; k < kConfPerThread / 4; ++k) {
+      const int i = start + 4 * (tid + k * kConfThreads);
+      if (i + 3 < end) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(row + i);
+        x[4 * k] = v[0];
+        x[4 * k + 1] = v[1];
+        x[4 * k + 2] = v[2];
+        x[4 * k + 3] = v[3];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[4 * k + e] = (i + e < end) ? row[i + e] : -INFINITY;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < kConfPerThread; ++k) {
+      const int i = start + tid + k * kConfThreads;
+      x[k] = (i < end) ? row[i] : -INFINITY;
+    }
+  }
+  // logical index of x[k], ascending in k
+  auto idx = [&](int k) {
+    return a.vec4 ? start + 4 * (tid + (k >> 2) * kConfThreads) + (k & 3) : start + tid + k * kConfThreads;
+  };
+  const float inv_t = a.inv_temp;
+  RowState s;
+  s.M = -INFINITY;
+  s.t1 = -INFINITY;
+  s.t2 = -INFINITY;
+  s.flag = 0;
+  s.i1 = INT32_MAX;
+#pragma unroll
+  for (int k = 0; k < kConfPerThread; ++k) {
+    const float v = x[k];
+    if (v != v || v == INFINITY) {
+      s.flag = 1;
+    } else {
+      s.M = fmaxf(s.M, v);
+      if constexpr (CH == kGreedy)
+        if (v > s.t1) s.i1 = idx(k);  // strict: the first of equal maxima stays
+      top2_insert(s.t1, s.t2, v);
+    }
+  }
+  s.S = 0.f;
+  s.T = 0.f;
+  s.ST = 0.f;
+  if (s.M > -INFINITY) {
+#pragma unroll
+    for (int k = 0; k < kConfPerThread; ++k) {
+      const float v = x[k];
+      if (v > -INFINITY && v < INFINITY) {  // finite (NaN fails both)
+        const float d = v - s.M;
+        const float e = exp_neg(d);
+        s.S += e;
+        s.T += d * e;
+        if constexpr (CH == kSample) s.ST += exp_neg(d * inv_t);
+      }
+    }
+  }
+  // wave reduction
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) s = merge<CH>(s, shfl_state<CH>(s, o), inv_t);
+  __shared__ RowState red[kConfThreads / 64];
+  const int w = tid >> 6;
+  if ((tid & 63) == 0) red[w] = s;
+  __syncthreads();
+  if (tid == 0) {
+    RowState r = red[0];
+    for (int i = 1; i < kConfThreads / 64; ++i) r = merge<CH>(r, red[i], inv_t);
+    float* p = a.partial + ((int64_t)b * a.nchunks + chunk) * kRec;
+    const f32x4 lo = {r.M, r.S, r.T, r.t1};
+    const f32x4 hi = {r.t2, __builtin_bit_cast(float, r.flag), r.ST, __builtin_bit_cast(float, r.i1)};
+    if (a.vecrec) {
+      reinterpret_cast<f32x4*>(p)[0] = lo;
+      reinterpret_cast<f32x4*>(p)[1] = hi;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        p[e] = lo[e];
+        p[4 + e] = hi[e];
+      }
+    }
+  }
+}
+
 // Row b, lane `lane` of one wave: lane i merges partials i, i+64, ... in
 // order, then a butterfly merge (commutative, so every lane ends with the
-// same state); then the next-token choice, the confidence and the budgets.
+// same state); then the next-token choice (into tok, every lane) and the
+// confidence, returned to every lane (NaN for non-finite logits).
 template <int CH>
-__device__ __forceinline__ void conf_final_row(const ConfArgs& a, const int b, const int lane) {
+__device__ __forceinline__ float conf_row_c(const ConfArgs& a, const int b, const int lane, int& tok) {
   const float* p = a.partial + (int64_t)b * a.nchunks * kRec;
   const float inv_t = a.inv_temp;
   auto load = [&](int i) {
@@ -135,8 +239,8 @@ __device__ __forceinline__ void conf_final_row(const ConfArgs& a, const int b, c
   for (int o = 1; o < 64; o <<= 1) r = merge<CH>(r, shfl_state<CH>(r, o), inv_t);
   const bool bad = r.flag != 0 || !(r.M > -INFINITY);
 
+  tok = -1;
   if constexpr (CH != kNoChoice) {  // next-token choice (uniform per row)
-    int tok = -1;
     if constexpr (CH == kGreedy) {
       if (!bad) tok = r.i1;
     } else if (!bad) {
@@ -219,15 +323,12 @@ __device__ __forceinline__ void conf_final_row(const ConfArgs& a, const int b, c
       }
       tok = __shfl(tok, src, 64);
     }
-    if (lane == 0) a.token_out[b] = tok;
   }
 
-  // every lane holds the merged state: each computes c, lane l writes the
-  // budgets of layers l, l + 64, ... (per-layer budgets in parallel)
+  // every lane holds the merged state and computes c
   float c;
   if (bad) {
     c = __builtin_nanf("");
-    if (lane == 0 && a.status) atomicOr(a.status, (uint32_t)CONFK_STATUS_NONFINITE_LOGITS);
   } else {
     const float H = logf(r.S) - r.T / r.S;
     const float Hn = H / logf((float)a.vocab);
@@ -236,13 +337,30 @@ __device__ __forceinline__ void conf_final_row(const ConfArgs& a, const int b, c
     const float p1 = 1.f / r.S;
     c = a.w_h * (1.f - Hn) + a.w_m * sig + a.w_p * p1;
   }
-  if (lane == 0) a.c_out[b] = c;
+  return c;
+}
+
+// Budget of budget row l (per-layer budgets when given) for confidence c.
+__device__ __forceinline__ int conf_budget(const ConfArgs& a, const int l, const float c) {
   const bool tight = c >= a.tau;  // false for NaN
-  for (int l = lane; l < a.nbl; l += 64) {
-    const int nh = a.layer_n_high ? a.layer_n_high[l] : a.n_high;
-    const int nlo = a.layer_n_low ? a.layer_n_low[l] : a.n_low;
-    a.budget_out[(int64_t)l * a.batch + b] = tight ? nh : nlo;
+  const int nh = a.layer_n_high ? a.layer_n_high[l] : a.n_high;
+  const int nlo = a.layer_n_low ? a.layer_n_low[l] : a.n_low;
+  return tight ? nh : nlo;
+}
+
+// The confidence call's final step for row b: c, the next token, the status
+// bit for non-finite logits, and the budgets of all nbl rows (lane l writes
+// rows l, l + 64, ...).
+template <int CH>
+__device__ __forceinline__ void conf_final_row(const ConfArgs& a, const int b, const int lane) {
+  int tok;
+  const float c = conf_row_c<CH>(a, b, lane, tok);
+  if (lane == 0) {
+    if (CH != kNoChoice) a.token_out[b] = tok;
+    a.c_out[b] = c;
+    if (c != c && a.status) atomicOr(a.status, (uint32_t)CONFK_STATUS_NONFINITE_LOGITS);
   }
+  for (int l = lane; l < a.nbl; l += 64) a.budget_out[(int64_t)l * a.batch + b] = conf_budget(a, l, c);
 }
 
 }  // namespace confm

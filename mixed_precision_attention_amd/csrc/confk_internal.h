@@ -63,11 +63,16 @@ struct AttnArgs {
   uint16_t* out;
   float* mass;
   float* spill;  // [nl*B*hkv][g][spill_stride] or null
-  // fused confidence call: the launch's first conf_groups workgroups merge the
-  // confidence rows of `conf` (one wave per row) before the units start
+  // Fused confidence work on `conf` (conf_mode, set by the caller):
+  //  kConfMerge: the launch's first conf_groups workgroups merge the
+  //    confidence rows (one wave per row) before the units start;
+  //  kConfPass: its last conf_tail workgroups run the confidence pass (one
+  //    chunk of one row each). The launcher sets the two counts.
   ConfArgs conf;
-  int32_t conf_groups;
+  int32_t conf_mode;
+  int32_t conf_groups, conf_tail;
 };
+enum { kConfNone = 0, kConfMerge = 1, kConfPass = 2 };
 
 struct EmaArgs {
   CacheView c;
@@ -102,6 +107,10 @@ struct CompactArgs {
   float* score_out;
   // fused form with the window step (token eviction: in the same kernel)
   int32_t quantize, window;
+  // whole-step call: each plan workgroup merges its sequence's confidence
+  // states (written by the attention launch) and takes its budget from them
+  ConfArgs conf;
+  int32_t conf_merge;
 };
 
 struct QuantArgs {
@@ -117,7 +126,9 @@ struct QuantArgs {
 hipError_t launch_confidence(const ConfArgs& a, hipStream_t s);
 size_t confidence_ws_bytes(int32_t batch, int32_t vocab);
 hipError_t launch_attention(const AttnArgs& a, int lds_bytes, hipStream_t s);
-// The confidence pass without the final merge (sets chunking and choice in a).
+// Chunking and next-token choice of the confidence pass, set in a.
+void confidence_prepare(ConfArgs& a);
+// The confidence pass without the final merge (prepares a first).
 hipError_t launch_confidence_partial(ConfArgs& a, hipStream_t s);
 int attention_lds_bytes(int d, int g, int n_lds);
 int attention_plan_n_lds(int d, int g, int cap, int* spill_stride);

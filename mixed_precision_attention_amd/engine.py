@@ -120,6 +120,23 @@ def confidence_attn_decode(logits, pol, c_out, budget_out, status, conf_ws, cach
         _stream()))
 
 
+def decode_step(logits, pol, c_out, budget_out, cache, t, q, k_new, v_new, out, mass, score, conf_ws, attn_ws,
+                compact_ws, layer_n_high=None, layer_n_low=None, token_out=None, temperature=0.0, uniform=None,
+                evicted=None, fuse_quantize=True, layer0=0, nlayers=None):
+    """confk_decode_step: confidence, attention, EMA + rank + compaction (and
+    the window step) in three launches, same results as the five calls."""
+    lib = L.load()
+    nbl = 1 if layer_n_high is None else int(layer_n_high.numel())
+    nl = cache.layers - layer0 if nlayers is None else nlayers
+    wsb = lambda w: 0 if w is None else w.numel() * w.element_size()  # noqa: E731
+    L.check("confk_decode_step", lib.confk_decode_step(
+        _p(logits), logits.stride(0), logits.shape[1], ctypes.byref(pol), _p(layer_n_high), _p(layer_n_low), nbl,
+        _p(c_out), _p(budget_out), _p(uniform), float(temperature), _p(token_out), cache.ref(), layer0, nl, int(t),
+        _p(q), _p(k_new), _p(v_new), _p(out), _p(mass), _p(score), _p(evicted),
+        L.FUSE_QUANTIZE if fuse_quantize else 0, _p(conf_ws), wsb(conf_ws), _p(attn_ws), wsb(attn_ws),
+        _p(compact_ws), wsb(compact_ws), _stream()))
+
+
 def attn_decode(cache, q, k_new, v_new, out, mass, ws, layer0=0, nlayers=None):
     lib = L.load()
     nl = cache.layers - layer0 if nlayers is None else nlayers
@@ -287,14 +304,16 @@ class DecodeEngine:
             ema_rank(self.cache, None, self.pol, t, self.score)
             self.step_compact(k_new, v_new)
             return
-        if self.side is None:
-            self.step_confidence_attention(logits, q, k_new, v_new)
-        else:
-            main = torch.cuda.current_stream()
-            self.side.wait_stream(main)  # the logits, and the previous step's use of the budget
-            with torch.cuda.stream(self.side):
-                self.step_confidence(logits)
-            self.conf_done.record(self.side)
-            self.step_attention(q, k_new, v_new)
-            torch.cuda.current_stream().wait_event(self.conf_done)
+        if self.side is None:  # one stream: the whole-step call (three launches)
+            decode_step(logits, self.pol, self.c, self.budget, self.cache, t, q, k_new, v_new, self.out,
+                        self.mass, self.score, self.conf_ws, self.attn_ws, self.compact_ws,
+                        self.layer_n_high, self.layer_n_low, evicted=self.evicted)
+            return
+        main = torch.cuda.current_stream()
+        self.side.wait_stream(main)  # the logits, and the previous step's use of the budget
+        with torch.cuda.stream(self.side):
+            self.step_confidence(logits)
+        self.conf_done.record(self.side)
+        self.step_attention(q, k_new, v_new)
+        main.wait_event(self.conf_done)
         self.step_ema_compact(t, k_new, v_new, fuse_quantize=True)

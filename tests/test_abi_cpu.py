@@ -52,7 +52,7 @@ def test_product_library_does_not_export_the_probe(lib):
 def test_library_exports_every_declared_symbol(lib):
     for n in declared():
         assert hasattr(lib, n), n
-    assert lib.confk_version() == 105
+    assert lib.confk_version() == 106
     assert lib.confk_strerror(-1) == b"invalid argument"
     assert lib.confk_strerror(12345) == b"unknown error"
 
@@ -144,6 +144,33 @@ def test_fused_confidence_attention_validation(lib):
     assert call(conf_wsb=4) == M.ERR_WORKSPACE
     assert call(temperature=0.8, token=FAKE) == M.ERR_INVALID_ARG   # sampling needs uniforms
     assert call(q=None) == M.ERR_INVALID_ARG
+    assert call(nl=3) == M.ERR_INVALID_ARG
+    assert call(cache=_fake_cache(d=96)) == M.ERR_UNSUPPORTED
+
+
+def test_decode_step_validation(lib):
+    """confk_decode_step validates the three calls' argument sets (and its
+    own) before anything is launched."""
+    pol = _pol()
+    c = _fake_cache()
+    big = 1 << 30
+
+    def call(logits=FAKE, nbl=1, lnh=None, lnl=None, mass=FAKE, t=5, flags=0, conf_ws=FAKE, attn_ws=FAKE,
+             compact_ws=FAKE, cwsb=big, q=FAKE, score=FAKE, cache=c, nl=2):
+        return lib.confk_decode_step(
+            logits, 10, 10, ctypes.byref(pol), lnh, lnl, nbl, FAKE, FAKE, None, 0.0, None, ctypes.byref(cache), 0,
+            nl, t, q, FAKE, FAKE, FAKE, mass, score, None, flags, conf_ws, big, attn_ws, big, compact_ws, cwsb,
+            None)
+    assert call(logits=None) == M.ERR_INVALID_ARG
+    assert call(mass=None) == M.ERR_INVALID_ARG
+    assert call(t=-1) == M.ERR_INVALID_ARG
+    assert call(flags=4) == M.ERR_INVALID_ARG
+    assert call(nbl=3, lnh=FAKE, lnl=FAKE) == M.ERR_INVALID_ARG   # neither 1 nor nlayers
+    assert call(conf_ws=None) == M.ERR_WORKSPACE
+    assert call(compact_ws=None) == M.ERR_WORKSPACE
+    assert call(cwsb=4) == M.ERR_WORKSPACE
+    assert call(q=None) == M.ERR_INVALID_ARG
+    assert call(score=None) == M.ERR_INVALID_ARG
     assert call(nl=3) == M.ERR_INVALID_ARG
     assert call(cache=_fake_cache(d=96)) == M.ERR_UNSUPPORTED
 

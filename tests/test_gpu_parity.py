@@ -608,9 +608,10 @@ def _split_step(e, lg, q, kn, vn, t):
 
 
 def test_qwen32b_full_launch_fused_matches_split():
-    """DecodeEngine.step (the confidence merge inside the attention launch and
-    EMA + compaction + window step fused, on one stream as bench.py times it;
-    and with the confidence on a second stream) against
+    """DecodeEngine.step (the whole-step call on one stream as bench.py times
+    it: the confidence pass inside the attention launch, the merge and the
+    budgets in the fused EMA + compaction + window-step launch; and with the
+    confidence on a second stream) against
     the five calls issued one after another, bit for bit, at the full
     64-layer, batch-8 size (the split calls themselves are checked against
     the oracle at this size above)."""
@@ -765,6 +766,51 @@ def test_fused_confidence_attention_matches_split(choice):
             assert torch.equal(engs[0].cache.meta, engs[1].cache.meta)
             for e in engs:
                 e.step_ema_compact(t, kd, vd, fuse_quantize=True)
+
+
+@pytest.mark.parametrize("choice", ["none", "greedy", "sample"])
+def test_decode_step_matches_split(choice):
+    """confk_decode_step (the confidence pass in the attention launch's last
+    workgroups, the merge and the budget in the plan kernel; with sampling
+    the confidence call's own kernels) against the five calls one after
+    another, bit for bit over several steps: the whole cache, c, budgets, the
+    next token, output, mass and scores. Shapes: the Qwen-32B shape with two
+    layers, a small ragged one from an empty cache (the window step
+    calibrates), and per-layer (pyramid) budgets."""
+    import mixed_precision_attention_amd as M
+    dev = _dev()
+    lo = (60, 52, 44)
+    cases = (synth.get_config("qwen32b").with_(layers=2), TINY["g3_d64_empty"],
+             _cfg("pyr", 3, 2, 10, 2, 128, 600, 120, max(lo) // 2, max(lo), 8, 24,
+                  layer_n_low=lo, layer_n_high=tuple(x // 2 for x in lo)))
+    for cfg in cases:
+        engs = [M.DecodeEngine(cfg, dev), M.DecodeEngine(cfg, dev)]
+        if cfg.prefill:
+            kp, vp = synth.prefill_kv(cfg, 7)
+            for e in engs:
+                e.prefill(_t(kp, dev), _t(vp, dev))
+        temp = None if choice == "none" else (0.0 if choice == "greedy" else 0.8)
+        steps = 8 if cfg.prefill else 40
+        for i in range(steps):
+            logits, q, kn, vn, t = _inputs(cfg, 7, i)
+            lg, qd, kd, vd = _t(logits, dev), _t(q, dev), _t(kn, dev), _t(vn, dev)
+            u = torch.rand(cfg.batch, generator=torch.Generator().manual_seed(i)).to(dev)
+            e = engs[0]
+            e.step_confidence(lg, temperature=temp, uniform=u)
+            e.step_attention(qd, kd, vd)
+            e.step_ema_rank(t)
+            e.step_compact(kd, vd)
+            e.step_quantize(t)
+            f = engs[1]
+            M.engine.decode_step(lg, f.pol, f.c, f.budget, f.cache, t, qd, kd, vd, f.out, f.mass, f.score,
+                                 f.conf_ws, f.attn_ws, f.compact_ws, f.layer_n_high, f.layer_n_low,
+                                 token_out=None if temp is None else f.token,
+                                 temperature=0.0 if temp is None else temp, uniform=u, evicted=f.evicted)
+            torch.cuda.synchronize()
+            if temp is not None:
+                assert torch.equal(e.token, f.token), (cfg.name, i, "token")
+        _assert_same_state(engs[0], engs[1])
+        assert int(engs[1].cache.status.cpu()[0]) == 0
 
 
 def test_long_context_pyramid_retains_planted_keys():
