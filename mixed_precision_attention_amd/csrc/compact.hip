@@ -254,29 +254,39 @@ __device__ __forceinline__ void plan_body(const CompactArgs& a) {
   const int base8 = meta[CONFK_META_BASE8];
   const int base16 = meta[CONFK_META_BASE16];
   const int P = a.protect;
-  int N;
-  if (a.conf_merge) {  // uniform (a kernel argument): the budget from this sequence's confidence
-    __shared__ float conf_c;
-    const int brow = a.conf.nbl > 1 ? l : 0;  // budget row of this layer
-    if (threadIdx.x < 64) {
-      int tok;
-      const float cc = a.conf.choice == confm::kGreedy
-                           ? confm::conf_row_c<confm::kGreedy>(a.conf, b, threadIdx.x, tok)
-                           : confm::conf_row_c<confm::kNoChoice>(a.conf, b, threadIdx.x, tok);
-      if (threadIdx.x == 0) {
-        conf_c = cc;
-        if (l == 0) {  // the call's first layer writes the sequence's outputs
-          a.conf.c_out[b] = cc;
-          if (a.conf.choice == confm::kGreedy) a.conf.token_out[b] = tok;
-          if (cc != cc && a.conf.status) atomicOr(a.conf.status, (uint32_t)CONFK_STATUS_NONFINITE_LOGITS);
-        }
-        if (brow == l) a.conf.budget_out[(int64_t)brow * a.conf.batch + b] = confm::conf_budget(a.conf, brow, cc);
+  // Whole-step call (a.conf_merge, uniform): the budget comes from this
+  // sequence's confidence. Wave 0 issues the loads of the per-chunk states
+  // now and finishes the merge inside the EMA phase (token eviction), or
+  // here (block eviction, which needs the budget first).
+  const bool merge_late = FUSE && !BLOCK && a.conf_merge;
+  const bool greedy = a.conf.choice == confm::kGreedy;
+  const int brow = a.conf.nbl > 1 ? l : 0;  // budget row of this layer
+  __shared__ float conf_c;
+  confm::RowState crs{};
+  if (a.conf_merge && threadIdx.x < 64)
+    crs = greedy ? confm::conf_lane_state<confm::kGreedy>(a.conf, b, threadIdx.x)
+                 : confm::conf_lane_state<confm::kNoChoice>(a.conf, b, threadIdx.x);
+  auto conf_finish = [&]() {  // wave 0: c to shared memory; the first layer writes the outputs
+    int tok;
+    const float cc = greedy ? confm::conf_row_finish<confm::kGreedy>(a.conf, b, threadIdx.x, crs, tok)
+                            : confm::conf_row_finish<confm::kNoChoice>(a.conf, b, threadIdx.x, crs, tok);
+    if (threadIdx.x == 0) {
+      conf_c = cc;
+      if (l == 0) {
+        a.conf.c_out[b] = cc;
+        if (greedy) a.conf.token_out[b] = tok;
+        if (cc != cc && a.conf.status) atomicOr(a.conf.status, (uint32_t)CONFK_STATUS_NONFINITE_LOGITS);
       }
+      if (brow == l) a.conf.budget_out[(int64_t)brow * a.conf.batch + b] = confm::conf_budget(a.conf, brow, cc);
     }
+  };
+  int N = P;  // merge_late: set after the merge
+  if (!a.conf_merge) {
+    N = max(a.budget[l * a.budget_stride + b], P);
+  } else if (!merge_late) {
+    if (threadIdx.x < 64) conf_finish();
     __syncthreads();
     N = max(confm::conf_budget(a.conf, brow, conf_c), P);
-  } else {
-    N = max(a.budget[l * a.budget_stride + b], P);
   }
   float* ema = c.ema + (size_t)lbc * cap;
   int32_t* pos = c.pos + (size_t)lbc * cap;
@@ -312,6 +322,7 @@ __device__ __forceinline__ void plan_body(const CompactArgs& a) {
   const int f = n - n8;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   if (!meta_ok(n, n8, base8, base16, cap, c.cap16)) {  // no room: flag, leave the cache as it is
+    if (merge_late && threadIdx.x < 64) conf_finish();  // the confidence outputs are still due
     if (threadIdx.x == 0) {
       atomicOr(c.status, (uint32_t)CONFK_STATUS_CAPACITY);
       meta[CONFK_META_EVICTED] = 0;
@@ -422,7 +433,12 @@ __device__ __forceinline__ void plan_body(const CompactArgs& a) {
       sh.rpmin[w] = pmin;
       sh.rpmax[w] = pmax;
     }
-    __syncthreads();  // the exchange, and the long-cache form's EMA writes, are visible
+    if (merge_late && w == 0) conf_finish();
+    __syncthreads();  // the exchange, the long-cache form's EMA writes and conf_c are visible
+    if (merge_late) {
+      N = max(confm::conf_budget(a.conf, brow, conf_c), P);
+      k = n > N ? n - N : 0;
+    }
     amax = sh.rmax[0];
     int p0 = sh.rpmin[0], p1 = sh.rpmax[0];
 #pragma unroll

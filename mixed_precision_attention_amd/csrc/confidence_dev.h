@@ -51,6 +51,8 @@ __device__ __forceinline__ void top2_insert(float& t1, float& t2, float x) {
 // inv_t: 1 / temperature (sampling only)
 template <int CH>
 __device__ __forceinline__ RowState merge(const RowState& a, const RowState& b, float inv_t) {
+  // no FMA contraction: the same arithmetic in every kernel that inlines it
+#pragma clang fp contract(off)
   RowState r;
   r.M = fmaxf(a.M, b.M);
   r.flag = a.flag | b.flag;
@@ -98,6 +100,8 @@ __device__ __forceinline__ RowState shfl_state(const RowState& s, int o) {
 // of row b to a state record in a.partial.
 template <int CH>
 __device__ __forceinline__ void conf_partial_block(const ConfArgs& a, const int chunk, const int b, const int tid) {
+  // no FMA contraction: the same arithmetic in every kernel that inlines it
+#pragma clang fp contract(off)
   const float* row = a.logits + (int64_t)b * a.ld;
   const int start = chunk * a.chunk;
   const int end = min(a.vocab, start + a.chunk);
@@ -195,36 +199,52 @@ __device__ __forceinline__ void conf_partial_block(const ConfArgs& a, const int 
 // order, then a butterfly merge (commutative, so every lane ends with the
 // same state); then the next-token choice (into tok, every lane) and the
 // confidence, returned to every lane (NaN for non-finite logits).
+// Record i of row b (two 16-byte words when the records are aligned).
+__device__ __forceinline__ RowState conf_record(const ConfArgs& a, const int b, const int i) {
+  const float* p = a.partial + ((int64_t)b * a.nchunks + i) * kRec;
+  f32x4 lo, hi;
+  if (a.vecrec) {
+    lo = reinterpret_cast<const f32x4*>(p)[0];
+    hi = reinterpret_cast<const f32x4*>(p)[1];
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      lo[e] = p[e];
+      hi[e] = p[4 + e];
+    }
+  }
+  RowState q;
+  q.M = lo[0];
+  q.S = lo[1];
+  q.T = lo[2];
+  q.t1 = lo[3];
+  q.t2 = hi[0];
+  // vector elements are copied to scalars before the bit casts (a bit cast
+  // of the element expression itself reads element 0)
+  const float flag_bits = hi[1], i1_bits = hi[3];
+  q.flag = __builtin_bit_cast(uint32_t, flag_bits);
+  q.ST = hi[2];
+  q.i1 = __builtin_bit_cast(int32_t, i1_bits);
+  return q;
+}
+
+template <int CH>
+__device__ __forceinline__ RowState conf_lane_state(const ConfArgs& a, const int b, const int lane);
+template <int CH>
+__device__ __forceinline__ float conf_row_finish(const ConfArgs& a, const int b, const int lane, RowState r,
+                                                 int& tok);
+
 template <int CH>
 __device__ __forceinline__ float conf_row_c(const ConfArgs& a, const int b, const int lane, int& tok) {
-  const float* p = a.partial + (int64_t)b * a.nchunks * kRec;
+  return conf_row_finish<CH>(a, b, lane, conf_lane_state<CH>(a, b, lane), tok);
+}
+
+// The first part of conf_row_c: lane `lane`'s merge of records lane,
+// lane + 64, ... (its loads can be issued early and the rest done later).
+template <int CH>
+__device__ __forceinline__ RowState conf_lane_state(const ConfArgs& a, const int b, const int lane) {
   const float inv_t = a.inv_temp;
-  auto load = [&](int i) {
-    f32x4 lo, hi;
-    if (a.vecrec) {
-      lo = reinterpret_cast<const f32x4*>(p + kRec * i)[0];
-      hi = reinterpret_cast<const f32x4*>(p + kRec * i)[1];
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        lo[e] = p[kRec * i + e];
-        hi[e] = p[kRec * i + 4 + e];
-      }
-    }
-    RowState q;
-    q.M = lo[0];
-    q.S = lo[1];
-    q.T = lo[2];
-    q.t1 = lo[3];
-    q.t2 = hi[0];
-    // vector elements are copied to scalars before the bit casts (a bit cast
-    // of the element expression itself reads element 0)
-    const float flag_bits = hi[1], i1_bits = hi[3];
-    q.flag = __builtin_bit_cast(uint32_t, flag_bits);
-    q.ST = hi[2];
-    q.i1 = __builtin_bit_cast(int32_t, i1_bits);
-    return q;
-  };
+  auto load = [&](int i) { return conf_record(a, b, i); };
   RowState r;
   r.M = -INFINITY;
   r.S = 0.f;
@@ -235,6 +255,18 @@ __device__ __forceinline__ float conf_row_c(const ConfArgs& a, const int b, cons
   r.ST = 0.f;
   r.i1 = INT32_MAX;
   for (int i = lane; i < a.nchunks; i += 64) r = merge<CH>(r, load(i), inv_t);
+  return r;
+}
+
+// The rest of conf_row_c: the butterfly merge of the lanes' states, the
+// next-token choice and c.
+template <int CH>
+__device__ __forceinline__ float conf_row_finish(const ConfArgs& a, const int b, const int lane, RowState r,
+                                                 int& tok) {
+  // no FMA contraction: the same arithmetic in every kernel that inlines it
+#pragma clang fp contract(off)
+  const float inv_t = a.inv_temp;
+  auto load = [&](int i) { return conf_record(a, b, i); };
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) r = merge<CH>(r, shfl_state<CH>(r, o), inv_t);
   const bool bad = r.flag != 0 || !(r.M > -INFINITY);
