@@ -493,8 +493,23 @@ def test_full_launch_sampled(name):
     L, B = cfg.layers, cfg.batch
     print(f"[parity] {name} full cap={cfg.cap} block={cfg.policy.block} order={cfg.policy.order}", flush=True)
     run = Run(cfg, seed=2, pairs=[(0, 0), (L // 2, min(4, B - 1)), (L - 1, B - 1)], device_prefill=True)
-    for i in range(2):
+    for i in range(4):
         run.step(i)
+
+
+def test_qwen32b_full_size_free_run():
+    """The throughput workload at full size (64 layers x batch 8) over its
+    first 160 decode steps after the prefill (the window the short benchmark
+    measures, with first evictions of about 1000 tokens, then one token per
+    step with stable packing into the steady state), five (layer, sequence)
+    pairs followed by the oracle after every step."""
+    cfg = synth.get_config("qwen32b")
+    L, B = cfg.layers, cfg.batch
+    print(f"[parity] qwen32b full size, 160 steps", flush=True)
+    run = Run(cfg, seed=9, pairs=[(0, 0), (13, 3), (31, 7), (48, 1), (L - 1, B - 3)], device_prefill=True)
+    events = sum(run.step(i) for i in range(160))
+    assert events > 0
+    assert run.band <= 2
 
 
 def test_full_kv_comparison_run_sampled():
@@ -517,7 +532,7 @@ def test_full_kv_comparison_run_sampled():
     orc = {(l, b): O.prefill(kp[l, b].cpu().numpy(), vp[l, b].cpu().numpy(), cfg.policy.window)
            for (l, b) in pairs}
     del kp, vp
-    for i in range(2):
+    for i in range(4):
         logits, q, kn, vn, t = _inputs(cfg, 4, i)
         eng.step(_t(logits, dev), _t(q, dev), _t(kn, dev), _t(vn, dev), t)
         torch.cuda.synchronize()
