@@ -205,9 +205,12 @@ int confk_confidence(const float* logits, int64_t ld, int32_t batch, int32_t voc
  *                 r >= R are left as they were. R = hkv (row j = kv head j)
  *                 unless the launch's units (layer, sequence, kv head) fill
  *                 at least two rounds of the GPU's resident workgroups; then
- *                 each workgroup runs two consecutive units (kv heads
- *                 fastest) and writes one row per (layer, sequence) of the
- *                 two, so R = hkv / 2 for an even hkv. NULL
+ *                 the workgroups run two consecutive units each (kv heads
+ *                 fastest), except the last round of dispatch, whose
+ *                 workgroups run one, and each writes one row per (layer,
+ *                 sequence) it touches: R = hkv / 2 for an even hkv, hkv in
+ *                 the last round, and in between where the two meet (pairs
+ *                 of kv heads first, then single heads). NULL
  *                 when the caller needs only the output (no workspace then;
  *                 the meta word is not touched)
  *   ws            >= confk_workspace_size(CONFK_WS_ATTENTION, ...) bytes

@@ -271,10 +271,11 @@ __host__ __device__ __forceinline__ int score_area_floats(int d, int g, int n_ld
 // 64-layer, batch-8 shape become 1024 workgroups, 1.33 rounds of 768).
 constexpr int kAccUnits = 2;
 
-// Workgroup that runs unit x when U units are split into G contiguous
-// ranges, range w = [floor(w U / G), floor((w + 1) U / G)).
-__device__ __forceinline__ int unit_owner(uint32_t x, uint32_t U, uint32_t G) {
-  return (int)(((x + 1) * G - 1) / U);
+// The unit ranges: workgroup w < P (P = acc_pairs) runs units [2w, 2w + 2),
+// a later one the single unit P + w, so the last workgroups dispatched are
+// one-unit ones and the launch's last round drains sooner.
+__device__ __forceinline__ int unit_owner(uint32_t x, uint32_t P) {
+  return (int)(x < 2 * P ? x >> 1 : x - P);
 }
 
 // SPILL: scores past the LDS budget go to global memory. Kept out of the
@@ -326,11 +327,10 @@ void attn_decode_kernel(AttnArgs a) {
   const CacheView& c = a.c;
   const int H = c.hkv;
   const int g = a.g;
-  const uint32_t U = (uint32_t)a.nl * c.B * H;  // units of this launch (U * G < 2^32)
-  const uint32_t G = ACC ? gridDim.x - a.conf_groups - a.conf_tail : U;
+  const uint32_t P = (uint32_t)a.acc_pairs;
   const int wg = blockIdx.x - a.conf_groups;
-  const int u_begin = ACC ? (int)((uint32_t)wg * U / G) : wg;
-  const int u_end = ACC ? (int)((uint32_t)(wg + 1) * U / G) : wg + 1;
+  const int u_begin = ACC ? ((uint32_t)wg < P ? 2 * wg : (int)P + wg) : wg;
+  const int u_end = ACC ? ((uint32_t)wg < P ? 2 * wg + 2 : (int)P + wg + 1) : wg + 1;
   // (layer, sequence, kv head) of the current unit, advanced without
   // divisions; a (layer, sequence) that starts inside this range has its
   // first unit here, so this workgroup writes its row 0
@@ -339,7 +339,7 @@ void attn_decode_kernel(AttnArgs a) {
   int b = lb % c.B;
   int l = lb / c.B;
   const int lb_first = lb;
-  const int mrow_first = ACC ? wg - unit_owner((uint32_t)(lb * H), U, G) : h;
+  const int mrow_first = ACC ? wg - unit_owner((uint32_t)(lb * H), P) : h;
 
   // the work of one unit; ACC runs it for each unit of the range in turn
   auto unit_body = [&](int u) __attribute__((always_inline)) {
@@ -376,7 +376,7 @@ void attn_decode_kernel(AttnArgs a) {
     return;
   }
   if (MASS && h == 0 && tid == 0)
-    meta[CONFK_META_MASSROWS] = ACC ? unit_owner((uint32_t)(lb * H + H - 1), U, G) - wg + 1 : H;
+    meta[CONFK_META_MASSROWS] = ACC ? unit_owner((uint32_t)(lb * H + H - 1), P) - wg + 1 : H;
   const int nt8 = (n8 + 15) >> 4;
   const int nt16 = (f + 1 + 15) >> 4;
   const int p16 = nt8 * 16;  // first score slot of the FP16 region
@@ -844,6 +844,9 @@ int resident_per_cu(const void* fn, int lds_bytes) {
   return occ;
 }
 
+#ifndef CONFK_ACC_TAIL
+#define CONFK_ACC_TAIL 8
+#endif
 template <int D>
 hipError_t launch_d(const AttnArgs& a, int lds_bytes, hipStream_t s) {
   const int64_t units = (int64_t)a.nl * a.c.B * a.c.hkv;
@@ -863,9 +866,14 @@ hipError_t launch_d(const AttnArgs& a, int lds_bytes, hipStream_t s) {
     const int occ_acc = resident_per_cu(acc, acc_bytes);
     const int64_t slots = (int64_t)occ_acc * device_cus();
     const int64_t groups = (units + kAccUnits - 1) / kAccUnits;
-    if (occ_acc > 0 && slots > 0 && groups >= slots && units * (groups + 1) < ((int64_t)1 << 32) &&
+    if (occ_acc > 0 && slots > 0 && groups >= slots && units < ((int64_t)1 << 31) &&
         occ_acc >= resident_per_cu(plain, lds_bytes)) {
-      hipLaunchKernelGGL((attn_decode_kernel<D, false, true, true>), dim3(groups + cg), block, acc_bytes, s, a);
+      // single-unit workgroups for the last CONFK_ACC_TAIL / 8 of a round
+      const int64_t tail = std::min<int64_t>(units, slots * CONFK_ACC_TAIL / 8);
+      AttnArgs b = a;
+      b.acc_pairs = (int32_t)((units - tail) / 2);
+      const int64_t g2 = b.acc_pairs + (units - 2 * (int64_t)b.acc_pairs);
+      hipLaunchKernelGGL((attn_decode_kernel<D, false, true, true>), dim3(g2 + cg), block, acc_bytes, s, b);
     } else {
       hipLaunchKernelGGL((attn_decode_kernel<D, false, true, false>), dim3(units + cg), block, lds_bytes, s, a);
     }

@@ -71,6 +71,9 @@ struct AttnArgs {
   ConfArgs conf;
   int32_t conf_mode;
   int32_t conf_groups, conf_tail;
+  // two kv heads per workgroup (set by the launcher): workgroups
+  // [0, acc_pairs) run two units each, the later ones one each
+  int32_t acc_pairs;
 };
 enum { kConfNone = 0, kConfMerge = 1, kConfPass = 2 };
 
