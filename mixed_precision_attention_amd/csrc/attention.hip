@@ -39,6 +39,7 @@
 // budget); once the waves' running maxima and normalisers are merged, each
 // key's mass sum_h 2^(s_h - M_h) / L_h is formed exactly.
 #include <mutex>
+#include <type_traits>
 
 #include "confidence_dev.h"
 #include "confk_internal.h"
@@ -283,8 +284,8 @@ __device__ __forceinline__ int unit_owner(uint32_t x, uint32_t P) {
 // counter unusable for partial waits (stores complete out of order).
 // MASS = false: no per-key mass (no score store; for callers that only need
 // the attention output, e.g. a full-cache baseline).
-// ACC: workgroup w of G runs the contiguous unit range [w U / G, (w+1) U / G)
-// (kv heads fastest, at most kAccUnits units) and sums the mass of the
+// ACC (an even hkv): workgroup w runs the unit range of unit_owner (kv heads
+// fastest, at most kAccUnits units) and sums the mass of the
 // consecutive kv heads of one (layer, sequence) in LDS, so it writes one
 // partial mass row per (layer, sequence) it touches instead of one per kv
 // head. Row r of a (layer, sequence) is the r-th workgroup that covers it;
@@ -341,8 +342,20 @@ void attn_decode_kernel(AttnArgs a) {
   const int lb_first = lb;
   const int mrow_first = ACC ? wg - unit_owner((uint32_t)(lb * H), P) : h;
 
-  // the work of one unit; ACC runs it for each unit of the range in turn
-  auto unit_body = [&](int u) __attribute__((always_inline)) {
+  // ACC: the next unit of a workgroup is the next kv head of the same
+  // (layer, sequence) (same cache header, same ring slots); its first loads
+  // (the query and scale pieces, each wave's first two INT8 tiles) go out
+  // when this unit's tiles are done, and arrive during its merge, mass pass
+  // and output.
+  u32x4 nx_piece[2];
+  Raw8<D> nx_a, nx_b;  // set before any read (no initial value: no copies where they are set)
+  bool nx_ok = false;
+
+  // the work of one unit; ACC runs it for each unit of the range in turn.
+  // NEXT (a compile-time flag): the first of a workgroup's two units, which
+  // issues the second one's first loads at its end.
+  auto unit_body = [&](int u, auto NEXT) __attribute__((always_inline)) {
+  constexpr bool next = decltype(NEXT)::value;
   if (u != u_begin) {
     if (++h == H) {
       h = 0;
@@ -442,31 +455,39 @@ void attn_decode_kernel(AttnArgs a) {
   const int krow0 = kpair ? (r16 & 7) : r16;
   const uint32_t kcol = 16 * kg + (kpair ? 64 * (r16 >> 3) : 0);
   const uint32_t kinc8 = 8u % cap;
-  uint32_t sk = (uint32_t)((base8 + 16 * tnext + krow0) % c.cap);
-  uint32_t sv = (uint32_t)((base8 + 16 * tnext + 4 * kg) % c.cap);
-  auto load8 = [&](Raw8<D>& r) {
+  const uint32_t sk0 = (uint32_t)((base8 + 16 * tnext + krow0) % c.cap);
+  const uint32_t sv0 = (uint32_t)((base8 + 16 * tnext + 4 * kg) % c.cap);
+  uint32_t sk = sk0, sv = sv0;
+  // one tile of the rings at kb / vb from ring slots s_k (K) and s_v (V)
+  auto ld8 = [&](Raw8<D>& r, const int8_t* kb, const int8_t* vb, uint32_t s_k, uint32_t s_v) {
     if constexpr (kpair) {
-      r.k[0] = stream_load(reinterpret_cast<const u32x4*>(k8 + sk * D + kcol));
-      r.k[1] = stream_load(reinterpret_cast<const u32x4*>(k8 + wrap(sk + kinc8) * D + kcol));
+      r.k[0] = stream_load(reinterpret_cast<const u32x4*>(kb + s_k * D + kcol));
+      r.k[1] = stream_load(reinterpret_cast<const u32x4*>(kb + wrap(s_k + kinc8) * D + kcol));
     } else {  // 64-byte rows: one instruction covers 16 consecutive rows
-      r.k[0] = stream_load(reinterpret_cast<const u32x4*>(k8 + sk * D + kcol));
+      r.k[0] = stream_load(reinterpret_cast<const u32x4*>(kb + s_k * D + kcol));
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t vo = wrap(sv + vinc[j]) * D + (D / 16) * r16;
+      const uint32_t vo = wrap(s_v + vinc[j]) * D + (D / 16) * r16;
       if constexpr (CB == 8) {
-        const u32x2 t2 = stream_load(reinterpret_cast<const u32x2*>(v8 + vo));
+        const u32x2 t2 = stream_load(reinterpret_cast<const u32x2*>(vb + vo));
         r.v[j][0] = t2[0];
         r.v[j][1] = t2[1];
       } else {
-        r.v[j][0] = stream_load(reinterpret_cast<const uint32_t*>(v8 + vo));
+        r.v[j][0] = stream_load(reinterpret_cast<const uint32_t*>(vb + vo));
       }
     }
+  };
+  auto adv8 = [&]() {  // the slots of this wave's next tile
     const bool adv = tnext + kWaves <= last8;
     const uint32_t by = adv ? step8 : 0u;
     tnext += adv ? kWaves : 0;
     sk = wrap(sk + by);
     sv = wrap(sv + by);
+  };
+  auto load8 = [&](Raw8<D>& r) {
+    ld8(r, k8, v8, sk, sv);
+    adv8();
   };
   auto row16 = [&](const uint16_t* ring, const uint16_t* nw, int jj) {  // FP16-local index jj
     if (jj >= f) return nw;  // the new token (also the clamp target of tail rows)
@@ -503,15 +524,26 @@ void attn_decode_kernel(AttnArgs a) {
   const u32x4* qsrc4 = reinterpret_cast<const u32x4*>(a.q + qoff);
   const u32x4* ks4 = reinterpret_cast<const u32x4*>(c.ks + hrow * D);
   const u32x4* vs4 = reinterpret_cast<const u32x4*>(c.vs + hrow * D);
-  u32x4 piece[2];
+  // the pieces of query block qs, K scales kss and V scales vss
+  auto load_pieces = [&](u32x4* pc, const u32x4* qs, const u32x4* kss, const u32x4* vss) {
 #pragma unroll
-  for (int z = 0; z < 2; ++z) {  // unconditional loads (spare threads re-read piece 0)
-    const int e = tid + z * kThreads;
-    const u32x4* src = e < qp             ? qsrc4 + e
-                       : e < qp + D / 4   ? ks4 + (e - qp)
-                       : e < npieces      ? vs4 + (e - qp - D / 4)
-                                          : qsrc4;
-    piece[z] = *src;
+    for (int z = 0; z < 2; ++z) {  // unconditional loads (spare threads re-read piece 0)
+      const int e = tid + z * kThreads;
+      const u32x4* src = e < qp             ? qs + e
+                         : e < qp + D / 4   ? kss + (e - qp)
+                         : e < npieces      ? vss + (e - qp - D / 4)
+                                            : qs;
+      pc[z] = *src;
+    }
+  };
+  // (uniform) this unit's first loads were issued by the previous unit
+  const bool pre = ACC && !next && nx_ok;
+  u32x4 piece[2];
+  if (pre) {
+    piece[0] = nx_piece[0];
+    piece[1] = nx_piece[1];
+  } else {
+    load_pieces(piece, qsrc4, ks4, vs4);
   }
   const bool has8 = nt8 > w;  // this wave has INT8 tiles (uniform per wave)
   // This wave's INT8 tiles are t_j = w + 4j, j < m8. Each is loaded exactly
@@ -520,8 +552,15 @@ void attn_decode_kernel(AttnArgs a) {
   // counter allows partial waits there.
   const int m8 = (nt8 - w + kWaves - 1) / kWaves;
   Raw8<D> ra8{}, rb8{}, rc8{};  // defined on every path (the unit loop carries no undefined values)
-  if (m8 >= 1) load8(ra8);
-  if (m8 >= 2) load8(rb8);
+  if (pre) {
+    ra8 = nx_a;
+    rb8 = nx_b;
+    if (m8 >= 1) adv8();
+    if (m8 >= 2) adv8();
+  } else {
+    if (m8 >= 1) load8(ra8);
+    if (m8 >= 2) load8(rb8);
+  }
 #pragma unroll
   for (int z = 0; z < 2; ++z) {
     const int e = tid + z * kThreads;
@@ -664,6 +703,31 @@ void attn_decode_kernel(AttnArgs a) {
     }
   }
 
+  if constexpr (ACC && next) {
+    {  // the next unit is kv head h + 1 of this (layer, sequence) (hkv is even)
+      const size_t hn = hrow + 1;
+      load_pieces(nx_piece, reinterpret_cast<const u32x4*>(a.q + qoff + (size_t)g * D),
+                  reinterpret_cast<const u32x4*>(c.ks + hn * D), reinterpret_cast<const u32x4*>(c.vs + hn * D));
+      // this wave's first two tiles in the next kv head's rings (the slots
+      // are ring slots whatever the tile count, so the loads need no test;
+      // the second is the first again when the wave has one tile)
+      const int8_t* k8n = k8 + (size_t)c.cap * D;
+      const int8_t* v8n = v8 + (size_t)c.cap * D;
+      // the first slots again, from an opaque thread index (nothing of
+      // the tile loops' state is held for this)
+      int t2 = threadIdx.x;
+      asm volatile("" : "+v"(t2));
+      const int l2 = t2 & 63, r2 = l2 & 15, g2 = l2 >> 4;
+      const int tn = min(w, last8);
+      const uint32_t s_k = (uint32_t)((base8 + 16 * tn + (kpair ? (r2 & 7) : r2)) % c.cap);
+      const uint32_t s_v = (uint32_t)((base8 + 16 * tn + 4 * g2) % c.cap);
+      const uint32_t by = tn + kWaves <= last8 ? step8 : 0u;
+      ld8(nx_a, k8n, v8n, s_k, s_v);
+      ld8(nx_b, k8n, v8n, wrap(s_k + by), wrap(s_v + by));
+      nx_ok = true;
+    }
+  }
+
   // -------------------------------------------------------------- merge
   __shared__ float wm[kWaves][16], wl[kWaves][16], Mh[16], iL[16];
   float lt = st.l + __shfl_xor(st.l, 16, 64);
@@ -771,11 +835,13 @@ void attn_decode_kernel(AttnArgs a) {
   if constexpr (ACC) {
     // written out once per unit rather than as a loop: a loop keeps values
     // live across its back edge and spills registers in the tile loops
-#pragma unroll
-    for (int k = 0; k < kAccUnits; ++k)
-      if (u_begin + k < u_end) unit_body(u_begin + k);
+    // a two-unit range starts at an even kv head (hkv is even, ranges
+    // start at even units), so both units share the (layer, sequence)
+    static_assert(kAccUnits == 2, "the units are written out below");
+    if (u_end - u_begin == 2) unit_body(u_begin, std::true_type{});  // uniform
+    unit_body(u_end - 1, std::false_type{});
   } else {
-    unit_body(u_begin);
+    unit_body(u_begin, std::false_type{});
   }
 }
 
@@ -866,7 +932,7 @@ hipError_t launch_d(const AttnArgs& a, int lds_bytes, hipStream_t s) {
     const int occ_acc = resident_per_cu(acc, acc_bytes);
     const int64_t slots = (int64_t)occ_acc * device_cus();
     const int64_t groups = (units + kAccUnits - 1) / kAccUnits;
-    if (occ_acc > 0 && slots > 0 && groups >= slots && units < ((int64_t)1 << 31) &&
+    if (occ_acc > 0 && slots > 0 && groups >= slots && units < ((int64_t)1 << 31) && a.c.hkv % 2 == 0 &&
         occ_acc >= resident_per_cu(plain, lds_bytes)) {
       // single-unit workgroups for the last CONFK_ACC_TAIL / 8 of a round
       const int64_t tail = std::min<int64_t>(units, slots * CONFK_ACC_TAIL / 8);
