@@ -281,7 +281,9 @@ __device__ __forceinline__ int unit_owner(uint32_t x, uint32_t P) {
 
 // SPILL: scores past the LDS budget go to global memory. Kept out of the
 // common instance because global stores in the tile loop make the load
-// counter unusable for partial waits (stores complete out of order).
+// counter unusable for partial waits (stores complete out of order); the
+// instance runs each unit whose scores fit the LDS budget in the form
+// without them.
 // MASS = false: no per-key mass (no score store; for callers that only need
 // the attention output, e.g. a full-cache baseline).
 // ACC (an even hkv): workgroup w runs the unit range of unit_owner (kv heads
@@ -352,10 +354,13 @@ void attn_decode_kernel(AttnArgs a) {
   bool nx_ok = false;
 
   // the work of one unit; ACC runs it for each unit of the range in turn.
-  // NEXT (a compile-time flag): the first of a workgroup's two units, which
-  // issues the second one's first loads at its end.
-  auto unit_body = [&](int u, auto NEXT) __attribute__((always_inline)) {
+  // Compile-time flags: NEXT, the first of a workgroup's two units, which
+  // issues the second one's first loads at its end; SPL, scores past the
+  // LDS budget go to the spill area (a unit whose scores fit runs the form
+  // without global stores in its tile loops).
+  auto unit_body = [&](int u, auto NEXT, auto SPL) __attribute__((always_inline)) {
   constexpr bool next = decltype(NEXT)::value;
+  constexpr bool spl = SPILL && decltype(SPL)::value;
   if (u != u_begin) {
     if (++h == H) {
       h = 0;
@@ -402,7 +407,7 @@ void attn_decode_kernel(AttnArgs a) {
   const size_t qoff = ((size_t)lb * c.hq + (size_t)h * g) * D;
   const uint16_t* kn = a.k_new + ((size_t)lb * H + h) * D;
   const uint16_t* vn = a.v_new + ((size_t)lb * H + h) * D;
-  float* spill = SPILL ? a.spill + (size_t)u * g * a.spill_stride : nullptr;
+  float* spill = spl ? a.spill + (size_t)u * g * a.spill_stride : nullptr;
 
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
@@ -429,7 +434,7 @@ void attn_decode_kernel(AttnArgs a) {
   auto store_scores = [&](int p0, float4_t s) {
     if (!MASS || !head_ok) return;
     const int p = p0 + 4 * kg;
-    if (!SPILL || p0 + 16 <= n_lds) {  // whole tiles stay in LDS (n_lds is not a multiple of 16)
+    if (!spl || p0 + 16 <= n_lds) {  // whole tiles stay in LDS (n_lds is not a multiple of 16)
       *reinterpret_cast<float4_t*>(sc + (size_t)r16 * n_lds + p) = s;
     } else {
       *reinterpret_cast<float4_t*>(spill + (size_t)r16 * a.spill_stride + p) = s;
@@ -752,7 +757,7 @@ void attn_decode_kernel(AttnArgs a) {
   // per-key mass (summed over this kv head's query heads, and with ACC
   // over this row's earlier kv heads)
   float* mout = a.mass + ((size_t)lb * H + mrow) * c.cap;
-  if constexpr (MASS && !SPILL) {
+  if constexpr (MASS && !spl) {
     // groups of 4 slots (both regions start 16-aligned; slots past a region
     // hold masked scores and are not written out); all heads' scores of a
     // group are fetched before the exponentials
@@ -838,10 +843,21 @@ void attn_decode_kernel(AttnArgs a) {
     // a two-unit range starts at an even kv head (hkv is even, ranges
     // start at even units), so both units share the (layer, sequence)
     static_assert(kAccUnits == 2, "the units are written out below");
-    if (u_end - u_begin == 2) unit_body(u_begin, std::true_type{});  // uniform
-    unit_body(u_end - 1, std::false_type{});
+    if (u_end - u_begin == 2) unit_body(u_begin, std::true_type{}, std::false_type{});  // uniform
+    unit_body(u_end - 1, std::false_type{}, std::false_type{});
+  } else if constexpr (SPILL) {
+    // the spill form only for a unit whose score slots (INT8 tiles, then
+    // FP16 tiles with the new token) pass the LDS budget: a capacity that
+    // needs the spill area says nothing of the current length
+    const int32_t* mt = c.meta + ((a.layer0 + l) * c.B + b) * CONFK_META_WORDS;
+    const int n0 = mt[CONFK_META_N], n80 = mt[CONFK_META_N8];
+    const int64_t slots = (int64_t)((n80 + 15) >> 4) * 16 + (int64_t)((n0 - n80 + 1 + 15) >> 4) * 16;
+    if (slots <= a.n_lds)  // uniform
+      unit_body(u_begin, std::false_type{}, std::false_type{});
+    else
+      unit_body(u_begin, std::false_type{}, std::true_type{});
   } else {
-    unit_body(u_begin, std::false_type{});
+    unit_body(u_begin, std::false_type{}, std::false_type{});
   }
 }
 
