@@ -7,7 +7,10 @@
 // online softmax keeps a running max and normaliser and is exact. The mass
 // feeds the EMA of the review's "前置知识"/"核心方法" sections.
 //
-// One workgroup (4 waves) per (layer, sequence, kv head). The g query heads
+// One workgroup (4 waves) per (layer, sequence, kv head), or, when the units
+// fill two or more rounds of resident workgroups, two consecutive kv heads of
+// one (layer, sequence) per workgroup (their mass summed in LDS) except in
+// the launch's last round, which runs one per workgroup. The g query heads
 // sharing the kv head form the N side of the matrix-core tiles, keys the M
 // side, so every K/V byte is read from HBM once per step:
 //   scores  S^T[16 keys x 16 heads] = K_tile[16 x d] . Q^T      (16x16x32 f16)
@@ -35,9 +38,12 @@
 // row (their scores are masked), so loads carry no branches.
 //
 // Mass: the log2-domain scores are kept in LDS (or, in a separate kernel
-// instance, partly in a global spill area for caches too long for the LDS
-// budget); once the waves' running maxima and normalisers are merged, each
-// key's mass sum_h 2^(s_h - M_h) / L_h is formed exactly.
+// instance chosen by the capacity, partly in a global spill area for a unit
+// whose scores exceed the LDS budget; its other units run the spill-free
+// form); once the waves' running maxima and normalisers are merged, each
+// key's mass sum_h 2^(s_h - M_h) / L_h is formed exactly. A two-unit
+// workgroup issues its second unit's first loads before its first unit's
+// merge, mass pass and output.
 #include <mutex>
 #include <type_traits>
 
