@@ -31,18 +31,30 @@ HBM_PEAK_GBS = 8000.0
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "attn_decode_qwen32b_b8_traffic.md")
 
 
+def code_sha256(path):
+    """SHA-256 of a source file's code: line comments, trailing blanks and
+    empty lines dropped, so that a change to the comments alone keeps it."""
+    import hashlib
+    import re
+    lines = []
+    for line in open(path, encoding="utf-8"):
+        line = re.sub(r"//.*", "", line).rstrip()
+        if line:
+            lines.append(line)
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()
+
+
 def counted_traffic(workload):
     """HBM bytes per attention launch from the committed counter summary, or
     None when the summary is missing, covers another workload, or the
-    attention source has changed since the counters were taken."""
-    import hashlib
+    attention code has changed since the counters were taken."""
     try:
         line = [l for l in open(TRAFFIC_SUMMARY) if l.startswith("traffic-json:")][-1]
         rec = json.loads(line.split(":", 1)[1])
-        src = open(os.path.join(ROOT, rec["source"]), "rb").read()
+        sha = code_sha256(os.path.join(ROOT, rec["source"]))
     except (OSError, IndexError, ValueError, KeyError):
         return None
-    if hashlib.sha256(src).hexdigest() != rec["source_sha256"] or rec.get("workload") != workload:
+    if sha != rec.get("source_code_sha256") or rec.get("workload") != workload:
         return None
     return int(rec["traffic_bytes_per_launch"])
 
