@@ -190,7 +190,7 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus N > 1 is not supported",
+        print(json.dumps({"error": "the library runs on one GPU; --gpus N > 1 is not supported",
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
 
