@@ -53,7 +53,7 @@ def test_step_bytes_full_cache_run_counts_kv_and_q_only():
 
 
 def test_bench_refuses_more_than_one_gpu():
-    """This build runs on one GPU: bench.py --gpus 2 exits with a message
+    """The library runs on one GPU: bench.py --gpus 2 exits with a message
     that says so, before touching a device."""
     import json
     import subprocess
