@@ -63,3 +63,20 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.returncode != 0
     msg = json.loads(r.stdout.strip().splitlines()[-1])
     assert "one GPU" in msg["error"] and msg["n_gpus"] == 2
+
+
+def test_traffic_summary_matches_the_attention_code(tmp_path):
+    """The counted traffic in bench.py's roofline line is tied to the attention
+    code by a hash that ignores line comments and blank lines: a comment edit
+    keeps it, a code edit voids it; the committed summary matches the
+    current code."""
+    b = _bench()
+    src = tmp_path / "k.hip"
+    src.write_text("// header\nint f(int x) {\n  return x + 1;  // one\n}\n\n")
+    h0 = b.code_sha256(str(src))
+    src.write_text("// another header\n\nint f(int x) {\n  return x + 1;   // changed note\n}\n")
+    assert b.code_sha256(str(src)) == h0
+    src.write_text("// header\nint f(int x) {\n  return x + 2;  // one\n}\n")
+    assert b.code_sha256(str(src)) != h0
+    assert b.counted_traffic("qwen32b") is not None
+    assert b.counted_traffic("qwen14b") is None
