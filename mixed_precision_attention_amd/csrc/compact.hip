@@ -34,7 +34,9 @@
 //     and may end with the window step of the quantisation.
 //  4. Token eviction in the stable order (kStable, the default) and block
 //     eviction (kBlock) pack both regions that way. A (layer, sequence)
-//     with nothing to move is finished here (append, window step); the
+//     with nothing to move is finished here (append, window step), and so
+//     is every pair of a launch over at most kPlanMovePairs pairs (its rows
+//     move in this workgroup, in rounds, as the move kernel moves them); the
 //     others are flagged for:
 // Move kernel (a fixed grid over the flagged (layer, sequence, kv head)
 // items): the planned rows of a head's rings move in rounds (read all rows
@@ -79,6 +81,7 @@ enum { H_MOV8 = 0, H_LEFT8, H_E8, H_JLO8, H_MOV16, H_LEFT16, H_E16, H_JLO16, H_B
        H_APPEND, H_Q, H_CAL, H_B8N, H_B16N, H_M8 };
 constexpr int kMoveThreads = 256;  // move kernel workgroup: one (layer, sequence, kv head) item at a time
 constexpr int kMoveGrid = 1024;    // move kernel workgroups at most (4 per compute unit)
+constexpr int kPlanMovePairs = 16; // launches over at most this many (layer, sequence) pairs move rows in the plan kernel
 
 // Order-preserving uint32 image of an fp32 score; NaN sorts above +inf
 // (0xFFFFFFFF stays free as the "not a candidate" key).
@@ -225,6 +228,65 @@ __device__ uint32_t radix_select(int& kk, int cnt, Part part, Val val, Shared& s
   return prefix;
 }
 
+// Stable packing of one ring kind (INT8, or FP16 with F16) of every kv head
+// of a (layer, sequence), in the plan workgroup (small launches, where a
+// second kernel's launch would cost more than the rounds here). lst holds
+// the movers' region-local old indices in move order; mover r goes to
+// region-local new index j = jlo + r (left) or jlo + mv - 1 - r, slot
+// base + j (+ e on the right side). A round reads kPlanMoveRound (mover,
+// head) rows of K and of V per thread, waits, and writes them; round r+1
+// reads only slots beyond round r's destinations in the packing direction
+// (per head), so a round needs one barrier. Thread t takes piece column
+// t % P of (mover, head) pairs t / P, t / P + cpp, ... in mover-major order;
+// loads and stores are unconditional (pairs past the last take the last
+// pair's piece and write it again: same bytes, same place).
+constexpr int kPlanMoveRound = 4;
+template <bool F16>
+__device__ __forceinline__ void move_ring(const CacheView& c, int lbc, int mv, int left, int e, int jlo, int base,
+                                          const int32_t* lst) {
+  typedef __attribute__((address_space(1))) u32x4 gvec;
+  constexpr int U = kPlanMoveRound;
+  if (mv == 0) return;  // uniform
+  const int H = c.hkv, d = c.d;
+  const int P = F16 ? d >> 3 : d >> 4;  // 16-byte pieces per row of one head
+  const uint32_t rowb = F16 ? 2u * (uint32_t)d : (uint32_t)d;
+  const int C = F16 ? c.cap16 : c.cap;
+  const uint32_t ring = (uint32_t)C * rowb;  // bytes per ring of one head
+  const size_t lbo = (size_t)lbc * H * ring;
+  gvec* kg = (gvec*)uniform_ptr((F16 ? reinterpret_cast<const unsigned char*>(c.k16)
+                                     : reinterpret_cast<const unsigned char*>(c.k8)) + lbo);
+  gvec* vg = (gvec*)uniform_ptr((F16 ? reinterpret_cast<const unsigned char*>(c.v16)
+                                     : reinterpret_cast<const unsigned char*>(c.v8)) + lbo);
+  const int cpp = kThreads / P;  // (mover, head) pairs per pass
+  const int q = threadIdx.x / P, pc = threadIdx.x - q * P;
+  const int npair = mv * H;
+  for (int c0 = 0; c0 < npair; c0 += U * cpp) {
+    u32x4 v[2 * U];
+    uint32_t dof[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int cu = min(c0 + q + u * cpp, npair - 1);
+      const int r = cu / H, h = cu - r * H;
+      int ss = base + lst[r];
+      ss = ss >= C ? ss - C : ss;
+      const uint32_t hb = (uint32_t)h * ring + (uint32_t)pc * 16u;
+      v[u] = kg[(hb + (uint32_t)ss * rowb) >> 4];
+      v[U + u] = vg[(hb + (uint32_t)ss * rowb) >> 4];
+      const int j = jlo + (left ? r : mv - 1 - r);
+      int ds = base + (left ? j : j + e);
+      ds = ds >= C ? ds - C : ds;
+      dof[u] = (hb + (uint32_t)ds * rowb) >> 4;
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // every source of the round has been read
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      kg[dof[u]] = v[u];
+      vg[dof[u]] = v[U + u];
+    }
+  }
+}
+
 // FUSE: the EMA update and rank scores of ema_rank_kernel run first, in this
 // kernel, with the same arithmetic and summation order (bit-identical).
 // REG: the form for a cache of at most kRegKeys * kThreads tokens with the
@@ -235,8 +297,9 @@ __device__ __forceinline__ void plan_body(const CompactArgs& a) {
   // MODE: kStable (token eviction, both regions packed stably), kBlock (block
   // eviction, packed stably) or kFill (token eviction, INT8 holes filled from
   // the INT8 tail). Stable packing leaves its row moves (and then the append
-  // and the window step) to the move kernel; the fill order moves its few
-  // rows here.
+  // and the window step) to the move kernel, except in launches over few
+  // (layer, sequence) pairs (a.plan_moves), which move them here as the fill
+  // order moves its few rows.
   constexpr bool BLOCK = MODE == kBlock;   // block selection
   constexpr bool MOVEK = MODE != kFill;    // rows moved by the move kernel
   const CacheView& c = a.c;
@@ -803,10 +866,18 @@ __device__ __forceinline__ void plan_body(const CompactArgs& a) {
     int slot = b16 + (f - r16.e);  // the new token's FP16 slot
     slot = slot >= c.cap16 ? slot - c.cap16 : slot;
     const int m8 = n8 - r8.e;
-    if (r8.movers + r16.movers == 0) {  // uniform
-      // nothing moves (the evicted tokens sat at the packing ends): append
-      // and window step here, the move kernel skips this (layer, sequence).
-      // The append slot is no FP16 source when no FP16 row moves.
+    if (a.plan_moves || r8.movers + r16.movers == 0) {  // uniform
+      // nothing moves (the evicted tokens sat at the packing ends), or a
+      // small launch moves its rows here: append and window step here, the
+      // move kernel skips this (layer, sequence). The append slot is no
+      // FP16 source when no FP16 row moves, and every FP16 source has been
+      // read (the last round's barrier) when one does.
+      if (r8.movers + r16.movers > 0) {  // uniform
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();  // the move lists in the workspace are complete
+        move_ring<false>(c, lbc, r8.movers, r8.left, r8.e, r8.jlo, base8, src8);
+        move_ring<true>(c, lbc, r16.movers, r16.left, r16.e, r16.jlo, base16, src16);
+      }
       append_rows(slot);
       if (threadIdx.x == 0) {
         a.jobs[lb] = 0;
@@ -815,8 +886,8 @@ __device__ __forceinline__ void plan_body(const CompactArgs& a) {
         meta[CONFK_META_BASE8] = b8;
         meta[CONFK_META_BASE16] = b16;
         meta[CONFK_META_EVICTED] = k;
-        meta[CONFK_META_MOVED] = 0;
-        meta[CONFK_META_MOVED16] = 0;
+        meta[CONFK_META_MOVED] = r8.movers;
+        meta[CONFK_META_MOVED16] = r16.movers;
         if (a.evicted_out) a.evicted_out[lb] = k;
       }
       if constexpr (FUSE) quantize_tail(nkeep, m8, b8, b16);
@@ -1393,9 +1464,13 @@ hipError_t launch_compact_t(const CompactArgs& a, hipStream_t s) {
   // stable packing (token eviction in the stable order, block eviction): the
   // plan kernel selects and plans, and finishes the (layer, sequence) pairs
   // with nothing to move; the move kernel does the rest, spread over kv heads
-  hipError_t e = a.block ? launch_plan<kBlock, FUSE>(a, s) : launch_plan<kStable, FUSE>(a, s);
-  if (e != hipSuccess) return e;
+  // a launch over few (layer, sequence) pairs moves its rows in the plan
+  // kernel: the move kernel's launch would cost more than the rounds there
+  CompactArgs b = a;
   const int npair = a.nl * a.c.B;
+  b.plan_moves = npair <= kPlanMovePairs;
+  hipError_t e = b.block ? launch_plan<kBlock, FUSE>(b, s) : launch_plan<kStable, FUSE>(b, s);
+  if (e != hipSuccess || b.plan_moves) return e;
   const dim3 mgrid(min(npair * a.c.hkv, kMoveGrid)), mblock(kMoveThreads);
   const size_t lds = (size_t)npair * sizeof(int);
   if (FUSE && a.quantize)

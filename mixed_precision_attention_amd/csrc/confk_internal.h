@@ -114,6 +114,9 @@ struct CompactArgs {
   // states (written by the attention launch) and takes its budget from them
   ConfArgs conf;
   int32_t conf_merge;
+  // stable packing of a small launch (set by the launcher): the plan kernel
+  // moves the rows itself and no move kernel follows
+  int32_t plan_moves;
 };
 
 struct QuantArgs {
