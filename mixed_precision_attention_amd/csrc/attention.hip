@@ -802,16 +802,41 @@ void attn_decode_kernel(AttnArgs a) {
       }
     }
   } else if constexpr (MASS) {
-    for (int i = tid; i < nk; i += kThreads) {
-      const int p = i < n8 ? i : p16 + (i - n8);
-      const float u = i < n8 ? usc[0] : usc[1];
-      float sum = 0.f;
-      for (int hh = 0; hh < g; ++hh) {
-        const float s = (p | 15) < n_lds ? sc[(size_t)hh * n_lds + p] : spill[(size_t)hh * a.spill_stride + p];
-        sum += exp2f(fmaf(s, u, -Mh[hh])) * iL[hh];
+    // the same groups of 4 slots. A 16-slot tile's scores are all in LDS or
+    // all in the spill area, and slots grow with the group index, so the
+    // groups in LDS come first: [0, gs) (the spill area is written and read
+    // by this workgroup only)
+    const int q8 = (n8 + 3) >> 2, q16 = (f + 1 + 3) >> 2;
+    const int t_lds = n_lds >> 4;  // tiles wholly in LDS
+    const int a8 = min(q8, 4 * t_lds);
+    const int gs = a8 < q8 ? a8 : q8 + min(q16, max(0, 4 * t_lds - (p16 >> 2)));
+    auto group = [&](int gi, const float* src, size_t stride) __attribute__((always_inline)) {
+      const bool r8 = gi < q8;
+      const int slot = r8 ? 4 * gi : p16 + 4 * (gi - q8);
+      const int i0 = r8 ? 4 * gi : n8 + 4 * (gi - q8);
+      const int lim = r8 ? n8 : nk;
+      const float u = usc[r8 ? 0 : 1];
+      float4_t sum = {0.f, 0.f, 0.f, 0.f};
+      for (int h0 = 0; h0 < g; h0 += 4) {
+        float4_t sv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (h0 + j < g) sv[j] = *reinterpret_cast<const float4_t*>(src + (size_t)(h0 + j) * stride + slot);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (h0 + j < g) {
+            const float m = Mh[h0 + j], il = iL[h0 + j];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) sum[v] += __builtin_amdgcn_exp2f(fmaf(sv[j][v], u, -m)) * il;
+          }
+        }
       }
-      mout[i] = sum;
-    }
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        if (i0 + v < lim) mout[i0 + v] = sum[v];
+    };
+    for (int gi = tid; gi < gs; gi += kThreads) group(gi, sc, (size_t)n_lds);
+    for (int gi = gs + tid; gi < q8 + q16; gi += kThreads) group(gi, spill, (size_t)a.spill_stride);
   }
   __syncthreads();
 
