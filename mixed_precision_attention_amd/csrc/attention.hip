@@ -358,6 +358,16 @@ void attn_decode_kernel(AttnArgs a) {
   u32x4 nx_piece[2];
   Raw8<D> nx_a, nx_b;  // set before any read (no initial value: no copies where they are set)
   bool nx_ok = false;
+  // The second unit of a range also takes the first one's cache header (the
+  // same (layer, sequence)), and the first unit's output waits in registers
+  // until the second unit's tile loops are done: a store still in flight
+  // would turn the second unit's first wait for its early loads into a wait
+  // for every memory operation (loads and stores share one counter and
+  // complete out of order with respect to each other).
+  int hd_n, hd_n8, hd_b8, hd_b16;
+  uint32_t oh[2];
+  bool oh_ok = false;
+  const int h_first = h;  // kv head of the range's first unit
 
   // the work of one unit; ACC runs it for each unit of the range in turn.
   // Compile-time flags: NEXT, the first of a workgroup's two units, which
@@ -389,18 +399,30 @@ void attn_decode_kernel(AttnArgs a) {
   const bool acc_last = !ACC || h == H - 1 || u == u_end - 1;  // last: write the row
 
   int32_t* meta = c.meta + lbc * CONFK_META_WORDS;
-  const int n = meta[CONFK_META_N];
-  const int n8 = meta[CONFK_META_N8];
-  const int base8 = meta[CONFK_META_BASE8];
-  const int base16 = meta[CONFK_META_BASE16];
+  int n, n8, base8, base16;
+  if (ACC && !next && nx_ok) {  // uniform
+    n = hd_n;
+    n8 = hd_n8;
+    base8 = hd_b8;
+    base16 = hd_b16;
+  } else {
+    n = meta[CONFK_META_N];
+    n8 = meta[CONFK_META_N8];
+    base8 = meta[CONFK_META_BASE8];
+    base16 = meta[CONFK_META_BASE16];
+  }
+  if constexpr (ACC && next) {
+    hd_n = n;
+    hd_n8 = n8;
+    hd_b8 = base8;
+    hd_b16 = base16;
+  }
   const int f = n - n8;
   const int nk = n + 1;
   if (!meta_ok(n, n8, base8, base16, c.cap, c.cap16)) {  // uniform per workgroup
     if (tid == 0) atomicOr(c.status, (uint32_t)CONFK_STATUS_CAPACITY);
     return;
   }
-  if (MASS && h == 0 && tid == 0)
-    meta[CONFK_META_MASSROWS] = ACC ? unit_owner((uint32_t)(lb * H + H - 1), P) - wg + 1 : H;
   const int nt8 = (n8 + 15) >> 4;
   const int nt16 = (f + 1 + 15) >> 4;
   const int p16 = nt8 * 16;  // first score slot of the FP16 region
@@ -739,6 +761,17 @@ void attn_decode_kernel(AttnArgs a) {
     }
   }
 
+  if constexpr (ACC && !next) {
+    if (oh_ok) {  // uniform: the previous unit's output (the query block before this one's)
+      uint16_t* op = a.out + qoff - (size_t)g * D;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int idx = tid + k * kThreads;
+        if (idx < g * D) op[idx] = (uint16_t)(oh[k >> 1] >> (16 * (k & 1)));
+      }
+    }
+  }
+
   // -------------------------------------------------------------- merge
   __shared__ float wm[kWaves][16], wl[kWaves][16], Mh[16], iL[16];
   float lt = st.l + __shfl_xor(st.l, 16, 64);
@@ -858,14 +891,29 @@ void attn_decode_kernel(AttnArgs a) {
   }
   __syncthreads();
   uint16_t* ob = a.out + qoff;
-  for (int idx = tid; idx < g * D; idx += kThreads) {
+  auto out_at = [&](int idx) {
     const int hh = idx / D, ch = idx - hh * D;
     const int off = hh * RR + (ch / (D / 4)) * RB + ch % (D / 4);
     float o = 0.f;
 #pragma unroll
     for (int q = 0; q < kWaves; ++q) o += red[(size_t)q * g * RR + off];
-    ob[idx] = float_to_half_bits(o);
+    return float_to_half_bits(o);
+  };
+  if (ACC && next && g * D <= 4 * kThreads) {  // uniform: held until the next unit's tile loops are done
+    oh[0] = oh[1] = 0u;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int idx = tid + k * kThreads;
+      if (idx < g * D) oh[k >> 1] |= (uint32_t)out_at(idx) << (16 * (k & 1));
+    }
+    oh_ok = true;
+  } else {
+    for (int idx = tid; idx < g * D; idx += kThreads) ob[idx] = out_at(idx);
   }
+  // the row count of the range's (layer, sequence), once its first kv head
+  // is done (written last: no store in flight at the next unit's start)
+  if (MASS && tid == 0 && u == u_end - 1 && h_first == 0)
+    meta[CONFK_META_MASSROWS] = ACC ? unit_owner((uint32_t)(lb * H + H - 1), P) - wg + 1 : H;
   if constexpr (ACC) __syncthreads();  // the next unit reuses the LDS
   };
   if constexpr (ACC) {
