@@ -767,6 +767,55 @@ def test_two_kv_heads_per_workgroup_mass_rows():
           f"for R = {H // 2}..{H}")
 
 
+def test_two_kv_heads_per_workgroup_wide_groups():
+    """Sixteen query heads per kv head (d = 128): a unit's output (2048
+    halves) is too large to be held in registers until the second unit's tile
+    loops are done, so the first unit of a two-head workgroup stores it
+    directly. 24 layers x batch 8 x 8 kv heads fill two rounds of resident
+    workgroups, so the launch runs two kv heads per workgroup; its output
+    equals the one-layer launches' (one kv head per workgroup) bit for bit,
+    and its mass rows are sums of runs of one or two kv heads' rows."""
+    import mixed_precision_attention_amd as M
+    dev = _dev()
+    cfg = _cfg("g16_pairs", 24, 8, 128, 8, 128, 1000, 300, 96, 200, 16, 64)
+    H = cfg.hkv
+    eng = M.DecodeEngine(cfg, dev)
+    kp, vp = synth.gen.prefill_kv_device(cfg, 3, dev)
+    eng.prefill(kp, vp)
+    del kp, vp
+    for s in range(2):
+        lg = synth.gen.logits_device(cfg, 3, s, dev)
+        q, kn, vn = synth.gen.decode_inputs_device(cfg, 3, s, dev)
+        eng.step(lg, q, kn, vn, cfg.prefill + s)
+    q, kn, vn = synth.gen.decode_inputs_device(cfg, 3, 2, dev)
+    print(f"[parity] g16 pairs: {cfg.layers * cfg.batch * H} units", flush=True)
+    M.engine.attn_decode(eng.cache, q, kn, vn, eng.out, eng.mass, eng.attn_ws)
+    torch.cuda.synchronize()
+    rows = eng.cache.mass_rows()
+    assert rows.min() >= H // 2 and (rows < H).any(), "the launch runs two kv heads per workgroup"
+    out_all, mass_all = eng.out.clone(), eng.mass.clone()
+    n = eng.cache.lengths()[0]
+    for l in (0, 11, cfg.layers - 1):
+        M.engine.attn_decode(eng.cache, q[l:], kn[l:], vn[l:], eng.out[l:], eng.mass[l:], eng.attn_ws,
+                             layer0=l, nlayers=1)
+        torch.cuda.synchronize()
+        assert torch.equal(out_all[l], eng.out[l]), f"l={l}: output"
+        for b in range(cfg.batch):
+            k = int(n[l, b]) + 1
+            per_head = eng.mass[l, b, :, :k].double().cpu().numpy()
+            summed = mass_all[l, b, :int(rows[l, b]), :k].double().cpu().numpy()
+            tol = 1e-6 * max(1.0, np.abs(per_head).sum(axis=0).max())
+            j = 0
+            for r in range(summed.shape[0]):
+                for m in (1, 2):
+                    if j + m <= H and np.abs(summed[r] - per_head[j:j + m].sum(axis=0)).max() <= tol:
+                        j += m
+                        break
+                else:
+                    raise AssertionError(f"l={l} b={b}: row {r} is no run of 1 or 2 kv heads from {j}")
+            assert j == H, f"l={l} b={b}: rows cover {j} of {H} kv heads"
+
+
 @pytest.mark.parametrize("choice", ["none", "greedy", "sample"])
 def test_fused_confidence_attention_matches_split(choice):
     """confk_confidence_attn_decode (the confidence merge inside the attention
