@@ -61,12 +61,27 @@ def counted_traffic(workload):
 
 def attn_kernel_name(cfg, eng, full):
     """Instance of the attention kernel the timed launches ran: spill store
-    (a workspace was needed), per-key mass (not in the full-cache run), and
-    the two-kv-heads-per-workgroup mass sum (fewer mass rows than kv heads)."""
-    spill = eng.attn_ws is not None and not full
+    (the workspace has a spill area), per-key mass (not in the full-cache
+    run), the two-kv-heads-per-workgroup mass sum (fewer mass rows than kv
+    heads), and split keys (the workspace holds the exchange area, the
+    launch has at most 64 units and fills at most 1/32 of the GPU's resident
+    workgroup slots, three per compute unit at this kernel's register count,
+    and its capacity allows units of at least three 32-tile pieces)."""
+    import torch
+
+    import mixed_precision_attention_amd as M
+    spill = not full and M.engine.workspace_bytes(M._lib.WS_ATTENTION_NOSPLIT, eng.cache, nlayers=cfg.layers) > 0
     acc = not full and bool((eng.cache.mass_rows() < cfg.hkv).any())
+    units = cfg.layers * cfg.batch * cfg.hkv
+    slots = 3 * torch.cuda.get_device_properties(0).multi_processor_count
+    xchg = eng.attn_ws is not None and M.engine.workspace_bytes(
+        M._lib.WS_ATTENTION, eng.cache, nlayers=cfg.layers) > M.engine.workspace_bytes(
+        M._lib.WS_ATTENTION_NOSPLIT, eng.cache, nlayers=cfg.layers)
+    wmax = (eng.cache.cap + 15) // 16 + 2 * ((eng.cache.cap16 + 15) // 16)  # INT8-tile weight bound of a unit
+    split = not full and xchg and units <= 64 and 32 * units <= slots and wmax >= 96
     b = lambda x: "true" if x else "false"  # noqa: E731
-    return f"attn_decode_kernel<{cfg.d}, {b(spill)}, {b(not full)}, {b(acc)}>"
+    name = f"attn_decode_kernel<{cfg.d}, {b(spill)}, {b(not full)}, {b(acc)}"
+    return name + (", true>" if split else ">")
 
 
 def parse():

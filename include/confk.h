@@ -61,6 +61,8 @@ extern "C" {
 /* ---- device status bits (cache->status[0] / status argument) ---------- */
 #define CONFK_STATUS_NONFINITE_LOGITS 1u /* NaN, +inf, all -inf logits      */
 #define CONFK_STATUS_CAPACITY 2u         /* a (layer, seq) ran out of slots */
+#define CONFK_STATUS_SPLIT_WAIT 4u       /* a split-key attention workgroup gave up
+                                            waiting for another split's values */
 
 /* ---- per-(layer, sequence) header words (cache->meta) ------------------ */
 #define CONFK_META_N 0       /* tokens retained                                 */
@@ -84,6 +86,7 @@ extern "C" {
 #define CONFK_WS_CONFIDENCE 0
 #define CONFK_WS_ATTENTION 1
 #define CONFK_WS_COMPACT 2
+#define CONFK_WS_ATTENTION_NOSPLIT 3 /* the score spill part alone */
 
 /*
  * Policy (hyper-parameters of the review's "复现评估" section and the
@@ -213,8 +216,23 @@ int confk_confidence(const float* logits, int64_t ld, int32_t batch, int32_t voc
  *                 of kv heads first, then single heads). NULL
  *                 when the caller needs only the output (no workspace then;
  *                 the meta word is not touched)
- *   ws            >= confk_workspace_size(CONFK_WS_ATTENTION, ...) bytes
- *                 (score spill for caches too long for on-chip memory)
+ *   ws            >= confk_workspace_size(CONFK_WS_ATTENTION_NOSPLIT, ...)
+ *                 bytes (score spill for caches too long for on-chip
+ *                 memory); with confk_workspace_size(CONFK_WS_ATTENTION,
+ *                 ...) bytes it also holds the split exchange area (below).
+ *                 The exchange area must be zero before its first use (the
+ *                 library keeps it consistent from then on); the spill part
+ *                 needs no initialisation
+ * Split keys: a launch of few units (at most 64 and at most 1/32 of the
+ * GPU's resident workgroup slots; e.g. one layer at batch 1), given the
+ * exchange area and a capacity that allows long units, runs each unit of
+ * more than 512 keys as several workgroups, each over one range of its
+ * keys (blockwise online softmax, review "前置知识"): they exchange each
+ * query head's running max and normaliser and their output partials through
+ * the exchange area with device-scope atomics, so the output and the
+ * per-key mass are those of the whole unit (up to rounding). A workgroup
+ * that waits too long for another's values sets CONFK_STATUS_SPLIT_WAIT and
+ * goes on. Two launches that share a workspace must not overlap in time.
  * Layers layer0 .. layer0+nlayers-1 of the cache are processed; tensor
  * arguments are indexed from layer0. Supported: d in {64, 128},
  * hq/hkv in 1..16.
@@ -404,7 +422,9 @@ int confk_quantize(const confk_cache* cache, int32_t layer0, int32_t nlayers, in
 /* Workspace bytes needed by confk_confidence (which = CONFK_WS_CONFIDENCE;
  * uses batch, vocab), confk_attn_decode (CONFK_WS_ATTENTION) or confk_compact
  * (CONFK_WS_COMPACT; both use the cache dims and nlayers). Returns 0 when
- * none is needed. */
+ * none is needed. CONFK_WS_ATTENTION_NOSPLIT gives the part of the attention
+ * workspace without the split exchange area: a workspace of that size (or
+ * none, when it is 0) makes every launch run one workgroup per unit. */
 size_t confk_workspace_size(int32_t which, const confk_cache* cache, int32_t nlayers,
                             int32_t batch, int32_t vocab);
 
@@ -415,7 +435,9 @@ const char* confk_strerror(int code);
  * argument of confk_ema_compact. 102: the stable survivor order is order 0
  * (the default) and the hole-filling order is 1. 103: confk_ema_compact_static.
  * 104: mass rows are partial sums over runs of kv heads (CONFK_META_MASSROWS).
- * 105: confk_confidence_attn_decode. 106: confk_decode_step. */
+ * 105: confk_confidence_attn_decode. 106: confk_decode_step. 107: split keys
+ * (the attention workspace's exchange area, CONFK_WS_ATTENTION_NOSPLIT,
+ * CONFK_STATUS_SPLIT_WAIT). */
 int confk_version(void);
 
 #ifdef __cplusplus

@@ -21,6 +21,7 @@ ERR_LAUNCH = -5
 
 STATUS_NONFINITE_LOGITS = 1
 STATUS_CAPACITY = 2
+STATUS_SPLIT_WAIT = 4
 
 (META_N, META_N8, META_BASE8, META_BASE16, META_CALIB, META_SAT, META_EVICTED, META_MOVED,
  META_MOVED16, META_MASSROWS) = range(10)
@@ -35,6 +36,7 @@ ORDER_FILL = 1
 WS_CONFIDENCE = 0
 WS_ATTENTION = 1
 WS_COMPACT = 2
+WS_ATTENTION_NOSPLIT = 3
 
 EXPORTS = [
     "confk_confidence", "confk_attn_decode", "confk_ema_rank", "confk_compact",

@@ -37,7 +37,7 @@ int launch_status(hipError_t e) { return e == hipSuccess ? CONFK_OK : CONFK_ERR_
 
 extern "C" {
 
-int confk_version(void) { return 106; }
+int confk_version(void) { return 107; }
 
 const char* confk_strerror(int code) {
   switch (code) {
@@ -51,6 +51,13 @@ const char* confk_strerror(int code) {
   }
 }
 
+namespace {
+// Byte offset of the split exchange area in the attention workspace: after
+// the score spill area, 256-byte aligned.
+size_t xchg_offset(size_t spill) { return (spill + 255) / 256 * 256; }
+
+}  // namespace
+
 size_t confk_workspace_size(int32_t which, const confk_cache* cache, int32_t nlayers, int32_t batch,
                             int32_t vocab) {
   if (which == CONFK_WS_CONFIDENCE) {
@@ -61,12 +68,15 @@ size_t confk_workspace_size(int32_t which, const confk_cache* cache, int32_t nla
     if (!cache || nlayers < 1 || cache->cap < 2) return 0;
     return compact_ws_bytes(nlayers, cache->batch, cache->cap);
   }
-  if (which == CONFK_WS_ATTENTION) {
+  if (which == CONFK_WS_ATTENTION || which == CONFK_WS_ATTENTION_NOSPLIT) {
     if (!cache || nlayers < 1 || cache->hkv < 1 || cache->hq % cache->hkv) return 0;
     const int g = cache->hq / cache->hkv;
     int stride = 0;
     attention_plan_n_lds(cache->d, g, cache->cap, &stride);
-    return (size_t)nlayers * cache->batch * cache->hkv * g * (size_t)stride * sizeof(float);
+    const int64_t units = (int64_t)nlayers * cache->batch * cache->hkv;
+    const size_t spill = (size_t)units * g * (size_t)stride * sizeof(float);
+    const size_t xchg = which == CONFK_WS_ATTENTION ? attention_xchg_bytes(units, g, cache->d) : 0;
+    return xchg ? xchg_offset(spill) + xchg : spill;
   }
   return 0;
 }
@@ -140,6 +150,11 @@ int attn_args(const confk_cache* cache, int32_t layer0, int32_t nlayers, const u
   a.out = out;
   a.mass = mass;
   a.spill = need ? (float*)ws : nullptr;
+  // the split exchange area, when the workspace holds it (otherwise the
+  // launch does not split keys)
+  const size_t xchg = mass ? attention_xchg_bytes((int64_t)nlayers * cache->batch * cache->hkv, g, cache->d) : 0;
+  if (xchg && ws && ((uintptr_t)ws & 7) == 0 && ws_bytes >= xchg_offset(need) + xchg)
+    a.xchg = reinterpret_cast<uint64_t*>(static_cast<unsigned char*>(ws) + xchg_offset(need));
   *res = a;
   *lds_bytes = attention_lds_bytes(cache->d, g, n_lds);
   return CONFK_OK;

@@ -285,6 +285,54 @@ __device__ __forceinline__ int unit_owner(uint32_t x, uint32_t P) {
   return (int)(x < 2 * P ? x >> 1 : x - P);
 }
 
+// Split keys: the INT8 tiles [t8a, t8b) of one of ns workgroups sharing a
+// unit, the last of which also takes the FP16 region with the new token.
+// The unit weighs nt8 + 2 nt16 INT8 tiles (an FP16 tile reads twice the
+// bytes) and is cut into ns = floor(weight / wtile) pieces of equal weight
+// (at least one, at most S), so a piece weighs at least wtile tiles; fewer
+// when a piece but the last would start past the INT8 region, so every
+// piece holds keys.
+struct SplitRange {
+  int ns, t8a, t8b;
+  bool fp;
+};
+__device__ __forceinline__ SplitRange split_range(int n, int n8, int S, int wtile, int sj) {
+  const int nt8 = (n8 + 15) >> 4, nt16 = (n - n8 + 1 + 15) >> 4;
+  const int wt = nt8 + 2 * nt16;
+  int ns = min(S, wt / wtile);
+  while (ns > 1 && (int)((int64_t)(ns - 2) * wt / ns) >= nt8) --ns;
+  ns = max(ns, 1);
+  SplitRange r;
+  r.ns = ns;
+  r.t8a = min(nt8, (int)((int64_t)sj * wt / ns));
+  r.t8b = sj >= ns - 1 ? nt8 : min(nt8, (int)((int64_t)(sj + 1) * wt / ns));
+  r.fp = sj == ns - 1;
+  return r;
+}
+
+// Split-key exchange words are (fp32 bits << 32 | tag) with tag = 2 e + 1
+// for the unit's epoch word e: a word written in an earlier launch (or a
+// zeroed one) never carries the current tag, so a reader waits until the
+// writer of this launch has stored it. Relaxed device-scope atomics keep
+// each word coherent across the chip's L2 caches without fences.
+constexpr int kSpinMax = 1 << 14;  // waits give up (and flag the status word) after this many polls
+__device__ __forceinline__ void xput(uint64_t* p, float v, uint32_t tag) {
+  __hip_atomic_store(p, ((uint64_t)__builtin_bit_cast(uint32_t, v) << 32) | tag, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float xget(const uint64_t* p, uint32_t tag, uint32_t* status) {
+  uint64_t v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int it = 0; (uint32_t)v != tag && it < kSpinMax; ++it) {
+    __builtin_amdgcn_s_sleep(1);
+    v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if ((uint32_t)v != tag) {
+    atomicOr(status, (uint32_t)CONFK_STATUS_SPLIT_WAIT);
+    return 0.f;
+  }
+  return __builtin_bit_cast(float, (uint32_t)(v >> 32));
+}
+
 // SPILL: scores past the LDS budget go to global memory. Kept out of the
 // common instance because global stores in the tile loop make the load
 // counter unusable for partial waits (stores complete out of order); the
@@ -298,13 +346,22 @@ __device__ __forceinline__ int unit_owner(uint32_t x, uint32_t P) {
 // partial mass row per (layer, sequence) it touches instead of one per kv
 // head. Row r of a (layer, sequence) is the r-th workgroup that covers it;
 // the row count goes to its metadata.
-template <int D, bool SPILL, bool MASS, bool ACC>
+// SPLIT (launches that fill few of the resident workgroup slots): a.split
+// consecutive workgroups per unit, each taking a range of the unit's keys
+// (split_range). They run the tile loops on their keys, publish each
+// head's running max and normaliser, take the unit's merged values from
+// every split's, write the mass of their own keys and (the later ones)
+// publish their output partial, which the first sums in split order. The
+// per-key mass stays exact without any score leaving the workgroup.
+template <int D, bool SPILL, bool MASS, bool ACC, bool SPLIT = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(CONFK_ATTN_OCCUPANCY)))
 void attn_decode_kernel(AttnArgs a) {
   constexpr int KC = Tile<D>::KC;
   constexpr int CB = Tile<D>::CB;
   constexpr int KU = Tile<D>::KU;
   static_assert(!ACC || (MASS && !SPILL), "mass rows are summed in LDS only with the LDS score store");
+  static_assert(!SPLIT || (MASS && !ACC), "split keys: one unit per workgroup group, with the mass");
+  static_assert(kMaxSplit * 16 <= kThreads, "one thread per (split, head) pair of the exchange");
   extern __shared__ float lds[];
 
   // Fused confidence call: the launch's first conf_groups workgroups merge
@@ -338,8 +395,11 @@ void attn_decode_kernel(AttnArgs a) {
   const int g = a.g;
   const uint32_t P = (uint32_t)a.acc_pairs;
   const int wg = blockIdx.x - a.conf_groups;
-  const int u_begin = ACC ? ((uint32_t)wg < P ? 2 * wg : (int)P + wg) : wg;
-  const int u_end = ACC ? ((uint32_t)wg < P ? 2 * wg + 2 : (int)P + wg + 1) : wg + 1;
+  // SPLIT: a.split consecutive workgroups per unit, split sj of it
+  const int u_split = SPLIT ? wg / a.split : 0;
+  const int sj = SPLIT ? wg - u_split * a.split : 0;
+  const int u_begin = ACC ? ((uint32_t)wg < P ? 2 * wg : (int)P + wg) : SPLIT ? u_split : wg;
+  const int u_end = ACC ? ((uint32_t)wg < P ? 2 * wg + 2 : (int)P + wg + 1) : u_begin + 1;
   // (layer, sequence, kv head) of the current unit, advanced without
   // divisions; a (layer, sequence) that starts inside this range has its
   // first unit here, so this workgroup writes its row 0
@@ -425,7 +485,25 @@ void attn_decode_kernel(AttnArgs a) {
   }
   const int nt8 = (n8 + 15) >> 4;
   const int nt16 = (f + 1 + 15) >> 4;
-  const int p16 = nt8 * 16;  // first score slot of the FP16 region
+  // SPLIT: this workgroup's INT8 tiles [t8a, t8b), and the FP16 region if
+  // it is the unit's last split (fp); score slot 0 is key so8. Otherwise
+  // the whole unit.
+  int t8a = 0, t8b = nt8, ns = 1;
+  bool fp = true;
+  if constexpr (SPLIT) {
+    const SplitRange sr = split_range(n, n8, a.split, a.split_tiles, sj);
+    if (sj >= sr.ns) return;  // uniform: the unit needs fewer workgroups
+    ns = sr.ns;
+    t8a = sr.t8a;
+    t8b = sr.t8b;
+    fp = sr.fp;
+  }
+  const int so8 = 16 * t8a;
+  const int p16 = (t8b - t8a) * 16;  // first score slot of the FP16 region
+  // split exchange: the unit's words and this launch's tag
+  uint64_t* xw = SPLIT ? a.xchg + (size_t)u * split_words(g, D) : nullptr;
+  uint32_t xtag = 0;
+  if (SPLIT && ns > 1) xtag = 2u * (uint32_t)__hip_atomic_load(xw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
 
   const size_t hrow = (size_t)lbc * H + h;
   const int8_t* k8 = c.k8 + hrow * c.cap * D;
@@ -435,7 +513,7 @@ void attn_decode_kernel(AttnArgs a) {
   const size_t qoff = ((size_t)lb * c.hq + (size_t)h * g) * D;
   const uint16_t* kn = a.k_new + ((size_t)lb * H + h) * D;
   const uint16_t* vn = a.v_new + ((size_t)lb * H + h) * D;
-  float* spill = spl ? a.spill + (size_t)u * g * a.spill_stride : nullptr;
+  float* spill = spl ? a.spill + (size_t)u * g * a.spill_stride + so8 : nullptr;
 
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
@@ -474,14 +552,14 @@ void attn_decode_kernel(AttnArgs a) {
   // row in the next tile this wave loads (tiles w, w+kWaves, ... in order;
   // the slot stops advancing at the wave's last tile). 32-bit byte offsets
   // from the uniform ring base.
-  const int last8 = max(nt8 - 1, 0);
+  const int last8 = max(t8b - 1, t8a);
   const uint32_t cap = (uint32_t)c.cap;
   auto wrap = [&](uint32_t x) { return min(x, x - cap); };  // x < 2 cap
   const uint32_t step8 = (uint32_t)(16 * kWaves) % cap;
   uint32_t vinc[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) vinc[j] = (uint32_t)j % cap;
-  int tnext = min(w, last8);  // tile of the next load (uniform)
+  int tnext = min(t8a + w, last8);  // tile of the next load (uniform)
   // 128-byte INT8 K rows are read in lane pairs (see unpair): each
   // instruction covers whole rows.
   constexpr bool kpair = KU == 2;
@@ -578,12 +656,12 @@ void attn_decode_kernel(AttnArgs a) {
   } else {
     load_pieces(piece, qsrc4, ks4, vs4);
   }
-  const bool has8 = nt8 > w;  // this wave has INT8 tiles (uniform per wave)
+  const bool has8 = t8b - t8a > w;  // this wave has INT8 tiles (uniform per wave)
   // This wave's INT8 tiles are t_j = w + 4j, j < m8. Each is loaded exactly
   // once: the loops below are peeled so that no load reaches past the last
   // tile, and the loads inside a loop body are unconditional, so the load
   // counter allows partial waits there.
-  const int m8 = (nt8 - w + kWaves - 1) / kWaves;
+  const int m8 = (t8b - t8a - w + kWaves - 1) / kWaves;
   Raw8<D> ra8{}, rb8{}, rc8{};  // defined on every path (the unit loop carries no undefined values)
   if (pre) {
     ra8 = nx_a;
@@ -638,7 +716,7 @@ void attn_decode_kernel(AttnArgs a) {
         for (int v = 0; v < 4; ++v)
           if (head_ok && i0 + 4 * kg + v >= n8) s[v] = -INFINITY;
       }
-      store_scores(i0, s);
+      store_scores(i0 - so8, s);
       const half4_t pT = softmax_tile<CB>(s, unscale, st, acc);
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
@@ -654,7 +732,7 @@ void attn_decode_kernel(AttnArgs a) {
     // tiles j+2..j+4 exist; the last 0-4 tiles follow it.
     int j = 0;
     for (; j + 5 <= m8; j += 3) {
-      const int t = w + kWaves * j;
+      const int t = t8a + w + kWaves * j;
       load8(rc8);
       tile8(ra8, t);
       load8(ra8);
@@ -662,7 +740,7 @@ void attn_decode_kernel(AttnArgs a) {
       load8(rb8);
       tile8(rc8, t + 2 * kWaves);
     }
-    const int rest = m8 - j, t = w + kWaves * j;
+    const int rest = m8 - j, t = t8a + w + kWaves * j;
     if (rest >= 3) {
       load8(rc8);
       tile8(ra8, t);
@@ -677,7 +755,7 @@ void attn_decode_kernel(AttnArgs a) {
   }
 
   // ------------------------------------------------------ FP16 region + new
-  const bool has16 = nt16 > w;
+  const bool has16 = fp && nt16 > w;
   Raw16<D> ra{}, rb{};
   if (has16) load16(ra, w);
   if (has8) {
@@ -788,8 +866,43 @@ void attn_decode_kernel(AttnArgs a) {
     float L = 0.f;
     for (int q = 0; q < kWaves; ++q)
       if (wl[q][hh] > 0.f) L += wl[q][hh] * exp2f(wm[q][hh] - M);
+    if (SPLIT && ns > 1) {  // publish this split's pair (uniform)
+      uint64_t* xs = xw + 2;  // [kMaxSplit][16 heads][max, normaliser]
+      xput(xs + sj * 32 + 2 * hh, M, xtag);
+      xput(xs + sj * 32 + 2 * hh + 1, L, xtag);
+    }
     Mh[hh] = M;
     iL[hh] = 1.f / L;
+  }
+  if (SPLIT && ns > 1) {  // uniform
+    // every split's pairs (thread j * g + h reads split j's pair of head h,
+    // both words requested at once), then each head merges them in split
+    // order, so every split forms the same values
+    __shared__ float xm[kMaxSplit][16], xl[kMaxSplit][16];
+    const uint64_t* xs = xw + 2;
+    if ((int)tid < ns * g) {
+      const int j = (int)tid / g, hh = (int)tid - j * g;
+      const uint64_t* pw = xs + j * 32 + 2 * hh;
+      const uint64_t v0 = __hip_atomic_load(pw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint64_t v1 = __hip_atomic_load(pw + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      xm[j][hh] = (uint32_t)v0 == xtag ? __builtin_bit_cast(float, (uint32_t)(v0 >> 32)) : xget(pw, xtag, c.status);
+      xl[j][hh] = (uint32_t)v1 == xtag ? __builtin_bit_cast(float, (uint32_t)(v1 >> 32)) : xget(pw + 1, xtag, c.status);
+    }
+    __syncthreads();
+    if ((int)tid < g) {
+      const int hh = tid;
+      float M = -INFINITY;
+      for (int j = 0; j < ns; ++j) M = fmaxf(M, xm[j][hh]);
+      float L = 0.f;
+      for (int j = 0; j < ns; ++j)
+        if (xl[j][hh] > 0.f) L += xl[j][hh] * exp2f(xm[j][hh] - M);
+      Mh[hh] = M;
+      iL[hh] = 1.f / L;
+    }
+    // every split has read the epoch (its pairs carry the tag): the unit's
+    // next launch takes the next one; this launch's words keep this tag
+    if (sj == 0 && tid == 0)
+      __hip_atomic_store(xw, (uint64_t)(((xtag - 1u) >> 1) + 1u), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
 
@@ -800,12 +913,15 @@ void attn_decode_kernel(AttnArgs a) {
     // groups of 4 slots (both regions start 16-aligned; slots past a region
     // hold masked scores and are not written out); all heads' scores of a
     // group are fetched before the exponentials
-    const int q8 = (n8 + 3) >> 2, q16 = (f + 1 + 3) >> 2;
+    // end of this workgroup's INT8 keys; an empty range (a last split with
+    // FP16 tiles only) starts past n8 at the padded tile boundary
+    const int lim8 = min(16 * t8b, n8);
+    const int q8 = max(0, (lim8 - so8 + 3) >> 2), q16 = fp ? (f + 1 + 3) >> 2 : 0;
     for (int gi = tid; gi < q8 + q16; gi += kThreads) {
       const bool r8 = gi < q8;
       const int slot = r8 ? 4 * gi : p16 + 4 * (gi - q8);
-      const int i0 = r8 ? 4 * gi : n8 + 4 * (gi - q8);
-      const int lim = r8 ? n8 : nk;
+      const int i0 = r8 ? so8 + 4 * gi : n8 + 4 * (gi - q8);
+      const int lim = r8 ? lim8 : nk;
       const float u = usc[r8 ? 0 : 1];
       float4_t sum = {0.f, 0.f, 0.f, 0.f};
       for (int h0 = 0; h0 < g; h0 += 4) {  // four heads' scores fetched before their exponentials
@@ -839,15 +955,18 @@ void attn_decode_kernel(AttnArgs a) {
     // all in the spill area, and slots grow with the group index, so the
     // groups in LDS come first: [0, gs) (the spill area is written and read
     // by this workgroup only)
-    const int q8 = (n8 + 3) >> 2, q16 = (f + 1 + 3) >> 2;
+    // end of this workgroup's INT8 keys; an empty range (a last split with
+    // FP16 tiles only) starts past n8 at the padded tile boundary
+    const int lim8 = min(16 * t8b, n8);
+    const int q8 = max(0, (lim8 - so8 + 3) >> 2), q16 = fp ? (f + 1 + 3) >> 2 : 0;
     const int t_lds = n_lds >> 4;  // tiles wholly in LDS
     const int a8 = min(q8, 4 * t_lds);
     const int gs = a8 < q8 ? a8 : q8 + min(q16, max(0, 4 * t_lds - (p16 >> 2)));
     auto group = [&](int gi, const float* src, size_t stride) __attribute__((always_inline)) {
       const bool r8 = gi < q8;
       const int slot = r8 ? 4 * gi : p16 + 4 * (gi - q8);
-      const int i0 = r8 ? 4 * gi : n8 + 4 * (gi - q8);
-      const int lim = r8 ? n8 : nk;
+      const int i0 = r8 ? so8 + 4 * gi : n8 + 4 * (gi - q8);
+      const int lim = r8 ? lim8 : nk;
       const float u = usc[r8 ? 0 : 1];
       float4_t sum = {0.f, 0.f, 0.f, 0.f};
       for (int h0 = 0; h0 < g; h0 += 4) {
@@ -891,15 +1010,37 @@ void attn_decode_kernel(AttnArgs a) {
   }
   __syncthreads();
   uint16_t* ob = a.out + qoff;
-  auto out_at = [&](int idx) {
+  auto out_sum = [&](int idx) {
     const int hh = idx / D, ch = idx - hh * D;
     const int off = hh * RR + (ch / (D / 4)) * RB + ch % (D / 4);
     float o = 0.f;
 #pragma unroll
     for (int q = 0; q < kWaves; ++q) o += red[(size_t)q * g * RR + off];
-    return float_to_half_bits(o);
+    return o;
   };
-  if (ACC && next && g * D <= 4 * kThreads) {  // uniform: held until the next unit's tile loops are done
+  auto out_at = [&](int idx) { return float_to_half_bits(out_sum(idx)); };
+  if (SPLIT && ns > 1) {  // uniform
+    // every split publishes its output partial; split j then adds all
+    // partials of its share of the output elements, in split order, and
+    // writes them (one round trip: a thread's loads go out together)
+    uint64_t* xo = xw + 2 + kMaxSplit * 32;  // [kMaxSplit][g][D]
+    const int gD = g * D;
+    for (int idx = tid; idx < gD; idx += kThreads) xput(xo + (size_t)sj * gD + idx, out_sum(idx), xtag);
+    const int e0 = (int)((int64_t)sj * gD / ns), e1 = (int)((int64_t)(sj + 1) * gD / ns);
+    for (int e = e0 + tid; e < e1; e += kThreads) {
+      uint64_t v[kMaxSplit];
+#pragma unroll
+      for (int j = 0; j < kMaxSplit; ++j)
+        v[j] = j < ns ? __hip_atomic_load(xo + (size_t)j * gD + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
+      float o = 0.f;
+#pragma unroll
+      for (int j = 0; j < kMaxSplit; ++j)
+        if (j < ns)
+          o += (uint32_t)v[j] == xtag ? __builtin_bit_cast(float, (uint32_t)(v[j] >> 32))
+                                      : xget(xo + (size_t)j * gD + e, xtag, c.status);
+      ob[e] = float_to_half_bits(o);
+    }
+  } else if (ACC && next && g * D <= 4 * kThreads) {  // uniform: held until the next unit's tile loops are done
     oh[0] = oh[1] = 0u;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -912,7 +1053,7 @@ void attn_decode_kernel(AttnArgs a) {
   }
   // the row count of the range's (layer, sequence), once its first kv head
   // is done (written last: no store in flight at the next unit's start)
-  if (MASS && tid == 0 && u == u_end - 1 && h_first == 0)
+  if (MASS && tid == 0 && u == u_end - 1 && h_first == 0 && sj == 0)
     meta[CONFK_META_MASSROWS] = ACC ? unit_owner((uint32_t)(lb * H + H - 1), P) - wg + 1 : H;
   if constexpr (ACC) __syncthreads();  // the next unit reuses the LDS
   };
@@ -930,7 +1071,11 @@ void attn_decode_kernel(AttnArgs a) {
     // needs the spill area says nothing of the current length
     const int32_t* mt = c.meta + ((a.layer0 + l) * c.B + b) * CONFK_META_WORDS;
     const int n0 = mt[CONFK_META_N], n80 = mt[CONFK_META_N8];
-    const int64_t slots = (int64_t)((n80 + 15) >> 4) * 16 + (int64_t)((n0 - n80 + 1 + 15) >> 4) * 16;
+    int64_t slots = (int64_t)((n80 + 15) >> 4) * 16 + (int64_t)((n0 - n80 + 1 + 15) >> 4) * 16;
+    if (SPLIT && n80 >= 0 && n80 <= n0 && n0 < c.cap) {  // this split's slots (a bad header fails in the body)
+      const SplitRange sr = split_range(n0, n80, a.split, a.split_tiles, sj);
+      slots = (int64_t)(sr.t8b - sr.t8a) * 16 + (sr.fp ? (int64_t)((n0 - n80 + 1 + 15) >> 4) * 16 : 0);
+    }
     if (slots <= a.n_lds)  // uniform
       unit_body(u_begin, std::false_type{}, std::false_type{});
     else
@@ -941,6 +1086,10 @@ void attn_decode_kernel(AttnArgs a) {
 }
 
 }  // namespace
+
+size_t attention_xchg_bytes(int64_t units, int g, int d) {
+  return units >= 1 ? (size_t)std::min<int64_t>(units, kSplitMaxUnits) * split_words(g, d) * 8 : 0;
+}
 
 int attention_lds_bytes(int d, int g, int n_lds) {
   // scores / output reduction, the query, K and V scales
@@ -1008,11 +1157,52 @@ int resident_per_cu(const void* fn, int lds_bytes) {
 #ifndef CONFK_ACC_TAIL
 #define CONFK_ACC_TAIL 8
 #endif
+// Split keys, for launches whose units fill at most 1/32 of the resident
+// workgroup slots: a unit weighing at least twice split_tiles INT8 tiles
+// (an FP16 tile counts twice) is cut into pieces of at least that weight, at
+// most min(kMaxSplit, 2 * slots / units) of them, and no more than the
+// capacity's largest unit needs. A piece weighs at least kMinSplitTiles
+// tiles (512 keys): the exchange costs two device-wide round trips, which
+// shorter pieces do not repay. Measured on one-layer launches of the
+// 64-layer GQA-5 shape: eight units over 2052 keys ran 1.37x and over 32001
+// keys 10.4x faster split; 64 units over 1028 keys ran no faster in 3
+// pieces, and 64 over 1966 keys slower (49.7 against 39.4 us) in 5, where
+// most of the launch's workgroups find no piece to run and exit.
+#ifndef CONFK_SPLIT_MIN_TILES
+#define CONFK_SPLIT_MIN_TILES 32
+#endif
+constexpr int kMinSplitTiles = CONFK_SPLIT_MIN_TILES;
+constexpr int kSplitTileScale = 160;
+
 template <int D>
 hipError_t launch_d(const AttnArgs& a, int lds_bytes, hipStream_t s) {
   const int64_t units = (int64_t)a.nl * a.c.B * a.c.hkv;
   const int64_t cg = a.conf_groups + a.conf_tail;  // workgroups of the fused confidence work
   const dim3 block(kThreads);
+  if (a.mass && a.xchg && units <= kSplitMaxUnits) {
+    // a launch that leaves resident workgroup slots idle splits its units'
+    // keys over several workgroups each
+    const void* fn = a.spill ? reinterpret_cast<const void*>(&attn_decode_kernel<D, true, true, false, true>)
+                             : reinterpret_cast<const void*>(&attn_decode_kernel<D, false, true, false, true>);
+    const int64_t slots = (int64_t)resident_per_cu(fn, lds_bytes) * device_cus();
+    const int64_t tiles = std::max<int64_t>(kMinSplitTiles, kSplitTileScale * units / std::max<int64_t>(slots, 1));
+    // the weight of the largest unit the capacity allows
+    const int64_t wmax = (a.c.cap + 15) / 16 + 2 * ((a.c.cap16 + 15) / 16);
+    const int64_t S = std::min<int64_t>({kMaxSplit, (2 * slots + units - 1) / units, (wmax + tiles - 1) / tiles});
+    // (a capacity whose largest unit makes fewer than three pieces gains too
+    // little to pay for the workgroups that find no piece once the cache is
+    // short: the 12-unit, 1026-slot launch ran 1 us slower split)
+    if (32 * units <= slots && wmax >= 3 * tiles && S >= 2) {
+      AttnArgs b = a;
+      b.split = (int32_t)S;
+      b.split_tiles = (int32_t)tiles;
+      if (a.spill)
+        hipLaunchKernelGGL((attn_decode_kernel<D, true, true, false, true>), dim3(units * S + cg), block, lds_bytes, s, b);
+      else
+        hipLaunchKernelGGL((attn_decode_kernel<D, false, true, false, true>), dim3(units * S + cg), block, lds_bytes, s, b);
+      return hipGetLastError();
+    }
+  }
   if (!a.mass) {
     hipLaunchKernelGGL((attn_decode_kernel<D, false, false, false>), dim3(units + cg), block, lds_bytes, s, a);
   } else if (a.spill) {

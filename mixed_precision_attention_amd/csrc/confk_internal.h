@@ -74,7 +74,25 @@ struct AttnArgs {
   // two kv heads per workgroup (set by the launcher): workgroups
   // [0, acc_pairs) run two units each, the later ones one each
   int32_t acc_pairs;
+  // Split keys (launches that leave most resident workgroup slots idle):
+  // xchg is the exchange area of the workspace (null: no split), laid out
+  // per unit as split_words() words (see attention.hip); split (set by the
+  // launcher) is the number of workgroups per unit, split_tiles the INT8
+  // tile weight one of them takes at most before a unit is split further.
+  uint64_t* xchg;
+  int32_t split, split_tiles;
 };
+// Split-key launches: at most this many workgroups per unit, and only for
+// launches of at most kSplitMaxUnits units (the workspace holds an exchange
+// area for that many units, whatever the layer count it is sized for, so
+// that a workspace sized for every layer also serves one-layer calls).
+constexpr int kMaxSplit = 16;
+constexpr int64_t kSplitMaxUnits = 64;
+// 64-bit words of the exchange area per unit: the epoch word (and a spare),
+// each split's (max, normaliser) per query head, each split's output partial.
+__host__ __device__ constexpr int64_t split_words(int g, int d) {
+  return 2 + (int64_t)kMaxSplit * 32 + (int64_t)kMaxSplit * g * d;
+}
 enum { kConfNone = 0, kConfMerge = 1, kConfPass = 2 };
 
 struct EmaArgs {
@@ -138,6 +156,9 @@ void confidence_prepare(ConfArgs& a);
 hipError_t launch_confidence_partial(ConfArgs& a, hipStream_t s);
 int attention_lds_bytes(int d, int g, int n_lds);
 int attention_plan_n_lds(int d, int g, int cap, int* spill_stride);
+// Bytes of the split exchange area for a launch of `units` units (0 when
+// such a launch never splits).
+size_t attention_xchg_bytes(int64_t units, int g, int d);
 hipError_t launch_ema_rank(const EmaArgs& a, hipStream_t s);
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
 size_t compact_ws_bytes(int nlayers, int batch, int cap);

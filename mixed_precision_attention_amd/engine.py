@@ -213,8 +213,13 @@ def workspace_bytes(which, cache=None, nlayers=0, batch=0, vocab=0):
 class DecodeEngine:
     """Buffers of one decode step for a workload config, and the step itself."""
 
-    def __init__(self, cfg, device="cuda", overlap=False):
+    def __init__(self, cfg, device="cuda", overlap=False, split_keys=True):
         self.cfg = cfg
+        # split_keys=False sizes the attention workspace without the split
+        # exchange area, so every attention launch runs one workgroup per
+        # (layer, sequence, kv head) (or two kv heads per workgroup) instead
+        # of spreading a unit's keys over several workgroups when the launch
+        # would leave most of the GPU idle.
         # overlap=True: confidence reads only the logits and feeds only the
         # compaction, so step() may run it on a second stream (default
         # priority) beside the attention launch. Off by default: in a model the
@@ -239,7 +244,7 @@ class DecodeEngine:
         self.budget = torch.zeros((nbl, B), dtype=torch.int32, device=device)
         cws = workspace_bytes(L.WS_CONFIDENCE, batch=B, vocab=cfg.vocab)
         self.conf_ws = torch.zeros(max(cws, 4), dtype=torch.uint8, device=device)
-        aws = workspace_bytes(L.WS_ATTENTION, self.cache, nlayers=Lr)
+        aws = workspace_bytes(L.WS_ATTENTION if split_keys else L.WS_ATTENTION_NOSPLIT, self.cache, nlayers=Lr)
         self.attn_ws = torch.zeros(aws, dtype=torch.uint8, device=device) if aws else None
         kws = workspace_bytes(L.WS_COMPACT, self.cache, nlayers=Lr)
         self.compact_ws = torch.zeros(kws, dtype=torch.uint8, device=device)

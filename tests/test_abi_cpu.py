@@ -52,9 +52,20 @@ def test_product_library_does_not_export_the_probe(lib):
 def test_library_exports_every_declared_symbol(lib):
     for n in declared():
         assert hasattr(lib, n), n
-    assert lib.confk_version() == 106
+    assert lib.confk_version() == 107
     assert lib.confk_strerror(-1) == b"invalid argument"
     assert lib.confk_strerror(12345) == b"unknown error"
+
+
+def test_binding_constants_match_header():
+    """Every constant the binding mirrors (status bits, workspace selectors,
+    modes) has the header's value."""
+    import re
+    vals = dict(re.findall(r"#define CONFK_(\w+) (-?\d+)u?\b", open(HEADER).read()))
+    mirrored = [n for n in vals if hasattr(_lib, n)]
+    assert {"STATUS_SPLIT_WAIT", "WS_ATTENTION", "WS_ATTENTION_NOSPLIT", "WS_COMPACT"} <= set(mirrored)
+    for n in mirrored:
+        assert getattr(_lib, n) == int(vals[n]), n
 
 
 def test_struct_layout_matches_header():
@@ -175,13 +186,31 @@ def test_decode_step_validation(lib):
     assert call(cache=_fake_cache(d=96)) == M.ERR_UNSUPPORTED
 
 
-def test_attention_workspace_needed_only_for_long_caches(lib):
-    small = _fake_cache(cap=300)
-    assert lib.confk_workspace_size(M._lib.WS_ATTENTION, ctypes.byref(small), 2, 0, 0) == 0
-    big = _fake_cache(cap=40000, hq=40, hkv=8)
-    need = lib.confk_workspace_size(M._lib.WS_ATTENTION, ctypes.byref(big), 2, 0, 0)
-    assert need > 0
-    assert lib.confk_attn_decode(ctypes.byref(big), 0, 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 4,
+def _split_words(g, d):
+    # per unit: the epoch word and a spare, 16 splits x 16 heads x (max,
+    # normaliser), 16 output partials of g x d values; 8 bytes each
+    return 2 + 16 * 32 + 16 * g * d
+
+
+def test_attention_workspace_sizes(lib):
+    """The attention workspace is the score spill area (caches too long for
+    on-chip memory), then the split exchange area for min(units, 64) (layer,
+    sequence, kv head) units at the next 256-byte boundary."""
+    ws = lambda c, nl, which=M._lib.WS_ATTENTION: lib.confk_workspace_size(which, ctypes.byref(c), nl, 0, 0)  # noqa: E731
+    small = _fake_cache(cap=300)  # 2 x 3 x 2 units, g = 5, d = 128; no spill
+    assert ws(small, 2, M._lib.WS_ATTENTION_NOSPLIT) == 0
+    assert ws(small, 2) == 12 * _split_words(5, 128) * 8
+    big = _fake_cache(cap=40000, hq=40, hkv=8)  # 48 units whose scores spill
+    spill = ws(big, 2, M._lib.WS_ATTENTION_NOSPLIT)
+    assert spill > 0
+    assert ws(big, 2) == (spill + 255) // 256 * 256 + 48 * _split_words(5, 128) * 8
+    many = _fake_cache(layers=64, batch=8, hq=40, hkv=8, cap=2050)  # 4096 units, no spill
+    assert ws(many, 64, M._lib.WS_ATTENTION_NOSPLIT) == 0
+    assert ws(many, 64) == 64 * _split_words(5, 128) * 8
+    wide = _fake_cache(layers=64, batch=2, hq=128, hkv=8, d=64, cap=300)  # g = 16, 1024 units, no spill
+    assert ws(wide, 64, M._lib.WS_ATTENTION_NOSPLIT) == 0
+    assert ws(wide, 64) == 64 * _split_words(16, 64) * 8
+    assert lib.confk_attn_decode(ctypes.byref(big), 0, 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, spill - 4,
                                  None) == M.ERR_WORKSPACE
     assert lib.confk_workspace_size(M._lib.WS_CONFIDENCE, None, 0, 8, 152064) == 8 * 38 * 8 * 4
 

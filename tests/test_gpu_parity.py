@@ -49,6 +49,15 @@ TINY = {
 }
 
 
+def _nosplit_ws(eng, nlayers):
+    """The engine's attention workspace cut to its part without the split
+    exchange area (None when that part is empty), for launches over
+    `nlayers` layers that must run one workgroup per kv head."""
+    import mixed_precision_attention_amd as M
+    nb = M.engine.workspace_bytes(M._lib.WS_ATTENTION_NOSPLIT, eng.cache, nlayers=nlayers)
+    return eng.attn_ws[:nb] if nb else None
+
+
 def _t(x, dev):
     return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
 
@@ -65,12 +74,12 @@ def _inputs(cfg, seed, i):
 class Run:
     """Device engine plus the oracle states of the checked (layer, seq) pairs."""
 
-    def __init__(self, cfg, seed, pairs=None, device_prefill=False):
+    def __init__(self, cfg, seed, pairs=None, device_prefill=False, split_keys=True):
         import mixed_precision_attention_amd as M
         self.dev = _dev()
         self.cfg, self.seed = cfg, seed
         self.pairs = pairs or [(l, b) for l in range(cfg.layers) for b in range(cfg.batch)]
-        self.eng = M.DecodeEngine(cfg, self.dev)
+        self.eng = M.DecodeEngine(cfg, self.dev, split_keys=split_keys)
         self.band = 0
         W = cfg.policy.window
         if cfg.prefill == 0:
@@ -160,12 +169,16 @@ class Run:
         return events
 
 
+@pytest.mark.parametrize("split_keys", [True, False], ids=["split", "nosplit"])
 @pytest.mark.parametrize("name", list(TINY))
-def test_parity_tiny(name):
+def test_parity_tiny(name, split_keys):
+    """The small shapes fill few of the GPU's workgroup slots, so attention
+    splits each unit's keys over several workgroups unless the workspace
+    leaves out the exchange area (nosplit): both forms against the oracle."""
     cfg = TINY[name]
     steps = 70 if cfg.prefill == 0 else 24
-    print(f"[parity] {name} steps={steps}", flush=True)
-    run = Run(cfg, seed=11)
+    print(f"[parity] {name} steps={steps} split_keys={split_keys}", flush=True)
+    run = Run(cfg, seed=11, split_keys=split_keys)
     events = sum(run.step(i) for i in range(steps))
     assert events > 0
     assert run.band <= 1
@@ -200,6 +213,31 @@ def test_parity_gpt2_stack_from_empty():
     assert events > 0
     assert (n8 > 0).all()  # the INT8 region was calibrated and populated
     assert run.band <= 4
+
+
+SPLIT_CASES = {
+    # one unit over 50001 keys: 16 pieces of about 3100 keys, whose scores
+    # spill past the LDS budget; later steps (about 1200 keys) split in 2
+    "g5_d128_spill": _cfg("split_spill", 1, 1, 5, 1, 128, 700, 50000, 600, 1200, 16, 64),
+    # four MHA units (g = 1, d = 64): 5 pieces each at first, ragged INT8 tails
+    "mha_d64": _cfg("split_mha", 1, 1, 4, 4, 64, 700, 2997, 1500, 2500, 8, 32),
+    # sixteen query heads per kv head: the largest output partials
+    "g16_d128": _cfg("split_g16", 1, 2, 16, 1, 128, 700, 2501, 900, 1900, 16, 48),
+}
+
+
+@pytest.mark.parametrize("case", list(SPLIT_CASES))
+def test_parity_split_keys(case):
+    """Launches of a few units split each unit's keys over up to eight
+    workgroups that exchange their softmax maxima and normalisers (and
+    output partials) through the workspace; output, per-key mass and the
+    rest of the step against the oracle, with the status word clear (no
+    split gave up waiting)."""
+    cfg = SPLIT_CASES[case]
+    print(f"[parity] split keys {case}", flush=True)
+    run = Run(cfg, seed=21)
+    for i in range(4):
+        run.step(i)
 
 
 def test_parity_pyramid_budgets():
@@ -741,7 +779,9 @@ def test_two_kv_heads_per_workgroup_mass_rows():
     out_all, mass_all = eng.out.clone(), eng.mass.clone()
     n = eng.cache.lengths()[0]
     for l in (0, 37, cfg.layers - 1):
-        M.engine.attn_decode(eng.cache, q[l:], kn[l:], vn[l:], eng.out[l:], eng.mass[l:], eng.attn_ws,
+        # the workspace without the split exchange area: one workgroup per
+        # kv head, no split keys
+        M.engine.attn_decode(eng.cache, q[l:], kn[l:], vn[l:], eng.out[l:], eng.mass[l:], _nosplit_ws(eng, 1),
                              layer0=l, nlayers=1)
         torch.cuda.synchronize()
         assert (eng.cache.mass_rows()[l] == H).all()
@@ -796,7 +836,9 @@ def test_two_kv_heads_per_workgroup_wide_groups():
     out_all, mass_all = eng.out.clone(), eng.mass.clone()
     n = eng.cache.lengths()[0]
     for l in (0, 11, cfg.layers - 1):
-        M.engine.attn_decode(eng.cache, q[l:], kn[l:], vn[l:], eng.out[l:], eng.mass[l:], eng.attn_ws,
+        # the workspace without the split exchange area: one workgroup per
+        # kv head, no split keys
+        M.engine.attn_decode(eng.cache, q[l:], kn[l:], vn[l:], eng.out[l:], eng.mass[l:], _nosplit_ws(eng, 1),
                              layer0=l, nlayers=1)
         torch.cuda.synchronize()
         assert torch.equal(out_all[l], eng.out[l]), f"l={l}: output"
