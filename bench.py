@@ -59,7 +59,7 @@ def counted_traffic(workload):
     return int(rec["traffic_bytes_per_launch"])
 
 
-def attn_kernel_name(cfg, eng, full):
+def attn_kernel_name(cfg, eng, full, nl=None):
     """Instance of the attention kernel the timed launches ran: spill store
     (the workspace has a spill area), per-key mass (not in the full-cache
     run), the two-kv-heads-per-workgroup mass sum (fewer mass rows than kv
@@ -72,7 +72,8 @@ def attn_kernel_name(cfg, eng, full):
     import mixed_precision_attention_amd as M
     spill = not full and M.engine.workspace_bytes(M._lib.WS_ATTENTION_NOSPLIT, eng.cache, nlayers=cfg.layers) > 0
     acc = not full and bool((eng.cache.mass_rows() < cfg.hkv).any())
-    units = cfg.layers * cfg.batch * cfg.hkv
+    nl = cfg.layers if nl is None else nl  # layers per attention launch
+    units = nl * cfg.batch * cfg.hkv
     slots = 3 * torch.cuda.get_device_properties(0).multi_processor_count
     xchg = eng.attn_ws is not None and M.engine.workspace_bytes(
         M._lib.WS_ATTENTION, eng.cache, nlayers=cfg.layers) > M.engine.workspace_bytes(
@@ -91,6 +92,13 @@ def parse():
                     help="timed steps (default: the workload's generated tokens minus the warmup)")
     ap.add_argument("--warmup", type=int, default=48)
     ap.add_argument("--config", default="qwen32b")
+    ap.add_argument("--no-split-keys", action="store_true",
+                    help="size the attention workspace without the split exchange area, so every "
+                         "attention launch runs one workgroup per unit")
+    ap.add_argument("--per-layer", action="store_true",
+                    help="issue attention as one launch per layer, as a model's forward pass does, instead "
+                         "of one launch over all layers (then the confidence pass and the fused EMA + "
+                         "compaction + window step launch on their own)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU time budget of the oracle baseline sample (0 disables it)")
@@ -219,6 +227,10 @@ def main():
     dev = torch.device("cuda:0")
     cfg = synth.get_config(args.config)
     pol = cfg.policy
+    if args.per_layer and cfg.mode == "full_kv":
+        print(json.dumps({"error": "--per-layer applies to the method's step, not the full-cache run"}), flush=True)
+        sys.exit(2)
+    layerwise = args.per_layer
     Wm = args.warmup
     K = args.steps if args.steps is not None else max(1, cfg.steps - Wm)
     S = K + Wm
@@ -226,7 +238,7 @@ def main():
     # one stream, in a model's order of dependence (the engine can also run the
     # confidence beside the attention on a second stream, which a model whose
     # logits come out of the same step's forward pass could not)
-    eng = M.DecodeEngine(cfg, dev)
+    eng = M.DecodeEngine(cfg, dev, split_keys=not args.no_split_keys)
     kp, vp = synth.gen.prefill_kv_device(cfg, args.seed, dev)
     inputs = []
     for s in range(S):
@@ -271,11 +283,13 @@ def main():
     E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     stream = torch.cuda.current_stream()
 
+    run_step = eng.step_layerwise if layerwise else eng.step
+
     def replay_to_warm():
         eng.prefill(kp, vp)
         for s in range(Wm):
             lg, q, kn, vn, t = inputs[s]
-            eng.step(lg, q, kn, vn, t)
+            run_step(lg, q, kn, vn, t)
         torch.cuda.synchronize()
 
     # ---- timed pass: the K steps back to back, same steps from the same prefill
@@ -284,7 +298,7 @@ def main():
     start.record(stream)
     for i in range(K):
         lg, q, kn, vn, t = inputs[Wm + i]
-        eng.step(lg, q, kn, vn, t)
+        run_step(lg, q, kn, vn, t)
     stop.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
@@ -294,6 +308,7 @@ def main():
     # so this pass is not used for the step rate)
     replay_to_warm()
     ev = [(E(), E(), E(), E()) for _ in range(K)]
+    lev = [[(E(), E()) for _ in range(cfg.layers)] for _ in range(K)] if layerwise else None
     for i in range(K):
         lg, q, kn, vn, t = inputs[Wm + i]
         a0, a1, c0, c1 = ev[i]
@@ -302,6 +317,12 @@ def main():
         a0.record(stream)
         if full:
             M.engine.attn_decode(eng.cache, q, kn, vn, eng.out, None, None)
+        elif layerwise:  # events around each layer's launch
+            for l in range(cfg.layers):
+                lev[i][l][0].record(stream)
+                M.engine.attn_decode(eng.cache, q[l:], kn[l:], vn[l:], eng.out[l:], eng.mass[l:], eng.attn_ws,
+                                     layer0=l, nlayers=1)
+                lev[i][l][1].record(stream)
         else:
             eng.step_attention(q, kn, vn)
         a1.record(stream)
@@ -315,7 +336,10 @@ def main():
         if not full:
             eng.step_quantize(t)
     torch.cuda.synchronize()
-    attn_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    if layerwise:  # the launches' own durations, without the gaps between them
+        attn_ms = [sum(x[0].elapsed_time(x[1]) for x in lev[i]) for i in range(K)]
+    else:
+        attn_ms = [e[0].elapsed_time(e[1]) for e in ev]
     comp_ms = [e[2].elapsed_time(e[3]) for e in ev]
 
     retention = None
@@ -369,6 +393,8 @@ def main():
                         + (", stable survivor order" if getattr(pol, "order", 0) and not pol.block else ""),
             "layers": cfg.layers, "batch": cfg.batch, "hq": cfg.hq, "hkv": cfg.hkv, "d": cfg.d,
             "prefill": cfg.prefill, "vocab": cfg.vocab, "parallelism": "single GPU",
+            "attention_launches": "one per layer" if layerwise else "one over all layers",
+            "split_keys": not args.no_split_keys,
         },
         "steps_per_s": round(1000.0 / ms_per_step, 2),
         "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
@@ -393,8 +419,8 @@ def main():
                                "attention source and workload, not in this run"
                                if counted_traffic(cfg.name) is not None else
                                "none: no counter summary matches this attention source and workload"),
-            "kernel": attn_kernel_name(cfg, eng, full),
-            "bytes_per_launch": int(attn_bytes),
+            "kernel": attn_kernel_name(cfg, eng, full, 1 if layerwise else None),
+            "bytes_per_launch": int(attn_bytes / (cfg.layers if layerwise else 1)),
         },
     }
     if ceiling is not None:

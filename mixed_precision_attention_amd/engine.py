@@ -299,6 +299,24 @@ class DecodeEngine:
     def step_quantize(self, t):
         quantize(self.cache, self.pol, t)
 
+    def step_attention_layerwise(self, q, k_new, v_new):
+        """step_attention as one launch per layer, in layer order, as a
+        model's forward pass issues it. A launch over one layer has few
+        units, so at batch 1 it may split each unit's keys over several
+        workgroups."""
+        for l in range(self.cfg.layers):
+            attn_decode(self.cache, q[l:], k_new[l:], v_new[l:], self.out[l:], self.mass[l:], self.attn_ws,
+                        layer0=l, nlayers=1)
+
+    def step_layerwise(self, logits, q, k_new, v_new, t):
+        """One step with attention issued per layer: the confidence pass, one
+        attention launch per layer, then the EMA, rank scores, compaction and
+        window step as one launch over all layers (the review's Algorithm 1
+        runs the per-layer eviction loop after the forward pass)."""
+        self.step_confidence(logits)
+        self.step_attention_layerwise(q, k_new, v_new)
+        self.step_ema_compact(t, k_new, v_new, fuse_quantize=True)
+
     def step(self, logits, q, k_new, v_new, t):
         if self.cfg.mode == "full_kv":
             # comparison run: attention output only, then the append (the

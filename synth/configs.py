@@ -150,6 +150,14 @@ CONFIGS = {
         policy=Policy(n_high=_PYR_HI[0], n_low=_PYR_LO[0], protect=64, window=256),
         layer_n_low=_PYR_LO, layer_n_high=_PYR_HI,
         plant_depths=(0.1, 0.3, 0.5, 0.7, 0.9), plant_beta=128 ** 0.5, plant_gamma=1.0),
+    # One decode layer of the Qwen-32B shape at batch 1 over a 32000-token
+    # cache whose budgets cover it (nothing is evicted; the cache grows by one
+    # token per step): eight long units, the shape where attention splits
+    # each unit's keys over several workgroups
+    "long32k_layer": Config(
+        name="long32k_layer", layers=1, batch=1, hq=40, hkv=8, d=128, vocab=152064,
+        prefill=32000, steps=64,
+        policy=Policy(n_high=32768, n_low=32768, protect=64, window=256)),
     # Long-context pyramid (CONF-KV-L), Qwen-32B layer shape, batch 1
     "qwen32b_pyramid": Config(
         name="qwen32b_pyramid", layers=64, batch=1, hq=40, hkv=8, d=128, vocab=152064,
