@@ -74,10 +74,11 @@ def _inputs(cfg, seed, i):
 class Run:
     """Device engine plus the oracle states of the checked (layer, seq) pairs."""
 
-    def __init__(self, cfg, seed, pairs=None, device_prefill=False, split_keys=True):
+    def __init__(self, cfg, seed, pairs=None, device_prefill=False, split_keys=True, per_layer=False):
         import mixed_precision_attention_amd as M
         self.dev = _dev()
         self.cfg, self.seed = cfg, seed
+        self.per_layer = per_layer  # attention as one launch per layer
         self.pairs = pairs or [(l, b) for l in range(cfg.layers) for b in range(cfg.batch)]
         self.eng = M.DecodeEngine(cfg, self.dev, split_keys=split_keys)
         self.band = 0
@@ -115,7 +116,10 @@ class Run:
         eng.step_confidence(lg)
         c_dev = eng.c.cpu().numpy().astype(np.float64)
         bud_dev = eng.budget.cpu().numpy()
-        eng.step_attention(qd, kd, vd)
+        if self.per_layer:
+            eng.step_attention_layerwise(qd, kd, vd)
+        else:
+            eng.step_attention(qd, kd, vd)
         out = eng.out.float().cpu().numpy()
         mass = eng.mass.cpu().numpy()
         rows = eng.cache.mass_rows()
@@ -237,6 +241,21 @@ def test_parity_split_keys(case):
     print(f"[parity] split keys {case}", flush=True)
     run = Run(cfg, seed=21)
     for i in range(4):
+        run.step(i)
+
+
+def test_parity_split_keys_per_layer_pyramid():
+    """Attention issued one layer at a time at batch 1 (as a forward pass
+    issues it): each launch has eight units of 1200-2400 keys, which split
+    into 2-4 pieces, with per-layer budgets falling from 2400 to 1200;
+    every layer against the oracle after every step."""
+    lo = (2400, 2000, 1600, 1200)
+    hi = tuple(x // 2 for x in lo)
+    cfg = _cfg("pyr_split", 4, 1, 40, 8, 128, 900, 2600, max(hi), max(lo), 64, 256,
+               layer_n_low=lo, layer_n_high=hi)
+    print("[parity] per-layer split pyramid", flush=True)
+    run = Run(cfg, seed=13, per_layer=True)
+    for i in range(5):
         run.step(i)
 
 
