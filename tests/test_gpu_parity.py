@@ -554,6 +554,23 @@ def test_full_launch_sampled(name):
         run.step(i)
 
 
+@pytest.mark.parametrize("name,steps", [("qwen32b_pyramid", 96), ("qwen14b", 48)])
+def test_long_prefill_workloads_longer_runs(name, steps):
+    """The long-prefill workloads at full size over more decode steps: the
+    batch-1 pyramid (64 layers, per-layer budgets, 32768-token prefill) and
+    the Qwen-14B shape (48 layers x batch 8, 8192-token prefill), three
+    (layer, sequence) pairs followed by the oracle after every step, past
+    the first large eviction into steady one-token steps."""
+    cfg = synth.get_config(name)
+    L, B = cfg.layers, cfg.batch
+    print(f"[parity] {name} full size, {steps} steps", flush=True)
+    run = Run(cfg, seed=4, pairs=[(0, 0), (L // 2, B // 2), (L - 1, B - 1)], device_prefill=True)
+    events = 0
+    for i in range(steps):
+        events += run.step(i)
+    assert events > 0
+
+
 def test_qwen32b_full_size_free_run():
     """The throughput workload at full size (64 layers x batch 8) over its
     first 160 decode steps after the prefill (the window the short benchmark
