@@ -470,19 +470,46 @@ __device__ __forceinline__ void plan_body(const CompactArgs& a) {
         }
       }
     } else {
-      for (int i = threadIdx.x; i < nn; i += kThreads) {
-        float m = 0.f;
-        for (int j = 0; j < H; ++j) m += mass[(size_t)j * cap + i];
-        if (i < n) {
-          const float v = fmaf(lam, ema[i], oml * (m * inv_hq));
-          ema[i] = v;
-          amax = fmaxf(amax, v);
-          const int p = pos[i];
-          pmin = min(pmin, p);
-          pmax = max(pmax, p);
-        } else {
-          ema[n] = oml * (m * inv_hq);
-          pos[n] = a.t;
+      // the same arithmetic over blocks of kRegKeys * kThreads tokens, a
+      // thread's loads of a block issued together
+      for (int base = 0; base < nn; base += kRegKeys * kThreads) {
+        float ms[kRegKeys], bv[kRegKeys];
+        int qv[kRegKeys];
+#pragma unroll
+        for (int r = 0; r < kRegKeys; ++r) {
+          const int i = base + threadIdx.x + r * kThreads;
+          ms[r] = 0.f;
+          bv[r] = i < n ? ema[i] : 0.f;
+          qv[r] = i < n ? pos[i] : 0;
+        }
+        for (int j0 = 0; j0 < H; j0 += 4) {  // four rows per round trip (register budget)
+          float t4[4][kRegKeys];
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int r = 0; r < kRegKeys; ++r) {
+              const int i = base + threadIdx.x + r * kThreads;
+              t4[q][r] = (j0 + q < H && i < nn) ? mass[(size_t)(j0 + q) * cap + i] : 0.f;
+            }
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int r = 0; r < kRegKeys; ++r)
+              if (j0 + q < H) ms[r] += t4[q][r];
+        }
+#pragma unroll
+        for (int r = 0; r < kRegKeys; ++r) {
+          const int i = base + threadIdx.x + r * kThreads;
+          if (i < n) {
+            const float v = fmaf(lam, bv[r], oml * (ms[r] * inv_hq));
+            ema[i] = v;
+            amax = fmaxf(amax, v);
+            pmin = min(pmin, qv[r]);
+            pmax = max(pmax, qv[r]);
+          } else if (i == n) {
+            ema[n] = oml * (ms[r] * inv_hq);
+            pos[n] = a.t;
+          }
         }
       }
     }
@@ -527,12 +554,23 @@ __device__ __forceinline__ void plan_body(const CompactArgs& a) {
           score_w[i] = sreg[r];
         }
       }
-    } else {
-      for (int r = 0; r < cnt; ++r) {
-        const int i = lo + r;
-        if (i < n) {
-          const float rh = p1 > p0 ? (float)(pos[i] - p0) * inv_r : 1.f;
-          score_w[i] = fmaf(alpha, ema[i] * inv_a, (1.f - alpha) * rh);
+    } else {  // lane-strided blocks, each thread's loads of a block together
+      for (int base = 0; base < n; base += kRegKeys * kThreads) {
+        float ev[kRegKeys];
+        int qv[kRegKeys];
+#pragma unroll
+        for (int r = 0; r < kRegKeys; ++r) {
+          const int i = base + threadIdx.x + r * kThreads;
+          ev[r] = i < n ? ema[i] : 0.f;
+          qv[r] = i < n ? pos[i] : 0;
+        }
+#pragma unroll
+        for (int r = 0; r < kRegKeys; ++r) {
+          const int i = base + threadIdx.x + r * kThreads;
+          if (i < n) {
+            const float rh = p1 > p0 ? (float)(qv[r] - p0) * inv_r : 1.f;
+            score_w[i] = fmaf(alpha, ev[r] * inv_a, (1.f - alpha) * rh);
+          }
         }
       }
       __syncthreads();  // scores are read back from memory below

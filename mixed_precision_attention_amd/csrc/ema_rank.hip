@@ -12,6 +12,9 @@
 // For up to kThreads * kPer tokens every thread issues all of its loads at
 // once and keeps the updated EMA and positions in registers for the score
 // pass, so the kernel costs one round trip to memory plus one barrier.
+// Longer caches run the same code over blocks of kThreads * kPer tokens (a
+// thread's loads of a block go out together), twice: the EMA pass, then,
+// once the extremes are known, the score pass.
 #include "confk_internal.h"
 
 namespace confk {
@@ -100,15 +103,42 @@ __global__ __launch_bounds__(kThreads) void ema_rank_kernel(EmaArgs a) {
       }
     }
   } else {
-    for (int i = threadIdx.x; i < n; i += kThreads) {
-      float m = 0.f;
-      for (int j = 0; j < H; ++j) m += mass[(size_t)j * cap + i];
-      const float v = fmaf(lam, ema[i], oml * (m * inv_hq));
-      ema[i] = v;
-      amax = fmaxf(amax, v);
-      const int p = pos[i];
-      pmin = min(pmin, p);
-      pmax = max(pmax, p);
+    for (int base = 0; base < n; base += kThreads * kPer) {
+      float ms[kPer], bv[kPer];
+      int qv[kPer];
+#pragma unroll
+      for (int r = 0; r < kPer; ++r) {
+        const int i = base + threadIdx.x + r * kThreads;
+        ms[r] = 0.f;
+        bv[r] = i < n ? ema[i] : 0.f;
+        qv[r] = i < n ? pos[i] : 0;
+      }
+      for (int j0 = 0; j0 < H; j0 += 8) {  // rows summed in row order, as above
+        float t8[8][kPer];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+#pragma unroll
+          for (int r = 0; r < kPer; ++r) {
+            const int i = base + threadIdx.x + r * kThreads;
+            t8[q][r] = (j0 + q < H && i < n) ? mass[(size_t)(j0 + q) * cap + i] : 0.f;
+          }
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+#pragma unroll
+          for (int r = 0; r < kPer; ++r)
+            if (j0 + q < H) ms[r] += t8[q][r];
+      }
+#pragma unroll
+      for (int r = 0; r < kPer; ++r) {
+        const int i = base + threadIdx.x + r * kThreads;
+        if (i < n) {
+          const float v = fmaf(lam, bv[r], oml * (ms[r] * inv_hq));
+          ema[i] = v;
+          amax = fmaxf(amax, v);
+          pmin = min(pmin, qv[r]);
+          pmax = max(pmax, qv[r]);
+        }
+      }
     }
   }
   if (threadIdx.x == 0) {
@@ -150,10 +180,24 @@ __global__ __launch_bounds__(kThreads) void ema_rank_kernel(EmaArgs a) {
         score[i] = fmaf(alpha, av[r] * inv_a, (1.f - alpha) * rh);
       }
     }
-  } else {
-    for (int i = threadIdx.x; i < n; i += kThreads) {
-      const float rh = p1 > p0 ? (float)(pos[i] - p0) * inv_r : 1.f;
-      score[i] = fmaf(alpha, ema[i] * inv_a, (1.f - alpha) * rh);
+  } else {  // each thread re-reads the EMA it wrote above
+    for (int base = 0; base < n; base += kThreads * kPer) {
+      float ev[kPer];
+      int qv[kPer];
+#pragma unroll
+      for (int r = 0; r < kPer; ++r) {
+        const int i = base + threadIdx.x + r * kThreads;
+        ev[r] = i < n ? ema[i] : 0.f;
+        qv[r] = i < n ? pos[i] : 0;
+      }
+#pragma unroll
+      for (int r = 0; r < kPer; ++r) {
+        const int i = base + threadIdx.x + r * kThreads;
+        if (i < n) {
+          const float rh = p1 > p0 ? (float)(qv[r] - p0) * inv_r : 1.f;
+          score[i] = fmaf(alpha, ev[r] * inv_a, (1.f - alpha) * rh);
+        }
+      }
     }
   }
 }
