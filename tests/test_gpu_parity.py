@@ -259,6 +259,48 @@ def test_parity_split_keys_per_layer_pyramid():
         run.step(i)
 
 
+def test_split_keys_graph_replay():
+    """A split-key attention launch captured in a HIP graph and replayed
+    several times, with the program's own eager launches (unsplit) and
+    synchronisations between the replays: every replay gives the eager
+    launch's output and mass bit for bit (the exchange words carry a
+    per-unit epoch that each launch advances, so a replay never reads a
+    word of an earlier one; no memory-set node is recorded)."""
+    import mixed_precision_attention_amd as M
+    dev = _dev()
+    cfg = SPLIT_CASES["mha_d64"]
+    eng = M.DecodeEngine(cfg, dev)
+    kp, vp = synth.prefill_kv(cfg, 21)
+    eng.prefill(_t(kp, dev), _t(vp, dev))
+    _, q, kn, vn, _ = _inputs(cfg, 21, 0)
+    qd, kd, vd = _t(q, dev), _t(kn, dev), _t(vn, dev)
+    print("[parity] split keys under graph replay", flush=True)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up off the capture (the library's device queries)
+        for _ in range(2):
+            M.engine.attn_decode(eng.cache, qd, kd, vd, eng.out, eng.mass, eng.attn_ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    out0, mass0 = eng.out.clone(), eng.mass.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        M.engine.attn_decode(eng.cache, qd, kd, vd, eng.out, eng.mass, eng.attn_ws)
+    nospl = _nosplit_ws(eng, cfg.layers)
+    for rep in range(4):
+        eng.out.zero_()
+        eng.mass.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(eng.out, out0), f"replay {rep}: output"
+        assert torch.equal(eng.mass, mass0), f"replay {rep}: mass"
+        assert int(eng.cache.status.cpu()[0]) == 0, f"replay {rep}: status"
+        # eager work between replays: an unsplit launch over the same cache
+        M.engine.attn_decode(eng.cache, qd, kd, vd, eng.out, eng.mass, nospl)
+        torch.cuda.synchronize()
+        assert rel_maxabs(eng.out.float().cpu().numpy(), out0.float().cpu().numpy()) <= OTOL / 2
+
+
 def test_parity_pyramid_budgets():
     lo = (60, 52, 44)
     hi = tuple(x // 2 for x in lo)
