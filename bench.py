@@ -95,6 +95,9 @@ def parse():
     ap.add_argument("--no-split-keys", action="store_true",
                     help="size the attention workspace without the split exchange area, so every "
                          "attention launch runs one workgroup per unit")
+    ap.add_argument("--graph", action="store_true",
+                    help="with --per-layer: replay the step's one-layer attention launches as one HIP graph "
+                         "(each step's q, k_new, v_new copied into the graph's buffers first)")
     ap.add_argument("--per-layer", action="store_true",
                     help="issue attention as one launch per layer, as a model's forward pass does, instead "
                          "of one launch over all layers (then the confidence pass and the fused EMA + "
@@ -284,6 +287,17 @@ def main():
     stream = torch.cuda.current_stream()
 
     run_step = eng.step_layerwise if layerwise else eng.step
+    graph = None
+    if layerwise and args.graph:
+        qb, kb, vb = (x.clone() for x in inputs[0][1:4])
+
+        def run_step(lg, q, kn, vn, t):  # noqa: F811  (the graph-replay form of step_layerwise)
+            eng.step_confidence(lg)
+            qb.copy_(q)
+            kb.copy_(kn)
+            vb.copy_(vn)
+            graph.replay()
+            eng.step_ema_compact(t, kn, vn, fuse_quantize=True)
 
     def replay_to_warm():
         eng.prefill(kp, vp)
@@ -293,6 +307,11 @@ def main():
         torch.cuda.synchronize()
 
     # ---- timed pass: the K steps back to back, same steps from the same prefill
+    if layerwise and args.graph:  # captured after one eager step (the library's device queries)
+        eng.prefill(kp, vp)
+        eng.step_layerwise(*inputs[0])
+        torch.cuda.synchronize()
+        graph = eng.capture_attention_layerwise(qb, kb, vb)
     replay_to_warm()
     start, stop = E(), E()
     start.record(stream)
@@ -393,7 +412,8 @@ def main():
                         + (", stable survivor order" if getattr(pol, "order", 0) and not pol.block else ""),
             "layers": cfg.layers, "batch": cfg.batch, "hq": cfg.hq, "hkv": cfg.hkv, "d": cfg.d,
             "prefill": cfg.prefill, "vocab": cfg.vocab, "parallelism": "single GPU",
-            "attention_launches": "one per layer" if layerwise else "one over all layers",
+            "attention_launches": ("one per layer" + (", replayed as one HIP graph" if args.graph else "")
+                                   if layerwise else "one over all layers"),
             "split_keys": not args.no_split_keys,
         },
         "steps_per_s": round(1000.0 / ms_per_step, 2),

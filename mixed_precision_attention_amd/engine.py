@@ -308,6 +308,19 @@ class DecodeEngine:
             attn_decode(self.cache, q[l:], k_new[l:], v_new[l:], self.out[l:], self.mass[l:], self.attn_ws,
                         layer0=l, nlayers=1)
 
+    def capture_attention_layerwise(self, q, k_new, v_new):
+        """A HIP graph of step_attention_layerwise over the buffers q, k_new
+        and v_new (the caller copies each step's inputs into them before a
+        replay): 64 one-layer launches cost one graph launch from the host.
+        The launches record no memory-set node, and split keys keep their
+        exchange words valid across replays (a per-unit epoch in device
+        memory). Call after a warm-up step, which makes the library's
+        one-time device queries outside the capture."""
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.step_attention_layerwise(q, k_new, v_new)
+        return graph
+
     def step_layerwise(self, logits, q, k_new, v_new, t):
         """One step with attention issued per layer: the confidence pass, one
         attention launch per layer, then the EMA, rank scores, compaction and
