@@ -1164,10 +1164,12 @@ int resident_per_cu(const void* fn, int lds_bytes) {
 // capacity's largest unit needs. A piece weighs at least kMinSplitTiles
 // tiles (512 keys): the exchange costs two device-wide round trips, which
 // shorter pieces do not repay. Measured on one-layer launches of the
-// 64-layer GQA-5 shape: eight units over 2052 keys ran 1.37x and over 32001
-// keys 10.4x faster split; 64 units over 1028 keys ran no faster in 3
-// pieces, and 64 over 1966 keys slower (49.7 against 39.4 us) in 5, where
-// most of the launch's workgroups find no piece to run and exit.
+// 64-layer GQA-5 shape, back to back: eight units over 32001 keys took 37
+// against 460 us (unsplit, those units take the score-spill form, whose
+// stores in the tile loop serialise the loads); eight units over 500-2000
+// keys take about 16.5 us split or not (latency-bound); 64 units over 1966
+// keys ran slower in 5 pieces (49.7 against 39.4 us), where most of the
+// launch's workgroups find no piece to run and exit.
 #ifndef CONFK_SPLIT_MIN_TILES
 #define CONFK_SPLIT_MIN_TILES 32
 #endif
