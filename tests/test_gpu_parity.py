@@ -945,7 +945,8 @@ def test_fused_confidence_attention_matches_split(choice):
     layers and at a small shape with a ragged vocabulary."""
     import mixed_precision_attention_amd as M
     dev = _dev()
-    for cfg in (synth.get_config("qwen32b").with_(layers=2), TINY["g5_d128"]):
+    # (the last shape's launches split keys: the merge workgroups lead the split units)
+    for cfg in (synth.get_config("qwen32b").with_(layers=2), TINY["g5_d128"], SPLIT_CASES["g16_d128"]):
         engs = [M.DecodeEngine(cfg, dev), M.DecodeEngine(cfg, dev)]
         kp, vp = synth.prefill_kv(cfg, 6)
         for e in engs:
@@ -976,13 +977,15 @@ def test_decode_step_matches_split(choice):
     another, bit for bit over several steps: the whole cache, c, budgets, the
     next token, output, mass and scores. Shapes: the Qwen-32B shape with two
     layers, a small ragged one from an empty cache (the window step
-    calibrates), and per-layer (pyramid) budgets."""
+    calibrates), per-layer (pyramid) budgets, and a launch that splits keys
+    (the confidence pass's workgroups follow the split units)."""
     import mixed_precision_attention_amd as M
     dev = _dev()
     lo = (60, 52, 44)
     cases = (synth.get_config("qwen32b").with_(layers=2), TINY["g3_d64_empty"],
              _cfg("pyr", 3, 2, 10, 2, 128, 600, 120, max(lo) // 2, max(lo), 8, 24,
-                  layer_n_low=lo, layer_n_high=tuple(x // 2 for x in lo)))
+                  layer_n_low=lo, layer_n_high=tuple(x // 2 for x in lo)),
+             SPLIT_CASES["mha_d64"])
     for cfg in cases:
         engs = [M.DecodeEngine(cfg, dev), M.DecodeEngine(cfg, dev)]
         if cfg.prefill:
